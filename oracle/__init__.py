@@ -1,0 +1,264 @@
+"""CPU oracle for the DeepSeek Sparse Attention (DSA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+the CPU-baseline leg of the benchmark may import this module; the product
+path (the HIP library and its Python binding) never does, and this module
+never imports the product path.  The two share no code: the only thing both
+sides consume is the seeded input generator in ``synth/``.
+
+Plain numpy in float64, written from the method's definition so that a
+reader can check it against the pages by eye:
+
+  DeepSeek-V3.2 model documentation, section "DeepSeek Sparse Attention
+  (DSA)":
+    * the lightning indexer: a light scorer with few heads computes an index
+      score between every query and all keys before it (the paragraph on the
+      lightning indexer); the scores are the same whether computed in FP8
+      after an orthogonal Hadamard rotation or directly in bf16/fp32;
+    * the indexer keeps its own per-token key cache with a single head of
+      width index_head_dim (the paragraph on the indexer cache);
+    * fine-grained token selection: each query keeps the index_topk most
+      relevant tokens and the main MLA attention runs over those tokens only,
+      through an additive mask (the paragraph on token selection);
+    * every layer runs its own indexer.
+  DeepSeek-V3.2 model documentation, section "DeepseekV32Config": the shape
+  defaults index_n_heads = 64, index_head_dim = 128, index_topk = 2048,
+  kv_lora_rank = 512, qk_rope_head_dim = 64, qk_nope_head_dim = 128,
+  num_attention_heads = 128.
+  DeepSeek-V4 model documentation, section on the attention mask layout: an
+  indexer entry of -1 means "no selection" and reaches the mask unchanged.
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes of the repository):
+  * score formula  I[t,s] = sum_h w[t,h] * ReLU(sum_d qI[t,h,d] * kI[s,d]),
+    no extra scale (any scale is part of w);
+  * "keys before the query" includes the query's own position: query t at
+    absolute position p = q_pos0 + t sees keys s <= p (and s < N);
+  * top-k ties go to the lower key index; the selection is emitted in
+    ascending key order, then padded with -1 when fewer than K keys exist;
+  * the MLA runs in absorbed latent form: each head's D-wide query meets one
+    D-wide latent row shared by all heads; the value is the row's first DV
+    entries; logits are scale * q.kv; negative indices are masked (additive
+    -inf); a row with no valid index gives o = 0 and lse = -inf;
+  * lse is the natural-log sum of exp(logits).
+
+Every function works on float64 copies of its inputs.  bf16 inputs arrive as
+uint16 bit patterns and are widened exactly by ``as_f64``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "as_f64", "bf16_bits_to_f64", "n_valid_keys", "index_scores", "index_scores_rows",
+    "topk_row", "topk", "sparse_mla", "sparse_mla_rows", "dense_masked_mla", "forward_rows",
+    "sylvester_hadamard",
+]
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64: a bf16 is the top half of an fp32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def as_f64(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    return np.asarray(x, dtype=np.float64)
+
+
+def n_valid_keys(t: int, q_pos0: int, N: int) -> int:
+    """Number of keys query t may see: positions 0..q_pos0+t, capped by the cache length."""
+    return max(0, min(N, q_pos0 + t + 1))
+
+
+# ----------------------------------------------------------------------------
+# Lightning indexer
+# ----------------------------------------------------------------------------
+
+def index_scores_rows(q_idx_b: np.ndarray, k_idx_b: np.ndarray, w_b: np.ndarray,
+                      ts, q_pos0: int) -> list:
+    """Index scores of queries `ts` of one sequence against their visible keys.
+
+    q_idx_b [Tq, H_I, D_I], k_idx_b [N, D_I], w_b [Tq, H_I] (any storage dtype).
+    Returns one float64 vector per query t, of length n_valid_keys(t):
+        I[s] = sum_h w[t,h] * max(0, sum_d qI[t,h,d] * kI[s,d]).
+    """
+    kI = as_f64(k_idx_b)
+    N = kI.shape[0]
+    out = []
+    for t in ts:
+        n = n_valid_keys(int(t), q_pos0, N)
+        qI = as_f64(q_idx_b[t])            # [H_I, D_I]
+        w = as_f64(w_b[t])                 # [H_I]
+        dots = kI[:n] @ qI.T               # [n, H_I]: per-head dot product q_h . k_s
+        out.append(np.maximum(dots, 0.0) @ w)
+    return out
+
+
+def index_scores(q_idx: np.ndarray, k_idx: np.ndarray, w: np.ndarray, q_pos0: int) -> np.ndarray:
+    """Full score tensor [B, Tq, N] (float64); entries a query may not see are NaN."""
+    B, Tq = q_idx.shape[:2]
+    N = k_idx.shape[1]
+    out = np.full((B, Tq, N), np.nan)
+    for b in range(B):
+        rows = index_scores_rows(q_idx[b], k_idx[b], w[b], range(Tq), q_pos0)
+        for t, r in enumerate(rows):
+            out[b, t, :len(r)] = r
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Top-k selection
+# ----------------------------------------------------------------------------
+
+def topk_row(scores: np.ndarray, K: int) -> np.ndarray:
+    """Keep the K highest-scoring of the n = len(scores) visible keys.
+
+    The decision is taken on float32 scores (the precision the GPU path stores
+    them in).  Order: score descending, then key index ascending, so equal
+    scores go to the lower index.  The kept indices are returned in ascending
+    order; if n <= K every key is kept and the row is padded with -1.
+    """
+    v = np.asarray(scores, dtype=np.float32)
+    n = v.shape[0]
+    out = np.full(K, -1, dtype=np.int32)
+    if n <= K:
+        out[:n] = np.arange(n, dtype=np.int32)
+        return out
+    keys = np.arange(n)
+    # np.lexsort sorts by the last key first: primary -v (i.e. v descending), secondary index
+    order = np.lexsort((keys, -v.astype(np.float64)))
+    out[:] = np.sort(order[:K]).astype(np.int32)
+    return out
+
+
+def topk(scores: np.ndarray, K: int, q_pos0: int) -> np.ndarray:
+    """scores [B, Tq, N] -> idx [B, Tq, K] int32 (row t uses its visible keys only)."""
+    B, Tq, N = scores.shape
+    out = np.empty((B, Tq, K), dtype=np.int32)
+    for b in range(B):
+        for t in range(Tq):
+            n = n_valid_keys(t, q_pos0, N)
+            out[b, t] = topk_row(scores[b, t, :n], K)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Sparse MLA (absorbed latent form)
+# ----------------------------------------------------------------------------
+
+def _softmax_attend(logits: np.ndarray, values: np.ndarray):
+    """Softmax over the last axis of logits [H, n] then weight values [n, DV].
+
+    Returns (o [H, DV], lse [H]).  n == 0 gives o = 0 and lse = -inf.
+    """
+    H = logits.shape[0]
+    if logits.shape[1] == 0:
+        return np.zeros((H, values.shape[1])), np.full(H, -np.inf)
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ values) / l
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def sparse_mla_rows(q_bt: np.ndarray, kv_rows: np.ndarray, idx_row: np.ndarray, scale: float, DV: int):
+    """One query: q_bt [H, D]; kv_rows maps a key index to its D-wide latent row.
+
+    kv_rows is either the whole cache [N, D] or a dict {index: row}.  Entries of
+    idx_row below zero are masked out.  Returns (o [H, DV], lse [H]) in float64.
+    """
+    sel = [int(i) for i in np.asarray(idx_row).reshape(-1) if int(i) >= 0]
+    if isinstance(kv_rows, dict):
+        rows = np.stack([as_f64(kv_rows[i]) for i in sel]) if sel else np.zeros((0, q_bt.shape[-1]))
+    else:
+        rows = as_f64(kv_rows[sel]) if sel else np.zeros((0, q_bt.shape[-1]))
+    q = as_f64(q_bt)
+    logits = scale * (q @ rows.T)             # [H, n]
+    return _softmax_attend(logits, rows[:, :DV])
+
+
+def sparse_mla(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, scale: float, DV: int):
+    """q [B,Tq,H,D], kv [B,N,D], idx [B,Tq,K] -> (o [B,Tq,H,DV], lse [B,Tq,H]) float64."""
+    B, Tq, H, _ = q.shape
+    o = np.empty((B, Tq, H, DV))
+    lse = np.empty((B, Tq, H))
+    for b in range(B):
+        kvb = as_f64(kv[b])
+        for t in range(Tq):
+            o[b, t], lse[b, t] = sparse_mla_rows(q[b, t], kvb, idx[b, t], scale, DV)
+    return o, lse
+
+
+def dense_masked_mla(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, scale: float, DV: int,
+                     q_pos0: int):
+    """The same attention written as dense causal attention plus an additive mask.
+
+    For query t, every visible key s (s <= q_pos0 + t, s < N) gets the logit
+    scale * q.kv[s] plus a mask term that is 0 when s is among the selected
+    indices and -inf otherwise; the softmax then runs over all visible keys.
+    """
+    B, Tq, H, _ = q.shape
+    N = kv.shape[1]
+    o = np.empty((B, Tq, H, DV))
+    lse = np.empty((B, Tq, H))
+    for b in range(B):
+        kvb = as_f64(kv[b])
+        for t in range(Tq):
+            n = n_valid_keys(t, q_pos0, N)
+            mask = np.full(n, -np.inf)
+            for i in np.asarray(idx[b, t]).reshape(-1):
+                if 0 <= int(i) < n:
+                    mask[int(i)] = 0.0
+            logits = scale * (as_f64(q[b, t]) @ kvb[:n].T) + mask[None, :]
+            keep = np.isfinite(mask)
+            if not keep.any():
+                o[b, t], lse[b, t] = 0.0, -np.inf
+                continue
+            m = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - m)                # exp(-inf) = 0 for masked keys
+            l = p.sum(axis=1, keepdims=True)
+            o[b, t] = (p @ kvb[:n, :DV]) / l
+            lse[b, t] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Composition: indexer -> top-k -> sparse MLA, for chosen query rows
+# ----------------------------------------------------------------------------
+
+def forward_rows(q_idx_b, k_idx_b, w_b, q_b, kv_b, ts, q_pos0: int, K: int, scale: float, DV: int):
+    """The three steps for queries `ts` of one sequence.
+
+    kv_b is the latent cache [N, D] of the sequence, or a callable that maps an
+    array of row indices to those rows (for caches too large to widen whole).
+    Returns a list of dicts with the query's float64 scores, its int32
+    indices, and its (o, lse).
+    """
+    res = []
+    scores = index_scores_rows(q_idx_b, k_idx_b, w_b, ts, q_pos0)
+    for t, s in zip(ts, scores):
+        idx = topk_row(s.astype(np.float32), K)
+        sel = idx[idx >= 0]
+        if callable(kv_b):
+            rows = {int(i): r for i, r in zip(sel, kv_b(sel))}
+        else:
+            rows = kv_b
+        o, lse = sparse_mla_rows(q_b[t], rows, idx, scale, DV)
+        res.append({"t": int(t), "scores": s, "idx": idx, "o": o, "lse": lse})
+    return res
+
+
+# ----------------------------------------------------------------------------
+# Test helper: the Sylvester Hadamard matrix (textbook construction)
+# ----------------------------------------------------------------------------
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]]; H H^T = n I (n a power of two)."""
+    assert n >= 1 and (n & (n - 1)) == 0
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h

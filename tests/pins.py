@@ -1,0 +1,282 @@
+"""Pins for the CPU oracle: facts fixed by the pages or by mathematics.
+
+Each check takes the oracle function it exercises as an argument and returns
+True when the fact holds, so the same checks can be run on the real oracle
+(they must all hold) and on deliberately broken copies of it (at least one
+must fail), which shows that a plausible mistake cannot slip through.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- indexer ---
+
+def pin_indexer_golden(index_scores_rows) -> bool:
+    """Hand-derived 3-query example (derivation stored with the fixture)."""
+    g = load_golden("indexer_topk_tiny.json")
+    q = np.array(g["q_idx"], dtype=np.float64)
+    k = np.array(g["k_idx"], dtype=np.float64)
+    w = np.array(g["w"], dtype=np.float64)
+    rows = index_scores_rows(q, k, w, range(q.shape[0]), g["q_pos0"])
+    return all(len(r) == len(e) and np.array_equal(r, np.array(e, dtype=np.float64))
+               for r, e in zip(rows, g["scores"]))
+
+
+def pin_indexer_hadamard(index_scores_rows, hadamard) -> bool:
+    """Hq.Hk = n q.k for the unnormalised Sylvester matrix (H H^T = n I); ReLU is
+    positively homogeneous, so rotated scores are exactly n times the plain ones."""
+    r = _rng(11)
+    T, HI, DI = 9, 4, 32
+    q = r.integers(-3, 4, size=(T, HI, DI)).astype(np.float64)
+    k = r.integers(-3, 4, size=(T, DI)).astype(np.float64)
+    w = r.choice([0.25, 0.5, 1.0, 2.0], size=(T, HI))
+    h = hadamard(DI)
+    if not np.array_equal(h @ h.T, DI * np.eye(DI)):
+        return False
+    a = index_scores_rows(q, k, w, range(T), 0)
+    b = index_scores_rows(q @ h.T, k @ h.T, w, range(T), 0)
+    return all(np.array_equal(DI * x, y) for x, y in zip(a, b))
+
+
+def pin_indexer_unit_queries(index_scores_rows) -> bool:
+    """Each head's query is a signed unit vector c_h * e_{i_h}: its dot product
+    with key s is c_h * k[s, i_h], read off by indexing."""
+    r = _rng(12)
+    T, HI, DI, N = 6, 5, 8, 6
+    k = r.integers(-4, 5, size=(N, DI)).astype(np.float64)
+    w = r.choice([-1.0, 0.5, 2.0], size=(T, HI))
+    pos = r.integers(0, DI, size=(T, HI))
+    sgn = r.choice([-1.0, 1.0, 3.0], size=(T, HI))
+    q = np.zeros((T, HI, DI))
+    for t in range(T):
+        for h in range(HI):
+            q[t, h, pos[t, h]] = sgn[t, h]
+    got = index_scores_rows(q, k, w, range(T), 0)
+    for t in range(T):
+        exp = np.zeros(t + 1)
+        for s in range(t + 1):
+            for h in range(HI):
+                exp[s] += w[t, h] * max(0.0, sgn[t, h] * k[s, pos[t, h]])
+        if not np.array_equal(got[t], exp):
+            return False
+    return True
+
+
+def pin_indexer_causal(index_scores_rows) -> bool:
+    """Query t at position q_pos0+t sees keys 0..q_pos0+t only (own key included):
+    row lengths are fixed, and keys after the query cannot change its row."""
+    r = _rng(13)
+    T, HI, DI, N, p0 = 7, 3, 4, 12, 3
+    q = r.integers(-3, 4, size=(T, HI, DI)).astype(np.float64)
+    k = r.integers(-3, 4, size=(N, DI)).astype(np.float64)
+    w = np.ones((T, HI))
+    a = index_scores_rows(q, k, w, range(T), p0)
+    if [len(x) for x in a] != [min(N, p0 + t + 1) for t in range(T)]:
+        return False
+    for t in range(T):
+        k2 = k.copy()
+        k2[p0 + t + 1:] = r.integers(-3, 4, size=k2[p0 + t + 1:].shape)
+        if not np.array_equal(index_scores_rows(q, k2, w, [t], p0)[0], a[t]):
+            return False
+        # the own key does matter: flip it to a key that surely scores differently
+        k3 = k.copy()
+        k3[p0 + t] = q[t, 0] * 7.0 + 1.0
+        if np.array_equal(index_scores_rows(q, k3, w, [t], p0)[0], a[t]):
+            return False
+    return True
+
+
+def pin_indexer_heads(index_scores_rows) -> bool:
+    """Heads are summed with their own weights: permuting heads together with
+    their weights changes nothing, and the score is linear in the weights."""
+    r = _rng(14)
+    T, HI, DI = 5, 6, 8
+    q = r.integers(-3, 4, size=(T, HI, DI)).astype(np.float64)
+    k = r.integers(-3, 4, size=(T, DI)).astype(np.float64)
+    w1 = r.choice([0.25, 0.5, 1.0, 2.0, -1.0], size=(T, HI))
+    w2 = r.choice([0.25, 0.5, 1.0, 2.0], size=(T, HI))
+    perm = r.permutation(HI)
+    a = index_scores_rows(q, k, w1, range(T), 0)
+    b = index_scores_rows(q[:, perm], k, w1[:, perm], range(T), 0)
+    c = index_scores_rows(q, k, w2, range(T), 0)
+    d = index_scores_rows(q, k, w1 + w2, range(T), 0)
+    # a single head with weight one is ReLU of the dot product: all-negative dots give 0
+    e = index_scores_rows(-np.abs(q[:, :1]) - 1, np.abs(k) , np.ones((T, 1)), range(T), 0)
+    return (all(np.array_equal(x, y) for x, y in zip(a, b))
+            and all(np.array_equal(x + y, z) for x, y, z in zip(a, c, d))
+            and all(not np.any(x) for x in e))
+
+
+# ------------------------------------------------------------------ top-k ---
+
+def rank_count_topk(v, K):
+    """Independent definition: key s is kept iff fewer than K keys precede it in
+    the order (score desc, index asc); the result is listed in ascending order."""
+    v = np.asarray(v, dtype=np.float32)
+    n = len(v)
+    keep = []
+    for s in range(n):
+        rank = sum(1 for s2 in range(n) if v[s2] > v[s] or (v[s2] == v[s] and s2 < s))
+        if rank < K:
+            keep.append(s)
+    out = np.full(K, -1, dtype=np.int32)
+    out[:len(keep)] = keep
+    return out
+
+
+def pin_topk_golden(topk_row) -> bool:
+    g = load_golden("topk_ties.json")
+    for c in g["cases"]:
+        v = np.array([float(x) for x in c["scores"]], dtype=np.float32)
+        if not np.array_equal(topk_row(v, c["K"]), np.array(c["idx"], dtype=np.int32)):
+            return False
+    g2 = load_golden("indexer_topk_tiny.json")
+    for s, e in zip(g2["scores"], g2["idx"]):
+        if not np.array_equal(topk_row(np.array(s, dtype=np.float32), g2["K"]), np.array(e)):
+            return False
+    return True
+
+
+def pin_topk_bruteforce(topk_row) -> bool:
+    """Agreement with the rank-count definition on many tiny rows with heavy ties."""
+    r = _rng(21)
+    for trial in range(300):
+        n = int(r.integers(1, 40))
+        K = int(r.integers(1, 45))
+        if trial % 3 == 0:
+            v = r.integers(0, 3, size=n).astype(np.float32)
+        elif trial % 3 == 1:
+            v = r.choice(np.array([-0.0, 0.0, -1.5, 2.0], dtype=np.float32), size=n)
+        else:
+            v = r.standard_normal(n).astype(np.float32)
+        if not np.array_equal(topk_row(v, K), rank_count_topk(v, K)):
+            return False
+    return True
+
+
+def pin_topk_short_rows(topk_row) -> bool:
+    """A row with n <= K visible keys is exactly [0, 1, ..., n-1, -1, ...]."""
+    r = _rng(22)
+    for n in range(0, 20):
+        K = 20
+        got = topk_row(r.standard_normal(n).astype(np.float32), K)
+        exp = np.array(list(range(n)) + [-1] * (K - n), dtype=np.int32)
+        if not np.array_equal(got, exp):
+            return False
+    return True
+
+
+# ------------------------------------------------------------- sparse MLA ---
+
+def pin_mla_golden(sparse_mla_rows) -> bool:
+    g = load_golden("sparse_mla_tiny.json")
+    o, lse = sparse_mla_rows(np.array(g["q"]), np.array(g["kv"]), np.array(g["idx"]),
+                             g["scale"], g["DV"])
+    return (np.allclose(o, np.array(g["o"]), rtol=0, atol=1e-12)
+            and np.allclose(lse, np.array(g["lse"]), rtol=0, atol=1e-12))
+
+
+def pin_mla_single_key(sparse_mla_rows) -> bool:
+    """One valid index: the output is that row's value part exactly, and the
+    log-sum-exp is the single logit scale*q.kv."""
+    r = _rng(31)
+    H, D, DV, N = 3, 10, 6, 9
+    q = r.standard_normal((H, D))
+    kv = r.standard_normal((N, D))
+    for j in range(N):
+        idx = np.array([-1, j, -1, -1])
+        o, lse = sparse_mla_rows(q, kv, idx, 0.3, DV)
+        if not (np.array_equal(o, np.broadcast_to(kv[j, :DV], (H, DV)))
+                and np.allclose(lse, 0.3 * (q @ kv[j]), rtol=1e-15, atol=1e-15)):
+            return False
+    return True
+
+
+def pin_mla_uniform(sparse_mla_rows) -> bool:
+    """q = 0 makes every logit 0: the output is the mean of the selected value rows
+    and lse = ln(number selected)."""
+    r = _rng(32)
+    H, D, DV, N = 2, 7, 4, 20
+    kv = r.standard_normal((N, D))
+    idx = np.array([3, 17, -1, 5, 0, 11])
+    sel = idx[idx >= 0]
+    o, lse = sparse_mla_rows(np.zeros((H, D)), kv, idx, 1.7, DV)
+    return (np.allclose(o, np.broadcast_to(kv[sel, :DV].mean(axis=0), (H, DV)), atol=1e-14)
+            and np.allclose(lse, math.log(len(sel)), atol=1e-14))
+
+
+def pin_mla_permutation_and_mask(sparse_mla_rows) -> bool:
+    """The selection is a set: shuffling it or sprinkling -1 entries into it leaves
+    the output unchanged up to rounding; an all-masked row gives o = 0, lse = -inf."""
+    r = _rng(33)
+    H, D, DV, N = 4, 12, 8, 50
+    q = r.standard_normal((H, D))
+    kv = r.standard_normal((N, D))
+    idx = r.choice(N, size=10, replace=False)
+    o1, l1 = sparse_mla_rows(q, kv, idx, 0.4, DV)
+    idx2 = np.concatenate([r.permutation(idx), [-1, -1, -7]])
+    idx2 = idx2[r.permutation(len(idx2))]
+    o2, l2 = sparse_mla_rows(q, kv, idx2, 0.4, DV)
+    o3, l3 = sparse_mla_rows(q, kv, np.array([-1, -1]), 0.4, DV)
+    return (np.allclose(o1, o2, atol=1e-13) and np.allclose(l1, l2, atol=1e-13)
+            and not np.any(o3) and np.all(np.isneginf(l3)))
+
+
+def pin_mla_sdpa(sparse_mla, dense_masked_mla) -> bool:
+    """With every visible key selected (K >= L), sparse attention is plain causal
+    attention: compare against torch's scaled_dot_product_attention on the CPU in
+    float64 (a library routine, with the latent row as key and its first DV
+    entries as value).  The dense additive-mask form must agree as well."""
+    import torch
+    r = _rng(34)
+    B, L, H, D, DV = 2, 13, 3, 10, 6
+    q = r.standard_normal((B, L, H, D))
+    kv = r.standard_normal((B, L, D))
+    idx = np.full((B, L, L), -1, dtype=np.int32)
+    for t in range(L):
+        idx[:, t, :t + 1] = r.permutation(t + 1)
+    scale = 0.37
+    o, lse = sparse_mla(q, kv, idx, scale, DV)
+    od, lsed = dense_masked_mla(q, kv, idx, scale, DV, 0)
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)                   # [B,H,L,D]
+    tk = torch.from_numpy(kv)[:, None].expand(B, H, L, D)
+    tv = torch.from_numpy(kv[..., :DV])[:, None].expand(B, H, L, DV)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    logits = torch.einsum("bhld,bhsd->bhls", tq, tk) * scale
+    causal = torch.ones(L, L, dtype=torch.bool).tril()
+    ref_lse = torch.logsumexp(logits.masked_fill(~causal, float("-inf")), dim=-1).permute(0, 2, 1).numpy()
+    return (np.allclose(o, ref, atol=1e-12) and np.allclose(od, ref, atol=1e-12)
+            and np.allclose(lse, ref_lse, atol=1e-12) and np.allclose(lsed, ref_lse, atol=1e-12))
+
+
+def pin_mla_sparse_equals_dense(sparse_mla, dense_masked_mla) -> bool:
+    """Gathering the selected rows equals the dense causal form with an additive
+    0/-inf mask (the selection mechanism named on the pages)."""
+    r = _rng(35)
+    B, L, H, D, DV, K = 1, 40, 3, 9, 5, 6
+    q = r.standard_normal((B, L, H, D))
+    kv = r.standard_normal((B, L, D))
+    idx = np.full((B, L, K), -1, dtype=np.int32)
+    for t in range(L):
+        n = min(K, t + 1)
+        idx[0, t, :n] = np.sort(r.choice(t + 1, size=n, replace=False))
+    o, lse = sparse_mla(q, kv, idx, 0.5, DV)
+    od, lsed = dense_masked_mla(q, kv, idx, 0.5, DV, 0)
+    return np.allclose(o, od, atol=1e-13) and np.allclose(lse, lsed, atol=1e-13)

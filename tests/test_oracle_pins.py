@@ -1,0 +1,199 @@
+"""The CPU oracle pinned to facts outside itself (runs without a GPU).
+
+Each pin in tests/pins.py must hold for the oracle, and for each planted
+mistake (a broken copy of an oracle function, made here on the CPU) at least
+one pin must fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+
+def test_indexer_golden():
+    assert pins.pin_indexer_golden(oracle.index_scores_rows)
+
+
+def test_indexer_hadamard_invariance():
+    assert pins.pin_indexer_hadamard(oracle.index_scores_rows, oracle.sylvester_hadamard)
+
+
+def test_indexer_unit_queries():
+    assert pins.pin_indexer_unit_queries(oracle.index_scores_rows)
+
+
+def test_indexer_causal():
+    assert pins.pin_indexer_causal(oracle.index_scores_rows)
+
+
+def test_indexer_heads():
+    assert pins.pin_indexer_heads(oracle.index_scores_rows)
+
+
+def test_topk_golden():
+    assert pins.pin_topk_golden(oracle.topk_row)
+
+
+def test_topk_bruteforce():
+    assert pins.pin_topk_bruteforce(oracle.topk_row)
+
+
+def test_topk_short_rows():
+    assert pins.pin_topk_short_rows(oracle.topk_row)
+
+
+def test_mla_golden():
+    assert pins.pin_mla_golden(oracle.sparse_mla_rows)
+
+
+def test_mla_single_key():
+    assert pins.pin_mla_single_key(oracle.sparse_mla_rows)
+
+
+def test_mla_uniform():
+    assert pins.pin_mla_uniform(oracle.sparse_mla_rows)
+
+
+def test_mla_permutation_and_mask():
+    assert pins.pin_mla_permutation_and_mask(oracle.sparse_mla_rows)
+
+
+def test_mla_sdpa_special_case():
+    assert pins.pin_mla_sdpa(oracle.sparse_mla, oracle.dense_masked_mla)
+
+
+def test_mla_sparse_equals_dense():
+    assert pins.pin_mla_sparse_equals_dense(oracle.sparse_mla, oracle.dense_masked_mla)
+
+
+def test_forward_rows_composes_the_steps():
+    """forward_rows is indexer -> top-k -> sparse MLA; with K >= L it is causal attention."""
+    r = np.random.default_rng(5)
+    T, HI, DI, H, D, DV = 12, 2, 4, 2, 6, 4
+    qI = r.integers(-3, 4, size=(T, HI, DI)).astype(np.float32)
+    kI = r.integers(-3, 4, size=(T, DI)).astype(np.float32)
+    w = np.ones((T, HI), dtype=np.float32)
+    q = r.standard_normal((T, H, D))
+    kv = r.standard_normal((T, D))
+    res = oracle.forward_rows(qI, kI, w, q, kv, range(T), 0, 3, 0.5, DV)
+    for x in res:
+        exp_idx = oracle.topk_row(x["scores"].astype(np.float32), 3)
+        assert np.array_equal(x["idx"], exp_idx)
+        o, lse = oracle.sparse_mla_rows(q[x["t"]], kv, exp_idx, 0.5, DV)
+        assert np.array_equal(o, x["o"]) and np.array_equal(lse, x["lse"])
+    full = oracle.forward_rows(qI, kI, w, q, kv, range(T), 0, T, 0.5, DV)
+    od, _ = oracle.dense_masked_mla(q[None], kv[None], np.stack([x["idx"] for x in full])[None], 0.5, DV, 0)
+    for x in full:
+        assert np.allclose(x["o"], od[0, x["t"]], atol=1e-13)
+
+
+# ----------------------------------------------------------- planted mistakes
+
+def _mut_no_relu(q_b, k_b, w_b, ts, p0):
+    kI = oracle.as_f64(k_b)
+    return [(kI[:oracle.n_valid_keys(t, p0, kI.shape[0])] @ oracle.as_f64(q_b[t]).T) @ oracle.as_f64(w_b[t])
+            for t in ts]
+
+
+def _mut_exclusive_diag(q_b, k_b, w_b, ts, p0):
+    return [r[:-1] for r in oracle.index_scores_rows(q_b, k_b, w_b, ts, p0)]
+
+
+def _mut_weight_order(q_b, k_b, w_b, ts, p0):
+    return oracle.index_scores_rows(q_b, k_b, np.asarray(w_b)[:, ::-1], ts, p0)
+
+
+def _mut_relu_after_sum(q_b, k_b, w_b, ts, p0):
+    kI = oracle.as_f64(k_b)
+    return [np.maximum((kI[:oracle.n_valid_keys(t, p0, kI.shape[0])] @ oracle.as_f64(q_b[t]).T)
+                       @ oracle.as_f64(w_b[t]), 0) for t in ts]
+
+
+def _mut_key_dim_reversed(q_b, k_b, w_b, ts, p0):
+    return oracle.index_scores_rows(q_b, np.asarray(k_b)[:, ::-1], w_b, ts, p0)
+
+
+@pytest.mark.parametrize("mutant", [_mut_no_relu, _mut_exclusive_diag, _mut_weight_order,
+                                    _mut_relu_after_sum, _mut_key_dim_reversed])
+def test_indexer_pins_catch_planted_mistakes(mutant):
+    checks = [pins.pin_indexer_golden(mutant), pins.pin_indexer_hadamard(mutant, oracle.sylvester_hadamard),
+              pins.pin_indexer_unit_queries(mutant), pins.pin_indexer_causal(mutant),
+              pins.pin_indexer_heads(mutant)]
+    assert not all(checks)
+
+
+def _mut_ties_high(v, K):
+    v = np.asarray(v, dtype=np.float32)
+    n = len(v)
+    out = np.full(K, -1, dtype=np.int32)
+    if n <= K:
+        out[:n] = np.arange(n)
+        return out
+    order = np.lexsort((-np.arange(n), -v.astype(np.float64)))
+    out[:] = np.sort(order[:K])
+    return out
+
+
+def _mut_rank_order(v, K):
+    v = np.asarray(v, dtype=np.float32)
+    n = len(v)
+    out = np.full(K, -1, dtype=np.int32)
+    if n <= K:
+        out[:n] = np.arange(n)
+        return out
+    out[:] = np.lexsort((np.arange(n), -v.astype(np.float64)))[:K]
+    return out
+
+
+def _mut_smallest(v, K):
+    return oracle.topk_row(-np.asarray(v, dtype=np.float32), K)
+
+
+def _mut_pad_zero(v, K):
+    out = oracle.topk_row(v, K)
+    out[out < 0] = 0
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_mut_ties_high, _mut_rank_order, _mut_smallest, _mut_pad_zero])
+def test_topk_pins_catch_planted_mistakes(mutant):
+    checks = [pins.pin_topk_golden(mutant), pins.pin_topk_bruteforce(mutant), pins.pin_topk_short_rows(mutant)]
+    assert not all(checks)
+
+
+def _mut_value_from_rope(q, kv, idx, scale, DV):
+    """value read from the last DV entries of the row instead of the first DV"""
+    kv = np.asarray(kv, dtype=np.float64)
+    swapped = np.concatenate([kv[:, -DV:], kv[:, :-DV]], axis=1)
+    o, _ = oracle.sparse_mla_rows(q, swapped, idx, scale, DV)
+    _, lse = oracle.sparse_mla_rows(q, kv, idx, scale, DV)
+    return o, lse
+
+
+def _mut_no_scale(q, kv, idx, scale, DV):
+    return oracle.sparse_mla_rows(q, kv, idx, 1.0, DV)
+
+
+def _mut_mask_ignored(q, kv, idx, scale, DV):
+    idx = np.where(np.asarray(idx) < 0, 0, idx)
+    return oracle.sparse_mla_rows(q, kv, idx, scale, DV)
+
+
+def _mut_lse_log2(q, kv, idx, scale, DV):
+    o, lse = oracle.sparse_mla_rows(q, kv, idx, scale, DV)
+    return o, lse / np.log(2.0)
+
+
+def _mut_no_max_shift_wrong_norm(q, kv, idx, scale, DV):
+    o, lse = oracle.sparse_mla_rows(q, kv, idx, scale, DV)
+    sel = [int(i) for i in np.asarray(idx) if int(i) >= 0]
+    return o * len(sel) / max(1, len(sel) + 1), lse
+
+
+@pytest.mark.parametrize("mutant", [_mut_value_from_rope, _mut_no_scale, _mut_mask_ignored, _mut_lse_log2,
+                                    _mut_no_max_shift_wrong_norm])
+def test_mla_pins_catch_planted_mistakes(mutant):
+    checks = [pins.pin_mla_golden(mutant), pins.pin_mla_single_key(mutant), pins.pin_mla_uniform(mutant),
+              pins.pin_mla_permutation_and_mask(mutant)]
+    assert not all(checks)
