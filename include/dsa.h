@@ -1,0 +1,171 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention forward.
+ *
+ * The library computes the three steps of DeepSeek Sparse Attention (DSA) as
+ * described in the DeepSeek-V3.2 model documentation, section "DeepSeek
+ * Sparse Attention (DSA)":
+ *
+ *   1. lightning indexer: a cheap scorer with few heads gives every query an
+ *      index score against each key at or before its position, using a
+ *      per-token, single-head indexer key cache of width index_head_dim;
+ *   2. fine-grained token selection: each query keeps its index_topk
+ *      best-scoring keys;
+ *   3. the main MLA attention runs over the kept keys only (on the pages this
+ *      is an additive mask over dense attention; here it is a gather over the
+ *      kept rows, which gives the same result).
+ *
+ * Shapes follow the DeepseekV32Config section of the same documentation
+ * (index_n_heads = 64, index_head_dim = 128, index_topk = 2048,
+ * num_attention_heads = 128, kv_lora_rank = 512, qk_rope_head_dim = 64).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers to dense, row-major, contiguous
+ *    buffers owned by the caller.  The library never allocates, frees or
+ *    keeps a pointer after the call returns, and never synchronises: work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *    call returns at once.  Errors raised by the device show up at the
+ *    caller's next synchronisation.
+ *  - Float tensors of one call share one storage type, `dtype`:
+ *    DSA_BF16 (bfloat16) or DSA_F32 (float32).  Scores are always float32,
+ *    indices always int32.  Every pointer must be 16-byte aligned.
+ *  - B sequences, Tq queries per sequence, N cached keys per sequence.  Query
+ *    t of a sequence sits at absolute position q_pos0 + t and sees keys
+ *    s = 0 .. min(N, q_pos0 + t + 1) - 1 (its own position included).
+ *    Prefill: q_pos0 = 0, Tq = N.  Decode of one new token whose key is the
+ *    last cache row: Tq = 1, q_pos0 = N - 1.
+ *  - Validation happens on the host before anything is enqueued.  On any
+ *    error the call returns a non-zero dsa_status, enqueues nothing and leaves
+ *    every output untouched; dsa_last_error() then describes the failure
+ *    (thread-local text).  A failed kernel launch returns DSA_ERR_HIP.
+ *  - Compiled shapes.  DSA_BF16: indexer H_I = 64, D_I = 128; MLA H = 128,
+ *    D = 576, DV = 512.  DSA_F32 (small reference-size problems): indexer
+ *    H_I <= 64, D_I <= 256; MLA H <= 128, D <= 1024, DV <= min(D, 512).
+ *    Other shapes return DSA_ERR_UNSUPPORTED.
+ *  - Sizes: 1 <= B, Tq, N; N < 2^31; 1 <= K <= 65536; q_pos0 >= 0.
+ *  - Calls are reentrant; concurrent calls on different streams may share
+ *    inputs but not outputs or workspaces.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer, bad dtype */
+  DSA_ERR_UNSUPPORTED = 2, /* valid request for a shape that is not compiled */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
+  DSA_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} dsa_status;
+
+typedef enum dsa_dtype { DSA_BF16 = 0, DSA_F32 = 1 } dsa_dtype;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dsa_version(void);
+
+/* Static text for a status code. */
+const char* dsa_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * Step 1 -- lightning indexer scores.
+ * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)",
+ *  paragraph on the lightning indexer and paragraph on its key cache.)
+ *
+ *   scores[b,t,s] = sum_{h < H_I} w[b,t,h] * max(0, sum_{d < D_I} q_idx[b,t,h,d] * k_idx[b,s,d])
+ *
+ * for s < min(N, q_pos0 + t + 1).  Entries of a row past that bound are not
+ * written.  No scale is applied (fold any scale into w).  Products are summed
+ * in float32: integer-valued inputs with power-of-two weights, whose sums stay
+ * below 2^24 steps, give exactly the real-number scores.
+ *
+ *   q_idx  [B, Tq, H_I, D_I]  indexer queries                  (dtype)
+ *   k_idx  [B, N, D_I]        single-head indexer key cache      (dtype)
+ *   w      [B, Tq, H_I]       per-token head weights             (dtype)
+ *   scores [B, Tq, N]         output                             (float32)
+ */
+dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                            int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I,
+                            int32_t D_I, int32_t dtype, void* stream);
+
+/*
+ * Step 2 -- per-query top-k.
+ * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)",
+ *  paragraph on fine-grained token selection; the -1 "no selection" entry of
+ *  the DeepSeek-V4 documentation, attention mask layout section.)
+ *
+ * Row (b,t) considers its n = min(N, q_pos0 + t + 1) visible scores.  If
+ * n <= K it returns 0, 1, ..., n-1 followed by K-n entries of -1.  Otherwise
+ * it returns the K keys ranked first under (score descending, key index
+ * ascending) -- equal scores go to the lower index, -0 equals +0 -- listed
+ * in ascending key order.  Scores must be finite (NaN gives an unspecified
+ * but in-range selection).
+ *
+ *   scores [B, Tq, N] float32;  idx [B, Tq, K] int32 output.
+ *   workspace: dsa_topk_workspace_size(...) bytes of device memory (may be
+ *   NULL when that size is 0); contents on entry do not matter.
+ */
+size_t dsa_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t K);
+dsa_status dsa_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N,
+                    int64_t q_pos0, int32_t K, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Step 3 -- sparse MLA in absorbed latent form over the selected keys.
+ * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)",
+ *  paragraph on fine-grained token selection: attention restricted to the
+ *  selected tokens; DeepseekV32Config section for kv_lora_rank = 512 and
+ *  qk_rope_head_dim = 64, hence D = 576 and DV = 512.)
+ *
+ * For every (b, t, h), with S = { idx[b,t,j] : 0 <= idx[b,t,j] < N }:
+ *   l_j          = scale * sum_{d < D} q[b,t,h,d] * kv[b,idx_j,d]
+ *   out[b,t,h,:] = sum_j softmax(l)_j * kv[b,idx_j,0:DV]
+ *   lse[b,t,h]   = ln sum_j exp(l_j)
+ * Entries of idx that are negative or >= N are masked (an additive -inf).
+ * An index row with no valid entry yields out = 0 and lse = -inf.  idx must
+ * not repeat a key within a row (the top-k step never does); causality is not
+ * checked here -- idx decides.  bf16 accumulates in float32 (MFMA) and rounds
+ * out to bf16 (nearest-even).
+ *
+ *   q   [B, Tq, H, D] (dtype);  kv [B, N, D] latent cache (dtype), value = the
+ *   first DV columns;  idx [B, Tq, K] int32;  out [B, Tq, H, DV] (dtype);
+ *   lse [B, Tq, H] float32, may be NULL.
+ *   workspace: dsa_sparse_mla_workspace_size(...) bytes (split-K partials).
+ */
+size_t dsa_sparse_mla_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t DV, int32_t K,
+                                     int32_t dtype);
+dsa_status dsa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, void* out,
+                              float* lse, int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t D,
+                              int32_t DV, int32_t K, float scale, int32_t dtype, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * Steps 1-3 in one call, stream-ordered, with no host synchronisation.
+ * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)":
+ *  each layer runs its own indexer, selection and sparse attention.)
+ *
+ * Same arguments as the three steps above.  The intermediate scores (and the
+ * indices, when idx_out is NULL) live in the workspace; pass idx_out
+ * [B, Tq, K] int32 to also receive the selection.  The result equals
+ * dsa_sparse_mla_fwd(dsa_topk(dsa_index_scores(...))) bit for bit.
+ */
+size_t dsa_forward_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t DV,
+                                  int32_t K, int32_t dtype);
+dsa_status dsa_forward(const void* q_idx, const void* k_idx, const void* w, const void* q,
+                       const void* kv, void* out, float* lse, int32_t* idx_out, int64_t B,
+                       int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t H,
+                       int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,221 @@
+"""Python binding of the MI355X (gfx950) DeepSeek Sparse Attention forward library.
+
+Thin ctypes layer over the C ABI declared in ``include/dsa.h`` and built into
+``libdsa.so`` next to this file.  It only checks and marshals arguments: every
+step of the computation runs in the library's HIP kernels.  PyTorch provides
+device memory and the stream (work is enqueued on the current stream unless
+one is given).  There is no fallback: if the library is missing, importing
+works but the first call raises.
+
+Functions mirror the C entry points:
+  index_scores(q_idx, k_idx, w, q_pos0=0)                 -> scores [B,Tq,N] float32
+  topk(scores, K, q_pos0=0)                               -> idx [B,Tq,K] int32
+  sparse_mla(q, kv, idx, scale, DV=512)                   -> (out [B,Tq,H,DV], lse [B,Tq,H])
+  forward(q_idx, k_idx, w, q, kv, K, scale, q_pos0=0, DV=512, return_idx=False)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dsa.h")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_BF16, DSA_F32 = 0, 1
+
+_lib = None
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+def _status_name(st: int) -> str:
+    return ["DSA_OK", "DSA_ERR_INVALID_ARG", "DSA_ERR_UNSUPPORTED", "DSA_ERR_WORKSPACE",
+            "DSA_ERR_HIP"][st] if 0 <= st <= 4 else f"status {st}"
+
+
+_i64, _i32, _f32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGNATURES = {
+    "dsa_version": (ctypes.c_int, []),
+    "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dsa_last_error": (ctypes.c_char_p, []),
+    "dsa_index_scores": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
+    "dsa_topk_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "dsa_topk": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]),
+    "dsa_sparse_mla_workspace_size": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32]),
+    "dsa_sparse_mla_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _f32,
+                                          _i32, _p, _sz, _p]),
+    "dsa_forward_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),
+    "dsa_forward": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
+                                   _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+}
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libdsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with long_context_sparse_14_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/dsa.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(rc: int):
+    if rc != DSA_OK:
+        raise DSAError(rc, library().dsa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _dev(t: torch.Tensor, name: str, ndim: int, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def index_scores(q_idx, k_idx, w, q_pos0: int = 0, scores=None, stream=None) -> torch.Tensor:
+    B, Tq, H_I, D_I = q_idx.shape
+    N = k_idx.shape[1]
+    dt = q_idx.dtype
+    pq = _dev(q_idx, "q_idx", 4)
+    pk = _dev(k_idx, "k_idx", 3, dt)
+    pw = _dev(w, "w", 3, dt)
+    if tuple(k_idx.shape) != (B, N, D_I) or tuple(w.shape) != (B, Tq, H_I):
+        raise ValueError("k_idx must be [B,N,D_I] and w [B,Tq,H_I]")
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q_idx.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if tuple(scores.shape) != (B, Tq, N):
+        raise ValueError("scores must be [B,Tq,N]")
+    _check(library().dsa_index_scores(pq, pk, pw, ps, B, Tq, N, q_pos0, H_I, D_I, _dtype_code(q_idx),
+                                      _stream(stream)))
+    return scores
+
+
+def topk(scores, K: int, q_pos0: int = 0, idx=None, workspace=None, stream=None) -> torch.Tensor:
+    B, Tq, N = scores.shape
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if idx is None:
+        idx = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+    pi = _dev(idx, "idx", 3, torch.int32)
+    if tuple(idx.shape) != (B, Tq, K):
+        raise ValueError("idx must be [B,Tq,K]")
+    lib = library()
+    ws, nbytes = _workspace(lib.dsa_topk_workspace_size(B, Tq, N, K), scores.device, workspace)
+    _check(lib.dsa_topk(ps, pi, B, Tq, N, q_pos0, K, ws.data_ptr() if ws is not None else None, nbytes,
+                        _stream(stream)))
+    return idx
+
+
+def sparse_mla(q, kv, idx, scale: float, DV: int = 512, out=None, lse=True, workspace=None, stream=None):
+    """Returns (out, lse); lse is None when lse=False."""
+    B, Tq, H, D = q.shape
+    N = kv.shape[1]
+    K = idx.shape[2]
+    pq = _dev(q, "q", 4)
+    pkv = _dev(kv, "kv", 3, q.dtype)
+    pi = _dev(idx, "idx", 3, torch.int32)
+    if tuple(kv.shape) != (B, N, D) or tuple(idx.shape[:2]) != (B, Tq):
+        raise ValueError("kv must be [B,N,D] and idx [B,Tq,K]")
+    if out is None:
+        out = torch.empty((B, Tq, H, DV), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", 4, q.dtype)
+    lse_t = None
+    if lse is True:
+        lse_t = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device)
+    elif isinstance(lse, torch.Tensor):
+        lse_t = lse
+    pl = _dev(lse_t, "lse", 3, torch.float32) if lse_t is not None else None
+    lib = library()
+    dt = _dtype_code(q)
+    ws, nbytes = _workspace(lib.dsa_sparse_mla_workspace_size(B, Tq, H, DV, K, dt), q.device, workspace)
+    _check(lib.dsa_sparse_mla_fwd(pq, pkv, pi, po, pl, B, Tq, N, H, D, DV, K, scale, dt,
+                                  ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    return out, lse_t
+
+
+def forward_workspace_size(B, Tq, N, H, DV, K, dtype) -> int:
+    dt = DSA_BF16 if dtype == torch.bfloat16 else DSA_F32
+    return int(library().dsa_forward_workspace_size(B, Tq, N, H, DV, K, dt))
+
+
+def forward(q_idx, k_idx, w, q, kv, K: int, scale: float, q_pos0: int = 0, DV: int = 512, out=None, lse=True,
+            idx_out=None, return_idx: bool = False, workspace=None, stream=None):
+    """Indexer -> top-K -> sparse MLA in one call.  Returns (out, lse, idx or None)."""
+    B, Tq, H_I, D_I = q_idx.shape
+    N = k_idx.shape[1]
+    H, D = q.shape[2], q.shape[3]
+    dt = q.dtype
+    pqi = _dev(q_idx, "q_idx", 4, dt)
+    pki = _dev(k_idx, "k_idx", 3, dt)
+    pw = _dev(w, "w", 3, dt)
+    pq = _dev(q, "q", 4, dt)
+    pkv = _dev(kv, "kv", 3, dt)
+    if tuple(q.shape[:2]) != (B, Tq) or tuple(kv.shape) != (B, N, D):
+        raise ValueError("q must be [B,Tq,H,D] and kv [B,N,D]")
+    if out is None:
+        out = torch.empty((B, Tq, H, DV), dtype=dt, device=q.device)
+    po = _dev(out, "out", 4, dt)
+    lse_t = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if lse is True else (
+        lse if isinstance(lse, torch.Tensor) else None)
+    pl = _dev(lse_t, "lse", 3, torch.float32) if lse_t is not None else None
+    if return_idx and idx_out is None:
+        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=q.device)
+    pi = _dev(idx_out, "idx_out", 3, torch.int32) if idx_out is not None else None
+    lib = library()
+    code = _dtype_code(q)
+    ws, nbytes = _workspace(lib.dsa_forward_workspace_size(B, Tq, N, H, DV, K, code), q.device, workspace)
+    _check(lib.dsa_forward(pqi, pki, pw, pq, pkv, po, pl, pi, B, Tq, N, q_pos0, H_I, D_I, H, D, DV, K, scale,
+                           code, ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    return out, lse_t, idx_out

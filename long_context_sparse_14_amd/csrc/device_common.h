@@ -1,0 +1,50 @@
+// Device helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte global load of eight bf16 values.
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits) {
+  return __uint_as_float(bits << 16);
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// One 32x32x16 bf16 matrix-core step: c += a * b (fp32 accumulate).
+// Operand layout (wave64): lane j supplies row (j % 32) of A and column
+// (j % 32) of B, each with eight consecutive k-slots chosen by j / 32.
+// Result layout: lane j holds column (j % 32), rows 8*(i/4) + 4*(j/32) + i%4
+// for register i = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int mfma_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+
+// Order-preserving map of a float32 to uint32 (larger float -> larger key);
+// -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t float_order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace dsa

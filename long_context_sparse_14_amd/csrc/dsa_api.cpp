@@ -1,0 +1,256 @@
+// C-ABI front end of the DSA forward library: argument validation, workspace
+// planning and kernel launches.  The contract of every entry point is stated
+// in include/dsa.h.  Validation is pure host code and runs before any HIP
+// call, so a rejected call never touches the device.
+#include "dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dsa_status ok() {
+  g_last_error[0] = '\0';
+  return DSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxN = 0x7fffffff;
+constexpr int32_t kMaxK = 65536;
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+dsa_status check_common(int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t dtype) {
+  if (B < 1 || Tq < 1 || N < 1) return fail(DSA_ERR_INVALID_ARG, "B, Tq and N must be >= 1 (got %lld, %lld, %lld)",
+                                            (long long)B, (long long)Tq, (long long)N);
+  if (N > kMaxN) return fail(DSA_ERR_INVALID_ARG, "N must be < 2^31 (got %lld)", (long long)N);
+  if (q_pos0 < 0) return fail(DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0 (got %lld)", (long long)q_pos0);
+  if (q_pos0 > kMaxN) return fail(DSA_ERR_INVALID_ARG, "q_pos0 must be < 2^31");
+  if (B > 65535) return fail(DSA_ERR_INVALID_ARG, "B must be <= 65535 (got %lld)", (long long)B);
+  if (B * Tq > kMaxGrid) return fail(DSA_ERR_INVALID_ARG, "B*Tq must be < 2^31");
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  return DSA_OK;
+}
+
+// Checks the indexer inputs; `scores` is checked only when check_scores is set
+// (the fused entry point keeps its scores in the workspace).
+dsa_status check_index_scores(const void* q_idx, const void* k_idx, const void* w, const float* scores, int64_t B,
+                              int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t dtype,
+                              bool check_scores) {
+  dsa_status st = check_common(B, Tq, N, q_pos0, dtype);
+  if (st != DSA_OK) return st;
+  if (!q_idx || !k_idx || !w || (check_scores && !scores)) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || (check_scores && !aligned16(scores)))
+    return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (H_I < 1 || D_I < 1) return fail(DSA_ERR_INVALID_ARG, "H_I and D_I must be >= 1");
+  if (dtype == DSA_BF16) {
+    if (H_I != 64 || D_I != 128)
+      return fail(DSA_ERR_UNSUPPORTED, "bf16 indexer is compiled for H_I=64, D_I=128 (got %d, %d)", H_I, D_I);
+  } else {
+    if (H_I > 64 || D_I > 256)
+      return fail(DSA_ERR_UNSUPPORTED, "fp32 indexer supports H_I <= 64, D_I <= 256 (got %d, %d)", H_I, D_I);
+    const int64_t chunks = (std::min<int64_t>(N, q_pos0 + Tq) + 255) / 256;
+    if (B * Tq * chunks > kMaxGrid) return fail(DSA_ERR_UNSUPPORTED, "fp32 indexer problem too large");
+  }
+  return DSA_OK;
+}
+
+dsa_status check_topk(const float* scores, const int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                      int32_t K, const void* workspace, size_t ws_bytes) {
+  dsa_status st = check_common(B, Tq, N, q_pos0, DSA_F32);
+  if (st != DSA_OK) return st;
+  if (!scores || !idx) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(scores) || !aligned16(idx)) return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (K < 1 || K > kMaxK) return fail(DSA_ERR_INVALID_ARG, "K must be in [1, 65536] (got %d)", K);
+  const size_t need = dsa::topk_workspace_bytes(B, Tq, N, K);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "top-k workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  return DSA_OK;
+}
+
+// Checks the sparse-MLA arguments; `idx` and the workspace are checked only
+// when check_idx_ws is set (the fused entry point produces both itself).
+dsa_status check_mla(const void* q, const void* kv, const int32_t* idx, const void* out, const float* lse, int64_t B,
+                     int64_t Tq, int64_t N, int32_t H, int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype,
+                     const void* workspace, size_t ws_bytes, bool check_idx_ws) {
+  dsa_status st = check_common(B, Tq, N, 0, dtype);
+  if (st != DSA_OK) return st;
+  if (!q || !kv || (check_idx_ws && !idx) || !out) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(kv) || (check_idx_ws && !aligned16(idx)) || !aligned16(out) ||
+      (lse && !aligned16(lse)))
+    return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (K < 1 || K > kMaxK) return fail(DSA_ERR_INVALID_ARG, "K must be in [1, 65536] (got %d)", K);
+  if (H < 1 || D < 1 || DV < 1 || DV > D) return fail(DSA_ERR_INVALID_ARG, "need H, D >= 1 and 1 <= DV <= D");
+  if (!(scale > 0.f) || scale != scale || scale > 3.0e38f)
+    return fail(DSA_ERR_INVALID_ARG, "scale must be a finite positive number");
+  if (dtype == DSA_BF16) {
+    if (H != 128 || D != 576 || DV != 512)
+      return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA is compiled for H=128, D=576, DV=512 (got %d, %d, %d)", H, D,
+                  DV);
+  } else {
+    if (H > 128 || D > 1024 || DV > 512)
+      return fail(DSA_ERR_UNSUPPORTED, "fp32 sparse MLA supports H <= 128, D <= 1024, DV <= 512");
+    if (B * Tq * H > kMaxGrid) return fail(DSA_ERR_UNSUPPORTED, "fp32 sparse MLA problem too large");
+  }
+  if (check_idx_ws) {
+    const size_t need = dsa::mla_workspace_bytes(B * Tq, H, DV, K, dtype == DSA_BF16);
+    if (need > 0 && (!workspace || ws_bytes < need))
+      return fail(DSA_ERR_WORKSPACE, "sparse MLA workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  }
+  return DSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct ForwardLayout {
+  size_t scores, idx, mla, total;
+};
+
+ForwardLayout forward_layout(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t DV, int32_t K, int32_t dtype) {
+  ForwardLayout L;
+  L.scores = 0;
+  L.idx = align256((size_t)B * Tq * N * sizeof(float));
+  L.mla = L.idx + align256((size_t)B * Tq * K * sizeof(int32_t));
+  L.total = L.mla + align256(dsa::mla_workspace_bytes(B * Tq, H, DV, K, dtype == DSA_BF16));
+  const size_t tk = dsa::topk_workspace_bytes(B, Tq, N, K);
+  if (tk > 0) L.total += align256(tk);  // top-k scratch follows the MLA partials
+  return L;
+}
+
+dsa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_version(void) { return 10000; }
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+    default: return "DSA_ERR_UNKNOWN";
+  }
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores, int64_t B,
+                            int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t dtype,
+                            void* stream) {
+  dsa_status st = check_index_scores(q_idx, k_idx, w, scores, B, Tq, N, q_pos0, H_I, D_I, dtype, true);
+  if (st != DSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == DSA_BF16)
+    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s);
+  else
+    e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
+                                     static_cast<const float*>(w), scores, B, Tq, N, q_pos0, H_I, D_I, s);
+  return hip_status(e, "index scores launch");
+}
+
+size_t dsa_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t K) {
+  if (B < 1 || Tq < 1 || N < 1 || K < 1) return 0;
+  return dsa::topk_workspace_bytes(B, Tq, N, K);
+}
+
+dsa_status dsa_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t K,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  return hip_status(dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, static_cast<hipStream_t>(stream)),
+                    "top-k launch");
+}
+
+size_t dsa_sparse_mla_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t DV, int32_t K, int32_t dtype) {
+  if (B < 1 || Tq < 1 || H < 1 || DV < 1 || K < 1) return 0;
+  return dsa::mla_workspace_bytes(B * Tq, H, DV, K, dtype == DSA_BF16);
+}
+
+dsa_status dsa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx, void* out, float* lse, int64_t B,
+                              int64_t Tq, int64_t N, int32_t H, int32_t D, int32_t DV, int32_t K, float scale,
+                              int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_mla(q, kv, idx, out, lse, B, Tq, N, H, D, DV, K, scale, dtype, workspace, ws_bytes, true);
+  if (st != DSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == DSA_BF16)
+    e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
+                                    static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, workspace, s);
+  else
+    e = dsa::launch_sparse_mla_f32(static_cast<const float*>(q), static_cast<const float*>(kv), idx,
+                                   static_cast<float*>(out), lse, B, Tq, N, H, D, DV, K, scale, s);
+  return hip_status(e, "sparse MLA launch");
+}
+
+size_t dsa_forward_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t DV, int32_t K,
+                                  int32_t dtype) {
+  if (B < 1 || Tq < 1 || N < 1 || H < 1 || DV < 1 || K < 1) return 0;
+  return forward_layout(B, Tq, N, H, DV, K, dtype).total;
+}
+
+dsa_status dsa_forward(const void* q_idx, const void* k_idx, const void* w, const void* q, const void* kv, void* out,
+                       float* lse, int32_t* idx_out, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I,
+                       int32_t D_I, int32_t H, int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_index_scores(q_idx, k_idx, w, nullptr, B, Tq, N, q_pos0, H_I, D_I, dtype, false);
+  if (st != DSA_OK) return st;
+  st = check_mla(q, kv, nullptr, out, lse, B, Tq, N, H, D, DV, K, scale, dtype, nullptr, 0, false);
+  if (st != DSA_OK) return st;
+  if (idx_out && !aligned16(idx_out)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 16-byte aligned");
+  const ForwardLayout L = forward_layout(B, Tq, N, H, DV, K, dtype);
+  if (!workspace || ws_bytes < L.total)
+    return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  void* mla_ws = ws + L.mla;
+  void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  if (dtype == DSA_BF16)
+    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s);
+  else
+    e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
+                                     static_cast<const float*>(w), scores, B, Tq, N, q_pos0, H_I, D_I, s);
+  if (e != hipSuccess) return hip_status(e, "index scores launch");
+  e = dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
+  if (e != hipSuccess) return hip_status(e, "top-k launch");
+  if (dtype == DSA_BF16)
+    e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
+                                    static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, mla_ws, s);
+  else
+    e = dsa::launch_sparse_mla_f32(static_cast<const float*>(q), static_cast<const float*>(kv), idx,
+                                   static_cast<float*>(out), lse, B, Tq, N, H, D, DV, K, scale, s);
+  return hip_status(e, "sparse MLA launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,241 @@
+// Lightning-indexer scores on gfx950.
+//
+// Computes, for query t of sequence b and every key s it may see,
+//   scores[b,t,s] = sum_h w[b,t,h] * max(0, sum_d q_idx[b,t,h,d] * k_idx[b,s,d])
+// (DeepSeek-V3.2 model documentation, section "DeepSeek Sparse Attention
+// (DSA)": a light scorer with few heads against every earlier key, over the
+// indexer's own single-head key cache; head count and width from the
+// DeepseekV32Config section: 64 heads of width 128.)
+//
+// bf16 path, matrix cores.  One 32x32x16 MFMA block has the 32 heads of a
+// query as rows (A = q) and 32 keys as columns (B = k), so after the
+// contraction each lane owns one key and 16 of the 32 heads: the ReLU and the
+// head-weighted sum are plain per-lane FMAs, and one exchange between lane j
+// and lane j+32 completes the 64-head sum.  The contraction order over the
+// 128 channels is free, so lane half h takes channels [64h, 64h+64): every
+// lane then reads 128 contiguous bytes of its key row, for q and k alike.
+//
+//  * stream kernel (few queries per sequence, i.e. decode): the key cache is
+//    read once from HBM straight into MFMA operand registers, one 8 KiB tile of
+//    32 keys per wave step, with the next tile's loads in flight while the
+//    current one is multiplied;
+//  * tiled kernel (prefill): 8 queries per workgroup (one per wave) share
+//    64-key tiles staged in LDS, double-buffered; the causal triangle is
+//    walked longest query block first.
+#include "device_common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int IH = 64;   // indexer heads
+constexpr int ID = 128;  // indexer head width
+
+struct QFrags {
+  bf16x8 a0[8], a1[8];  // heads [0,32) and [32,64); channels 64*half + 8*s + [0,8)
+  float w0[16], w1[16]; // weights of the accumulator rows this lane holds
+};
+
+__device__ __forceinline__ void load_query(QFrags& f, const uint16_t* __restrict__ q_idx,
+                                           const uint16_t* __restrict__ w, int64_t row, int half, int col) {
+  const uint16_t* qr = q_idx + row * (IH * ID) + 64 * half;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    f.a0[s] = load_bf16x8(qr + col * ID + 8 * s);
+    f.a1[s] = load_bf16x8(qr + (32 + col) * ID + 8 * s);
+  }
+  const uint16_t* wr = w + row * IH;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    f.w0[i] = bf16_bits_to_float(wr[mfma_row(i, half)]);
+    f.w1[i] = bf16_bits_to_float(wr[32 + mfma_row(i, half)]);
+  }
+}
+
+// Score of this lane's key (valid in lanes 0..31) from the two head blocks.
+__device__ __forceinline__ float weighted_relu_sum(const QFrags& f, const f32x16& c0, const f32x16& c1) {
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    part = fmaf(f.w0[i], fmaxf(c0[i], 0.f), part);
+    part = fmaf(f.w1[i], fmaxf(c1[i], 0.f), part);
+  }
+  return part + __shfl_xor(part, 32);
+}
+
+template <int WAVES, int TPW>
+__global__ __launch_bounds__(WAVES * 64) void indexer_stream_bf16(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
+    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int64_t t = blockIdx.y, b = blockIdx.z;
+  const int64_t row = b * Tq + t;
+  const int64_t n_valid = min(N, q_pos0 + t + 1);
+  const int64_t k_begin = (int64_t)blockIdx.x * (WAVES * TPW * 32);
+  if (k_begin >= n_valid) return;
+
+  QFrags f;
+  load_query(f, q_idx, w, row, half, col);
+  const uint16_t* kb = k_idx + b * N * ID + 64 * half;
+  float* sr = scores + row * N;
+
+  bf16x8 cur[8], nxt[8];
+  int64_t k0 = k_begin + (int64_t)wave * 32;
+  {
+    const int64_t key = min(k0 + col, n_valid - 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) cur[s] = load_bf16x8(kb + key * ID + 8 * s);
+  }
+  for (int it = 0; it < TPW; ++it) {
+    if (k0 >= n_valid) break;
+    const int64_t k1 = k0 + WAVES * 32;
+    if (it + 1 < TPW && k1 < n_valid) {
+      const int64_t key = min(k1 + col, n_valid - 1);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) nxt[s] = load_bf16x8(kb + key * ID + 8 * s);
+    }
+    f32x16 c0 = {}, c1 = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      c0 = mfma32x32x16(f.a0[s], cur[s], c0);
+      c1 = mfma32x32x16(f.a1[s], cur[s], c1);
+    }
+    const float sc = weighted_relu_sum(f, c0, c1);
+    if (half == 0 && k0 + col < n_valid) sr[k0 + col] = sc;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) cur[s] = nxt[s];
+    k0 = k1;
+  }
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
+    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, int64_t nqb) {
+  constexpr int TK = 64;          // keys per LDS tile
+  constexpr int PITCH = ID + 8;   // bf16 per LDS row (272 B): spreads rows over the banks
+  constexpr int CHUNKS = TK * ID / 8;
+  constexpr int PER_T = CHUNKS / (WAVES * 64);
+  static_assert(PER_T * WAVES * 64 == CHUNKS, "tile chunks must divide evenly");
+  __shared__ __align__(16) uint16_t ks[2][TK * PITCH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int64_t qb = nqb - 1 - (int64_t)blockIdx.x;  // longest rows first
+  const int64_t b = blockIdx.y;
+  const int64_t t0 = qb * WAVES;
+  const int64_t t_last = min(Tq, t0 + WAVES) - 1;
+  const int64_t t = t0 + wave;
+  const bool active = t < Tq;
+  const int64_t n_valid = active ? min(N, q_pos0 + t + 1) : 0;
+  const int64_t n_blk = min(N, q_pos0 + t_last + 1);
+  const int64_t row = b * Tq + (active ? t : t_last);
+
+  QFrags f;
+  load_query(f, q_idx, w, row, half, col);
+  const uint16_t* kb = k_idx + b * N * ID;
+  float* sr = scores + row * N;
+
+  u32x4 pre[PER_T];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int c = tid + u * WAVES * 64;
+      const int64_t key = min(k0 + (c >> 4), N - 1);
+      pre[u] = *reinterpret_cast<const u32x4*>(kb + key * ID + 8 * (c & 15));
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int c = tid + u * WAVES * 64;
+      *reinterpret_cast<u32x4*>(&ks[buf][(c >> 4) * PITCH + 8 * (c & 15)]) = pre[u];
+    }
+  };
+
+  const int ntiles = (int)((n_blk + TK - 1) / TK);
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int64_t k0 = (int64_t)it * TK;
+    if (it + 1 < ntiles) gload(k0 + TK);
+#pragma unroll
+    for (int nb = 0; nb < TK / 32; ++nb) {
+      const int64_t kk0 = k0 + 32 * nb;
+      if (kk0 < n_valid) {
+        const uint16_t* lp = &ks[buf][(32 * nb + col) * PITCH + 64 * half];
+        f32x16 c0 = {}, c1 = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lp + 8 * s);
+          c0 = mfma32x32x16(f.a0[s], bv, c0);
+          c1 = mfma32x32x16(f.a1[s], bv, c1);
+        }
+        const float sc = weighted_relu_sum(f, c0, c1);
+        if (half == 0 && kk0 + col < n_valid) sr[kk0 + col] = sc;
+      }
+    }
+    if (it + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void indexer_f32(const float* __restrict__ q, const float* __restrict__ k,
+                                                   const float* __restrict__ w, float* __restrict__ scores,
+                                                   int64_t Tq, int64_t N, int64_t q_pos0, int H_I, int D_I,
+                                                   int64_t chunks) {
+  const int64_t blk = blockIdx.x;
+  const int64_t rowi = blk / chunks;
+  const int64_t s = (blk % chunks) * 256 + threadIdx.x;
+  const int64_t t = rowi % Tq, b = rowi / Tq;
+  const int64_t n_valid = min(N, q_pos0 + t + 1);
+  if (s >= n_valid) return;
+  const float* qr = q + rowi * H_I * D_I;
+  const float* kr = k + (b * N + s) * D_I;
+  const float* wr = w + rowi * H_I;
+  float acc = 0.f;
+  for (int h = 0; h < H_I; ++h) {
+    float dot = 0.f;
+    for (int d = 0; d < D_I; ++d) dot = fmaf(qr[h * D_I + d], kr[d], dot);
+    acc = fmaf(wr[h], fmaxf(dot, 0.f), acc);
+  }
+  scores[rowi * N + s] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
+                                    float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                                    hipStream_t stream) {
+  if (Tq <= 4) {
+    constexpr int WAVES = 4, TPW = 8;
+    const int64_t chunk = WAVES * TPW * 32;
+    const int64_t nmax = min(N, q_pos0 + Tq);
+    dim3 grid((unsigned)((nmax + chunk - 1) / chunk), (unsigned)Tq, (unsigned)B);
+    hipLaunchKernelGGL((indexer_stream_bf16<WAVES, TPW>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w,
+                       scores, Tq, N, q_pos0);
+  } else {
+    constexpr int WAVES = 8;
+    const int64_t nqb = (Tq + WAVES - 1) / WAVES;
+    dim3 grid((unsigned)nqb, (unsigned)B);
+    hipLaunchKernelGGL((indexer_tiled_bf16<WAVES>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w, scores,
+                       Tq, N, q_pos0, nqb);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const float* w, float* scores,
+                                   int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int H_I, int D_I,
+                                   hipStream_t stream) {
+  const int64_t chunks = (min(N, q_pos0 + Tq) + 255) / 256;
+  dim3 grid((unsigned)(B * Tq * chunks));
+  hipLaunchKernelGGL(indexer_f32, grid, dim3(256), 0, stream, q_idx, k_idx, w, scores, Tq, N, q_pos0, H_I, D_I,
+                     chunks);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Indexer scores and top-k indices must match bit for bit (the inputs are
+integer-valued with power-of-two weights, so fp32 sums are exact); attention
+outputs must match within |d| <= 2e-2 + 1e-2|ref| (bf16) or
+|d| <= 1e-5|ref| + 1e-6 (fp32).  Small cases run whole; the full-size
+workloads compare sampled rows and check properties on every row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_close, assert_lse_close, causal_scores_equal, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.WORKLOADS
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _dsa():
+    import long_context_sparse_14_amd as dsa
+    dsa.library()
+    return dsa
+
+
+def _forward_reference(wl, x, ts, b=0):
+    kv = oracle.as_f64(x["kv"][b])
+    return oracle.forward_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], x["q"][b], kv, ts, wl.q_pos0,
+                               wl.K, wl.scale, wl.DV)
+
+
+# ------------------------------------------------------------------ small
+
+def test_tiny_prefill_f32_full_forward():
+    dsa = _dsa()
+    wl = WL["tiny_prefill_f32"]
+    x = synth.make_inputs(wl)
+    d = {k: dev(v) for k, v in x.items()}
+    scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], wl.q_pos0)
+    idx = dsa.topk(scores, wl.K, wl.q_pos0)
+    out, lse = dsa.sparse_mla(d["q"], d["kv"], idx, wl.scale, wl.DV)
+    fout, flse, fidx = dsa.forward(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale,
+                                   wl.q_pos0, wl.DV, return_idx=True)
+    torch.cuda.synchronize()
+    ts = list(range(wl.Tq))
+    ref = _forward_reference(wl, x, ts)
+    causal_scores_equal(scores[0].cpu().numpy(), [r["scores"] for r in ref], ts, "scores")
+    ref_idx = np.stack([r["idx"] for r in ref])
+    assert np.array_equal(idx[0].cpu().numpy(), ref_idx)
+    assert_close(host64(out[0]), np.stack([r["o"] for r in ref]), "f32", "out")
+    assert_lse_close(host64(lse[0]), np.stack([r["lse"] for r in ref]), "lse", tol=1e-5)
+    # the fused entry point is the staged calls, bit for bit
+    assert torch.equal(fidx, idx) and torch.equal(fout, out) and torch.equal(flse, lse)
+
+
+def test_tiny_prefill_f32_dense_equivalence():
+    """K >= L selects every visible key: the result is dense causal attention."""
+    dsa = _dsa()
+    wl = WL["tiny_prefill_f32"].replace(K=256)
+    x = synth.make_inputs(wl)
+    d = {k: dev(v) for k, v in x.items()}
+    out, lse, idx = dsa.forward(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale,
+                                wl.q_pos0, wl.DV, return_idx=True)
+    L = wl.Tq
+    all_idx = np.full((1, L, L), -1, dtype=np.int32)
+    for t in range(L):
+        all_idx[0, t, :t + 1] = np.arange(t + 1)
+    assert np.array_equal(idx.cpu().numpy(), all_idx)
+    od, lsed = oracle.dense_masked_mla(x["q"], x["kv"], all_idx, wl.scale, wl.DV, 0)
+    assert_close(host64(out), od, "f32", "dense-equivalent out")
+    assert_lse_close(host64(lse), lsed, "lse", tol=1e-5)
+
+
+def _bf16_indexer_case(Tq, N, q_pos0, B=1, dist_w=None):
+    wl = WL["indexer_topk_prefill_8k"].replace(B=B, Tq=Tq, N=N, q_pos0=q_pos0)
+    if dist_w is not None:
+        wl = wl.replace(dists=dict(wl.dists, w=dist_w))
+    return wl, synth.make_inputs(wl)
+
+
+@pytest.mark.parametrize("B,Tq,N,q_pos0", [
+    (1, 333, 333, 0),        # prefill, ragged against the 8-query and 64-key tiles
+    (2, 77, 200, 50),        # chunked prefill: queries at positions 50..126 of a 200-row cache
+    (3, 1, 5000, 4999),      # decode, streamed keys
+    (2, 3, 1000, 997),       # decode of 3 tokens
+    (1, 1, 1, 0),            # a single key
+    (1, 9, 9, 0),            # tiled path with a single short tile
+])
+def test_indexer_bf16_exact(B, Tq, N, q_pos0):
+    dsa = _dsa()
+    wl, x = _bf16_indexer_case(Tq, N, q_pos0, B)
+    scores = dsa.index_scores(dev(x["q_idx"]), dev(x["k_idx"]), dev(x["w"]), q_pos0).cpu().numpy()
+    for b in range(B):
+        ts = list(range(Tq))
+        ref = oracle.index_scores_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], ts, q_pos0)
+        causal_scores_equal(scores[b], ref, ts, f"scores b={b}")
+
+
+def test_indexer_bf16_negative_weights_exact():
+    dsa = _dsa()
+    wl, x = _bf16_indexer_case(70, 70, 0, 1, synth.Dist("choice", values=(-1.0, 0.5, -0.25, 2.0)))
+    scores = dsa.index_scores(dev(x["q_idx"]), dev(x["k_idx"]), dev(x["w"]), 0).cpu().numpy()
+    ts = list(range(70))
+    causal_scores_equal(scores[0], oracle.index_scores_rows(x["q_idx"][0], x["k_idx"][0], x["w"][0], ts, 0),
+                        ts, "scores")
+
+
+@pytest.mark.parametrize("N,K,q_pos0,Tq", [
+    (3000, 5, 2900, 37),     # rows staged in LDS, all longer than K
+    (3000, 2048, 0, 40),     # short rows: closed form 0..t, -1
+    (20000, 2048, 19900, 6), # rows longer than the LDS stage: streamed passes
+    (20000, 1, 19990, 4),    # K = 1
+    (17, 16, 0, 17),         # n == K and n == K + 1 boundary
+])
+def test_topk_exact_with_ties(N, K, q_pos0, Tq):
+    dsa = _dsa()
+    rng = np.random.default_rng(N + K)
+    B = 2
+    vals = rng.integers(0, 4, size=(B, Tq, N)).astype(np.float32)
+    vals[0, :, ::7] = -0.0
+    vals[1, :, 1::5] = rng.standard_normal((Tq, len(range(1, N, 5)))).astype(np.float32)
+    idx = dsa.topk(torch.from_numpy(vals).cuda(), K, q_pos0).cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            n = oracle.n_valid_keys(t, q_pos0, N)
+            exp = oracle.topk_row(vals[b, t, :n], K)
+            assert np.array_equal(idx[b, t], exp), f"row {b},{t} (n={n})"
+
+
+def _mla_case(B, Tq, N, K, seed, n_masked=3, empty_row=False):
+    wl = WL["sparse_mla_decode_b64_32k"].replace(B=B, Tq=Tq, N=N, K=K)
+    x = {"q": synth.tensor(wl, "q", seed), "kv": synth.tensor(wl, "kv", seed)}
+    rng = np.random.default_rng(seed)
+    idx = np.empty((B, Tq, K), dtype=np.int32)
+    for b in range(B):
+        for t in range(Tq):
+            row = rng.choice(N, size=K, replace=False).astype(np.int32)
+            row[rng.choice(K, size=min(n_masked, K), replace=False)] = -1
+            idx[b, t] = row
+    if empty_row:
+        idx[0, 0, :] = -1
+    x["idx"] = idx
+    return wl, x
+
+
+@pytest.mark.parametrize("B,Tq,N,K", [
+    (2, 3, 700, 100),    # six queries: split-K partials + combine; ragged last tile
+    (1, 300, 400, 64),   # 300 queries: one workgroup per query, no split
+    (1, 1, 50, 1),       # K = 1
+])
+def test_sparse_mla_bf16_small(B, Tq, N, K):
+    dsa = _dsa()
+    wl, x = _mla_case(B, Tq, N, K, seed=B * 100 + Tq, n_masked=0 if K == 1 else 3, empty_row=(K == 100))
+    out, lse = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), dev(x["idx"]), wl.scale, wl.DV)
+    o_ref, l_ref = oracle.sparse_mla(x["q"], x["kv"], x["idx"], wl.scale, wl.DV)
+    assert_close(host64(out), o_ref, "bf16", "out")
+    assert_lse_close(host64(lse), l_ref, "lse")
+    if K == 100:
+        assert not host64(out[0, 0]).any() and np.isneginf(host64(lse[0, 0])).all()
+
+
+def test_sparse_mla_single_valid_key_is_exact():
+    """One valid index: the output is that latent row's first 512 entries, exactly."""
+    dsa = _dsa()
+    wl, x = _mla_case(2, 2, 300, 40, seed=7, n_masked=0)
+    x["idx"][:, :, 1:] = -1
+    out, lse = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), dev(x["idx"]), wl.scale, wl.DV)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(2):
+        for t in range(2):
+            assert np.array_equal(got[b, t], np.broadcast_to(x["kv"][b, x["idx"][b, t, 0], :512], (128, 512)))
+
+
+def test_causality_perturbation_bf16():
+    """Keys after a query's position cannot change its scores, indices or output."""
+    dsa = _dsa()
+    wl = WL["dsa_prefill_16k"].replace(Tq=300, N=300, K=64)
+    x = synth.make_inputs(wl)
+    t0 = 150
+    x2 = dict(x)
+    x2["k_idx"] = x["k_idx"].copy()
+    x2["kv"] = x["kv"].copy()
+    x2["k_idx"][0, t0 + 1:] = x["k_idx"][0, t0 + 1:][::-1]
+    x2["kv"][0, t0 + 1:] = 0
+    res = []
+    for xx in (x, x2):
+        d = {k: dev(v) for k, v in xx.items()}
+        out, lse, idx = dsa.forward(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale, 0, wl.DV,
+                                    return_idx=True)
+        res.append((out[0, :t0 + 1].clone(), idx[0, :t0 + 1].clone()))
+    assert torch.equal(res[0][1], res[1][1]) and torch.equal(res[0][0], res[1][0])
+
+
+# ------------------------------------------------------------- full sizes
+
+def test_indexer_topk_prefill_8k():
+    """L=8192, 64x128 indexer, top-2048: sampled rows exact; selection properties on every row."""
+    dsa = _dsa()
+    wl = WL["indexer_topk_prefill_8k"]
+    x = synth.make_inputs(wl)
+    d = {k: dev(v) for k, v in x.items()}
+    scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], 0)
+    idx = dsa.topk(scores, wl.K, 0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    ts = sorted(set([0, 1, 2, 2046, 2047, 2048, 2049, 4095, 8191] + rng.integers(0, 8192, 23).tolist()))
+    ref = oracle.index_scores_rows(x["q_idx"][0], x["k_idx"][0], x["w"][0], ts, 0)
+    sc = scores[0].cpu().numpy()
+    causal_scores_equal(sc, ref, ts, "scores")
+    ix = idx[0].cpu().numpy()
+    for t, r in zip(ts, ref):
+        assert np.array_equal(ix[t], oracle.topk_row(r.astype(np.float32), wl.K)), f"idx row {t}"
+    _check_selection_properties(scores[0], idx[0], 0, wl.K)
+
+
+def _check_selection_properties(scores, idx, q_pos0, K):
+    """Every row: ascending valid indices, -1 padded, count min(n, K); every kept score
+    >= every dropped one, and equal scores split by index (kept ones first)."""
+    T, N = scores.shape
+    n = torch.clamp(torch.arange(T, device=scores.device) + q_pos0 + 1, max=N)
+    cnt = (idx >= 0).sum(1)
+    assert torch.equal(cnt, torch.clamp(n, max=K).to(cnt.dtype))
+    pos = torch.arange(K, device=idx.device)
+    assert bool(((idx >= 0) == (pos[None, :] < cnt[:, None])).all())
+    assert bool(((idx[:, 1:] > idx[:, :-1]) | (idx[:, 1:] < 0)).all()), "kept indices must be strictly ascending"
+    assert bool((idx < n[:, None]).all())
+    visible = torch.arange(N, device=scores.device)[None, :] < n[:, None]
+    kept = torch.zeros((T, N), dtype=torch.bool, device=scores.device)
+    kept.scatter_(1, idx.clamp(min=0).long(), idx >= 0)
+    s = torch.where(visible, scores, torch.full_like(scores, -float("inf")))
+    kmin = torch.where(kept, s, torch.full_like(s, float("inf"))).min(1).values
+    dmax = torch.where(kept | ~visible, torch.full_like(s, -float("inf")), s).max(1).values
+    assert bool((dmax <= kmin).all()), "a dropped score beats a kept one"
+    tie_kept_max = torch.where(kept & (s == kmin[:, None]), torch.arange(N, device=s.device)[None, :], -1).max(1).values
+    tie_drop_min = torch.where(~kept & visible & (s == kmin[:, None]), torch.arange(N, device=s.device)[None, :],
+                               N).min(1).values
+    assert bool((tie_drop_min > tie_kept_max).all()), "ties must go to the lower index"
+
+
+def test_sparse_mla_decode_b64_32k():
+    """Batch-64 decode over 32768-row caches, 2048 given indices: every query against the oracle."""
+    dsa = _dsa()
+    wl = WL["sparse_mla_decode_b64_32k"]
+    x = synth.make_inputs(wl)
+    out, lse = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), dev(x["idx"]), wl.scale, wl.DV)
+    o = host64(out)
+    ls = host64(lse)
+    for b in range(wl.B):
+        rows = {int(i): x["kv"][b, i] for i in x["idx"][b, 0]}
+        o_ref, l_ref = oracle.sparse_mla_rows(x["q"][b, 0], rows, x["idx"][b, 0], wl.scale, wl.DV)
+        assert_close(o[b, 0], o_ref, "bf16", f"out b={b}")
+        assert_lse_close(ls[b, 0], l_ref, f"lse b={b}")
+
+
+def test_dsa_prefill_16k():
+    """L=16384 full forward: sampled rows exact (indices) and within tolerance (output);
+    the fused call equals the staged calls bit for bit."""
+    dsa = _dsa()
+    wl = WL["dsa_prefill_16k"]
+    x = synth.make_inputs(wl)
+    d = {k: dev(v) for k, v in x.items()}
+    out, lse, idx = dsa.forward(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale, 0, wl.DV,
+                                return_idx=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    ts = sorted(set([0, 1, 2047, 2048, 2049, 16383] + rng.integers(0, 16384, 10).tolist()))
+    ref = _forward_reference(wl, x, ts)
+    ix = idx[0].cpu().numpy()
+    o = host64(out[0])
+    ls = host64(lse[0])
+    for r in ref:
+        t = r["t"]
+        assert np.array_equal(ix[t], r["idx"]), f"idx row {t}"
+        assert_close(o[t], r["o"], "bf16", f"out row {t}")
+        assert_lse_close(ls[t], r["lse"], f"lse row {t}")
+    scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], 0)
+    idx2 = dsa.topk(scores, wl.K, 0)
+    out2, lse2 = dsa.sparse_mla(d["q"], d["kv"], idx2, wl.scale, wl.DV)
+    assert torch.equal(idx2, idx) and torch.equal(out2, out) and torch.equal(lse2, lse)
+    _check_selection_properties(scores[0], idx[0], 0, wl.K)
+
+
+def test_dsa_decode_b32_128k():
+    """Batch-32 decode at 131072 context: sampled sequences against the oracle, properties on all;
+    two runs give identical bits."""
+    dsa = _dsa()
+    wl = WL["dsa_decode_b32_128k"]
+    x = synth.make_inputs(wl)
+    d = {k: dev(v) for k, v in x.items()}
+    out, lse, idx = dsa.forward(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale, wl.q_pos0,
+                                wl.DV, return_idx=True)
+    out_b, lse_b, idx_b = dsa.forward(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale,
+                                      wl.q_pos0, wl.DV, return_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_b) and torch.equal(idx, idx_b) and torch.equal(lse, lse_b)
+    ix = idx.cpu().numpy()
+    o = host64(out)
+    ls = host64(lse)
+    for b in (0, 11, 31):
+        ref = _forward_reference(wl, x, [0], b)[0]
+        assert np.array_equal(ix[b, 0], ref["idx"]), f"idx b={b}"
+        assert_close(o[b, 0], ref["o"], "bf16", f"out b={b}")
+        assert_lse_close(ls[b, 0], ref["lse"], f"lse b={b}")
+    scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], wl.q_pos0)
+    for b in range(wl.B):
+        _check_selection_properties(scores[b], idx[b], wl.q_pos0, wl.K)
