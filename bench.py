@@ -1,0 +1,302 @@
+"""Benchmark of the DSA forward hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+lightning-indexer scores -> per-query top-k -> sparse MLA (absorbed latent
+form), enqueued through the C ABI on the current stream.  The default
+workload is batch-32 decode at 131072-token context (one new query per
+sequence, 128-head MLA over its 2048 selected latent rows).
+
+Prints one JSON line: throughput in queries/s over the timed steps (inputs
+resident in HBM), the roofline position of the dominant kernel measured with
+HIP events on the launch stream, and the CPU oracle timed on a bounded sample
+of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --calib-copy     (plain 1 GiB device copy, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DSA fwd queries/s (indexer+top-k+sparse MLA) at 128K ctx; % MFMA / % HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+DEFAULT_WORKLOAD = "dsa_decode_b32_128k"
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--fused", action="store_true",
+                    help="time the single dsa_forward call (no per-stage events)")
+    ap.add_argument("--calib-copy", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    """Digest of the HIP sources; stored counter readings are only valid for it."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_sparse_14_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the rocprofv3 counter passes kept under profiles/,
+    if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_digest") != kernel_sources_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def dominant_stage(wl):
+    """Stage that bounds the workload, its roofline and its algorithmic work per launch."""
+    B, Tq, N, q0, K = wl.B, wl.Tq, wl.N, wl.q_pos0, wl.K
+    vis = [min(N, q0 + t + 1) for t in range(Tq)]
+    keys = B * sum(vis)                                  # (query, visible key) pairs
+    sel = B * sum(min(v, K) for v in vis)                # (query, selected key) pairs
+    if "mla" in wl.stages and Tq > 4:
+        # prefill: the sparse MLA (K selected rows x 128 heads x 1088 MACs each) dominates
+        flops = 2 * wl.H * (wl.D + wl.DV) * sel
+        return "mla", "sparse_mla_bf16_kernel", "mfma", flops, "flop"
+    if "index" in wl.stages and Tq <= 4:
+        # decode indexer: each visible key row (256 B) read once, its fp32 score written once
+        nbytes = B * N * wl.D_I * 2 + keys * 4 + B * Tq * wl.H_I * (wl.D_I + 1) * 2
+        return "index", "indexer_stream_bf16", "hbm", nbytes, "B"
+    if "index" in wl.stages:
+        flops = 2 * wl.H_I * wl.D_I * keys
+        return "index", "indexer_tiled_bf16", "mfma", flops, "flop"
+    if Tq <= 4:
+        nbytes = sel * wl.D * 2 + B * Tq * wl.H * (wl.D + wl.DV) * 2 + B * Tq * K * 4
+        return "mla", "sparse_mla_bf16_kernel", "hbm", nbytes, "B"
+    flops = 2 * wl.H * (wl.D + wl.DV) * sel
+    return "mla", "sparse_mla_bf16_kernel", "mfma", flops, "flop"
+
+
+def calib_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(wl, x, budget_s: float):
+    """The oracle, as it stands, on whole queries of the same workload until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rows = [(b, t) for b in range(wl.B) for t in range(wl.Tq)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(rows))
+    done = 0
+    t0 = time.perf_counter()
+    for i in order:
+        b, t = rows[i]
+        if "index" in wl.stages:
+            oracle.forward_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], x["q"][b],
+                                lambda sel, b=b: x["kv"][b][sel], [t], wl.q_pos0, wl.K, wl.scale, wl.DV)
+        else:
+            rows_kv = {int(j): x["kv"][b, j] for j in x["idx"][b, t] if j >= 0}
+            oracle.sparse_mla_rows(x["q"][b, t], rows_kv, x["idx"][b, t], wl.scale, wl.DV)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(rows)} queries of {wl.name} (whole path per query), {el:.1f} s"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the batch shards by sequence with no "
+              f"exchange, so per-GPU throughput is the one-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    import long_context_sparse_14_amd as dsa
+    import synth
+
+    dsa.library()
+    wl = synth.WORKLOADS[args.workload]
+    x = synth.make_inputs(wl)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    dtt = (d["q"] if "q" in d else d["q_idx"]).dtype
+    B, Tq, N = wl.B, wl.Tq, wl.N
+    has_idx = "index" in wl.stages
+    has_mla = "mla" in wl.stages
+    scores = torch.empty((B, Tq, N), dtype=torch.float32, device="cuda") if has_idx else None
+    idx = torch.empty((B, Tq, wl.K), dtype=torch.int32, device="cuda") if has_idx else d["idx"]
+    out = torch.empty((B, Tq, wl.H, wl.DV), dtype=dtt, device="cuda") if has_mla else None
+    lse = torch.empty((B, Tq, wl.H), dtype=torch.float32, device="cuda") if has_mla else None
+    lib = dsa.library()
+    code = dsa.DSA_BF16 if dtt == torch.bfloat16 else dsa.DSA_F32
+
+    def buf(nbytes):
+        return torch.empty(max(256, nbytes), dtype=torch.uint8, device="cuda")
+
+    mla_ws = buf(lib.dsa_sparse_mla_workspace_size(B, Tq, wl.H, wl.DV, wl.K, code))
+    topk_ws = buf(lib.dsa_topk_workspace_size(B, Tq, N, wl.K))
+    fwd_ws = buf(lib.dsa_forward_workspace_size(B, Tq, N, wl.H, wl.DV, wl.K, code)) if (has_idx and has_mla) else None
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def ptr(t):
+        return t.data_ptr() if t is not None else None
+
+    # Argument tuples built once: the timed loop only enqueues work through the C ABI.
+    calls = {}
+    if has_idx:
+        calls["index"] = (lib.dsa_index_scores, (ptr(d["q_idx"]), ptr(d["k_idx"]), ptr(d["w"]), ptr(scores), B, Tq,
+                                                 N, wl.q_pos0, wl.H_I, wl.D_I, code, sp))
+        calls["topk"] = (lib.dsa_topk, (ptr(scores), ptr(idx), B, Tq, N, wl.q_pos0, wl.K, ptr(topk_ws),
+                                        topk_ws.numel(), sp))
+    if has_mla:
+        calls["mla"] = (lib.dsa_sparse_mla_fwd, (ptr(d["q"]), ptr(d["kv"]), ptr(idx), ptr(out), ptr(lse), B, Tq, N,
+                                                 wl.H, wl.D, wl.DV, wl.K, wl.scale, code, ptr(mla_ws),
+                                                 mla_ws.numel(), sp))
+    if has_idx and has_mla:
+        calls["fused"] = (lib.dsa_forward, (ptr(d["q_idx"]), ptr(d["k_idx"]), ptr(d["w"]), ptr(d["q"]), ptr(d["kv"]),
+                                            ptr(out), ptr(lse), None, B, Tq, N, wl.q_pos0, wl.H_I, wl.D_I, wl.H,
+                                            wl.D, wl.DV, wl.K, wl.scale, code, ptr(fwd_ws), fwd_ws.numel(), sp))
+
+    def run(name):
+        fn, a = calls[name]
+        rc = fn(*a)
+        if rc != 0:
+            raise RuntimeError(f"{name}: {lib.dsa_last_error().decode()}")
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        if has_idx:
+            run("index")
+            if evs is not None:
+                evs[1].record(stream)
+            run("topk")
+        if evs is not None:
+            evs[2].record(stream)
+        if has_mla:
+            run("mla")
+        if evs is not None:
+            evs[3].record(stream)
+
+    def fused_step():
+        run("fused")
+
+    use_fused = args.fused and has_idx and has_mla
+    for _ in range(args.warmup):
+        fused_step() if use_fused else step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if use_fused:
+            fused_step()
+        else:
+            step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    stage_ms = {}
+    if not use_fused:
+        for name, (a, b) in {"index": (0, 1), "topk": (1, 2), "mla": (2, 3)}.items():
+            if (name != "mla" and not has_idx) or (name == "mla" and not has_mla):
+                continue
+            stage_ms[name] = float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+
+    queries = B * Tq
+    value = queries / (ms_per_step / 1e3)
+    stage, kname, bound, work, wunit = dominant_stage(wl)
+    roof = None
+    if stage in stage_ms:
+        sec = stage_ms[stage] / 1e3
+        if bound == "hbm":
+            ach = work / sec / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4)}
+        else:
+            ach = work / sec / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+        roof["traffic"] = stored_traffic(wl.name, kname)
+        roof["kernel"] = kname
+        roof["kernel_avg_us"] = round(stage_ms[stage] * 1e3, 2)
+        roof["algorithmic_" + ("bytes" if wunit == "B" else "flops") + "_per_launch"] = int(work)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dtt == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded generator; integer-valued indexer inputs, N(0,1) latents)",
+        "config": {"workload": wl.name, "batch": B, "queries_per_seq": Tq, "context": N, "index_topk": wl.K,
+                   "indexer_heads": wl.H_I, "indexer_dim": wl.D_I, "mla_heads": wl.H, "latent_dim": wl.D,
+                   "value_dim": wl.DV, "timed": "fused dsa_forward" if use_fused else "staged C-ABI calls",
+                   "parallelism": "single GPU"},
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "tokens_per_s": round(value, 1),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

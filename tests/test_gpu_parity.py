@@ -122,12 +122,15 @@ def test_indexer_bf16_negative_weights_exact():
     (20000, 2048, 19900, 6), # rows longer than the LDS stage: streamed passes
     (20000, 1, 19990, 4),    # K = 1
     (17, 16, 0, 17),         # n == K and n == K + 1 boundary
+    (70000, 2048, 69990, 3), # segmented long-row method, 5 segments, last one ragged
+    (131072, 4096, 131071, 1),  # the largest K of the segmented method
+    (40000, 4097, 39999, 1), # K above the segmented method's limit: one workgroup per row
 ])
 def test_topk_exact_with_ties(N, K, q_pos0, Tq):
     dsa = _dsa()
     rng = np.random.default_rng(N + K)
     B = 2
-    vals = rng.integers(0, 4, size=(B, Tq, N)).astype(np.float32)
+    vals = rng.integers(0, 4000, size=(B, Tq, N)).astype(np.float32) / 16
     vals[0, :, ::7] = -0.0
     vals[1, :, 1::5] = rng.standard_normal((Tq, len(range(1, N, 5)))).astype(np.float32)
     idx = dsa.topk(torch.from_numpy(vals).cuda(), K, q_pos0).cpu().numpy()
@@ -136,6 +139,27 @@ def test_topk_exact_with_ties(N, K, q_pos0, Tq):
             n = oracle.n_valid_keys(t, q_pos0, N)
             exp = oracle.topk_row(vals[b, t, :n], K)
             assert np.array_equal(idx[b, t], exp), f"row {b},{t} (n={n})"
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "few_values", "boundary_ties"])
+def test_topk_long_rows_heavy_ties(kind):
+    """Many keys equal to the K-th value: the segmented method's candidate lists
+    overflow and the row falls back to the one-workgroup method (or not, for
+    moderate ties); the result must still be exact."""
+    dsa = _dsa()
+    rng = np.random.default_rng(3)
+    N, K = 50000, 2048
+    if kind == "all_equal":
+        vals = np.full((1, 2, N), 3.5, dtype=np.float32)
+    elif kind == "few_values":
+        vals = rng.integers(0, 3, size=(1, 2, N)).astype(np.float32)
+    else:
+        vals = rng.standard_normal((1, 2, N)).astype(np.float32)
+        vals[0, :, rng.choice(N, 3000, replace=False)] = 2.5   # ~1500 keys tie at the cut
+    idx = dsa.topk(torch.from_numpy(vals).cuda(), K, N - 2).cpu().numpy()
+    for t in range(2):
+        exp = oracle.topk_row(vals[0, t, :oracle.n_valid_keys(t, N - 2, N)], K)
+        assert np.array_equal(idx[0, t], exp), f"{kind} row {t}"
 
 
 def _mla_case(B, Tq, N, K, seed, n_masked=3, empty_row=False):
@@ -236,8 +260,9 @@ def _check_selection_properties(scores, idx, q_pos0, K):
     assert bool(((idx[:, 1:] > idx[:, :-1]) | (idx[:, 1:] < 0)).all()), "kept indices must be strictly ascending"
     assert bool((idx < n[:, None]).all())
     visible = torch.arange(N, device=scores.device)[None, :] < n[:, None]
-    kept = torch.zeros((T, N), dtype=torch.bool, device=scores.device)
-    kept.scatter_(1, idx.clamp(min=0).long(), idx >= 0)
+    kept = torch.zeros((T, N + 1), dtype=torch.bool, device=scores.device)   # column N absorbs the -1 padding
+    kept.scatter_(1, torch.where(idx >= 0, idx, N).long(), True)
+    kept = kept[:, :N]
     s = torch.where(visible, scores, torch.full_like(scores, -float("inf")))
     kmin = torch.where(kept, s, torch.full_like(s, float("inf"))).min(1).values
     dmax = torch.where(kept | ~visible, torch.full_like(s, -float("inf")), s).max(1).values
