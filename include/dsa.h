@@ -41,7 +41,9 @@
  *  - Compiled shapes.  DSA_BF16: indexer H_I = 64, D_I = 128; MLA H = 128,
  *    D = 576, DV = 512.  DSA_F32 (small reference-size problems): indexer
  *    H_I <= 64, D_I <= 256; MLA H <= 128, D <= 1024, DV <= min(D, 512).
- *    Other shapes return DSA_ERR_UNSUPPORTED.
+ *    Other shapes return DSA_ERR_UNSUPPORTED.  The bf16 sparse MLA also needs
+ *    one sequence's latent cache below 4 GiB (N * 1152 bytes < 2^32, i.e.
+ *    N <= 3728270).
  *  - Sizes: 1 <= B, Tq, N; N < 2^31; 1 <= K <= 65536; q_pos0 >= 0.
  *  - Calls are reentrant; concurrent calls on different streams may share
  *    inputs but not outputs or workspaces.

@@ -103,6 +103,9 @@ dsa_status check_mla(const void* q, const void* kv, const int32_t* idx, const vo
     if (H != 128 || D != 576 || DV != 512)
       return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA is compiled for H=128, D=576, DV=512 (got %d, %d, %d)", H, D,
                   DV);
+    if (N * (int64_t)D * 2 > 0xffffffffLL)
+      return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA addresses a sequence's latent cache with 32-bit offsets: "
+                  "N*1152 bytes must stay below 4 GiB (N=%lld)", (long long)N);
   } else {
     if (H > 128 || D > 1024 || DV > 512)
       return fail(DSA_ERR_UNSUPPORTED, "fp32 sparse MLA supports H <= 128, D <= 1024, DV <= 512");

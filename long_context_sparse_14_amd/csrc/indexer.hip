@@ -17,7 +17,7 @@
 //
 //  * stream kernel (few queries per sequence, i.e. decode): the key cache is
 //    read once from HBM straight into MFMA operand registers, one 8 KiB tile of
-//    32 keys per wave step, with the next tile's loads in flight while the
+//    32 keys per wave step, with the next two tiles' loads in flight while the
 //    current one is multiplied;
 //  * tiled kernel (prefill): 8 queries per workgroup (one per wave) share
 //    64-key tiles staged in LDS, double-buffered; the causal triangle is
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_stream_bf16(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
     float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int64_t t = blockIdx.y, b = blockIdx.z;
   const int64_t row = b * Tq + t;
@@ -81,32 +81,34 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_stream_bf16(
   const uint16_t* kb = k_idx + b * N * ID + 64 * half;
   float* sr = scores + row * N;
 
-  bf16x8 cur[8], nxt[8];
-  int64_t k0 = k_begin + (int64_t)wave * 32;
-  {
-    const int64_t key = min(k0 + col, n_valid - 1);
+  // Three register buffers: the keys of tiles it+1 and it+2 are in flight
+  // while tile it is multiplied (two 8 KiB tiles per wave, 128 KiB per CU).
+  bf16x8 buf[3][8];
+  auto tile_key = [&](int it) -> int64_t { return k_begin + (int64_t)(it * WAVES + wave) * 32; };
+  auto fetch = [&](bf16x8 (&dst)[8], int it) {
+    const int64_t k0 = tile_key(it);
+    if (it < TPW && k0 < n_valid) {
+      const int64_t key = min(k0 + col, n_valid - 1);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) cur[s] = load_bf16x8(kb + key * ID + 8 * s);
-  }
+      for (int s = 0; s < 8; ++s) dst[s] = load_bf16x8(kb + key * ID + 8 * s);
+    }
+  };
+  fetch(buf[0], 0);
+  fetch(buf[1], 1);
+#pragma unroll
   for (int it = 0; it < TPW; ++it) {
-    if (k0 >= n_valid) break;
-    const int64_t k1 = k0 + WAVES * 32;
-    if (it + 1 < TPW && k1 < n_valid) {
-      const int64_t key = min(k1 + col, n_valid - 1);
+    fetch(buf[(it + 2) % 3], it + 2);
+    const int64_t k0 = tile_key(it);
+    if (k0 < n_valid) {
+      f32x16 c0 = {}, c1 = {};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) nxt[s] = load_bf16x8(kb + key * ID + 8 * s);
+      for (int s = 0; s < 8; ++s) {
+        c0 = mfma32x32x16(f.a0[s], buf[it % 3][s], c0);
+        c1 = mfma32x32x16(f.a1[s], buf[it % 3][s], c1);
+      }
+      const float sc = weighted_relu_sum(f, c0, c1);
+      if (half == 0 && k0 + col < n_valid) sr[k0 + col] = sc;
     }
-    f32x16 c0 = {}, c1 = {};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      c0 = mfma32x32x16(f.a0[s], cur[s], c0);
-      c1 = mfma32x32x16(f.a1[s], cur[s], c1);
-    }
-    const float sc = weighted_relu_sum(f, c0, c1);
-    if (half == 0 && k0 + col < n_valid) sr[k0 + col] = sc;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) cur[s] = nxt[s];
-    k0 = k1;
   }
 }
 
@@ -212,7 +214,9 @@ hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
                                     hipStream_t stream) {
   if (Tq <= 4) {
-    constexpr int WAVES = 4, TPW = 8;
+    // 4096 keys per workgroup: long enough runs to amortise the query/weight
+    // loads, short enough that 131072-key rows still give 1024+ workgroups
+    constexpr int WAVES = 4, TPW = 32;
     const int64_t chunk = WAVES * TPW * 32;
     const int64_t nmax = min(N, q_pos0 + Tq);
     dim3 grid((unsigned)((nmax + chunk - 1) / chunk), (unsigned)Tq, (unsigned)B);

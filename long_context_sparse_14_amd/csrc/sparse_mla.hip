@@ -8,10 +8,11 @@
 // kv_lora_rank 512 + qk_rope_head_dim 64.)
 //
 // bf16 kernel: one workgroup (8 waves, two per SIMD) per (query, split of
-// the index list).  Each step gathers 32 selected latent rows (1152 B each)
-// straight into LDS with direct-to-LDS 16-byte loads (no staging registers;
-// the next tile's loads are in flight during the current tile's math) and
-// shares them across all 128 heads:
+// the index list, at most 2048 indices, staged once in LDS).  Each step
+// gathers 32 selected latent rows (1152 B each) straight into LDS with
+// direct-to-LDS 16-byte loads (no staging registers) into one of three tile
+// buffers, so two tiles' gathers (72 KiB) are in flight during the current
+// tile's math, and shares the rows across all 128 heads:
 //   * S^T = KV_tile . Q^T on 16x16x32 MFMAs: wave w owns heads [16w, 16w+16)
 //     and keeps their queries in registers (18 k-steps of 32 channels);
 //   * online softmax in fp32 with exp2 on log2e-prescaled logits; the four
@@ -22,11 +23,16 @@
 //     every V element is read from LDS once per tile; rescaling is skipped when
 //     no head of a block changed its running max.
 // The LDS tile is chunk-major: 16-byte chunk p (channels 8p..8p+7) of tile
-// row r sits at slot 32*p + r.  A gather instruction then fills 64 slots =
-// two chunk columns, so every lane always fetches from the same latent row
-// (one index per lane per tile), and every operand read in the math below is
-// a per-lane base plus a compile-time offset.  The QK^T reads of 16 rows hit
-// 256 contiguous bytes (no bank conflicts).
+// row r sits at slot 32*p + (r ^ 4*(p & 3)).  A gather instruction fills 64
+// slots = two chunk columns, so every lane always fetches from the same latent
+// row (one index per lane per tile); every operand read below is a per-lane
+// base plus a compile-time offset; the XOR keeps the reads at the minimum of
+// two passes per 512 bytes.  The PV operand (eight keys of one value column
+// per lane) comes from the gfx950 transposing LDS read ds_read_b64_tr_b16:
+// within each 16-lane group, lane i receives element (i & 3) of the 8 bytes
+// addressed by lane 4c + (i >> 2), c = 0..3 -- so lanes that address four
+// consecutive value columns of four consecutive keys hand every lane four
+// keys of its own column.
 // With more than one split, each split writes its normalised partial output
 // and its log2-sum-exp to the workspace and a combine kernel merges them.
 #include "device_common.h"
@@ -40,25 +46,35 @@ constexpr int ROW_CHUNKS = MD / 8;          // 72 chunks of 16 B per latent row
 constexpr int TILE_CHUNKS = NT * ROW_CHUNKS; // 2304
 constexpr int PP = NT + 8;                   // bf16 per LDS probability row
 constexpr int MLA_WAVES = 8;
+constexpr int NBUF = 3;                      // latent tile buffers (two gathers in flight)
+constexpr int MAX_SPLIT_KEYS = 2048;         // indices handled by one workgroup
 constexpr int MLA_THREADS = MLA_WAVES * 64;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16-byte direct-to-LDS load: every lane reads 16 B at `src` and the wave
-// writes them to LDS bytes [lds_addr + 16*lane, +16).  Written as inline asm so
-// that the compiler does not track it: otherwise it cannot tell that reads of
-// the current tile buffer do not alias the gather into the other buffer and
-// waits for the gather before every read.  The instruction has no register
-// result; completion is awaited explicitly (vmcnt) before the barrier that
-// hands the buffer to the readers.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr)
+// 16-byte direct-to-LDS load: every lane reads 16 B at base + voff and the
+// wave writes them to LDS bytes [lds_addr + 16*lane, +16).  base is
+// wave-uniform (scalar registers), voff a 32-bit per-lane byte offset; the
+// instruction offset stays 0 because it would move the LDS destination too.
+// Written as inline asm so that the compiler does not track it: otherwise it
+// cannot tell that reads of the current tile buffer do not alias the gathers
+// into the other buffers and waits for them before every read.  The
+// instruction has no register result; completion is awaited explicitly
+// (vmcnt) before the barrier that hands the buffer to the readers.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(lds_addr), "s"(base)
                : "memory", "m0");
 }
 
@@ -67,22 +83,18 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p));
 }
 
-// Barriers without the memory fence that __syncthreads() adds: the fence
-// would also wait for the in-flight direct-to-LDS gather of the next tile.
+// Barrier without the memory fence that __syncthreads() adds: the fence would
+// also wait for the in-flight direct-to-LDS gathers of the next tiles.
 __device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Full wait (all counters) through the builtin, so the compiler's own wait
-// tracking knows that nothing is outstanding afterwards, then a barrier.
-__device__ __forceinline__ void sync_all() {
-  __builtin_amdgcn_s_waitcnt(0);
-  asm volatile("s_barrier" ::: "memory");
-}
+
 
 __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
     int64_t R, int64_t Tq, int64_t N, int K, int splits, int keys_per_split, float scale_log2) {
-  __shared__ __align__(16) uint16_t kvs[2][NT * MD];  // double-buffered latent tile
-  __shared__ __align__(16) int32_t vflag[2][NT];       // row valid flags per buffer
+  __shared__ __align__(16) uint16_t kvs[NBUF][NT * MD];  // latent tiles, chunk-major (see above)
+  __shared__ __align__(16) int32_t vflag[NBUF][NT];      // row valid flags per buffer
+  __shared__ __align__(16) int32_t sidx[MAX_SPLIT_KEYS];  // this split's index list
   __shared__ __align__(16) uint16_t ps[MH * PP];
   __shared__ float alpha_s[MH];
   __shared__ float m_s[MH], l_s[MH];
@@ -111,7 +123,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   const int64_t b = r / Tq;
   const int kb = sp * keys_per_split;
   const int ke = min(K, kb + keys_per_split);
-  const int ntiles = ke > kb ? (ke - kb + NT - 1) / NT : 0;
+  const int nkeys = max(ke - kb, 0);
+  const int ntiles = (nkeys + NT - 1) / NT;
 
   // Queries of heads 16*wave + c16, channels 32*s + 8*g16 + [0, 8).
   bf16x8 qf[MD / 32];
@@ -120,46 +133,81 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
     for (int s = 0; s < MD / 32; ++s) qf[s] = load_bf16x8(qp + 32 * s);
   }
+  {
+    const int32_t* ip = idx + r * K + kb;
+    for (int j = tid; j < ntiles * NT; j += MLA_THREADS) sidx[j] = j < nkeys ? ip[j] : -1;
+  }
   f32x16 o[2][4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-
-  const int32_t* ip = idx + r * K;
   const uint16_t* kvb = kv + b * N * (int64_t)MD;
+  // Queries and indices are in place; from here on the only memory loads in
+  // flight are the gathers below, which the compiler does not see.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  // Gather of one tile: instruction u of wave w fills slots [64*ii, 64*ii+64)
+  // Gather of tile `it`: instruction u of wave w fills slots [64*ii, 64*ii+64)
   // of the tile, ii = w + 8u (36 instructions in all): chunk columns 2*ii and
   // 2*ii+1, rows 0..31.  Lane l always fetches row l%32, chunk 2*ii + l/32.
+  // Waves 0-3 issue 5 instructions per tile, waves 4-7 issue 4.
   constexpr int GU = (TILE_CHUNKS / 64 + MLA_WAVES - 1) / MLA_WAVES;  // 5
-  const int grow = lane & 31;
-  int32_t gidx = -1;
-  auto load_idx = [&](int it) {
-    const int j = kb + it * NT + grow;
-    gidx = (j < ke) ? ip[j] : -1;
+  // Slot 32*p + s of the tile holds row s ^ 4*(p & 3); for this wave's
+  // instructions p = 2*ii + lane/32 with ii = wave + 8u, so p & 3 is fixed.
+  const int grow = (lane & 31) ^ (4 * ((2 * (wave & 1) + (lane >> 5)) & 3));
+  // byte address of chunk 2*ii + lane/32 of row v: kvw + [v*1152 + 16*(lane/32)] + 256*u,
+  // with kvw = this sequence's cache + 32*wave (scalar) and ii = wave + 8u
+  const uint8_t* kvw = reinterpret_cast<const uint8_t*>(kvb) + 32 * wave;
+  auto gather = [&](int it) {
+    const int buf = it % NBUF;
+    const int32_t v = sidx[it * NT + grow];
+    const bool ok = v >= 0 && (int64_t)v < N;
+    const uint32_t voff = (uint32_t)(ok ? v : 0) * (uint32_t)(MD * 2) + 16u * (uint32_t)(lane >> 5);
+    const uint32_t lds0 = lds_address(&kvs[buf][512 * wave]);
+    dma16(kvw, voff, lds0);
+    dma16(kvw + 256, voff, lds0 + 8192);
+    dma16(kvw + 512, voff, lds0 + 16384);
+    dma16(kvw + 768, voff, lds0 + 24576);
+    if (wave + 4 * MLA_WAVES < TILE_CHUNKS / 64) dma16(kvw + 1024, voff, lds0 + 32768);
+    if (wave == 0 && lane < 32) vflag[buf][grow] = ok;  // wave 0, lanes 0..31: row == lane
   };
-  auto gather = [&](uint16_t* dst, int32_t* vfl) {
-    const bool ok = gidx >= 0 && (int64_t)gidx < N;
-    const uint16_t* src = kvb + (int64_t)(ok ? gidx : 0) * MD + 8 * (lane >> 5);
+  // Wait until this wave's gathers of all but the most recently issued tile
+  // are complete (vmcnt counts this wave's loads, oldest first).
+  auto wait_all_but_newest = [&](bool newest_in_flight) {
+    if (!newest_in_flight) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (wave < TILE_CHUNKS / 64 - (GU - 1) * MLA_WAVES) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  };
+  static_assert(GU == 5 && TILE_CHUNKS / 64 - (GU - 1) * MLA_WAVES == 4, "per-wave gather counts");
+
+  // QK^T operand: key row 16*kb2 + c16, chunk p = 4*s + g16 (p & 3 == g16)
+  //   -> slot 32*p + 16*kb2 + (c16 ^ 4*g16)   [bf16 element = 8 * slot]
+  const int abase = 256 * g16 + 8 * (c16 ^ (4 * g16));
+  // PV operand, read rd (keys 4rd..4rd+3 of this lane half) of block (ks, mb):
+  // 16-lane group G = lane/16, source lane j = lane%16 addresses key
+  // 16*ks + 8*half + 4*rd + j/4, value columns 64*wave + 32*mb + 16*(G&1) + 4*(j&3) + [0,4),
+  // i.e. chunk p = 8*wave + 4*mb + 2*(G&1) + (j&3)/2, byte 8*(j&1) of it.
+  int vbase[2];
+  {
+    const int G = lane >> 4, j = lane & 15, b = (j & 3) >> 1;
+    const int pl = 2 * (G & 1) + b;  // chunk offset within the 4-chunk group (p & 3)
 #pragma unroll
-    for (int u = 0; u < GU; ++u) {
-      const int ii = wave + MLA_WAVES * u;
-      if (ii < TILE_CHUNKS / 64) dma16(src + 16 * ii, lds_address(dst + 512 * ii));
+    for (int rd = 0; rd < 2; ++rd) {
+      const int key = 8 * half + 4 * rd + (j >> 2);              // + 16*ks (compile-time)
+      vbase[rd] = 256 * (8 * wave + pl) + 8 * (key ^ (4 * pl)) + 4 * (j & 1);
     }
-    if (wave == 0 && lane < 32) vfl[grow] = ok;
-  };
+  }
 
-  // QK^T operand: key row 16*kb2 + c16, chunk 4*s + g16 -> slot 32*(4*s + g16) + 16*kb2 + c16.
-  const int abase = 256 * g16 + 8 * c16;
-  // PV operand: value column 64*wave + 32*mb + col of key 16*ks + 8*half + e ->
-  // slot 32*(8*wave + 4*mb + col/8) + 16*ks + 8*half + e, element col%8.
-  const int vbase = 2048 * wave + 256 * (col >> 3) + 64 * half + (col & 7);
-
-  auto step = [&](const uint16_t* cur, const int32_t* vcur, uint16_t* nxt, int32_t* vnxt, int it) {
-    if (it + 1 < ntiles) gather(nxt, vnxt);
-    if (it + 2 < ntiles) load_idx(it + 2);
+  if (ntiles > 0) gather(0);
+  if (ntiles > 1) gather(1);
+  wait_all_but_newest(ntiles > 1);
+  sync_lds();
+  for (int it = 0; it < ntiles; ++it) {
+    const uint16_t* cur = kvs[it % NBUF];
+    const int32_t* vcur = vflag[it % NBUF];
+    if (it + 2 < ntiles) gather(it + 2);
 
     // S^T[key][head] for this wave's 16 heads, keys in two blocks of 16.
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
@@ -167,7 +215,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     for (int s = 0; s < MD / 32; ++s) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(cur + abase + 1024 * s + 128 * kb2);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(cur + abase + 1024 * s + 128 * kb2);  // p = 4s + g16
         sacc[kb2] = mfma16x16x32(av, qf[s], sacc[kb2]);
       }
       if ((s & 1) == 1) __builtin_amdgcn_sched_barrier(0);
@@ -232,10 +280,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
       bf16x8 av[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        u16x8 t;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = cur[vbase + 1024 * mb + 128 * ks + 8 * e];
-        av[mb] = __builtin_bit_cast(bf16x8, t);
+        // 16*ks rows and 4*mb chunks: slot += 16*ks + 128*mb (the XOR term is unchanged)
+        const s16x4 lo = lds_read_tr16(cur + vbase[0] + 1024 * mb + 128 * ks);
+        const s16x4 hi = lds_read_tr16(cur + vbase[1] + 1024 * mb + 128 * ks);
+        av[mb] = __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
       }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
@@ -245,18 +293,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    sync_all();
-  };
-
-  if (ntiles > 0) {
-    load_idx(0);
-    gather(kvs[0], vflag[0]);
-  }
-  if (ntiles > 1) load_idx(1);
-  sync_all();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    step(kvs[buf], vflag[buf], kvs[buf ^ 1], vflag[buf ^ 1], it);
+    // tile it+1 must have landed; tile it+2 may stay in flight
+    wait_all_but_newest(it + 2 < ntiles);
+    sync_lds();
   }
 
   if (g16 == 0) {
@@ -390,6 +429,9 @@ int mla_num_splits(int64_t rows, int K) {
   int64_t want = (256 + rows - 1) / rows;  // about one workgroup per compute unit
   if (want > 32) want = 32;
   if (want > tiles) want = tiles;
+  // one workgroup stages at most MAX_SPLIT_KEYS indices
+  const int64_t need = (K + MAX_SPLIT_KEYS - 1) / MAX_SPLIT_KEYS;
+  if (want < need) want = need;
   return want < 1 ? 1 : (int)want;
 }
 

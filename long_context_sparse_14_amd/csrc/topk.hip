@@ -17,8 +17,8 @@
 //
 // Two schedules:
 //  * rows of up to 16384 keys (prefill): one 1024-thread workgroup per row,
-//    the row staged once in LDS, four 8-bit histogram passes, then an
-//    in-order compaction with block prefix sums;
+//    the row staged once in LDS, three histogram passes (11, 11 and 10 bits),
+//    then an in-order compaction with one block prefix sum per 16384 keys;
 //  * long rows (decode at long context): each row is cut into 16384-key
 //    segments, one workgroup per segment holds its keys in registers, and
 //    four short kernels replace the serial passes:
@@ -33,6 +33,10 @@
 //    Per-segment histograms are plain stores (no atomics, no zeroing); a row
 //    whose candidates overflow their buffers falls back to the one-workgroup
 //    method reading the row from global memory.
+// Scores of one row usually share their top bits, so the first histogram
+// pass aggregates equal bins across a wave before touching LDS (same-address
+// LDS atomics would serialise).  Each thread owns a run of consecutive keys,
+// so one block-wide prefix sum orders a whole chunk.
 #include "device_common.h"
 #include "launch.h"
 
@@ -46,9 +50,12 @@ constexpr int SEG = 16384;            // segment length of the long-row method
 constexpr int SEG_PER_T = SEG / TK_THREADS;
 constexpr int HB = 2048;              // bins of an 11-bit digit
 constexpr int CAND_CAP = 1024;        // candidates a segment may hand over
-constexpr int ROW_CAND_CAP = 8192;    // candidates the final step can hold for one row
+constexpr int ROW_CAND_CAP = 2048;    // candidates the final step can hold for one row
 constexpr int LONG_MAX_K = 4096;      // largest K of the long-row method
 constexpr int64_t LONG_MAX_SEGS = 4096;  // bound on rows x segments (workspace size)
+constexpr int LONG_MAX_G = TK_THREADS;   // bound on segments per row (one thread per segment)
+constexpr int RUN = 16;                  // consecutive keys per thread in a chunk
+constexpr int CHUNK = RUN * TK_THREADS;  // keys ordered by one block prefix sum
 
 __device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N, int64_t q_pos0) {
   return min(N, q_pos0 + row % Tq + 1);
@@ -102,6 +109,46 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32
   return d;
 }
 
+// h[bin] += 1 for every lane with `valid`, where many lanes of the wave may
+// share a bin: up to four rounds elect the bin of the lowest pending lane and
+// add the number of lanes holding it with one atomic; lanes still pending
+// after that add one each.
+__device__ __forceinline__ void hist_add_aggregated(uint32_t* h, uint32_t bin, bool valid) {
+  const int lane = threadIdx.x & 63;
+  uint64_t pend = __ballot(valid);
+  bool mine = valid;
+#pragma unroll
+  for (int round = 0; round < 4; ++round) {
+    if (pend == 0) break;
+    const int leader = __ffsll((unsigned long long)pend) - 1;
+    const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
+    const uint64_t same = __ballot(mine && bin == lb);
+    if (lane == leader) atomicAdd(&h[lb], (uint32_t)__popcll(same));
+    if (bin == lb) mine = false;
+    pend &= ~same;
+  }
+  if (mine) atomicAdd(&h[bin], 1u);
+}
+
+// Writes the kept keys of the run [i0, i0 + RUN) (clipped to n) of one chunk:
+// gt/eq are the per-thread counts before this thread within the whole row.
+template <typename KeyAt>
+__device__ __forceinline__ void emit_run(KeyAt key_at, int64_t i0, int64_t n, uint32_t T, uint32_t keq,
+                                         uint32_t gt, uint32_t eq, int32_t* __restrict__ out) {
+  for (int u = 0; u < RUN; ++u) {
+    const int64_t i = i0 + u;
+    if (i >= n) break;
+    const uint32_t k = key_at(i);
+    if (k > T) {
+      out[gt + min(eq, keq)] = (int32_t)i;
+      ++gt;
+    } else if (k == T) {
+      if (eq < keq) out[gt + eq] = (int32_t)i;
+      ++eq;
+    }
+  }
+}
+
 // The one-workgroup method for one row.  skey: LDS stage of TK_CAP keys, or
 // nullptr to read the row from global memory on every pass.
 __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int32_t* __restrict__ out,
@@ -117,11 +164,13 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
   }
   auto key_at = [&](int64_t i) -> uint32_t { return skey != nullptr ? skey[i] : float_order_key(src[i]); };
 
+  // three passes: key bits 31..21, 20..10, 9..0
   uint32_t prefix = 0, mask = 0, kk = (uint32_t)K;
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : HB;
+    for (int b = tid; b < nb; b += TK_THREADS) hist[b] = 0;
     __syncthreads();
     for (int64_t base = tid; base < n; base += 8 * TK_THREADS) {
       uint32_t k[8];
@@ -133,32 +182,36 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t i = base + (int64_t)u * TK_THREADS;
-        if (i < n && (k[u] & mask) == prefix) atomicAdd(&hist[(k[u] >> shift) & 255u], 1u);
+        const bool hit = i < n && (k[u] & mask) == prefix;
+        const uint32_t bin = (k[u] >> shift) & (uint32_t)(nb - 1);
+        if (pass == 0) hist_add_aggregated(hist, bin, hit);
+        else if (hit) atomicAdd(&hist[bin], 1u);
       }
     }
     __syncthreads();
     uint32_t above;
-    const uint32_t d = find_digit(hist, 256, kk, above, sbuf, s_res);
+    const uint32_t d = find_digit(hist, nb, kk, above, sbuf, s_res);
     prefix |= d << shift;
-    mask |= 255u << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
     kk -= above;
   }
   const uint32_t T = prefix, keq = kk;
 
+  // in-order compaction: thread t owns keys [base + RUN*t, base + RUN*t + RUN)
   uint32_t run_gt = 0, run_eq = 0;
-  for (int64_t base = 0; base < n; base += TK_THREADS) {
-    const int64_t i = base + tid;
+  for (int64_t base = 0; base < n; base += CHUNK) {
+    const int64_t i0 = base + (int64_t)RUN * tid;
     uint32_t gt = 0, eq = 0;
-    if (i < n) {
+    for (int u = 0; u < RUN; ++u) {
+      const int64_t i = i0 + u;
+      if (i >= n) break;
       const uint32_t k = key_at(i);
-      gt = k > T;
-      eq = k == T;
+      gt += k > T;
+      eq += k == T;
     }
     uint32_t tot;
     const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sbuf);
-    const uint32_t gb = run_gt + (ex & 0xffffu), eb = run_eq + (ex >> 16);
-    if (gt) out[gb + min(eb, keq)] = (int32_t)i;
-    else if (eq && eb < keq) out[gb + eb] = (int32_t)i;
+    emit_run(key_at, i0, n, T, keq, run_gt + (ex & 0xffffu), run_eq + (ex >> 16), out);
     run_gt += tot & 0xffffu;
     run_eq += tot >> 16;
   }
@@ -168,7 +221,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(const float* __re
                                                                int32_t* __restrict__ idx, int64_t Tq,
                                                                int64_t N, int64_t q_pos0, int K) {
   __shared__ uint32_t skey[TK_CAP];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[HB];
   __shared__ uint32_t sbuf[TK_WAVES];
   __shared__ uint32_t s_res[2];
   const int64_t row = blockIdx.x;
@@ -208,134 +261,188 @@ size_t long_ws_bytes(int64_t R, int G, int K) {
          align_up((size_t)R * G * CAND_CAP * 8);
 }
 
-// Keys of this workgroup's segment, SEG_PER_T per thread (index seg0 + tid + 1024*u).
+// Keys of this workgroup's segment: thread t holds the run
+// [seg0 + RUN*t, seg0 + RUN*t + RUN), 16-byte loads when the row allows.
 __device__ __forceinline__ void load_segment(const float* __restrict__ src, int64_t seg0, int64_t n,
                                              uint32_t (&k)[SEG_PER_T]) {
+  const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && i0 + RUN <= n) {
 #pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u) {
-    const int64_t i = seg0 + threadIdx.x + (int64_t)u * TK_THREADS;
-    k[u] = i < n ? float_order_key(src[i]) : 0u;
+    for (int u = 0; u < SEG_PER_T / 4; ++u) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + i0 + 4 * u);
+      k[4 * u + 0] = float_order_key(v.x);
+      k[4 * u + 1] = float_order_key(v.y);
+      k[4 * u + 2] = float_order_key(v.z);
+      k[4 * u + 3] = float_order_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < SEG_PER_T; ++u) k[u] = i0 + u < n ? float_order_key(src[i0 + u]) : 0u;
   }
 }
 
-// hs[b] = sum over the row's nseg segment histograms h[seg][b].
+// hs[b] = sum over the row's nseg segment histograms h[seg][b]; loads are
+// issued eight segments at a time so their latencies overlap.
 __device__ __forceinline__ void sum_hist(const uint32_t* __restrict__ h, int nseg, uint32_t* hs) {
   for (int b = threadIdx.x; b < HB; b += TK_THREADS) {
     uint32_t s = 0;
-    for (int g = 0; g < nseg; ++g) s += h[(size_t)g * HB + b];
+    for (int g0 = 0; g0 < nseg; g0 += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = g0 + u < nseg ? h[(size_t)(g0 + u) * HB + b] : 0u;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
     hs[b] = s;
   }
   __syncthreads();
 }
 
+// Shared memory of the three segment steps.
+struct SegSmem {
+  uint32_t h[HB];
+  uint32_t hs[HB];
+  uint32_t sbuf[TK_WAVES];
+  uint32_t s_res[2];
+};
+
+// Step 1: histogram of key bits 31..21 of this segment.
+__device__ void seg_hist1(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t n, uint32_t* __restrict__ dst,
+                          SegSmem& sm) {
+  for (int b = threadIdx.x; b < HB; b += TK_THREADS) sm.h[b] = 0;
+  __syncthreads();
+  const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < SEG_PER_T; ++u) hist_add_aggregated(sm.h, k[u] >> 21, i0 + u < n);
+  __syncthreads();
+  for (int b = threadIdx.x; b < HB; b += TK_THREADS) dst[b] = sm.h[b];
+}
+
+// Step 2: digit 31..21 of T from the row's step-1 histograms, then a
+// histogram of bits 20..10 of this segment's keys that share it.
+__device__ void seg_hist2(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t n, int K, int nseg,
+                          const uint32_t* __restrict__ row_hist1, uint32_t* __restrict__ dst, SegSmem& sm) {
+  for (int b = threadIdx.x; b < HB; b += TK_THREADS) sm.h[b] = 0;
+  sum_hist(row_hist1, nseg, sm.hs);
+  uint32_t above;
+  const uint32_t d1 = find_digit(sm.hs, HB, (uint32_t)K, above, sm.sbuf, sm.s_res);
+  const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < SEG_PER_T; ++u)
+    if (i0 + u < n && (k[u] >> 21) == d1) atomicAdd(&sm.h[(k[u] >> 10) & (HB - 1)], 1u);
+  __syncthreads();
+  for (int b = threadIdx.x; b < HB; b += TK_THREADS) dst[b] = sm.h[b];
+}
+
+// Step 3: bits 31..10 of T, then this segment's keys above that prefix
+// (definite) and on it (candidates), in index order.
+__device__ void seg_classify(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t n, int K, int nseg,
+                             const uint32_t* __restrict__ row_hist1, const uint32_t* __restrict__ row_hist2,
+                             const LongWs& ws, size_t sidx, SegSmem& sm) {
+  uint32_t above;
+  sum_hist(row_hist1, nseg, sm.hs);
+  const uint32_t d1 = find_digit(sm.hs, HB, (uint32_t)K, above, sm.sbuf, sm.s_res);
+  const uint32_t kk1 = (uint32_t)K - above;
+  sum_hist(row_hist2, nseg, sm.hs);
+  const uint32_t d2 = find_digit(sm.hs, HB, kk1, above, sm.sbuf, sm.s_res);
+  const uint32_t p22 = (d1 << 11) | d2;
+
+  int32_t* defi = ws.defi + sidx * K;
+  uint2* cand = ws.cand + sidx * CAND_CAP;
+  const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
+  uint32_t nd = 0, nc = 0;
+#pragma unroll
+  for (int u = 0; u < SEG_PER_T; ++u) {
+    const bool valid = i0 + u < n;
+    nd += valid && (k[u] >> 10) > p22;
+    nc += valid && (k[u] >> 10) == p22;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan((nc << 16) | nd, tot, sm.sbuf);
+  uint32_t pd = ex & 0xffffu, pc = ex >> 16;
+#pragma unroll
+  for (int u = 0; u < SEG_PER_T; ++u) {
+    if (i0 + u >= n) break;
+    const uint32_t top = k[u] >> 10;
+    if (top > p22) defi[pd++] = (int32_t)(i0 + u);
+    else if (top == p22) {
+      if (pc < CAND_CAP) cand[pc] = make_uint2(k[u] & 1023u, (uint32_t)(i0 + u));
+      ++pc;
+    }
+  }
+  if (threadIdx.x == 0) {
+    ws.defc[sidx] = tot & 0xffffu;
+    ws.candc[sidx] = tot >> 16;
+  }
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_hist1(const float* __restrict__ scores, LongWs ws,
                                                              int64_t Tq, int64_t N, int64_t q_pos0, int K, int G) {
-  __shared__ uint32_t h[HB];
+  __shared__ SegSmem sm;
   const int64_t row = blockIdx.y;
   const int g = blockIdx.x;
   const int64_t n = n_visible(row, Tq, N, q_pos0);
   const int64_t seg0 = (int64_t)g * SEG;
   if (n <= K || seg0 >= n) return;
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) h[b] = 0;
   uint32_t k[SEG_PER_T];
   load_segment(scores + row * N, seg0, n, k);
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u)
-    if (seg0 + threadIdx.x + (int64_t)u * TK_THREADS < n) atomicAdd(&h[k[u] >> 21], 1u);
-  __syncthreads();
-  uint32_t* dst = ws.hist1 + ((size_t)row * G + g) * HB;
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) dst[b] = h[b];
+  seg_hist1(k, seg0, n, ws.hist1 + ((size_t)row * G + g) * HB, sm);
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_hist2(const float* __restrict__ scores, LongWs ws,
                                                              int64_t Tq, int64_t N, int64_t q_pos0, int K, int G) {
-  __shared__ uint32_t h[HB];
-  __shared__ uint32_t hs[HB];
-  __shared__ uint32_t sbuf[TK_WAVES];
-  __shared__ uint32_t s_res[2];
+  __shared__ SegSmem sm;
   const int64_t row = blockIdx.y;
   const int g = blockIdx.x;
   const int64_t n = n_visible(row, Tq, N, q_pos0);
   const int64_t seg0 = (int64_t)g * SEG;
   if (n <= K || seg0 >= n) return;
-  const int nseg = (int)((n + SEG - 1) / SEG);
   uint32_t k[SEG_PER_T];
   load_segment(scores + row * N, seg0, n, k);
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) h[b] = 0;
-  sum_hist(ws.hist1 + (size_t)row * G * HB, nseg, hs);
-  uint32_t above;
-  const uint32_t d1 = find_digit(hs, HB, (uint32_t)K, above, sbuf, s_res);
-#pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u)
-    if (seg0 + threadIdx.x + (int64_t)u * TK_THREADS < n && (k[u] >> 21) == d1)
-      atomicAdd(&h[(k[u] >> 10) & (HB - 1)], 1u);
-  __syncthreads();
-  uint32_t* dst = ws.hist2 + ((size_t)row * G + g) * HB;
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) dst[b] = h[b];
+  seg_hist2(k, seg0, n, K, (int)((n + SEG - 1) / SEG), ws.hist1 + (size_t)row * G * HB,
+            ws.hist2 + ((size_t)row * G + g) * HB, sm);
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __restrict__ scores, LongWs ws,
                                                                 int64_t Tq, int64_t N, int64_t q_pos0, int K,
                                                                 int G) {
-  __shared__ uint32_t hs[HB];
-  __shared__ uint32_t sbuf[TK_WAVES];
-  __shared__ uint32_t s_res[2];
+  __shared__ SegSmem sm;
   const int64_t row = blockIdx.y;
   const int g = blockIdx.x;
   const int64_t n = n_visible(row, Tq, N, q_pos0);
   const int64_t seg0 = (int64_t)g * SEG;
   if (n <= K || seg0 >= n) return;
-  const int nseg = (int)((n + SEG - 1) / SEG);
   uint32_t k[SEG_PER_T];
   load_segment(scores + row * N, seg0, n, k);
-  uint32_t above;
-  sum_hist(ws.hist1 + (size_t)row * G * HB, nseg, hs);
-  const uint32_t d1 = find_digit(hs, HB, (uint32_t)K, above, sbuf, s_res);
-  const uint32_t kk1 = (uint32_t)K - above;
-  sum_hist(ws.hist2 + (size_t)row * G * HB, nseg, hs);
-  const uint32_t d2 = find_digit(hs, HB, kk1, above, sbuf, s_res);
-  const uint32_t p22 = (d1 << 11) | d2;
-
-  const size_t sidx = (size_t)row * G + g;
-  int32_t* defi = ws.defi + sidx * K;
-  uint2* cand = ws.cand + sidx * CAND_CAP;
-  uint32_t run_def = 0, run_cand = 0;
-#pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u) {
-    const int64_t i = seg0 + threadIdx.x + (int64_t)u * TK_THREADS;
-    const bool valid = i < n;
-    const uint32_t top = k[u] >> 10;
-    const uint32_t isdef = valid && top > p22, iscand = valid && top == p22;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan((iscand << 16) | isdef, tot, sbuf);
-    if (isdef) defi[run_def + (ex & 0xffffu)] = (int32_t)i;
-    if (iscand) {
-      const uint32_t pos = run_cand + (ex >> 16);
-      if (pos < CAND_CAP) cand[pos] = make_uint2(k[u] & 1023u, (uint32_t)i);
-    }
-    run_def += tot & 0xffffu;
-    run_cand += tot >> 16;
-  }
-  if (threadIdx.x == 0) {
-    ws.defc[sidx] = run_def;
-    ws.candc[sidx] = run_cand;
-  }
+  seg_classify(k, seg0, n, K, (int)((n + SEG - 1) / SEG), ws.hist1 + (size_t)row * G * HB,
+               ws.hist2 + (size_t)row * G * HB, ws, (size_t)row * G + g, sm);
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __restrict__ scores, LongWs ws,
-                                                             int32_t* __restrict__ idx, int64_t Tq, int64_t N,
-                                                             int64_t q_pos0, int K, int G) {
-  __shared__ uint32_t ck[ROW_CAND_CAP];   // candidate low key bits, index order
-  __shared__ int32_t ci[ROW_CAND_CAP];    // candidate indices
-  __shared__ int32_t dl[LONG_MAX_K];      // definite indices, ascending
-  __shared__ int32_t sl[LONG_MAX_K];      // kept candidate indices, ascending
-  __shared__ uint32_t h[1024];
-  __shared__ uint32_t sbuf[TK_WAVES];
-  __shared__ uint32_t s_res[2];
-  __shared__ uint32_t s_off[2];
+// Shared memory of the final step.
+struct FinalSmem {
+  uint32_t ck[ROW_CAND_CAP];   // candidate low key bits, index order
+  int32_t ci[ROW_CAND_CAP];    // candidate indices
+  int32_t dl[LONG_MAX_K];      // definite indices, ascending
+  int32_t sl[LONG_MAX_K];      // kept candidate indices, ascending
+  uint32_t h[HB];              // 1024 bins here; 2048 in the fallback
+  uint32_t sbuf[TK_WAVES];
+  uint32_t s_res[2];
+  uint32_t s_doff[LONG_MAX_G + 1];
+  uint32_t s_coff[LONG_MAX_G + 1];
+};
+
+__device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws, int32_t* __restrict__ idx,
+                              int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, int K, int G, FinalSmem& sm) {
+  uint32_t* ck = sm.ck;
+  int32_t* ci = sm.ci;
+  int32_t* dl = sm.dl;
+  int32_t* sl = sm.sl;
+  uint32_t* h = sm.h;
+  uint32_t* sbuf = sm.sbuf;
+  uint32_t* s_res = sm.s_res;
+  uint32_t* s_doff = sm.s_doff;
+  uint32_t* s_coff = sm.s_coff;
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
   const int64_t n = n_visible(row, Tq, N, q_pos0);
   int32_t* out = idx + row * K;
   if (n <= K) {
@@ -344,31 +451,49 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __rest
   }
   const int nseg = (int)((n + SEG - 1) / SEG);
   const size_t s0 = (size_t)row * G;
-  uint32_t ndef = 0, ncand = 0;
-  bool overflow = false;
-  for (int g = 0; g < nseg; ++g) {
-    const uint32_t c = ws.candc[s0 + g];
-    overflow |= c > CAND_CAP;
-    ndef += ws.defc[s0 + g];
-    ncand += c;
+  // per-segment list offsets: exclusive prefix sums of the counts (nseg <= TK_THREADS)
+  {
+    const uint32_t dc = tid < nseg ? ws.defc[s0 + tid] : 0u;
+    const uint32_t cc = tid < nseg ? ws.candc[s0 + tid] : 0u;
+    uint32_t dtot, ctot, otot;
+    const uint32_t dex = block_excl_scan(dc, dtot, sbuf);
+    const uint32_t cex = block_excl_scan(cc, ctot, sbuf);
+    block_excl_scan(cc > CAND_CAP ? 1u : 0u, otot, sbuf);
+    if (tid < nseg) {
+      s_doff[tid] = dex;
+      s_coff[tid] = cex;
+    }
+    if (tid == 0) {
+      s_doff[nseg] = dtot;
+      s_coff[nseg] = otot ? 0xffffffffu : ctot;
+    }
+    __syncthreads();
   }
-  if (overflow || ncand > ROW_CAND_CAP) {
+  const uint32_t ndef = s_doff[nseg], ncand = s_coff[nseg];
+  if (ncand > ROW_CAND_CAP) {
     // many equal keys at the boundary: exact one-workgroup method over the whole row
     select_row(scores + row * N, n, K, out, nullptr, h, sbuf, s_res);
     return;
   }
-  // gather both lists in segment order (ascending index)
-  uint32_t doff = 0, coff = 0;
-  for (int g = 0; g < nseg; ++g) {
-    const uint32_t dc = ws.defc[s0 + g], cc = ws.candc[s0 + g];
-    for (uint32_t j = tid; j < dc; j += TK_THREADS) dl[doff + j] = ws.defi[(s0 + g) * K + j];
-    for (uint32_t j = tid; j < cc; j += TK_THREADS) {
-      const uint2 v = ws.cand[(s0 + g) * CAND_CAP + j];
-      ck[coff + j] = v.x;
-      ci[coff + j] = (int32_t)v.y;
+  // gather both lists in segment order (ascending index); every load independent
+  auto seg_of = [&](const uint32_t* off, uint32_t j) {
+    int lo = 0, hi = nseg;  // largest g with off[g] <= j
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= j) lo = mid;
+      else hi = mid;
     }
-    doff += dc;
-    coff += cc;
+    return lo;
+  };
+  for (uint32_t j = tid; j < ndef; j += TK_THREADS) {
+    const int g = seg_of(s_doff, j);
+    dl[j] = ws.defi[(s0 + g) * K + (j - s_doff[g])];
+  }
+  for (uint32_t j = tid; j < ncand; j += TK_THREADS) {
+    const int g = seg_of(s_coff, j);
+    const uint2 v = ws.cand[(s0 + g) * CAND_CAP + (j - s_coff[g])];
+    ck[j] = v.x;
+    ci[j] = (int32_t)v.y;
   }
   for (int b = tid; b < 1024; b += TK_THREADS) h[b] = 0;
   __syncthreads();
@@ -408,13 +533,19 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __rest
   };
   for (uint32_t j = tid; j < ndef; j += TK_THREADS) out[j + lower(sl, kk, dl[j])] = dl[j];
   for (uint32_t j = tid; j < kk; j += TK_THREADS) out[j + lower(dl, ndef, sl[j])] = sl[j];
-  (void)s_off;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __restrict__ scores, LongWs ws,
+                                                             int32_t* __restrict__ idx, int64_t Tq, int64_t N,
+                                                             int64_t q_pos0, int K, int G) {
+  __shared__ FinalSmem sm;
+  seg_final_row(scores, ws, idx, blockIdx.x, Tq, N, q_pos0, K, G, sm);
 }
 
 int long_segments(int64_t N) { return (int)((N + SEG - 1) / SEG); }
 
 bool use_long_path(int64_t B, int64_t Tq, int64_t N, int K) {
-  return N > TK_CAP && K <= LONG_MAX_K && B * Tq * long_segments(N) <= LONG_MAX_SEGS;
+  return N > TK_CAP && K <= LONG_MAX_K && long_segments(N) <= LONG_MAX_G && B * Tq * long_segments(N) <= LONG_MAX_SEGS;
 }
 
 }  // namespace

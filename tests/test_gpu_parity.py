@@ -162,6 +162,18 @@ def test_topk_long_rows_heavy_ties(kind):
         assert np.array_equal(idx[0, t], exp), f"{kind} row {t}"
 
 
+def test_topk_long_rows_many_rows():
+    """More segment workgroups than fit on the GPU at once (160 rows x 2 segments):
+    the segmented method runs as separate kernels instead of one cooperative one."""
+    dsa = _dsa()
+    rng = np.random.default_rng(9)
+    B, N, K = 160, 32768, 2048
+    vals = (rng.integers(0, 30000, size=(B, 1, N)) / 16).astype(np.float32)
+    idx = dsa.topk(torch.from_numpy(vals).cuda(), K, N - 1).cpu().numpy()
+    for b in range(0, B, 7):
+        assert np.array_equal(idx[b, 0], oracle.topk_row(vals[b, 0], K)), f"row {b}"
+
+
 def _mla_case(B, Tq, N, K, seed, n_masked=3, empty_row=False):
     wl = WL["sparse_mla_decode_b64_32k"].replace(B=B, Tq=Tq, N=N, K=K)
     x = {"q": synth.tensor(wl, "q", seed), "kv": synth.tensor(wl, "kv", seed)}
