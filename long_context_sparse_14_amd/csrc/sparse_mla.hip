@@ -7,21 +7,26 @@
 // the selected tokens only; DeepseekV32Config section: 128 heads,
 // kv_lora_rank 512 + qk_rope_head_dim 64.)
 //
-// bf16 kernel: one workgroup (8 waves, two per SIMD) per (query, split of
-// the index list, at most 2048 indices, staged once in LDS).  Each step
-// gathers 32 selected latent rows (1152 B each) straight into LDS with
-// direct-to-LDS 16-byte loads (no staging registers) into one of three tile
-// buffers, so two tiles' gathers (72 KiB) are in flight during the current
-// tile's math, and shares the rows across all 128 heads:
-//   * S^T = KV_tile . Q^T on 16x16x32 MFMAs: wave w owns heads [16w, 16w+16)
-//     and keeps their queries in registers (18 k-steps of 32 channels);
-//   * online softmax in fp32 with exp2 on log2e-prescaled logits; the four
-//     lanes that share a head reduce with two lane exchanges;
-//   * P (bf16) and the per-head rescale factors go through LDS, then
-//     O^T = V^T . P^T on 32x32x16 MFMAs: wave w owns value columns
-//     [64w, 64w+64) for all 128 heads (128 fp32 accumulators per lane), so
-//     every V element is read from LDS once per tile; rescaling is skipped when
-//     no head of a block changed its running max.
+// bf16 kernel: one workgroup (4 waves, one per SIMD, 512 registers each) per
+// (query, split of the index list, at most 2048 indices, staged once in
+// LDS).  Each step gathers 32 selected latent rows (1152 B each) straight into
+// LDS with direct-to-LDS 16-byte loads (no staging registers) into one of
+// three tile buffers, so two tiles' gathers (72 KiB) are in flight during the
+// current tile's math, and shares the rows across all 128 heads:
+//   * S^T = KV_tile . Q^T on 32x32x16 MFMAs: wave w owns heads [32w, 32w+32)
+//     and keeps their queries in registers (36 k-steps of 16 channels);
+//   * softmax in fp32 with exp2 on log2e-prescaled logits against a fixed
+//     per-head reference: the first non-empty tile's maximum.  The
+//     accumulators are therefore never rescaled (that would need all 256 of
+//     them in vector registers at once); should a later logit exceed the
+//     reference by more than 64 (log2 units), the split is recomputed with
+//     the true maximum as reference, so exp2 stays far below the fp32/bf16
+//     range in every case.  A lane owns one head (16 of its keys, the other
+//     16 in lane j^32);
+//   * P (bf16) goes through LDS, then O^T = V^T . P^T on 32x32x16 MFMAs:
+//     wave w owns value columns [128w, 128w+128) for all 128 heads (256 fp32
+//     accumulators per lane), so every V element is read from LDS once per
+//     tile.
 // The LDS tile is chunk-major: 16-byte chunk p (channels 8p..8p+7) of tile
 // row r sits at slot 32*p + (r ^ 4*(p & 3)).  A gather instruction fills 64
 // slots = two chunk columns, so every lane always fetches from the same latent
@@ -45,9 +50,10 @@ constexpr int MH = 128, MD = 576, MDV = 512, NT = 32;
 constexpr int ROW_CHUNKS = MD / 8;          // 72 chunks of 16 B per latent row
 constexpr int TILE_CHUNKS = NT * ROW_CHUNKS; // 2304
 constexpr int PP = NT + 8;                   // bf16 per LDS probability row
-constexpr int MLA_WAVES = 8;
+constexpr int MLA_WAVES = 4;
 constexpr int NBUF = 3;                      // latent tile buffers (two gathers in flight)
 constexpr int MAX_SPLIT_KEYS = 2048;         // indices handled by one workgroup
+constexpr int SLOOK = 9;                     // QK^T k-steps whose operands may be in flight
 constexpr int MLA_THREADS = MLA_WAVES * 64;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -96,13 +102,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   __shared__ __align__(16) int32_t vflag[NBUF][NT];      // row valid flags per buffer
   __shared__ __align__(16) int32_t sidx[MAX_SPLIT_KEYS];  // this split's index list
   __shared__ __align__(16) uint16_t ps[MH * PP];
-  __shared__ float alpha_s[MH];
   __shared__ float m_s[MH], l_s[MH];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lives in a scalar register
-  const int half = lane >> 5, col = lane & 31;   // 32x32 operand/result roles
-  const int g16 = lane >> 4, c16 = lane & 15;    // 16x16 operand/result roles
+  const int half = lane >> 5, col = lane & 31;
 
   // Work item.  When the rows split evenly over the 8 XCDs (workgroups are
   // dealt round-robin to them), all splits of a query run on one XCD so its
@@ -126,39 +130,35 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   const int nkeys = max(ke - kb, 0);
   const int ntiles = (nkeys + NT - 1) / NT;
 
-  // Queries of heads 16*wave + c16, channels 32*s + 8*g16 + [0, 8).
-  bf16x8 qf[MD / 32];
-  {
-    const uint16_t* qp = q + (r * MH + 16 * wave + c16) * (int64_t)MD + 8 * g16;
-#pragma unroll
-    for (int s = 0; s < MD / 32; ++s) qf[s] = load_bf16x8(qp + 32 * s);
-  }
+  // Indices first, then queries: the index loads are awaited while the
+  // query loads are still in flight.
   {
     const int32_t* ip = idx + r * K + kb;
     for (int j = tid; j < ntiles * NT; j += MLA_THREADS) sidx[j] = j < nkeys ? ip[j] : -1;
   }
-  f32x16 o[2][4];
+  // Queries of heads 32*wave + col, channels 16*s + 8*half + [0, 8).
+  bf16x8 qf[MD / 16];
+  {
+    const uint16_t* qp = q + (r * MH + 32 * wave + col) * (int64_t)MD + 8 * half;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int s = 0; s < MD / 16; ++s) qf[s] = load_bf16x8(qp + 16 * s);
+  }
+  f32x16 o[4][4];
+  float m_ref = -INFINITY;  // exponent reference of this lane's head (log2 units)
+  float m_max = -INFINITY;  // largest logit seen
+  float l_run = 0.f;
   const uint16_t* kvb = kv + b * N * (int64_t)MD;
-  // Queries and indices are in place; from here on the only memory loads in
-  // flight are the gathers below, which the compiler does not see.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  sync_lds();
 
   // Gather of tile `it`: instruction u of wave w fills slots [64*ii, 64*ii+64)
-  // of the tile, ii = w + 8u (36 instructions in all): chunk columns 2*ii and
-  // 2*ii+1, rows 0..31.  Lane l always fetches row l%32, chunk 2*ii + l/32.
-  // Waves 0-3 issue 5 instructions per tile, waves 4-7 issue 4.
-  constexpr int GU = (TILE_CHUNKS / 64 + MLA_WAVES - 1) / MLA_WAVES;  // 5
-  // Slot 32*p + s of the tile holds row s ^ 4*(p & 3); for this wave's
-  // instructions p = 2*ii + lane/32 with ii = wave + 8u, so p & 3 is fixed.
+  // of the tile, ii = w + 4u (36 instructions, 9 per wave): chunk columns 2*ii
+  // and 2*ii+1.  Slot 32*p + s holds row s ^ 4*(p & 3); for this wave's
+  // instructions p = 2*ii + lane/32 and p & 3 is fixed.
+  constexpr int GU = TILE_CHUNKS / 64 / MLA_WAVES;  // 9
+  static_assert(GU * 64 * MLA_WAVES == TILE_CHUNKS && GU == 9, "gather instructions per wave");
   const int grow = (lane & 31) ^ (4 * ((2 * (wave & 1) + (lane >> 5)) & 3));
-  // byte address of chunk 2*ii + lane/32 of row v: kvw + [v*1152 + 16*(lane/32)] + 256*u,
-  // with kvw = this sequence's cache + 32*wave (scalar) and ii = wave + 8u
+  // byte address of chunk 2*ii + lane/32 of row v: kvw + [v*1152 + 16*(lane/32)] + 128*u,
+  // with kvw = this sequence's cache + 32*wave (scalar) and ii = wave + 4u
   const uint8_t* kvw = reinterpret_cast<const uint8_t*>(kvb) + 32 * wave;
   auto gather = [&](int it) {
     const int buf = it % NBUF;
@@ -166,141 +166,138 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     const bool ok = v >= 0 && (int64_t)v < N;
     const uint32_t voff = (uint32_t)(ok ? v : 0) * (uint32_t)(MD * 2) + 16u * (uint32_t)(lane >> 5);
     const uint32_t lds0 = lds_address(&kvs[buf][512 * wave]);
-    dma16(kvw, voff, lds0);
-    dma16(kvw + 256, voff, lds0 + 8192);
-    dma16(kvw + 512, voff, lds0 + 16384);
-    dma16(kvw + 768, voff, lds0 + 24576);
-    if (wave + 4 * MLA_WAVES < TILE_CHUNKS / 64) dma16(kvw + 1024, voff, lds0 + 32768);
+#pragma unroll
+    for (int u = 0; u < GU; ++u) dma16(kvw + 128 * u, voff, lds0 + 4096 * u);
     if (wave == 0 && lane < 32) vflag[buf][grow] = ok;  // wave 0, lanes 0..31: row == lane
   };
   // Wait until this wave's gathers of all but the most recently issued tile
   // are complete (vmcnt counts this wave's loads, oldest first).
   auto wait_all_but_newest = [&](bool newest_in_flight) {
-    if (!newest_in_flight) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (wave < TILE_CHUNKS / 64 - (GU - 1) * MLA_WAVES) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    if (newest_in_flight) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  static_assert(GU == 5 && TILE_CHUNKS / 64 - (GU - 1) * MLA_WAVES == 4, "per-wave gather counts");
 
-  // QK^T operand: key row 16*kb2 + c16, chunk p = 4*s + g16 (p & 3 == g16)
-  //   -> slot 32*p + 16*kb2 + (c16 ^ 4*g16)   [bf16 element = 8 * slot]
-  const int abase = 256 * g16 + 8 * (c16 ^ (4 * g16));
+  // QK^T operand (A): key row col, channels 16*s + 8*half + e, i.e. chunk
+  // p = 2s + half, p & 3 = 2*(s & 1) + half  ->  slot 32p + (col ^ 4*(p & 3)).
+  int abase[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) abase[par] = 256 * half + 8 * (col ^ (4 * ((2 * par + half) & 3)));
   // PV operand, read rd (keys 4rd..4rd+3 of this lane half) of block (ks, mb):
   // 16-lane group G = lane/16, source lane j = lane%16 addresses key
-  // 16*ks + 8*half + 4*rd + j/4, value columns 64*wave + 32*mb + 16*(G&1) + 4*(j&3) + [0,4),
-  // i.e. chunk p = 8*wave + 4*mb + 2*(G&1) + (j&3)/2, byte 8*(j&1) of it.
+  // 16*ks + 8*half + 4*rd + j/4, value columns 128*wave + 32*mb + 16*(G&1) + 4*(j&3) + [0,4),
+  // i.e. chunk p = 16*wave + 4*mb + 2*(G&1) + (j&3)/2, byte 8*(j&1) of it.
   int vbase[2];
   {
-    const int G = lane >> 4, j = lane & 15, b = (j & 3) >> 1;
-    const int pl = 2 * (G & 1) + b;  // chunk offset within the 4-chunk group (p & 3)
+    const int G = lane >> 4, j = lane & 15, bq = (j & 3) >> 1;
+    const int pl = 2 * (G & 1) + bq;  // p & 3
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
-      const int key = 8 * half + 4 * rd + (j >> 2);              // + 16*ks (compile-time)
-      vbase[rd] = 256 * (8 * wave + pl) + 8 * (key ^ (4 * pl)) + 4 * (j & 1);
+      const int key = 8 * half + 4 * rd + (j >> 2);  // + 16*ks (compile-time)
+      vbase[rd] = 256 * (16 * wave + pl) + 8 * (key ^ (4 * pl)) + 4 * (j & 1);
     }
   }
 
+  for (int pass = 0; pass < 2; ++pass) {
+  if (pass == 1) {
+    // a logit ran more than 64 above its reference in some head: redo the
+    // split with the true maximum as reference (never the case for ordinary data)
+    m_ref = m_max;
+    l_run = 0.f;
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
+  bool overflow = false;
   if (ntiles > 0) gather(0);
   if (ntiles > 1) gather(1);
-  wait_all_but_newest(ntiles > 1);
+  // queries and tiles 0 (and 1) in place; the compiler now sees no load in flight
+  __builtin_amdgcn_s_waitcnt(0);
   sync_lds();
   for (int it = 0; it < ntiles; ++it) {
     const uint16_t* cur = kvs[it % NBUF];
     const int32_t* vcur = vflag[it % NBUF];
     if (it + 2 < ntiles) gather(it + 2);
 
-    // S^T[key][head] for this wave's 16 heads, keys in two blocks of 16.
-    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    // S^T[key][head] for this wave's 32 heads.
+    f32x16 sacc = {};
 #pragma unroll
-    for (int s = 0; s < MD / 32; ++s) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(cur + abase + 1024 * s + 128 * kb2);  // p = 4s + g16
-        sacc[kb2] = mfma16x16x32(av, qf[s], sacc[kb2]);
-      }
-      if ((s & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < MD / 16; ++s) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(cur + abase[s & 1] + 512 * s);
+      sacc = mfma32x32x16(av, qf[s], sacc);
+      if (s % SLOOK == SLOOK - 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand reads in flight
     }
 
-    // Online softmax; this lane holds head 16*wave+c16, keys 16*kb2 + 4*g16 + i.
-    float x[8];
+    // Online softmax; this lane holds head 32*wave+col, keys mfma_row(i, half).
+    float x[16];
     float mt = -INFINITY;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int4 vf = *reinterpret_cast<const int4*>(&vcur[16 * kb2 + 4 * g16]);
+    for (int a = 0; a < 4; ++a) {
+      const int4 vf = *reinterpret_cast<const int4*>(&vcur[8 * a + 4 * half]);
       const int fl[4] = {vf.x, vf.y, vf.z, vf.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[4 * kb2 + i] = fl[i] ? sacc[kb2][i] * scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[4 * kb2 + i]);
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * a + c;
+        x[i] = fl[c] ? sacc[i] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[i]);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    float alpha = 1.f, lsum = 0.f;
-    if (m_new == -INFINITY) {
+    m_max = fmaxf(m_max, mt);
+    if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated yet: start the reference here
+    overflow |= mt > m_ref + 64.f;
+    float lsum = 0.f;
+    if (m_ref == -INFINITY) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = 0.f;
     } else {
-      alpha = exp2f(m_run - m_new);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[i] = exp2f(x[i] - m_new);
+      for (int i = 0; i < 16; ++i) {
+        x[i] = exp2f(x[i] - m_ref);
         lsum += x[i];
       }
     }
-    lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
+    l_run += lsum;
     {
-      uint16_t* pp = &ps[(16 * wave + c16) * PP + 4 * g16];
+      uint16_t* pp = &ps[(32 * wave + col) * PP + 4 * half];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int a = 0; a < 4; ++a) {
         u32x2 pk;
-        pk.x = float_to_bf16_bits(x[4 * kb2 + 0]) | (float_to_bf16_bits(x[4 * kb2 + 1]) << 16);
-        pk.y = float_to_bf16_bits(x[4 * kb2 + 2]) | (float_to_bf16_bits(x[4 * kb2 + 3]) << 16);
-        *reinterpret_cast<u32x2*>(pp + 16 * kb2) = pk;
+        pk.x = float_to_bf16_bits(x[4 * a + 0]) | (float_to_bf16_bits(x[4 * a + 1]) << 16);
+        pk.y = float_to_bf16_bits(x[4 * a + 2]) | (float_to_bf16_bits(x[4 * a + 3]) << 16);
+        *reinterpret_cast<u32x2*>(pp + 8 * a) = pk;
       }
-      if (g16 == 0) alpha_s[16 * wave + c16] = alpha;
     }
     sync_lds();
 
-    // O^T[dv][head] += V^T . P^T for dv in [64*wave, 64*wave+64), all heads.
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const float an = alpha_s[32 * nb + col];
-      if (__any(an != 1.f)) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) o[mb][nb] *= an;
-      }
-    }
+    // O^T[dv][head] += V^T . P^T for dv in [128*wave, 128*wave+128), all heads.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 av[2];
+      bf16x8 pb[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int nb = 0; nb < 4; ++nb)
+        pb[nb] = *reinterpret_cast<const bf16x8*>(&ps[(32 * nb + col) * PP + 16 * ks + 8 * half]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
         // 16*ks rows and 4*mb chunks: slot += 16*ks + 128*mb (the XOR term is unchanged)
         const s16x4 lo = lds_read_tr16(cur + vbase[0] + 1024 * mb + 128 * ks);
         const s16x4 hi = lds_read_tr16(cur + vbase[1] + 1024 * mb + 128 * ks);
-        av[mb] = __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
-      }
+        const bf16x8 av = __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8 pb = *reinterpret_cast<const bf16x8*>(&ps[(32 * nb + col) * PP + 16 * ks + 8 * half]);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) o[mb][nb] = mfma32x32x16(av[mb], pb, o[mb][nb]);
+        for (int nb = 0; nb < 4; ++nb) o[mb][nb] = mfma32x32x16(av, pb[nb], o[mb][nb]);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     // tile it+1 must have landed; tile it+2 may stay in flight
     wait_all_but_newest(it + 2 < ntiles);
     sync_lds();
   }
+  if (!__syncthreads_or(overflow)) break;
+  }
 
-  if (g16 == 0) {
-    l_s[16 * wave + c16] = l_run;
-    m_s[16 * wave + c16] = m_run;
+  if (half == 0) {
+    l_s[32 * wave + col] = l_run;
+    m_s[32 * wave + col] = m_ref;
   }
   sync_lds();
 #pragma unroll
@@ -309,10 +306,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     const float l = l_s[h], m = m_s[h];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
+    // one accumulator block at a time (keeps the vector registers this needs small)
     if (splits == 1) {
-      uint16_t* op = out + (r * MH + h) * (int64_t)MDV + 64 * wave + 4 * half;
+      uint16_t* op = out + (r * MH + h) * (int64_t)MDV + 128 * wave + 4 * half;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const f32x16& v = o[mb][nb];
@@ -321,17 +320,20 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
           pk.y = float_to_bf16_bits(v[4 * a + 2] * inv) | (float_to_bf16_bits(v[4 * a + 3] * inv) << 16);
           *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * a) = pk;
         }
+      }
       if (lse != nullptr && wave == 0 && half == 0) lse[r * MH + h] = lse2 * LN2;
     } else {
-      float* po = part_o + (((int64_t)sp * R + r) * MH + h) * MDV + 64 * wave + 4 * half;
+      float* po = part_o + (((int64_t)sp * R + r) * MH + h) * MDV + 128 * wave + 4 * half;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const f32x16& v = o[mb][nb];
           f32x4 st = {v[4 * a + 0] * inv, v[4 * a + 1] * inv, v[4 * a + 2] * inv, v[4 * a + 3] * inv};
           *reinterpret_cast<f32x4*>(po + 32 * mb + 8 * a) = st;
         }
+      }
       if (wave == 0 && half == 0) part_lse[((int64_t)sp * R + r) * MH + h] = lse2;
     }
   }
