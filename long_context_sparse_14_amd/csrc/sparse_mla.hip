@@ -52,8 +52,9 @@ constexpr int TILE_CHUNKS = NT * ROW_CHUNKS; // 2304
 constexpr int PP = NT + 8;                   // bf16 per LDS probability row
 constexpr int MLA_WAVES = 4;
 constexpr int NBUF = 3;                      // latent tile buffers (two gathers in flight)
+constexpr int SLOOK = 6;                     // QK^T key-operand reads in flight
+constexpr int PVLOOK = 2;                    // PV value-operand reads in flight
 constexpr int MAX_SPLIT_KEYS = 2048;         // indices handled by one workgroup
-constexpr int SLOOK = 9;                     // QK^T k-steps whose operands may be in flight
 constexpr int MLA_THREADS = MLA_WAVES * 64;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -66,8 +67,29 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
 }
 
-__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// QK^T MFMAs with their accumulators in ordinary vector registers.  The
+// 256 output accumulators of a wave fill the accumulation registers, so the
+// logits must live in vector registers; builtin MFMAs would place them in
+// accumulation registers and force copies.  The compiler does not look into
+// these statements, so each one carries the wait states it needs: two before
+// the MFMA (a vector write of an operand just before it), and, after the last
+// MFMA of the chain, more than the 19 that any read of an MFMA result needs.
+// Between MFMAs of one chain (source C = destination, same shape) the
+// hardware forwards the accumulator and needs none.
+__device__ __forceinline__ f32x16 mfma_s_first(bf16x8 a, bf16x8 b) {
+  f32x16 c;
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  return c;
+}
+__device__ __forceinline__ void mfma_s(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_last2(f32x16& c0, bf16x8 a0, bf16x8 b0, f32x16& c1, bf16x8 a1, bf16x8 b1) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(c0), "+v"(c1)
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
 
 // 16-byte direct-to-LDS load: every lane reads 16 B at base + voff and the
@@ -219,13 +241,37 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     const int32_t* vcur = vflag[it % NBUF];
     if (it + 2 < ntiles) gather(it + 2);
 
-    // S^T[key][head] for this wave's 32 heads.
-    f32x16 sacc = {};
+    // S^T[key][head] for this wave's 32 heads: two independent accumulation
+    // chains (even and odd k-steps) so that consecutive MFMAs do not wait for
+    // each other.
+    // The key operands stream through a ring of SLOOK registers, each read
+    // issued SLOOK k-steps ahead of its MFMA; the scheduling barriers keep the
+    // compiler from collapsing the ring.
+    f32x16 sacc;
+    {
+      constexpr int KS = MD / 16;
+      auto aop = [&](int s) { return *reinterpret_cast<const bf16x8*>(cur + abase[s & 1] + 512 * s); };
+      bf16x8 ring[SLOOK];
 #pragma unroll
-    for (int s = 0; s < MD / 16; ++s) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(cur + abase[s & 1] + 512 * s);
-      sacc = mfma32x32x16(av, qf[s], sacc);
-      if (s % SLOOK == SLOOK - 1) __builtin_amdgcn_sched_barrier(0);  // bound the operand reads in flight
+      for (int s = 0; s < SLOOK; ++s) ring[s] = aop(s);
+      f32x16 s0, s1;
+#pragma unroll
+      for (int s = 0; s < KS; s += 2) {
+        const bf16x8 a0 = ring[s % SLOOK], a1 = ring[(s + 1) % SLOOK];
+        if (s + SLOOK < KS) ring[s % SLOOK] = aop(s + SLOOK);
+        if (s + 1 + SLOOK < KS) ring[(s + 1) % SLOOK] = aop(s + 1 + SLOOK);
+        if (s == 0) {
+          s0 = mfma_s_first(a0, qf[0]);
+          s1 = mfma_s_first(a1, qf[1]);
+        } else if (s + 2 < KS) {
+          mfma_s(s0, a0, qf[s]);
+          mfma_s(s1, a1, qf[s + 1]);
+        } else {
+          mfma_s_last2(s0, a0, qf[s], s1, a1, qf[s + 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sacc = s0 + s1;
     }
 
     // Online softmax; this lane holds head 32*wave+col, keys mfma_row(i, half).
@@ -272,20 +318,33 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     sync_lds();
 
     // O^T[dv][head] += V^T . P^T for dv in [128*wave, 128*wave+128), all heads.
+    // Eight steps (ks, mb); the value operand of step st+PVLOOK is read
+    // while step st runs its four MFMAs.
+    {
+      bf16x8 pb[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pb[4];
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        pb[nb] = *reinterpret_cast<const bf16x8*>(&ps[(32 * nb + col) * PP + 16 * ks + 8 * half]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+        for (int nb = 0; nb < 4; ++nb)
+          pb[ks][nb] = *reinterpret_cast<const bf16x8*>(&ps[(32 * nb + col) * PP + 16 * ks + 8 * half]);
+      auto vop = [&](int st) {
         // 16*ks rows and 4*mb chunks: slot += 16*ks + 128*mb (the XOR term is unchanged)
+        const int ks = st >> 2, mb = st & 3;
         const s16x4 lo = lds_read_tr16(cur + vbase[0] + 1024 * mb + 128 * ks);
         const s16x4 hi = lds_read_tr16(cur + vbase[1] + 1024 * mb + 128 * ks);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+        return __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+      };
+      bf16x8 vring[PVLOOK];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) o[mb][nb] = mfma32x32x16(av, pb[nb], o[mb][nb]);
+      for (int st = 0; st < PVLOOK; ++st) vring[st] = vop(st);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int ks = st >> 2, mb = st & 3;
+        const bf16x8 av = vring[st % PVLOOK];
+        if (st + PVLOOK < 8) vring[st % PVLOOK] = vop(st + PVLOOK);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) o[mb][nb] = mfma32x32x16(av, pb[ks][nb], o[mb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // tile it+1 must have landed; tile it+2 may stay in flight
