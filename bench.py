@@ -13,6 +13,9 @@ of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --calib-copy     (plain 1 GiB device copy, for counter scaling)
+  python bench.py --record-traffic --workload NAME --pmc-fetch F.csv --pmc-write W.csv
+                  --calib-fetch CF.csv --calib-write CW.csv --commands "..."
+                                   (store the dominant kernel's HBM bytes per launch)
 """
 from __future__ import annotations
 
@@ -44,30 +47,112 @@ def _parse():
     ap.add_argument("--fused", action="store_true",
                     help="time the single dsa_forward call (no per-stage events)")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--record-traffic", action="store_true",
+                    help="store the dominant kernel's HBM traffic from four rocprofv3 -f csv counter files")
+    ap.add_argument("--pmc-fetch")
+    ap.add_argument("--pmc-write")
+    ap.add_argument("--calib-fetch")
+    ap.add_argument("--calib-write")
+    ap.add_argument("--commands", default="", help="the rocprofv3 command lines, recorded with the traffic")
     return ap.parse_args()
 
 
-def kernel_sources_digest() -> str:
-    """Digest of the HIP sources; stored counter readings are only valid for it."""
+# Source files each timed kernel is built from: stored counter readings stay
+# valid until one of them changes.
+KERNEL_SOURCES = {
+    "indexer_stream_bf16": ["indexer.hip", "device_common.h"],
+    "indexer_tiled_bf16": ["indexer.hip", "device_common.h"],
+    "sparse_mla_bf16_kernel": ["sparse_mla.hip", "device_common.h"],
+}
+
+
+def kernel_sources_digest(kernel: str) -> str:
+    """Digest of the HIP sources of one kernel."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_sparse_14_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload: str, kernel: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+
+
 def stored_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the rocprofv3 counter passes kept under profiles/,
-    if they were taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if they were taken on the current sources of that kernel."""
+    path = traffic_path(workload, kernel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sources_digest") != kernel_sources_digest():
+    if rec.get("kernel_sources_digest") != kernel_sources_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _pmc_rows(csv_path: str, counter: str):
+    """(kernel name, value) per dispatch for one counter of a rocprofv3 -f csv
+    counter_collection file."""
+    import csv
+    out = []
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                out.append((row.get("Kernel_Name", ""), float(row["Counter_Value"])))
+    if not out:
+        raise SystemExit(f"{csv_path}: no {counter} rows")
+    return out
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def record_traffic(args):
+    """Turn four counter passes (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, over
+    this benchmark and over the plain-copy calibration) into the stored HBM
+    traffic of the dominant kernel."""
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    _, kname, _, work, wunit = dominant_stage(wl)
+    calib_bytes = 1 << 30
+
+    def per_dispatch(csv_path, counter, name_part):
+        vals = [v * 1024.0 for k, v in _pmc_rows(csv_path, counter) if name_part in k]
+        if not vals:
+            raise SystemExit(f"{csv_path}: no dispatch of a kernel matching {name_part!r}")
+        return _median(vals), len(vals)
+
+    cf, _ = per_dispatch(args.calib_fetch, "FETCH_SIZE", "copy")
+    cw, _ = per_dispatch(args.calib_write, "WRITE_SIZE", "copy")
+    kf, nf = per_dispatch(args.pmc_fetch, "FETCH_SIZE", kname)
+    kw, nw = per_dispatch(args.pmc_write, "WRITE_SIZE", kname)
+    f_scale, w_scale = calib_bytes / cf, calib_bytes / cw
+    rec = {
+        "workload": wl.name,
+        "kernel": kname,
+        "kernel_sources_digest": kernel_sources_digest(kname),
+        "fetch_bytes_per_launch_raw": kf,
+        "write_bytes_per_launch_raw": kw,
+        "calib_copy_bytes": calib_bytes,
+        "calib_fetch_bytes_raw": cf,
+        "calib_write_bytes_raw": cw,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "hbm_bytes_per_launch": round(kf * f_scale + kw * w_scale),
+        "algorithmic_work_per_launch": int(work),
+        "algorithmic_unit": wunit,
+        "dispatches": {"fetch": nf, "write": nw},
+        "commands": args.commands,
+    }
+    with open(traffic_path(wl.name, kname), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def dominant_stage(wl):
@@ -145,6 +230,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the batch shards by sequence with no "
               f"exchange, so per-GPU throughput is the one-GPU figure.", file=sys.stderr)
         sys.exit(2)
+    if args.record_traffic:
+        record_traffic(args)
+        return
     import numpy as np
     import torch
 
