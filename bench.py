@@ -60,7 +60,7 @@ def _parse():
 # Source files each timed kernel is built from: stored counter readings stay
 # valid until one of them changes.
 KERNEL_SOURCES = {
-    "indexer_stream_bf16": ["indexer.hip", "device_common.h"],
+    "indexer_dma_bf16": ["indexer.hip", "device_common.h"],
     "indexer_tiled_bf16": ["indexer.hip", "device_common.h"],
     "sparse_mla_bf16_kernel": ["sparse_mla.hip", "device_common.h"],
 }
@@ -168,7 +168,7 @@ def dominant_stage(wl):
     if "index" in wl.stages and Tq <= 4:
         # decode indexer: each visible key row (256 B) read once, its fp32 score written once
         nbytes = B * N * wl.D_I * 2 + keys * 4 + B * Tq * wl.H_I * (wl.D_I + 1) * 2
-        return "index", "indexer_stream_bf16", "hbm", nbytes, "B"
+        return "index", "indexer_dma_bf16", "hbm", nbytes, "B"
     if "index" in wl.stages:
         flops = 2 * wl.H_I * wl.D_I * keys
         return "index", "indexer_tiled_bf16", "mfma", flops, "flop"

@@ -47,4 +47,24 @@ __device__ __forceinline__ uint32_t float_order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// 16-byte direct-to-LDS load: every lane reads 16 B at base + voff and the
+// wave writes them to LDS bytes [lds_addr + 16*lane, +16).  base is
+// wave-uniform (scalar registers), voff a 32-bit per-lane byte offset; the
+// instruction offset stays 0 because it would move the LDS destination too.
+// Written as inline asm so that the compiler does not track it: otherwise it
+// cannot tell that reads of one LDS buffer do not alias loads into another and
+// waits for them before every read.  The instruction has no register result;
+// its completion is awaited explicitly with vmcnt, which counts it like any
+// other vector memory load of the wave.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(lds_addr), "s"(base)
+               : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  typedef const __attribute__((address_space(3))) char* lds_ptr;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p));
+}
+
 }  // namespace dsa

@@ -15,10 +15,10 @@
 // 128 channels is free, so lane half h takes channels [64h, 64h+64): every
 // lane then reads 128 contiguous bytes of its key row, for q and k alike.
 //
-//  * stream kernel (few queries per sequence, i.e. decode): the key cache is
-//    read once from HBM straight into MFMA operand registers, one 8 KiB tile of
-//    32 keys per wave step, with the next two tiles' loads in flight while the
-//    current one is multiplied;
+//  * decode kernel (few queries per sequence): the key cache is read once
+//    from HBM into per-wave LDS rings with direct-to-LDS loads of 1 KiB of
+//    consecutive bytes each, three 8 KiB tiles of 32 keys in flight per wave,
+//    and the scores leave in one burst per workgroup;
 //  * tiled kernel (prefill): 8 queries per workgroup (one per wave) share
 //    64-key tiles staged in LDS, double-buffered; the causal triangle is
 //    walked longest query block first.
@@ -63,52 +63,114 @@ __device__ __forceinline__ float weighted_relu_sum(const QFrags& f, const f32x16
   return part + __shfl_xor(part, 32);
 }
 
-template <int WAVES, int TPW>
-__global__ __launch_bounds__(WAVES * 64) void indexer_stream_bf16(
+// Decode kernel with the key tiles staged through LDS.  A wave owns a ring
+// of NBUF tiles of 32 keys (8 KiB) in LDS and keeps NBUF-1 of them in flight
+// with direct-to-LDS loads.  Each load instruction fetches 1 KiB of
+// consecutive cache bytes (four key rows), which the memory system serves at
+// the full streaming rate; loading the MFMA operands straight from global
+// memory would touch a different 128-byte line in every lane.  No other wave
+// touches a wave's ring, so the key loop has no barriers.  The workgroup's
+// scores (at most SCAP) collect in LDS and leave in one contiguous burst at
+// the end: small score writes spread through the key stream cost the read
+// stream far more than their own bytes.
+//
+// Tile layout: lane L of load u (0..7) of a tile fetches 16-byte chunk
+// c = (L & 15) ^ (key & 15) of key 4u + L/16 and lands at slot 64u + L, i.e.
+// chunk c of tile key r sits at slot 16r + (c ^ (r & 15)).  The operand read
+// of k-step s (chunk 8*half + s of key col) then spreads every 16 lanes over
+// all 64 banks.
+template <int WAVES, int NBUF, int SCAP>
+__global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
-    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0) {
+    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, int64_t keys_per_wg) {
+  constexpr int TILE_BYTES = 32 * ID * 2;
+  static_assert(NBUF >= 2 && NBUF <= 5, "the vmcnt waits below cover up to four tiles in flight");
+  static_assert(WAVES * NBUF * TILE_BYTES + SCAP * 4 <= 160 * 1024, "LDS budget");
+  __shared__ __align__(16) uint16_t kt[WAVES][NBUF][32 * ID];
+  __shared__ __align__(16) float sl[SCAP];  // this workgroup's scores; keys_per_wg <= SCAP
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int64_t t = blockIdx.y, b = blockIdx.z;
   const int64_t row = b * Tq + t;
   const int64_t n_valid = min(N, q_pos0 + t + 1);
-  const int64_t k_begin = (int64_t)blockIdx.x * (WAVES * TPW * 32);
-  if (k_begin >= n_valid) return;
+  const int64_t k_begin = (int64_t)blockIdx.x * keys_per_wg;  // a multiple of 32
+  const int64_t k_end = min(n_valid, k_begin + keys_per_wg);
+  if (k_begin >= k_end) return;
+  const int total_tiles = (int)((k_end - k_begin + 31) / 32);
+  const int nt = total_tiles > wave ? (total_tiles - wave + WAVES - 1) / WAVES : 0;
 
-  QFrags f;
-  load_query(f, q_idx, w, row, half, col);
-  const uint16_t* kb = k_idx + b * N * ID + 64 * half;
-  float* sr = scores + row * N;
-
-  // Three register buffers: the keys of tiles it+1 and it+2 are in flight
-  // while tile it is multiplied (two 8 KiB tiles per wave, 128 KiB per CU).
-  bf16x8 buf[3][8];
-  auto tile_key = [&](int it) -> int64_t { return k_begin + (int64_t)(it * WAVES + wave) * 32; };
-  auto fetch = [&](bf16x8 (&dst)[8], int it) {
-    const int64_t k0 = tile_key(it);
-    if (it < TPW && k0 < n_valid) {
-      const int64_t key = min(k0 + col, n_valid - 1);
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(k_idx + b * N * ID);
+  const uint32_t ring = lds_address(&kt[wave][0][0]);
+  // per-lane part of the source offset of load u, for u & 3 (the XOR term repeats every 4 loads)
+  const int kk = lane >> 4, jj = lane & 15;
+  uint32_t voff[4];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) dst[s] = load_bf16x8(kb + key * ID + 8 * s);
+  for (int v = 0; v < 4; ++v) voff[v] = 256u * kk + 16u * (uint32_t)(jj ^ (4 * v + kk));
+  auto key0_of = [&](int it) { return k_begin + 32 * (int64_t)(it * WAVES + wave); };
+  auto dma_tile = [&](int it) {
+    const int64_t key0 = key0_of(it);
+    const uint32_t dst = ring + (uint32_t)((it % NBUF) * TILE_BYTES);
+    if (key0 + 32 <= N) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dma16(kb + (key0 + 4 * u) * (ID * 2), voff[u & 3], dst + 1024u * u);
+    } else {
+      // last rows of the cache: clamp to a real row (those keys are never scored)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t kbase = min(key0 + 4 * u, N - 1);
+        const int64_t key = min(key0 + 4 * u + kk, N - 1);
+        const uint32_t off = (uint32_t)(key - kbase) * 256u + (voff[u & 3] & 255u);
+        dma16(kb + kbase * (ID * 2), off, dst + 1024u * u);
+      }
     }
   };
-  fetch(buf[0], 0);
-  fetch(buf[1], 1);
+  QFrags f;
+  load_query(f, q_idx, w, row, half, col);
+  __builtin_amdgcn_sched_barrier(0);  // query loads first, so one wait covers them and the first tiles
 #pragma unroll
-  for (int it = 0; it < TPW; ++it) {
-    fetch(buf[(it + 2) % 3], it + 2);
-    const int64_t k0 = tile_key(it);
-    if (k0 < n_valid) {
-      f32x16 c0 = {}, c1 = {};
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nt) dma_tile(p);
+  // queries in registers and the first tiles in LDS; the compiler now sees no load in flight
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // operand read of k-step s: chunk 8*half + s of key col
+  const uint32_t rbase = 256u * col;
+  const int x = (8 * half) ^ (col & 15);
+  float* sr = scores + row * N;
+  for (int it = 0; it < nt; ++it) {
+    if (it + NBUF - 1 < nt) dma_tile(it + NBUF - 1);
+    // loads issued after tile it's: those of the next min(NBUF-1, nt-1-it) tiles
+    // (score stores in between only make the wait longer)
+    const int after = min(NBUF - 1, nt - 1 - it);
+    if (after >= 4) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    else if (after == 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (after == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (after == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint16_t* tile = &kt[wave][it % NBUF][0];
+    f32x16 c0 = {}, c1 = {};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        c0 = mfma32x32x16(f.a0[s], buf[it % 3][s], c0);
-        c1 = mfma32x32x16(f.a1[s], buf[it % 3][s], c1);
-      }
-      const float sc = weighted_relu_sum(f, c0, c1);
-      if (half == 0 && k0 + col < n_valid) sr[k0 + col] = sc;
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(tile) + rbase +
+                                                         16u * (uint32_t)(x ^ s));
+      c0 = mfma32x32x16(f.a0[s], bv, c0);
+      c1 = mfma32x32x16(f.a1[s], bv, c1);
     }
+    const float sc = weighted_relu_sum(f, c0, c1);
+    if (half == 0) sl[key0_of(it) - k_begin + col] = sc;  // slots past k_end are never copied out
+  }
+  __syncthreads();
+  const int n = (int)(k_end - k_begin);
+  float* dst = sr + k_begin;
+  if (((row * N) & 3) == 0) {  // 16-byte aligned row segment (k_begin is a multiple of 32)
+    for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * WAVES * 64) {
+      if (i + 4 <= n) *reinterpret_cast<f32x4*>(dst + i) = *reinterpret_cast<const f32x4*>(&sl[i]);
+      else
+        for (int e = i; e < n; ++e) dst[e] = sl[e];
+    }
+  } else {
+    for (int i = (int)threadIdx.x; i < n; i += WAVES * 64) dst[i] = sl[i];
   }
 }
 
@@ -214,14 +276,17 @@ hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
                                     hipStream_t stream) {
   if (Tq <= 4) {
-    // 4096 keys per workgroup: long enough runs to amortise the query/weight
-    // loads, short enough that 131072-key rows still give 1024+ workgroups
-    constexpr int WAVES = 4, TPW = 32;
-    const int64_t chunk = WAVES * TPW * 32;
+    // Roughly two workgroups per compute unit over the launch (one fits at a
+    // time: it holds all of LDS), whole tiles for every wave, at most SCAP keys.
+    constexpr int WAVES = 4, NBUF = 4, SCAP = 8192;
     const int64_t nmax = min(N, q_pos0 + Tq);
-    dim3 grid((unsigned)((nmax + chunk - 1) / chunk), (unsigned)Tq, (unsigned)B);
-    hipLaunchKernelGGL((indexer_stream_bf16<WAVES, TPW>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w,
-                       scores, Tq, N, q_pos0);
+    int64_t kpw = (nmax * B * Tq + 511) / 512;
+    kpw = (kpw + 32 * WAVES - 1) / (32 * WAVES) * (32 * WAVES);
+    if (kpw > SCAP) kpw = SCAP;
+    if (kpw < 32 * WAVES) kpw = 32 * WAVES;
+    dim3 grid((unsigned)((nmax + kpw - 1) / kpw), (unsigned)Tq, (unsigned)B);
+    hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w,
+                       scores, Tq, N, q_pos0, kpw);
   } else {
     constexpr int WAVES = 8;
     const int64_t nqb = (Tq + WAVES - 1) / WAVES;

@@ -92,25 +92,6 @@ __device__ __forceinline__ void mfma_s_last2(f32x16& c0, bf16x8 a0, bf16x8 b0, f
       : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
 
-// 16-byte direct-to-LDS load: every lane reads 16 B at base + voff and the
-// wave writes them to LDS bytes [lds_addr + 16*lane, +16).  base is
-// wave-uniform (scalar registers), voff a 32-bit per-lane byte offset; the
-// instruction offset stays 0 because it would move the LDS destination too.
-// Written as inline asm so that the compiler does not track it: otherwise it
-// cannot tell that reads of the current tile buffer do not alias the gathers
-// into the other buffers and waits for them before every read.  The
-// instruction has no register result; completion is awaited explicitly
-// (vmcnt) before the barrier that hands the buffer to the readers.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(lds_addr), "s"(base)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  typedef const __attribute__((address_space(3))) char* lds_ptr;
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p));
-}
-
 // Barrier without the memory fence that __syncthreads() adds: the fence would
 // also wait for the in-flight direct-to-LDS gathers of the next tiles.
 __device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -94,6 +94,9 @@ def _bf16_indexer_case(Tq, N, q_pos0, B=1, dist_w=None):
     (2, 77, 200, 50),        # chunked prefill: queries at positions 50..126 of a 200-row cache
     (3, 1, 5000, 4999),      # decode, streamed keys
     (2, 3, 1000, 997),       # decode of 3 tokens
+    (2, 2, 1001, 999),       # decode rows whose score rows are not 16-byte aligned
+    (2, 1, 40000, 39999),    # decode, several workgroups per row and a ragged last one
+    (1, 4, 70, 10),          # decode queries seeing only part of the cache
     (1, 1, 1, 0),            # a single key
     (1, 9, 9, 0),            # tiled path with a single short tile
 ])
@@ -350,5 +353,9 @@ def test_dsa_decode_b32_128k():
         assert_close(o[b, 0], ref["o"], "bf16", f"out b={b}")
         assert_lse_close(ls[b, 0], ref["lse"], f"lse b={b}")
     scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], wl.q_pos0)
+    sc = scores.cpu().numpy()
+    for b in (0, 31):  # full score rows, bit for bit, in the launch shape the benchmark times
+        ref = oracle.index_scores_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], [0], wl.q_pos0)
+        causal_scores_equal(sc[b], ref, [0], f"scores b={b}")
     for b in range(wl.B):
         _check_selection_properties(scores[b], idx[b], wl.q_pos0, wl.K)
