@@ -37,6 +37,27 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even,
+// with the gfx950 conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// Max / sum of the values of lanes j and j ^ 32.  v_permlane32_swap with both
+// operands equal to v leaves the lower half's values in one result register
+// and the upper half's in the other, in every lane, so a symmetric combination
+// of the two is the same in lane j and lane j ^ 32.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int mfma_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
 // Order-preserving map of a float32 to uint32 (larger float -> larger key);

@@ -103,6 +103,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     int64_t R, int64_t Tq, int64_t N, int K, int splits, int keys_per_split, float scale_log2) {
   __shared__ __align__(16) uint16_t kvs[NBUF][NT * MD];  // latent tiles, chunk-major (see above)
   __shared__ __align__(16) int32_t vflag[NBUF][NT];      // row valid flags per buffer
+  __shared__ int32_t tfull[NBUF];                          // 1 if every row of the buffer is valid
   __shared__ __align__(16) int32_t sidx[MAX_SPLIT_KEYS];  // this split's index list
   __shared__ __align__(16) uint16_t ps[MH * PP];
   __shared__ float m_s[MH], l_s[MH];
@@ -171,7 +172,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     const uint32_t lds0 = lds_address(&kvs[buf][512 * wave]);
 #pragma unroll
     for (int u = 0; u < GU; ++u) dma16(kvw + 128 * u, voff, lds0 + 4096 * u);
-    if (wave == 0 && lane < 32) vflag[buf][grow] = ok;  // wave 0, lanes 0..31: row == lane
+    if (wave == 0) {
+      if (lane < 32) vflag[buf][grow] = ok;  // lanes 0..31: row == lane
+      const bool full = __ballot(ok) == ~0ull;  // lanes 32..63 cover the 32 rows again
+      if (lane == 0) tfull[buf] = full;
+    }
   };
   // Wait until this wave's gathers of all but the most recently issued tile
   // are complete (vmcnt counts this wave's loads, oldest first).
@@ -255,44 +260,50 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
       sacc = s0 + s1;
     }
 
-    // Online softmax; this lane holds head 32*wave+col, keys mfma_row(i, half).
-    float x[16];
-    float mt = -INFINITY;
+    // Online softmax in log2 units.  This lane holds head 32*wave+col for keys
+    // mfma_row(i, half); lane j^32 holds the other 16 keys of the tile.  The
+    // scale is positive, so the scaled maximum is the maximum of the scaled
+    // logits, and each weight is one fused multiply-add and one exp2.
+    if (!__builtin_amdgcn_readfirstlane(tfull[it % NBUF])) {
+      // some row of this tile is masked: its logit is -inf (weight 0)
+      const int32_t* vcur = vflag[it % NBUF];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int4 vf = *reinterpret_cast<const int4*>(&vcur[8 * a + 4 * half]);
-      const int fl[4] = {vf.x, vf.y, vf.z, vf.w};
+      for (int a = 0; a < 4; ++a) {
+        const int4 vf = *reinterpret_cast<const int4*>(&vcur[8 * a + 4 * half]);
+        const int fl[4] = {vf.x, vf.y, vf.z, vf.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * a + c;
-        x[i] = fl[c] ? sacc[i] * scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[i]);
+        for (int c = 0; c < 4; ++c)
+          if (!fl[c]) sacc[4 * a + c] = -INFINITY;
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float mh = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mh = fmaxf(mh, sacc[i]);
+    const float mt = max_halves(mh * scale_log2);  // this head's largest scaled logit in the tile
     m_max = fmaxf(m_max, mt);
     if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated yet: start the reference here
     overflow |= mt > m_ref + 64.f;
+    float x[16];
     float lsum = 0.f;
     if (m_ref == -INFINITY) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = 0.f;
     } else {
+      // arguments are at most 64 here (else the split is redone); exp2(-inf) = 0
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        x[i] = exp2f(x[i] - m_ref);
+        x[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -m_ref));
         lsum += x[i];
       }
     }
-    lsum += __shfl_xor(lsum, 32);
-    l_run += lsum;
+    l_run += lsum;  // this half's keys; the halves are added at the end
     {
       uint16_t* pp = &ps[(32 * wave + col) * PP + 4 * half];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         u32x2 pk;
-        pk.x = float_to_bf16_bits(x[4 * a + 0]) | (float_to_bf16_bits(x[4 * a + 1]) << 16);
-        pk.y = float_to_bf16_bits(x[4 * a + 2]) | (float_to_bf16_bits(x[4 * a + 3]) << 16);
+        pk.x = pack_bf16x2(x[4 * a + 0], x[4 * a + 1]);
+        pk.y = pack_bf16x2(x[4 * a + 2], x[4 * a + 3]);
         *reinterpret_cast<u32x2*>(pp + 8 * a) = pk;
       }
     }
@@ -335,6 +346,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   if (!__syncthreads_or(overflow)) break;
   }
 
+  l_run = sum_halves(l_run);
   if (half == 0) {
     l_s[32 * wave + col] = l_run;
     m_s[32 * wave + col] = m_ref;
@@ -356,8 +368,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
         for (int a = 0; a < 4; ++a) {
           const f32x16& v = o[mb][nb];
           u32x2 pk;
-          pk.x = float_to_bf16_bits(v[4 * a + 0] * inv) | (float_to_bf16_bits(v[4 * a + 1] * inv) << 16);
-          pk.y = float_to_bf16_bits(v[4 * a + 2] * inv) | (float_to_bf16_bits(v[4 * a + 3] * inv) << 16);
+          pk.x = pack_bf16x2(v[4 * a + 0] * inv, v[4 * a + 1] * inv);
+          pk.y = pack_bf16x2(v[4 * a + 2] * inv, v[4 * a + 3] * inv);
           *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * a) = pk;
         }
       }
@@ -404,8 +416,8 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
     }
   }
   u32x2 pk;
-  pk.x = float_to_bf16_bits(acc.x) | (float_to_bf16_bits(acc.y) << 16);
-  pk.y = float_to_bf16_bits(acc.z) | (float_to_bf16_bits(acc.w) << 16);
+  pk.x = pack_bf16x2(acc.x, acc.y);
+  pk.y = pack_bf16x2(acc.z, acc.w);
   *reinterpret_cast<u32x2*>(out + rh * MDV + 4 * tid) = pk;
   if (lse != nullptr && tid == 0) lse[rh] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * LN2;
 }
