@@ -134,7 +134,10 @@ dsa_status dsa_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, in
  * An index row with no valid entry yields out = 0 and lse = -inf.  idx must
  * not repeat a key within a row (the top-k step never does); causality is not
  * checked here -- idx decides.  bf16 accumulates in float32 (MFMA) and rounds
- * out to bf16 (nearest-even).
+ * out to bf16 (nearest-even).  When there are fewer query rows than compute
+ * units, a row's index list is split over several workgroups; each split's
+ * normalised output is then rounded to bf16 in the workspace and the splits
+ * are merged in float32 (so such rows are rounded twice).
  *
  *   q   [B, Tq, H, D] (dtype);  kv [B, N, D] latent cache (dtype), value = the
  *   first DV columns;  idx [B, Tq, K] int32;  out [B, Tq, H, DV] (dtype);

@@ -39,7 +39,8 @@
 // consecutive value columns of four consecutive keys hand every lane four
 // keys of its own column.
 // With more than one split, each split writes its normalised partial output
-// and its log2-sum-exp to the workspace and a combine kernel merges them.
+// (bf16) and its log2-sum-exp (fp32) to the workspace and a combine kernel
+// merges them in fp32.
 #include "device_common.h"
 #include "launch.h"
 
@@ -99,7 +100,7 @@ __device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\
 
 __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
     int64_t R, int64_t Tq, int64_t N, int K, int splits, int keys_per_split, float scale_log2) {
   __shared__ __align__(16) uint16_t kvs[NBUF][NT * MD];  // latent tiles, chunk-major (see above)
   __shared__ __align__(16) int32_t vflag[NBUF][NT];      // row valid flags per buffer
@@ -134,25 +135,18 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   const int nkeys = max(ke - kb, 0);
   const int ntiles = (nkeys + NT - 1) / NT;
 
-  // Indices first, then queries: the index loads are awaited while the
-  // query loads are still in flight.
+  // Prologue: this split's indices into LDS, then the gathers of the first
+  // two tiles, then the queries, so the query loads overlap the gathers.
   {
     const int32_t* ip = idx + r * K + kb;
     for (int j = tid; j < ntiles * NT; j += MLA_THREADS) sidx[j] = j < nkeys ? ip[j] : -1;
-  }
-  // Queries of heads 32*wave + col, channels 16*s + 8*half + [0, 8).
-  bf16x8 qf[MD / 16];
-  {
-    const uint16_t* qp = q + (r * MH + 32 * wave + col) * (int64_t)MD + 8 * half;
-#pragma unroll
-    for (int s = 0; s < MD / 16; ++s) qf[s] = load_bf16x8(qp + 16 * s);
   }
   f32x16 o[4][4];
   float m_ref = -INFINITY;  // exponent reference of this lane's head (log2 units)
   float m_max = -INFINITY;  // largest logit seen
   float l_run = 0.f;
   const uint16_t* kvb = kv + b * N * (int64_t)MD;
-  sync_lds();
+  __syncthreads();
 
   // Gather of tile `it`: instruction u of wave w fills slots [64*ii, 64*ii+64)
   // of the tile, ii = w + 4u (36 instructions, 9 per wave): chunk columns 2*ii
@@ -205,20 +199,30 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     }
   }
 
+  if (ntiles > 0) gather(0);
+  if (ntiles > 1) gather(1);
+  // Queries of heads 32*wave + col, channels 16*s + 8*half + [0, 8).
+  bf16x8 qf[MD / 16];
+  {
+    const uint16_t* qp = q + (r * MH + 32 * wave + col) * (int64_t)MD + 8 * half;
+#pragma unroll
+    for (int s = 0; s < MD / 16; ++s) qf[s] = load_bf16x8(qp + 16 * s);
+  }
+
   for (int pass = 0; pass < 2; ++pass) {
   if (pass == 1) {
     // a logit ran more than 64 above its reference in some head: redo the
     // split with the true maximum as reference (never the case for ordinary data)
     m_ref = m_max;
     l_run = 0.f;
+    if (ntiles > 0) gather(0);
+    if (ntiles > 1) gather(1);
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
   bool overflow = false;
-  if (ntiles > 0) gather(0);
-  if (ntiles > 1) gather(1);
   // queries and tiles 0 (and 1) in place; the compiler now sees no load in flight
   __builtin_amdgcn_s_waitcnt(0);
   sync_lds();
@@ -375,15 +379,17 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
       }
       if (lse != nullptr && wave == 0 && half == 0) lse[r * MH + h] = lse2 * LN2;
     } else {
-      float* po = part_o + (((int64_t)sp * R + r) * MH + h) * MDV + 128 * wave + 4 * half;
+      uint16_t* po = part_o + (((int64_t)sp * R + r) * MH + h) * MDV + 128 * wave + 4 * half;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const f32x16& v = o[mb][nb];
-          f32x4 st = {v[4 * a + 0] * inv, v[4 * a + 1] * inv, v[4 * a + 2] * inv, v[4 * a + 3] * inv};
-          *reinterpret_cast<f32x4*>(po + 32 * mb + 8 * a) = st;
+          u32x2 pk;
+          pk.x = pack_bf16x2(v[4 * a + 0] * inv, v[4 * a + 1] * inv);
+          pk.y = pack_bf16x2(v[4 * a + 2] * inv, v[4 * a + 3] * inv);
+          *reinterpret_cast<u32x2*>(po + 32 * mb + 8 * a) = pk;
         }
       }
       if (wave == 0 && half == 0) part_lse[((int64_t)sp * R + r) * MH + h] = lse2;
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 }
 
 // Merge the split partials of one (query, head): weights 2^(lse_s - lse_max).
-__global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                          const float* __restrict__ part_lse,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse,
                                                          int64_t R, int splits) {
@@ -410,7 +416,9 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
     for (int s = 0; s < splits; ++s) {
       const float wgt = exp2f(part_lse[s * stride + rh] - M) * inv;
       if (wgt != 0.f) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (s * stride + rh) * MDV + 4 * tid);
+        const u32x2 pk = *reinterpret_cast<const u32x2*>(part_o + (s * stride + rh) * MDV + 4 * tid);
+        const f32x4 v = {bf16_bits_to_float(pk.x & 0xffffu), bf16_bits_to_float(pk.x >> 16),
+                         bf16_bits_to_float(pk.y & 0xffffu), bf16_bits_to_float(pk.y >> 16)};
         acc += wgt * v;
       }
     }
@@ -498,7 +506,8 @@ size_t mla_workspace_bytes(int64_t rows, int H, int DV, int K, int is_bf16) {
   if (!is_bf16) return 0;
   const int s = mla_num_splits(rows, K);
   if (s <= 1) return 0;
-  return (size_t)s * rows * H * DV * sizeof(float) + (size_t)s * rows * H * sizeof(float);
+  // bf16 normalised partial outputs, then fp32 log2-sum-exps
+  return (size_t)s * rows * H * DV * sizeof(uint16_t) + (size_t)s * rows * H * sizeof(float);
 }
 
 hipError_t launch_sparse_mla_bf16(const uint16_t* q, const uint16_t* kv, const int32_t* idx, uint16_t* out,
@@ -507,11 +516,11 @@ hipError_t launch_sparse_mla_bf16(const uint16_t* q, const uint16_t* kv, const i
   const int64_t R = B * Tq;
   const int splits = mla_num_splits(R, K);
   const int kps = mla_keys_per_split(K, splits);
-  float* part_o = nullptr;
+  uint16_t* part_o = nullptr;
   float* part_lse = nullptr;
   if (splits > 1) {
-    part_o = static_cast<float*>(workspace);
-    part_lse = part_o + (size_t)splits * R * MH * MDV;
+    part_o = static_cast<uint16_t*>(workspace);
+    part_lse = reinterpret_cast<float*>(part_o + (size_t)splits * R * MH * MDV);
   }
   hipLaunchKernelGGL(sparse_mla_bf16_kernel, dim3((unsigned)(R * splits)), dim3(MLA_THREADS), 0, stream, q, kv,
                      idx, out, lse, part_o, part_lse, R, Tq, N, K, splits, kps, scale * LOG2E);
