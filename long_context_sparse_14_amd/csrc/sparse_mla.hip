@@ -27,17 +27,17 @@
 //     wave w owns value columns [128w, 128w+128) for all 128 heads (256 fp32
 //     accumulators per lane), so every V element is read from LDS once per
 //     tile.
-// The LDS tile is chunk-major: 16-byte chunk p (channels 8p..8p+7) of tile
-// row r sits at slot 32*p + (r ^ 4*(p & 3)).  A gather instruction fills 64
-// slots = two chunk columns, so every lane always fetches from the same latent
-// row (one index per lane per tile); every operand read below is a per-lane
-// base plus a compile-time offset; the XOR keeps the reads at the minimum of
-// two passes per 512 bytes.  The PV operand (eight keys of one value column
-// per lane) comes from the gfx950 transposing LDS read ds_read_b64_tr_b16:
-// within each 16-lane group, lane i receives element (i & 3) of the 8 bytes
-// addressed by lane 4c + (i >> 2), c = 0..3 -- so lanes that address four
-// consecutive value columns of four consecutive keys hand every lane four
-// keys of its own column.
+// LDS tile layout: row r of the tile (0..31) is 72 chunks of 16 bytes; chunk c
+// sits at slot 64*(9*(r/8) + c/8) + 8*(r%8) + ((c%8) ^ f(r)), with
+// f(r) = 2*((r>>1)&3) + ((r>>3)&1).  One gather instruction therefore fills a
+// 1 KiB block of 64 slots from 8 whole 128-byte cache lines (8 rows), and the
+// XOR term spreads both operand reads below over all banks.  Every operand
+// read is a per-lane base plus a compile-time offset.  The PV operand (eight
+// keys of one value column per lane) comes from the gfx950 transposing LDS
+// read ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i & 3) of the 8 bytes addressed by lane 4c + (i >> 2), c = 0..3 -- so lanes
+// that address four consecutive value columns of four consecutive keys hand
+// every lane four keys of its own column.
 // With more than one split, each split writes its normalised partial output
 // (bf16) and its log2-sum-exp (fp32) to the workspace and a combine kernel
 // merges them in fp32.
@@ -52,8 +52,8 @@ constexpr int ROW_CHUNKS = MD / 8;          // 72 chunks of 16 B per latent row
 constexpr int TILE_CHUNKS = NT * ROW_CHUNKS; // 2304
 constexpr int PP = NT + 8;                   // bf16 per LDS probability row
 constexpr int MLA_WAVES = 4;
-constexpr int NBUF = 3;                      // latent tile buffers (two gathers in flight)
-constexpr int SLOOK = 6;                     // QK^T key-operand reads in flight
+constexpr int NBUF = 3;                      // latent tile buffers
+constexpr int SLOOK = 4;                     // QK^T key-operand reads in flight
 constexpr int PVLOOK = 2;                    // PV value-operand reads in flight
 constexpr int MAX_SPLIT_KEYS = 2048;         // indices handled by one workgroup
 constexpr int MLA_THREADS = MLA_WAVES * 64;
@@ -62,6 +62,9 @@ constexpr float LN2 = 0.6931471805599453f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// XOR swizzle of tile row r (see the layout note above).
+__device__ __forceinline__ int row_swizzle(int r) { return 2 * ((r >> 1) & 3) + ((r >> 3) & 1); }
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
@@ -85,12 +88,11 @@ __device__ __forceinline__ f32x16 mfma_s_first(bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_s(f32x16& c, bf16x8 a, bf16x8 b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_s_last2(f32x16& c0, bf16x8 a0, bf16x8 b0, f32x16& c1, bf16x8 a1, bf16x8 b1) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1\n\t"
+__device__ __forceinline__ void mfma_s_last(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
       "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-      : "+v"(c0), "+v"(c1)
-      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+      : "+v"(c)
+      : "v"(a), "v"(b));
 }
 
 // Barrier without the memory fence that __syncthreads() adds: the fence would
@@ -104,9 +106,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     int64_t R, int64_t Tq, int64_t N, int K, int splits, int keys_per_split, float scale_log2) {
   __shared__ __align__(16) uint16_t kvs[NBUF][NT * MD];  // latent tiles, chunk-major (see above)
   __shared__ __align__(16) int32_t vflag[NBUF][NT];      // row valid flags per buffer
-  __shared__ int32_t tfull[NBUF];                          // 1 if every row of the buffer is valid
+  __shared__ __align__(16) int32_t tfull[NBUF][MLA_WAVES]; // per wave: 1 if its 8 rows of the buffer are valid
   __shared__ __align__(16) int32_t sidx[MAX_SPLIT_KEYS];  // this split's index list
-  __shared__ __align__(16) uint16_t ps[MH * PP];
+  __shared__ __align__(16) uint16_t ps[2][MH * PP];       // bf16 P of two consecutive tiles
   __shared__ float m_s[MH], l_s[MH];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -146,57 +148,57 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   float m_max = -INFINITY;  // largest logit seen
   float l_run = 0.f;
   const uint16_t* kvb = kv + b * N * (int64_t)MD;
+  const uint8_t* kvb8 = reinterpret_cast<const uint8_t*>(kvb);
   __syncthreads();
 
-  // Gather of tile `it`: instruction u of wave w fills slots [64*ii, 64*ii+64)
-  // of the tile, ii = w + 4u (36 instructions, 9 per wave): chunk columns 2*ii
-  // and 2*ii+1.  Slot 32*p + s holds row s ^ 4*(p & 3); for this wave's
-  // instructions p = 2*ii + lane/32 and p & 3 is fixed.
-  constexpr int GU = TILE_CHUNKS / 64 / MLA_WAVES;  // 9
-  static_assert(GU * 64 * MLA_WAVES == TILE_CHUNKS && GU == 9, "gather instructions per wave");
-  const int grow = (lane & 31) ^ (4 * ((2 * (wave & 1) + (lane >> 5)) & 3));
-  // byte address of chunk 2*ii + lane/32 of row v: kvw + [v*1152 + 16*(lane/32)] + 128*u,
-  // with kvw = this sequence's cache + 32*wave (scalar) and ii = wave + 4u
-  const uint8_t* kvw = reinterpret_cast<const uint8_t*>(kvb) + 32 * wave;
-  auto gather = [&](int it) {
+  // Gather of tile `it`: wave w fetches rows 8w..8w+7, one 128-byte line of
+  // each per instruction (instruction u: bytes [128u, 128u+128) of every row,
+  // u = 0..8), so an instruction touches 8 cache lines and a tile 288.  Lane L
+  // takes row 8w + L/8 and, within the line, 16-byte chunk (L % 8) ^ f(row);
+  // it lands at slot 64*(9w + u) + L (see the layout note at the top).
+  constexpr int GU = ROW_CHUNKS / 8;  // 9 lines per row
+  static_assert(GU * 8 == ROW_CHUNKS && NT == 8 * MLA_WAVES, "gather geometry");
+  const int grow = 8 * wave + (lane >> 3);
+  const uint32_t gsw = (uint32_t)((lane & 7) ^ row_swizzle(grow));
+  // gather_begin records the rows' validity and returns the per-lane source
+  // offset; gather_line(u) then issues instruction u.
+  auto gather_begin = [&](int it, uint32_t& lds0) {
     const int buf = it % NBUF;
     const int32_t v = sidx[it * NT + grow];
     const bool ok = v >= 0 && (int64_t)v < N;
-    const uint32_t voff = (uint32_t)(ok ? v : 0) * (uint32_t)(MD * 2) + 16u * (uint32_t)(lane >> 5);
-    const uint32_t lds0 = lds_address(&kvs[buf][512 * wave]);
-#pragma unroll
-    for (int u = 0; u < GU; ++u) dma16(kvw + 128 * u, voff, lds0 + 4096 * u);
-    if (wave == 0) {
-      if (lane < 32) vflag[buf][grow] = ok;  // lanes 0..31: row == lane
-      const bool full = __ballot(ok) == ~0ull;  // lanes 32..63 cover the 32 rows again
-      if (lane == 0) tfull[buf] = full;
-    }
+    lds0 = lds_address(&kvs[buf][512 * GU * wave]);
+    if ((lane & 7) == 0) vflag[buf][grow] = ok;
+    const bool full = __ballot(ok) == ~0ull;
+    if (lane == 0) tfull[buf][wave] = full;
+    return (uint32_t)(ok ? v : 0) * (uint32_t)(MD * 2) + 16u * gsw;
   };
-  // Wait until this wave's gathers of all but the most recently issued tile
-  // are complete (vmcnt counts this wave's loads, oldest first).
-  auto wait_all_but_newest = [&](bool newest_in_flight) {
-    if (newest_in_flight) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  auto gather_line = [&](uint32_t voff, uint32_t lds0, int u) { dma16(kvb8 + 128 * u, voff, lds0 + 1024 * u); };
+  auto gather = [&](int it) {
+    uint32_t lds0;
+    const uint32_t voff = gather_begin(it, lds0);
+#pragma unroll
+    for (int u = 0; u < GU; ++u) gather_line(voff, lds0, u);
   };
 
-  // QK^T operand (A): key row col, channels 16*s + 8*half + e, i.e. chunk
-  // p = 2s + half, p & 3 = 2*(s & 1) + half  ->  slot 32p + (col ^ 4*(p & 3)).
-  int abase[2];
+  // QK^T operand (A) of k-step s: key row col, channels 16s + 8*half + e,
+  // i.e. chunk p = 2s + half: slot 64*(9*(col/8) + s/4) + 8*(col%8) + ((2*(s%4) + half) ^ f(col)).
+  int abase[4];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) abase[par] = 256 * half + 8 * (col ^ (4 * ((2 * par + half) & 3)));
-  // PV operand, read rd (keys 4rd..4rd+3 of this lane half) of block (ks, mb):
+  for (int s4 = 0; s4 < 4; ++s4)
+    abase[s4] = 8 * (576 * (col >> 3) + 8 * (col & 7) + ((2 * s4 + half) ^ row_swizzle(col)));
+  // PV operand, read rd (keys 4rd..4rd+3 of this lane half) of step (ks, mb):
   // 16-lane group G = lane/16, source lane j = lane%16 addresses key
-  // 16*ks + 8*half + 4*rd + j/4, value columns 128*wave + 32*mb + 16*(G&1) + 4*(j&3) + [0,4),
-  // i.e. chunk p = 16*wave + 4*mb + 2*(G&1) + (j&3)/2, byte 8*(j&1) of it.
-  int vbase[2];
+  // k = 16*ks + 8*half + 4*rd + j/4 and value columns
+  // 128*wave + 32*mb + 16*(G&1) + 4*(j&3) + [0,4), i.e. byte 8*(j&1) of chunk
+  // p = 16*wave + 4*mb + 2*(G&1) + (j&3)/2.  With f(k) = 4rd + 2(j>>3) + half,
+  // its slot is 64*(9*(2ks + half) + 2*wave + mb/2) + 8*(k%8) + ((p%8) ^ f(k))
+  //   = vlane + 64*(18ks + mb/2) + 32rd + 4*((mb&1) ^ rd),
+  // vlane = 64*(9*half + 2*wave) + 8*(j>>2) + ((2*(G&1) + (j&3)/2) ^ (2*(j>>3) + half)).
+  int vlane;
   {
-    const int G = lane >> 4, j = lane & 15, bq = (j & 3) >> 1;
-    const int pl = 2 * (G & 1) + bq;  // p & 3
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      const int key = 8 * half + 4 * rd + (j >> 2);  // + 16*ks (compile-time)
-      vbase[rd] = 256 * (16 * wave + pl) + 8 * (key ^ (4 * pl)) + 4 * (j & 1);
-    }
+    const int G = lane >> 4, j = lane & 15;
+    const int y = (2 * (G & 1) + ((j & 3) >> 1)) ^ (2 * (j >> 3) + half);
+    vlane = 8 * (64 * (9 * half + 2 * wave) + 8 * (j >> 2) + y) + 4 * (j & 1);
   }
 
   if (ntiles > 0) gather(0);
@@ -209,68 +211,118 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     for (int s = 0; s < MD / 16; ++s) qf[s] = load_bf16x8(qp + 16 * s);
   }
 
-  for (int pass = 0; pass < 2; ++pass) {
-  if (pass == 1) {
-    // a logit ran more than 64 above its reference in some head: redo the
-    // split with the true maximum as reference (never the case for ordinary data)
-    m_ref = m_max;
-    l_run = 0.f;
-    if (ntiles > 0) gather(0);
-    if (ntiles > 1) gather(1);
-  }
+  // ---- pieces of one tile ----
+  constexpr int KS = MD / 16;  // QK^T k-steps (16 channels each)
+  auto aop = [&](const uint16_t* t, int s) {
+    return *reinterpret_cast<const bf16x8*>(t + abase[s & 3] + 512 * (s >> 2));
+  };
+  auto vop = [&](const uint16_t* t, int st) {
+    const int ks = st >> 2, mb = st & 3;
+    const s16x4 lo = lds_read_tr16(t + vlane + 8 * (64 * (18 * ks + (mb >> 1)) + 4 * (mb & 1)));
+    const s16x4 hi = lds_read_tr16(t + vlane + 8 * (64 * (18 * ks + (mb >> 1)) + 32 + 4 * ((mb & 1) ^ 1)));
+    return __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+  };
+  auto pbop = [&](const uint16_t* pbuf, int ks, int nb) {
+    return *reinterpret_cast<const bf16x8*>(&pbuf[(32 * nb + col) * PP + 16 * ks + 8 * half]);
+  };
+  // k-steps s and s+1 of S^T[key][head] = KV_tile . Q^T for this wave's 32
+  // heads, accumulated in sacc; the key operands stream through a ring of
+  // SLOOK registers read SLOOK k-steps ahead of their MFMA.
+  auto s_pair = [&](const uint16_t* t, int s, bf16x8 (&ring)[SLOOK], f32x16& sacc) {
+    const bf16x8 a0 = ring[s % SLOOK], a1 = ring[(s + 1) % SLOOK];
+    if (s + SLOOK < KS) ring[s % SLOOK] = aop(t, s + SLOOK);
+    if (s + 1 + SLOOK < KS) ring[(s + 1) % SLOOK] = aop(t, s + 1 + SLOOK);
+    if (s == 0) sacc = mfma_s_first(a0, qf[0]);
+    else mfma_s(sacc, a0, qf[s]);
+    if (s + 2 < KS) mfma_s(sacc, a1, qf[s + 1]);
+    else mfma_s_last(sacc, a1, qf[s + 1]);
+  };
+  // step st = (ks, mb) of O^T[dv][head] += V^T . P^T for dv in
+  // [128*wave, 128*wave+128) and all 128 heads; the value operand of step
+  // st+PVLOOK is read while step st runs.
+  auto pv_step = [&](const uint16_t* t, int st, bf16x8 (&vring)[PVLOOK], const bf16x8 (&pb)[4]) {
+    const int mb = st & 3;
+    const bf16x8 av = vring[st % PVLOOK];
+    if (st + PVLOOK < 8) vring[st % PVLOOK] = vop(t, st + PVLOOK);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < 4; ++nb) o[mb][nb] = mfma32x32x16(av, pb[nb], o[mb][nb]);
+  };
+  // QK^T of tile tS alone (the first tile of a pass).
+  auto tile_s = [&](const uint16_t* tS) {
+    bf16x8 ring[SLOOK];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
-  bool overflow = false;
-  // queries and tiles 0 (and 1) in place; the compiler now sees no load in flight
-  __builtin_amdgcn_s_waitcnt(0);
-  sync_lds();
-  for (int it = 0; it < ntiles; ++it) {
-    const uint16_t* cur = kvs[it % NBUF];
-    const int32_t* vcur = vflag[it % NBUF];
-    if (it + 2 < ntiles) gather(it + 2);
-
-    // S^T[key][head] for this wave's 32 heads: two independent accumulation
-    // chains (even and odd k-steps) so that consecutive MFMAs do not wait for
-    // each other.
-    // The key operands stream through a ring of SLOOK registers, each read
-    // issued SLOOK k-steps ahead of its MFMA; the scheduling barriers keep the
-    // compiler from collapsing the ring.
+    for (int s = 0; s < SLOOK; ++s) ring[s] = aop(tS, s);
     f32x16 sacc;
-    {
-      constexpr int KS = MD / 16;
-      auto aop = [&](int s) { return *reinterpret_cast<const bf16x8*>(cur + abase[s & 1] + 512 * s); };
-      bf16x8 ring[SLOOK];
 #pragma unroll
-      for (int s = 0; s < SLOOK; ++s) ring[s] = aop(s);
-      f32x16 s0, s1;
-#pragma unroll
-      for (int s = 0; s < KS; s += 2) {
-        const bf16x8 a0 = ring[s % SLOOK], a1 = ring[(s + 1) % SLOOK];
-        if (s + SLOOK < KS) ring[s % SLOOK] = aop(s + SLOOK);
-        if (s + 1 + SLOOK < KS) ring[(s + 1) % SLOOK] = aop(s + 1 + SLOOK);
-        if (s == 0) {
-          s0 = mfma_s_first(a0, qf[0]);
-          s1 = mfma_s_first(a1, qf[1]);
-        } else if (s + 2 < KS) {
-          mfma_s(s0, a0, qf[s]);
-          mfma_s(s1, a1, qf[s + 1]);
-        } else {
-          mfma_s_last2(s0, a0, qf[s], s1, a1, qf[s + 1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      sacc = s0 + s1;
+    for (int g = 0; g < KS / 2; ++g) {
+      s_pair(tS, 2 * g, ring, sacc);
+      __builtin_amdgcn_sched_barrier(0);  // keep the ring
     }
-
-    // Online softmax in log2 units.  This lane holds head 32*wave+col for keys
-    // mfma_row(i, half); lane j^32 holds the other 16 keys of the tile.  The
-    // scale is positive, so the scaled maximum is the maximum of the scaled
-    // logits, and each weight is one fused multiply-add and one exp2.
-    if (!__builtin_amdgcn_readfirstlane(tfull[it % NBUF])) {
+    return sacc;
+  };
+  // PV of tile tV alone (the last tile of a pass).
+  auto tile_pv = [&](const uint16_t* tV, const uint16_t* pbuf) {
+    bf16x8 pb[4], vring[PVLOOK];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) pb[nb] = pbop(pbuf, 0, nb);
+#pragma unroll
+    for (int st = 0; st < PVLOOK; ++st) vring[st] = vop(tV, st);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      pv_step(tV, st, vring, pb);
+      if (st == 3)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) pb[nb] = pbop(pbuf, 1, nb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // PV of tile tV interleaved with QK^T of the next tile tS: three k-step
+  // pairs per PV step, so the matrix cores always have independent work while
+  // the LDS serves both operand streams, and the logits are complete two PV
+  // steps before the end: the softmax that follows issues while those last
+  // PV MFMAs still run.
+  // The gather of tile gt (if gt >= 0) is spread over the first nine k-step
+  // pairs: an instruction waits at issue until the memory pipeline takes it,
+  // and the MFMAs already issued keep the matrix cores busy meanwhile.
+  auto tile_pv_s = [&](const uint16_t* tV, const uint16_t* pbuf, const uint16_t* tS, int gt) {
+    uint32_t g_lds0 = 0, g_voff = 0;
+    if (gt >= 0) g_voff = gather_begin(gt, g_lds0);
+    bf16x8 ring[SLOOK], pb[4], vring[PVLOOK];
+#pragma unroll
+    for (int s = 0; s < SLOOK; ++s) ring[s] = aop(tS, s);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) pb[nb] = pbop(pbuf, 0, nb);
+#pragma unroll
+    for (int st = 0; st < PVLOOK; ++st) vring[st] = vop(tV, st);
+    f32x16 sacc;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+#pragma unroll
+      for (int rep = 0; rep < 3; ++rep) {
+        const int g = 3 * st + rep;
+        if (g < KS / 2) s_pair(tS, 2 * g, ring, sacc);
+        if (g < GU && gt >= 0) gather_line(g_voff, g_lds0, g);
+        __builtin_amdgcn_sched_barrier(0);  // keep the ring
+      }
+      pv_step(tV, st, vring, pb);
+      if (st == 3)  // second half of the tile's keys: the P operands of ks = 1
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) pb[nb] = pbop(pbuf, 1, nb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return sacc;
+  };
+  bool overflow = false;
+  // Online softmax of tile `t` in log2 units; writes its bf16 P to pbuf.  This
+  // lane holds head 32*wave+col for keys mfma_row(i, half); lane j^32 holds
+  // the other 16 keys of the tile.  The scale is positive, so the scaled
+  // maximum is the maximum of the scaled logits, and each weight is one fused
+  // multiply-add and one exp2.
+  auto softmax_p = [&](f32x16 sacc, int t, uint16_t* pbuf) {
+    const int4 tf = *reinterpret_cast<const int4*>(&tfull[t % NBUF][0]);
+    if (!__builtin_amdgcn_readfirstlane(tf.x && tf.y && tf.z && tf.w)) {
       // some row of this tile is masked: its logit is -inf (weight 0)
-      const int32_t* vcur = vflag[it % NBUF];
+      const int32_t* vcur = vflag[t % NBUF];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int4 vf = *reinterpret_cast<const int4*>(&vcur[8 * a + 4 * half]);
@@ -301,53 +353,52 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
       }
     }
     l_run += lsum;  // this half's keys; the halves are added at the end
-    {
-      uint16_t* pp = &ps[(32 * wave + col) * PP + 4 * half];
+    uint16_t* pp = &pbuf[(32 * wave + col) * PP + 4 * half];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 pk;
-        pk.x = pack_bf16x2(x[4 * a + 0], x[4 * a + 1]);
-        pk.y = pack_bf16x2(x[4 * a + 2], x[4 * a + 3]);
-        *reinterpret_cast<u32x2*>(pp + 8 * a) = pk;
-      }
+    for (int a = 0; a < 4; ++a) {
+      u32x2 pk;
+      pk.x = pack_bf16x2(x[4 * a + 0], x[4 * a + 1]);
+      pk.y = pack_bf16x2(x[4 * a + 2], x[4 * a + 3]);
+      *reinterpret_cast<u32x2*>(pp + 8 * a) = pk;
     }
-    sync_lds();
+  };
 
-    // O^T[dv][head] += V^T . P^T for dv in [128*wave, 128*wave+128), all heads.
-    // Eight steps (ks, mb); the value operand of step st+PVLOOK is read
-    // while step st runs its four MFMAs.
-    {
-      bf16x8 pb[2][4];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          pb[ks][nb] = *reinterpret_cast<const bf16x8*>(&ps[(32 * nb + col) * PP + 16 * ks + 8 * half]);
-      auto vop = [&](int st) {
-        // 16*ks rows and 4*mb chunks: slot += 16*ks + 128*mb (the XOR term is unchanged)
-        const int ks = st >> 2, mb = st & 3;
-        const s16x4 lo = lds_read_tr16(cur + vbase[0] + 1024 * mb + 128 * ks);
-        const s16x4 hi = lds_read_tr16(cur + vbase[1] + 1024 * mb + 128 * ks);
-        return __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
-      };
-      bf16x8 vring[PVLOOK];
-#pragma unroll
-      for (int st = 0; st < PVLOOK; ++st) vring[st] = vop(st);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int ks = st >> 2, mb = st & 3;
-        const bf16x8 av = vring[st % PVLOOK];
-        if (st + PVLOOK < 8) vring[st % PVLOOK] = vop(st + PVLOOK);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) o[mb][nb] = mfma32x32x16(av, pb[ks][nb], o[mb][nb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  // ---- the tile pipeline ----
+  // Iteration it runs PV(it) together with QK^T(it+1) and the gather of tile
+  // it+2, then the softmax of tile it+1, then one barrier.  Tile it+2 goes into
+  // the buffer of tile it-1, which every wave finished before that barrier; P
+  // alternates between two LDS buffers.
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      // a logit ran more than 64 above its reference in some head: redo the
+      // split with the true maximum as reference (never the case for ordinary data)
+      m_ref = m_max;
+      l_run = 0.f;
+      if (ntiles > 0) gather(0);
+      if (ntiles > 1) gather(1);
     }
-    // tile it+1 must have landed; tile it+2 may stay in flight
-    wait_all_but_newest(it + 2 < ntiles);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
+    overflow = false;
+    // queries and tiles 0 (and 1) in place; the compiler now sees no load in flight
+    __builtin_amdgcn_s_waitcnt(0);
     sync_lds();
-  }
-  if (!__syncthreads_or(overflow)) break;
+    if (ntiles > 0) {
+      softmax_p(tile_s(kvs[0]), 0, ps[0]);
+      sync_lds();  // P(0) visible
+    }
+    for (int it = 0; it + 1 < ntiles; ++it) {
+      const f32x16 sacc =
+          tile_pv_s(kvs[it % NBUF], ps[it & 1], kvs[(it + 1) % NBUF], it + 2 < ntiles ? it + 2 : -1);
+      softmax_p(sacc, it + 1, ps[(it + 1) & 1]);
+      // tile it+2 (the only gather in flight) must have landed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      sync_lds();  // P(it+1) and tile it+2 visible; every wave is done with tile it and P(it)
+    }
+    if (ntiles > 0) tile_pv(kvs[(ntiles - 1) % NBUF], ps[(ntiles - 1) & 1]);  // the last tile has no successor
+    if (!__syncthreads_or(overflow)) break;
   }
 
   l_run = sum_halves(l_run);
