@@ -25,7 +25,8 @@
 //      1. per-segment histogram of key bits 31..21 (2048 bins);
 //      2. every segment sums the row's bit-31..21 histograms, finds that
 //         digit of T, and histograms bits 20..10 of the keys that share it;
-//      3. every segment finds bits 31..10 of T and writes, in index order,
+//      3. every segment finds bits 31..10 of T (the top digit recorded by
+//         step 2) and writes, in index order,
 //         the keys above that prefix ("definite") and the keys on it
 //         ("candidates", low 10 bits + index);
 //      4. one workgroup per row resolves the last 10 bits of T among the
@@ -33,10 +34,10 @@
 //    Per-segment histograms are plain stores (no atomics, no zeroing); a row
 //    whose candidates overflow their buffers falls back to the one-workgroup
 //    method reading the row from global memory.
-// Scores of one row usually share their top bits, so the first histogram
-// pass aggregates equal bins across a wave before touching LDS (same-address
-// LDS atomics would serialise).  Each thread owns a run of consecutive keys,
-// so one block-wide prefix sum orders a whole chunk.
+// Histograms use plain LDS atomics: even for rows whose scores crowd into a
+// few top-bit bins this measured faster than combining equal bins across a
+// wave first.  Each thread owns a run of consecutive keys, so one block-wide
+// prefix sum orders a whole chunk.
 #include "device_common.h"
 #include "launch.h"
 
@@ -109,27 +110,6 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32
   return d;
 }
 
-// h[bin] += 1 for every lane with `valid`, where many lanes of the wave may
-// share a bin: up to four rounds elect the bin of the lowest pending lane and
-// add the number of lanes holding it with one atomic; lanes still pending
-// after that add one each.
-__device__ __forceinline__ void hist_add_aggregated(uint32_t* h, uint32_t bin, bool valid) {
-  const int lane = threadIdx.x & 63;
-  uint64_t pend = __ballot(valid);
-  bool mine = valid;
-#pragma unroll
-  for (int round = 0; round < 4; ++round) {
-    if (pend == 0) break;
-    const int leader = __ffsll((unsigned long long)pend) - 1;
-    const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
-    const uint64_t same = __ballot(mine && bin == lb);
-    if (lane == leader) atomicAdd(&h[lb], (uint32_t)__popcll(same));
-    if (bin == lb) mine = false;
-    pend &= ~same;
-  }
-  if (mine) atomicAdd(&h[bin], 1u);
-}
-
 // Writes the kept keys of the run [i0, i0 + RUN) (clipped to n) of one chunk:
 // gt/eq are the per-thread counts before this thread within the whole row.
 template <typename KeyAt>
@@ -184,8 +164,7 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
         const int64_t i = base + (int64_t)u * TK_THREADS;
         const bool hit = i < n && (k[u] & mask) == prefix;
         const uint32_t bin = (k[u] >> shift) & (uint32_t)(nb - 1);
-        if (pass == 0) hist_add_aggregated(hist, bin, hit);
-        else if (hit) atomicAdd(&hist[bin], 1u);
+        if (hit) atomicAdd(&hist[bin], 1u);
       }
     }
     __syncthreads();
@@ -236,6 +215,7 @@ struct LongWs {
   uint32_t* hist2;  // [R][G][HB]
   uint32_t* defc;   // [R][G] definite keys per segment
   uint32_t* candc;  // [R][G] candidates per segment (may exceed CAND_CAP: overflow)
+  uint32_t* rowd1;  // [R][2] digit 31..21 of the row's threshold and the count of keys above it
   int32_t* defi;    // [R][G][K] definite key indices, ascending within a segment
   uint2* cand;      // [R][G][CAND_CAP] (low 10 key bits, index)
 };
@@ -250,14 +230,16 @@ __host__ __device__ inline LongWs long_ws(void* base, int64_t R, int G, int K) {
   w.hist2 = reinterpret_cast<uint32_t*>(p + hs);
   w.defc = reinterpret_cast<uint32_t*>(p + 2 * hs);
   w.candc = w.defc + (size_t)R * G;
-  const size_t cs = align_up((size_t)R * G * 8);
+  w.rowd1 = w.candc + (size_t)R * G;
+  const size_t cs = align_up((size_t)R * G * 8 + (size_t)R * 8);
   w.defi = reinterpret_cast<int32_t*>(p + 2 * hs + cs);
   w.cand = reinterpret_cast<uint2*>(p + 2 * hs + cs + align_up((size_t)R * G * K * 4));
   return w;
 }
 
 size_t long_ws_bytes(int64_t R, int G, int K) {
-  return 2 * align_up((size_t)R * G * HB * 4) + align_up((size_t)R * G * 8) + align_up((size_t)R * G * K * 4) +
+  return 2 * align_up((size_t)R * G * HB * 4) + align_up((size_t)R * G * 8 + (size_t)R * 8) +
+         align_up((size_t)R * G * K * 4) +
          align_up((size_t)R * G * CAND_CAP * 8);
 }
 
@@ -313,7 +295,8 @@ __device__ void seg_hist1(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t 
   __syncthreads();
   const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u) hist_add_aggregated(sm.h, k[u] >> 21, i0 + u < n);
+  for (int u = 0; u < SEG_PER_T; ++u)
+    if (i0 + u < n) atomicAdd(&sm.h[k[u] >> 21], 1u);
   __syncthreads();
   for (int b = threadIdx.x; b < HB; b += TK_THREADS) dst[b] = sm.h[b];
 }
@@ -321,11 +304,16 @@ __device__ void seg_hist1(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t 
 // Step 2: digit 31..21 of T from the row's step-1 histograms, then a
 // histogram of bits 20..10 of this segment's keys that share it.
 __device__ void seg_hist2(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t n, int K, int nseg,
-                          const uint32_t* __restrict__ row_hist1, uint32_t* __restrict__ dst, SegSmem& sm) {
+                          const uint32_t* __restrict__ row_hist1, uint32_t* __restrict__ dst,
+                          uint32_t* __restrict__ row_d1, bool first, SegSmem& sm) {
   for (int b = threadIdx.x; b < HB; b += TK_THREADS) sm.h[b] = 0;
   sum_hist(row_hist1, nseg, sm.hs);
   uint32_t above;
   const uint32_t d1 = find_digit(sm.hs, HB, (uint32_t)K, above, sm.sbuf, sm.s_res);
+  if (first && threadIdx.x == 0) {  // every segment finds the same digit; the first records it for step 3
+    row_d1[0] = d1;
+    row_d1[1] = above;
+  }
   const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
 #pragma unroll
   for (int u = 0; u < SEG_PER_T; ++u)
@@ -337,12 +325,11 @@ __device__ void seg_hist2(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t 
 // Step 3: bits 31..10 of T, then this segment's keys above that prefix
 // (definite) and on it (candidates), in index order.
 __device__ void seg_classify(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t n, int K, int nseg,
-                             const uint32_t* __restrict__ row_hist1, const uint32_t* __restrict__ row_hist2,
+                             const uint32_t* __restrict__ row_d1, const uint32_t* __restrict__ row_hist2,
                              const LongWs& ws, size_t sidx, SegSmem& sm) {
   uint32_t above;
-  sum_hist(row_hist1, nseg, sm.hs);
-  const uint32_t d1 = find_digit(sm.hs, HB, (uint32_t)K, above, sm.sbuf, sm.s_res);
-  const uint32_t kk1 = (uint32_t)K - above;
+  const uint32_t d1 = row_d1[0];
+  const uint32_t kk1 = (uint32_t)K - row_d1[1];
   sum_hist(row_hist2, nseg, sm.hs);
   const uint32_t d2 = find_digit(sm.hs, HB, kk1, above, sm.sbuf, sm.s_res);
   const uint32_t p22 = (d1 << 11) | d2;
@@ -400,7 +387,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_hist2(const float* __rest
   uint32_t k[SEG_PER_T];
   load_segment(scores + row * N, seg0, n, k);
   seg_hist2(k, seg0, n, K, (int)((n + SEG - 1) / SEG), ws.hist1 + (size_t)row * G * HB,
-            ws.hist2 + ((size_t)row * G + g) * HB, sm);
+            ws.hist2 + ((size_t)row * G + g) * HB, ws.rowd1 + 2 * row, g == 0, sm);
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __restrict__ scores, LongWs ws,
@@ -414,7 +401,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __r
   if (n <= K || seg0 >= n) return;
   uint32_t k[SEG_PER_T];
   load_segment(scores + row * N, seg0, n, k);
-  seg_classify(k, seg0, n, K, (int)((n + SEG - 1) / SEG), ws.hist1 + (size_t)row * G * HB,
+  seg_classify(k, seg0, n, K, (int)((n + SEG - 1) / SEG), ws.rowd1 + 2 * row,
                ws.hist2 + (size_t)row * G * HB, ws, (size_t)row * G + g, sm);
 }
 
