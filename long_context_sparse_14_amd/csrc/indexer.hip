@@ -53,14 +53,17 @@ __device__ __forceinline__ void load_query(QFrags& f, const uint16_t* __restrict
 }
 
 // Score of this lane's key (valid in lanes 0..31) from the two head blocks.
+// ReLU is a median of three (one instruction for finite scores; fmaxf would
+// add a NaN-quieting instruction), and the two halves of the wave are added
+// with a lane swap.
 __device__ __forceinline__ float weighted_relu_sum(const QFrags& f, const f32x16& c0, const f32x16& c1) {
   float part = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    part = fmaf(f.w0[i], fmaxf(c0[i], 0.f), part);
-    part = fmaf(f.w1[i], fmaxf(c1[i], 0.f), part);
+    part = fmaf(f.w0[i], __builtin_amdgcn_fmed3f(c0[i], 0.f, 3.0e38f), part);
+    part = fmaf(f.w1[i], __builtin_amdgcn_fmed3f(c1[i], 0.f, 3.0e38f), part);
   }
-  return part + __shfl_xor(part, 32);
+  return sum_halves(part);
 }
 
 // Decode kernel with the key tiles staged through LDS.  A wave owns a ring
@@ -232,12 +235,16 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
       const int64_t kk0 = k0 + 32 * nb;
       if (kk0 < n_valid) {
         const uint16_t* lp = &ks[buf][(32 * nb + col) * PITCH + 64 * half];
+        // all eight key operands of the block in flight before the first MFMA
+        bf16x8 bv[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) bv[s] = *reinterpret_cast<const bf16x8*>(lp + 8 * s);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 c0 = {}, c1 = {};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lp + 8 * s);
-          c0 = mfma32x32x16(f.a0[s], bv, c0);
-          c1 = mfma32x32x16(f.a1[s], bv, c1);
+          c0 = mfma32x32x16(f.a0[s], bv[s], c0);
+          c1 = mfma32x32x16(f.a1[s], bv[s], c1);
         }
         const float sc = weighted_relu_sum(f, c0, c1);
         if (half == 0 && kk0 + col < n_valid) sr[kk0 + col] = sc;
