@@ -20,8 +20,9 @@
 //    consecutive bytes each, three 8 KiB tiles of 32 keys in flight per wave,
 //    and the scores leave in one burst per workgroup;
 //  * tiled kernel (prefill): 8 queries per workgroup (one per wave) share
-//    64-key tiles staged in LDS, double-buffered; the causal triangle is
-//    walked longest query block first.
+//    128-key tiles staged in LDS, double-buffered; within a tile each wave
+//    overlaps the MFMAs of one 32-key block with the epilogue of the previous
+//    one; the causal triangle is walked longest query block first.
 #include "device_common.h"
 #include "launch.h"
 
@@ -177,11 +178,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
   }
 }
 
-template <int WAVES>
+// PRIO: a wave raises its issue priority while it issues a block's MFMAs, so
+// the two waves sharing a SIMD drift into alternating MFMA and vector phases.
+template <int WAVES, int TK, int PRIO>
 __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
     float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, int64_t nqb) {
-  constexpr int TK = 64;          // keys per LDS tile
+  // TK keys per LDS tile
   constexpr int PITCH = ID + 8;   // bf16 per LDS row (272 B): spreads rows over the banks
   constexpr int CHUNKS = TK * ID / 8;
   constexpr int PER_T = CHUNKS / (WAVES * 64);
@@ -230,26 +233,44 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
     const int buf = it & 1;
     const int64_t k0 = (int64_t)it * TK;
     if (it + 1 < ntiles) gload(k0 + TK);
+    // Blocks of 32 keys, software-pipelined: the MFMAs of block nb are issued
+    // before the ReLU / weighted-sum epilogue of block nb-1, so the vector
+    // units work while the matrix cores run.  Blocks past this query's last
+    // key are skipped (only on the diagonal tiles).
+    constexpr int NBK = TK / 32;
+    const int64_t left = n_valid - k0;
+    const int nbv = left <= 0 ? 0 : (left >= TK ? NBK : (int)((left + 31) / 32));
+    f32x16 c[2][2];
+    auto mma_block = [&](int nb, f32x16 (&cc)[2]) {
+      const uint16_t* lp = &ks[buf][(32 * nb + col) * PITCH + 64 * half];
+      bf16x8 bv[8];  // all eight key operands of the block in flight before the first MFMA
 #pragma unroll
-    for (int nb = 0; nb < TK / 32; ++nb) {
-      const int64_t kk0 = k0 + 32 * nb;
-      if (kk0 < n_valid) {
-        const uint16_t* lp = &ks[buf][(32 * nb + col) * PITCH + 64 * half];
-        // all eight key operands of the block in flight before the first MFMA
-        bf16x8 bv[8];
+      for (int s = 0; s < 8; ++s) bv[s] = *reinterpret_cast<const bf16x8*>(lp + 8 * s);
+      __builtin_amdgcn_sched_barrier(0);
+      cc[0] = f32x16{};
+      cc[1] = f32x16{};
+      if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) bv[s] = *reinterpret_cast<const bf16x8*>(lp + 8 * s);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 c0 = {}, c1 = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          c0 = mfma32x32x16(f.a0[s], bv[s], c0);
-          c1 = mfma32x32x16(f.a1[s], bv[s], c1);
-        }
-        const float sc = weighted_relu_sum(f, c0, c1);
-        if (half == 0 && kk0 + col < n_valid) sr[kk0 + col] = sc;
+      for (int s = 0; s < 8; ++s) {
+        cc[0] = mfma32x32x16(f.a0[s], bv[s], cc[0]);
+        cc[1] = mfma32x32x16(f.a1[s], bv[s], cc[1]);
       }
+      if (PRIO) __builtin_amdgcn_s_setprio(0);
+    };
+    auto epi_block = [&](int nb, const f32x16 (&cc)[2]) {
+      const int64_t kk0 = k0 + 32 * nb;
+      const float sc = weighted_relu_sum(f, cc[0], cc[1]);
+      if (half == 0 && kk0 + col < n_valid) sr[kk0 + col] = sc;
+    };
+    if (nbv > 0) mma_block(0, c[0]);
+#pragma unroll
+    for (int nb = 1; nb < NBK; ++nb) {
+      if (nb < nbv) mma_block(nb, c[nb & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (nb - 1 < nbv) epi_block(nb - 1, c[(nb - 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (NBK - 1 < nbv) epi_block(NBK - 1, c[(NBK - 1) & 1]);
     if (it + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();
   }
@@ -298,7 +319,7 @@ hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx
     constexpr int WAVES = 8;
     const int64_t nqb = (Tq + WAVES - 1) / WAVES;
     dim3 grid((unsigned)nqb, (unsigned)B);
-    hipLaunchKernelGGL((indexer_tiled_bf16<WAVES>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w, scores,
+    hipLaunchKernelGGL((indexer_tiled_bf16<WAVES, 128, 1>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w, scores,
                        Tq, N, q_pos0, nqb);
   }
   return hipGetLastError();
