@@ -169,7 +169,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
   float* dst = sr + k_begin;
   if (((row * N) & 3) == 0) {  // 16-byte aligned row segment (k_begin is a multiple of 32)
     for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * WAVES * 64) {
-      if (i + 4 <= n) *reinterpret_cast<f32x4*>(dst + i) = *reinterpret_cast<const f32x4*>(&sl[i]);
+      // streaming stores: the scores are read back once, by the top-k
+      if (i + 4 <= n) __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sl[i]), reinterpret_cast<f32x4*>(dst + i));
       else
         for (int e = i; e < n; ++e) dst[e] = sl[e];
     }

@@ -382,12 +382,22 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
     overflow = false;
-    // queries and tiles 0 (and 1) in place; the compiler now sees no load in flight
-    __builtin_amdgcn_s_waitcnt(0);
+    // Tile 0 must have landed.  Loads complete in issue order: tile 0's nine
+    // gather instructions, then tile 1's nine, then (first pass only) the 36
+    // query loads, so the wait lets tile 1 and the queries stay in flight; the
+    // compiler waits for each query register before the MFMA that reads it.
+    if (pass == 0) {
+      if (ntiles > 1) asm volatile("s_waitcnt vmcnt(45)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
+    } else {
+      if (ntiles > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     sync_lds();
     if (ntiles > 0) {
       softmax_p(tile_s(kvs[0]), 0, ps[0]);
-      sync_lds();  // P(0) visible
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile 1 landed
+      sync_lds();  // P(0) and tile 1 visible
     }
     for (int it = 0; it + 1 < ntiles; ++it) {
       const f32x16 sacc =
