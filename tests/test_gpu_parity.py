@@ -209,6 +209,51 @@ def test_sparse_mla_bf16_small(B, Tq, N, K):
         assert not host64(out[0, 0]).any() and np.isneginf(host64(lse[0, 0])).all()
 
 
+def _times64_bf16(bits):
+    """bf16 bit patterns times 64, exactly (exponent + 6; zeros stay zero)."""
+    b = bits.astype(np.uint32)
+    return np.where((b & 0x7FFF) != 0, b + (6 << 7), b).astype(np.uint16)
+
+
+def test_sparse_mla_recompute_pass():
+    """A latent row 64 times larger than the rest, selected in the fourth tile of every
+    query's list: its logit exceeds the reference taken from the first tile by far more
+    than 2^64, so every workgroup recomputes with the true maximum; one workgroup per
+    query (256 queries), five tiles each."""
+    dsa = _dsa()
+    wl, x = _mla_case(1, 256, 400, 160, seed=11, n_masked=0)
+    big = 399
+    x["kv"][0, big] = _times64_bf16(x["kv"][0, big])
+    rng = np.random.default_rng(5)
+    for t in range(256):
+        row = rng.choice(399, size=160, replace=False).astype(np.int32)
+        row[100] = big  # tile 3 of 5
+        x["idx"][0, t] = row
+    # the case does what it is for: some head's logit runs more than 64 (log2 units)
+    # above the largest logit of its first tile
+    q64, kv64 = oracle.as_f64(x["q"][0]), oracle.as_f64(x["kv"][0])
+    first = np.einsum("thd,tjd->thj", q64, kv64[x["idx"][0, :, :32]]).max(-1)
+    gap = (np.einsum("thd,td->th", q64, kv64[x["idx"][0, :, 100]]) - first) * wl.scale / np.log(2.0)
+    assert (gap > 64).any()
+    out, lse = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), dev(x["idx"]), wl.scale, wl.DV)
+    o_ref, l_ref = oracle.sparse_mla(x["q"], x["kv"], x["idx"], wl.scale, wl.DV)
+    assert_close(host64(out), o_ref, "bf16", "out")
+    assert_lse_close(host64(lse), l_ref, "lse")
+
+
+def test_sparse_mla_masked_tiles_and_three_tile_pipeline():
+    """Three tiles per query with the whole middle tile masked, and four tiles with the
+    first tile masked: the software pipeline's short and masked paths."""
+    dsa = _dsa()
+    for K, lo, hi in ((96, 32, 64), (128, 0, 32)):
+        wl, x = _mla_case(1, 256, 500, K, seed=K, n_masked=0)
+        x["idx"][0, :, lo:hi] = -1
+        out, lse = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), dev(x["idx"]), wl.scale, wl.DV)
+        o_ref, l_ref = oracle.sparse_mla(x["q"], x["kv"], x["idx"], wl.scale, wl.DV)
+        assert_close(host64(out), o_ref, "bf16", f"out K={K}")
+        assert_lse_close(host64(lse), l_ref, f"lse K={K}")
+
+
 def test_sparse_mla_single_valid_key_is_exact():
     """One valid index: the output is that latent row's first 512 entries, exactly."""
     dsa = _dsa()
