@@ -110,6 +110,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   __shared__ __align__(16) int32_t sidx[MAX_SPLIT_KEYS];  // this split's index list
   __shared__ __align__(16) uint16_t ps[2][MH * PP];       // bf16 P of two consecutive tiles
   __shared__ float m_s[MH], l_s[MH];
+  __shared__ __align__(16) int32_t ovf_s[MLA_WAVES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lives in a scalar register
@@ -399,16 +400,27 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile 1 landed
       sync_lds();  // P(0) and tile 1 visible
     }
-    for (int it = 0; it + 1 < ntiles; ++it) {
-      const f32x16 sacc =
-          tile_pv_s(kvs[it % NBUF], ps[it & 1], kvs[(it + 1) % NBUF], it + 2 < ntiles ? it + 2 : -1);
+    // (the iteration without a gather is peeled, so the loop body has no branch)
+    for (int it = 0; it + 2 < ntiles; ++it) {
+      const f32x16 sacc = tile_pv_s(kvs[it % NBUF], ps[it & 1], kvs[(it + 1) % NBUF], it + 2);
       softmax_p(sacc, it + 1, ps[(it + 1) & 1]);
       // tile it+2 (the only gather in flight) must have landed
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       sync_lds();  // P(it+1) and tile it+2 visible; every wave is done with tile it and P(it)
     }
+    if (ntiles > 1) {
+      const int it = ntiles - 2;
+      const f32x16 sacc = tile_pv_s(kvs[it % NBUF], ps[it & 1], kvs[(it + 1) % NBUF], -1);
+      softmax_p(sacc, it + 1, ps[(it + 1) & 1]);
+      sync_lds();
+    }
     if (ntiles > 0) tile_pv(kvs[(ntiles - 1) % NBUF], ps[(ntiles - 1) & 1]);  // the last tile has no successor
-    if (!__syncthreads_or(overflow)) break;
+    // any overflow in the workgroup?  (one flag per wave; each pass rewrites all four before the barrier)
+    const bool wave_ovf = __ballot(overflow) != 0ull;
+    if (lane == 0) ovf_s[wave] = wave_ovf;
+    sync_lds();  // also: every wave is done with the tile buffers
+    const int4 of = *reinterpret_cast<const int4*>(ovf_s);
+    if (!__builtin_amdgcn_readfirstlane(of.x | of.y | of.z | of.w)) break;
   }
 
   l_run = sum_halves(l_run);
@@ -417,43 +429,65 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     m_s[32 * wave + col] = m_ref;
   }
   sync_lds();
+  // Output rows (normalised; bf16).  splits == 1: out[r]; else this split's
+  // partial row block in the workspace, plus its log2-sum-exp.
+  float inv[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int h = 32 * nb + col;
     const float l = l_s[h], m = m_s[h];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    inv[nb] = l > 0.f ? 1.f / l : 0.f;
     const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
-    // one accumulator block at a time (keeps the vector registers this needs small)
-    if (splits == 1) {
-      uint16_t* op = out + (r * MH + h) * (int64_t)MDV + 128 * wave + 4 * half;
+    if (wave == 0 && half == 0) {
+      if (splits == 1) {
+        if (lse != nullptr) lse[r * MH + h] = lse2 * LN2;
+      } else {
+        part_lse[((int64_t)sp * R + r) * MH + h] = lse2;
+      }
+    }
+  }
+  uint16_t* const dst = splits == 1 ? out + r * (int64_t)(MH * MDV) : part_o + ((int64_t)sp * R + r) * (MH * MDV);
+  // Two rounds of 64 heads staged in the (now idle) tile buffers, rows of
+  // EPITCH bf16: each wave writes its 128 value columns of every head, then
+  // copies 16 whole rows (1 KiB each, one store instruction per row) out.
+  // The lane index is taken afresh from the execution mask here, so that no
+  // lane-dependent value has to stay live (or be spilled) across the tiles.
+  constexpr int EPITCH = MDV + 8;
+  static_assert(64 * EPITCH <= NBUF * NT * MD, "output staging fits the tile buffers");
+  uint16_t* const stage = &kvs[0][0];
+  const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int wbase = (elane & 31) * EPITCH + 128 * wave + 4 * (elane >> 5);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        __builtin_amdgcn_sched_barrier(0);
+  for (int q = 0; q < 2; ++q) {
+    if (q == 1) sync_lds();  // every wave has copied out round 0
+#pragma unroll
+    for (int n2 = 0; n2 < 2; ++n2) {
+      const int nb = 2 * q + n2;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const f32x16& v = o[mb][nb];
           u32x2 pk;
-          pk.x = pack_bf16x2(v[4 * a + 0] * inv, v[4 * a + 1] * inv);
-          pk.y = pack_bf16x2(v[4 * a + 2] * inv, v[4 * a + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * a) = pk;
+          pk.x = pack_bf16x2(v[4 * a + 0] * inv[nb], v[4 * a + 1] * inv[nb]);
+          pk.y = pack_bf16x2(v[4 * a + 2] * inv[nb], v[4 * a + 3] * inv[nb]);
+          *reinterpret_cast<u32x2*>(stage + wbase + 32 * n2 * EPITCH + 32 * mb + 8 * a) = pk;
         }
-      }
-      if (lse != nullptr && wave == 0 && half == 0) lse[r * MH + h] = lse2 * LN2;
-    } else {
-      uint16_t* po = part_o + (((int64_t)sp * R + r) * MH + h) * MDV + 128 * wave + 4 * half;
+    }
+    sync_lds();
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x16& v = o[mb][nb];
-          u32x2 pk;
-          pk.x = pack_bf16x2(v[4 * a + 0] * inv, v[4 * a + 1] * inv);
-          pk.y = pack_bf16x2(v[4 * a + 2] * inv, v[4 * a + 3] * inv);
-          *reinterpret_cast<u32x2*>(po + 32 * mb + 8 * a) = pk;
-        }
-      }
-      if (wave == 0 && half == 0) part_lse[((int64_t)sp * R + r) * MH + h] = lse2;
+    for (int g = 0; g < 4; ++g) {  // four row reads in flight, then their four stores
+      const uint16_t* sp4 = stage + (16 * wave + 4 * g) * EPITCH + 8 * elane;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(sp4);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(sp4 + EPITCH);
+      const uint4 v2 = *reinterpret_cast<const uint4*>(sp4 + 2 * EPITCH);
+      const uint4 v3 = *reinterpret_cast<const uint4*>(sp4 + 3 * EPITCH);
+      __builtin_amdgcn_sched_barrier(0);
+      uint16_t* dp4 = dst + (64 * q + 16 * wave + 4 * g) * MDV + 8 * elane;
+      *reinterpret_cast<uint4*>(dp4) = v0;
+      *reinterpret_cast<uint4*>(dp4 + MDV) = v1;
+      *reinterpret_cast<uint4*>(dp4 + 2 * MDV) = v2;
+      *reinterpret_cast<uint4*>(dp4 + 3 * MDV) = v3;
     }
   }
 }
