@@ -138,11 +138,33 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   const int nkeys = max(ke - kb, 0);
   const int ntiles = (nkeys + NT - 1) / NT;
 
-  // Prologue: this split's indices into LDS, then the gathers of the first
-  // two tiles, then the queries, so the query loads overlap the gathers.
+  // Prologue: this split's index loads, then the query loads (issued while
+  // the indices are in flight), then, once the indices are in LDS, the
+  // gathers of the first two tiles.
+  constexpr int IPT = MAX_SPLIT_KEYS / MLA_THREADS;  // index entries per thread
+  int32_t iv[IPT];
   {
     const int32_t* ip = idx + r * K + kb;
-    for (int j = tid; j < ntiles * NT; j += MLA_THREADS) sidx[j] = j < nkeys ? ip[j] : -1;
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int j = tid + MLA_THREADS * k;
+      iv[k] = -1;
+      if (j < nkeys) iv[k] = ip[j];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Queries of heads 32*wave + col, channels 16*s + 8*half + [0, 8).
+  bf16x8 qf[MD / 16];
+  {
+    const uint16_t* qp = q + (r * MH + 32 * wave + col) * (int64_t)MD + 8 * half;
+#pragma unroll
+    for (int s = 0; s < MD / 16; ++s) qf[s] = load_bf16x8(qp + 16 * s);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    const int j = tid + MLA_THREADS * k;
+    if (j < ntiles * NT) sidx[j] = iv[k];
   }
   f32x16 o[4][4];
   float m_ref = -INFINITY;  // exponent reference of this lane's head (log2 units)
@@ -150,7 +172,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   float l_run = 0.f;
   const uint16_t* kvb = kv + b * N * (int64_t)MD;
   const uint8_t* kvb8 = reinterpret_cast<const uint8_t*>(kvb);
-  __syncthreads();
+  sync_lds();  // indices visible (the query loads stay in flight)
 
   // Gather of tile `it`: wave w fetches rows 8w..8w+7, one 128-byte line of
   // each per instruction (instruction u: bytes [128u, 128u+128) of every row,
@@ -204,13 +226,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 
   if (ntiles > 0) gather(0);
   if (ntiles > 1) gather(1);
-  // Queries of heads 32*wave + col, channels 16*s + 8*half + [0, 8).
-  bf16x8 qf[MD / 16];
-  {
-    const uint16_t* qp = q + (r * MH + 32 * wave + col) * (int64_t)MD + 8 * half;
-#pragma unroll
-    for (int s = 0; s < MD / 16; ++s) qf[s] = load_bf16x8(qp + 16 * s);
-  }
 
   // ---- pieces of one tile ----
   constexpr int KS = MD / 16;  // QK^T k-steps (16 channels each)
@@ -383,17 +398,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
     overflow = false;
-    // Tile 0 must have landed.  Loads complete in issue order: tile 0's nine
-    // gather instructions, then tile 1's nine, then (first pass only) the 36
-    // query loads, so the wait lets tile 1 and the queries stay in flight; the
-    // compiler waits for each query register before the MFMA that reads it.
-    if (pass == 0) {
-      if (ntiles > 1) asm volatile("s_waitcnt vmcnt(45)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
-    } else {
-      if (ntiles > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    // Tile 0 (and, in the first pass, the queries issued before it) must
+    // have landed.  Loads complete in issue order, so the wait lets tile 1's
+    // nine gather instructions stay in flight.
+    if (ntiles > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     sync_lds();
     if (ntiles > 0) {
       softmax_p(tile_s(kvs[0]), 0, ps[0]);
@@ -493,36 +502,56 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 }
 
 // Merge the split partials of one (query, head): weights 2^(lse_s - lse_max).
-__global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
-                                                         const float* __restrict__ part_lse,
-                                                         uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                         int64_t R, int splits) {
-  const int64_t rh = blockIdx.x;
-  const int tid = threadIdx.x;
+// One wave per (query, head); lane l owns value columns 8l..8l+7, so every
+// partial row is one 1 KiB load, and the splits' loads are independent.
+constexpr int COMBINE_WAVES = 4;
+constexpr int COMBINE_CHUNK = 8;  // partial rows in flight per lane
+__global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
+                                                                        const float* __restrict__ part_lse,
+                                                                        uint16_t* __restrict__ out,
+                                                                        float* __restrict__ lse, int64_t R,
+                                                                        int splits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * COMBINE_WAVES + (threadIdx.x >> 6);
   const int64_t stride = R * MH;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_lse[s * stride + rh]);
-  float den = 0.f;
-  if (M != -INFINITY)
-    for (int s = 0; s < splits; ++s) den += exp2f(part_lse[s * stride + rh] - M);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    const float inv = 1.f / den;
-    for (int s = 0; s < splits; ++s) {
-      const float wgt = exp2f(part_lse[s * stride + rh] - M) * inv;
-      if (wgt != 0.f) {
-        const u32x2 pk = *reinterpret_cast<const u32x2*>(part_o + (s * stride + rh) * MDV + 4 * tid);
-        const f32x4 v = {bf16_bits_to_float(pk.x & 0xffffu), bf16_bits_to_float(pk.x >> 16),
-                         bf16_bits_to_float(pk.y & 0xffffu), bf16_bits_to_float(pk.y >> 16)};
-        acc += wgt * v;
+  if (rh >= stride) return;  // whole waves only
+  // lane s < splits holds split s's log2-sum-exp (splits <= 32)
+  const float ls = lane < splits ? part_lse[lane * stride + rh] : -INFINITY;
+  float M = ls;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float e = M == -INFINITY ? 0.f : exp2f(ls - M);  // exp2(-inf) = 0 for empty splits
+  float den = e;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint16_t* base = part_o + rh * MDV + 8 * lane;
+  for (int s0 = 0; s0 < splits; s0 += COMBINE_CHUNK) {
+    uint4 v[COMBINE_CHUNK];
+#pragma unroll
+    for (int c = 0; c < COMBINE_CHUNK; ++c) {  // past the last split: reread it with weight 0
+      const int s = min(s0 + c, splits - 1);
+      v[c] = *reinterpret_cast<const uint4*>(base + s * stride * MDV);
+    }
+#pragma unroll
+    for (int c = 0; c < COMBINE_CHUNK; ++c) {
+      const float w = s0 + c < splits ? __shfl(e, s0 + c) * inv : 0.f;
+      const uint32_t wd[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += w * bf16_bits_to_float(wd[k] & 0xffffu);
+        acc[2 * k + 1] += w * bf16_bits_to_float(wd[k] >> 16);
       }
     }
   }
-  u32x2 pk;
-  pk.x = pack_bf16x2(acc.x, acc.y);
-  pk.y = pack_bf16x2(acc.z, acc.w);
-  *reinterpret_cast<u32x2*>(out + rh * MDV + 4 * tid) = pk;
-  if (lse != nullptr && tid == 0) lse[rh] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * LN2;
+  uint4 pk;
+  pk.x = pack_bf16x2(acc[0], acc[1]);
+  pk.y = pack_bf16x2(acc[2], acc[3]);
+  pk.z = pack_bf16x2(acc[4], acc[5]);
+  pk.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(out + rh * MDV + 8 * lane) = pk;
+  if (lse != nullptr && lane == 0) lse[rh] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * LN2;
 }
 
 // Generic fp32 kernel for small problems: one wave per (query, head), keys in
@@ -621,8 +650,10 @@ hipError_t launch_sparse_mla_bf16(const uint16_t* q, const uint16_t* kv, const i
                      idx, out, lse, part_o, part_lse, R, Tq, N, K, splits, kps, scale * LOG2E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(R * MH)), dim3(128), 0, stream, part_o, part_lse, out, lse,
-                     R, splits);
+  if (splits > 64) return hipErrorInvalidValue;  // the combine holds one split per lane
+  const int64_t cwg = (R * MH + COMBINE_WAVES - 1) / COMBINE_WAVES;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)cwg), dim3(64 * COMBINE_WAVES), 0, stream, part_o, part_lse,
+                     out, lse, R, splits);
   return hipGetLastError();
 }
 
