@@ -20,24 +20,25 @@
 //    the row staged once in LDS, three histogram passes (11, 11 and 10 bits),
 //    then an in-order compaction with one block prefix sum per 16384 keys;
 //  * long rows (decode at long context): each row is cut into 16384-key
-//    segments, one workgroup per segment holds its keys in registers, and
-//    four short kernels replace the serial passes:
-//      1. per-segment histogram of key bits 31..21 (2048 bins);
-//      2. every segment sums the row's bit-31..21 histograms, finds that
-//         digit of T, and histograms bits 20..10 of the keys that share it;
-//      3. every segment finds bits 31..10 of T (the top digit recorded by
-//         step 2) and writes, in index order,
-//         the keys above that prefix ("definite") and the keys on it
-//         ("candidates", low 10 bits + index);
-//      4. one workgroup per row resolves the last 10 bits of T among the
-//         candidates and merges the two ascending lists into the output.
-//    Per-segment histograms are plain stores (no atomics, no zeroing); a row
-//    whose candidates overflow their buffers falls back to the one-workgroup
+//    segments, and two kernels replace the serial passes:
+//      1. one workgroup per segment holds its keys in registers, finds bounds
+//         t_lo <= t_hi on T from a 4096-key sample of the row (exact selects
+//         at two sample ranks around the one expected to hold T; every
+//         segment of a row derives the same bounds), and writes, in index
+//         order, its keys above t_hi ("definite") and its keys in
+//         [t_lo, t_hi] ("candidates", key + index);
+//      2. one workgroup per row checks that at most K keys are definite and
+//         at least K are definite or candidates, selects the K - #definite
+//         best candidates exactly, and merges the two ascending lists into
+//         the output.
+//    The scores are read once (plus the sample).  A row whose bounds miss or
+//    whose candidates overflow their buffers (scores ordered by position, a
+//    large block of equal keys at the cut) falls back to the one-workgroup
 //    method reading the row from global memory.
-// Histograms use plain LDS atomics: even for rows whose scores crowd into a
-// few top-bit bins this measured faster than combining equal bins across a
-// wave first.  Each thread owns a run of consecutive keys, so one block-wide
-// prefix sum orders a whole chunk.
+// Histograms use plain LDS atomics; where the keys crowd into a narrow range
+// (a sample, a candidate list) each thread first counts its own repeated bins
+// in registers.  Each thread owns a run of consecutive keys, so one
+// block-wide prefix sum orders a whole chunk.
 #include "device_common.h"
 #include "launch.h"
 
@@ -51,7 +52,7 @@ constexpr int SEG = 16384;            // segment length of the long-row method
 constexpr int SEG_PER_T = SEG / TK_THREADS;
 constexpr int HB = 2048;              // bins of an 11-bit digit
 constexpr int CAND_CAP = 1024;        // candidates a segment may hand over
-constexpr int ROW_CAND_CAP = 2048;    // candidates the final step can hold for one row
+constexpr int ROW_CAND_CAP = 4096;    // candidates the final step can hold for one row
 constexpr int LONG_MAX_K = 4096;      // largest K of the long-row method
 constexpr int64_t LONG_MAX_SEGS = 4096;  // bound on rows x segments (workspace size)
 constexpr int LONG_MAX_G = TK_THREADS;   // bound on segments per row (one thread per segment)
@@ -65,12 +66,7 @@ __device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N,
 // Exclusive block-wide prefix sum of v; `total` receives the block sum.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, uint32_t* sbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sbuf[wave] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;
@@ -210,14 +206,17 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(const float* __re
 
 // ---------------------------------------------------------------- long rows
 
+constexpr int SAMPLE_BLOCKS = 64;                        // runs of consecutive keys in a row's sample
+constexpr int SAMPLE_RUN = 64;                           // keys per run
+constexpr int SAMPLES = SAMPLE_BLOCKS * SAMPLE_RUN;      // 4096
+constexpr int SAMPLE_PER_T = SAMPLES / TK_THREADS;       // 4
+static_assert(SAMPLE_PER_T * TK_THREADS == SAMPLES && SAMPLE_RUN % SAMPLE_PER_T == 0, "sample geometry");
+
 struct LongWs {
-  uint32_t* hist1;  // [R][G][HB]
-  uint32_t* hist2;  // [R][G][HB]
-  uint32_t* defc;   // [R][G] definite keys per segment
+  uint32_t* defc;   // [R][G] definite keys per segment (may exceed K: the bounds missed)
   uint32_t* candc;  // [R][G] candidates per segment (may exceed CAND_CAP: overflow)
-  uint32_t* rowd1;  // [R][2] digit 31..21 of the row's threshold and the count of keys above it
   int32_t* defi;    // [R][G][K] definite key indices, ascending within a segment
-  uint2* cand;      // [R][G][CAND_CAP] (low 10 key bits, index)
+  uint2* cand;      // [R][G][CAND_CAP] (key, index), ascending index within a segment
 };
 
 __host__ __device__ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -225,22 +224,16 @@ __host__ __device__ inline size_t align_up(size_t x) { return (x + 255) & ~size_
 __host__ __device__ inline LongWs long_ws(void* base, int64_t R, int G, int K) {
   char* p = static_cast<char*>(base);
   LongWs w;
-  const size_t hs = align_up((size_t)R * G * HB * 4);
-  w.hist1 = reinterpret_cast<uint32_t*>(p);
-  w.hist2 = reinterpret_cast<uint32_t*>(p + hs);
-  w.defc = reinterpret_cast<uint32_t*>(p + 2 * hs);
+  const size_t cs = align_up((size_t)R * G * 8);
+  w.defc = reinterpret_cast<uint32_t*>(p);
   w.candc = w.defc + (size_t)R * G;
-  w.rowd1 = w.candc + (size_t)R * G;
-  const size_t cs = align_up((size_t)R * G * 8 + (size_t)R * 8);
-  w.defi = reinterpret_cast<int32_t*>(p + 2 * hs + cs);
-  w.cand = reinterpret_cast<uint2*>(p + 2 * hs + cs + align_up((size_t)R * G * K * 4));
+  w.defi = reinterpret_cast<int32_t*>(p + cs);
+  w.cand = reinterpret_cast<uint2*>(p + cs + align_up((size_t)R * G * K * 4));
   return w;
 }
 
 size_t long_ws_bytes(int64_t R, int G, int K) {
-  return 2 * align_up((size_t)R * G * HB * 4) + align_up((size_t)R * G * 8 + (size_t)R * 8) +
-         align_up((size_t)R * G * K * 4) +
-         align_up((size_t)R * G * CAND_CAP * 8);
+  return align_up((size_t)R * G * 8) + align_up((size_t)R * G * K * 4) + align_up((size_t)R * G * CAND_CAP * 8);
 }
 
 // Keys of this workgroup's segment: thread t holds the run
@@ -263,133 +256,218 @@ __device__ __forceinline__ void load_segment(const float* __restrict__ src, int6
   }
 }
 
-// hs[b] = sum over the row's nseg segment histograms h[seg][b]; loads are
-// issued eight segments at a time so their latencies overlap.
-__device__ __forceinline__ void sum_hist(const uint32_t* __restrict__ h, int nseg, uint32_t* hs) {
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) {
-    uint32_t s = 0;
-    for (int g0 = 0; g0 < nseg; g0 += 8) {
-      uint32_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = g0 + u < nseg ? h[(size_t)(g0 + u) * HB + b] : 0u;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+// Histogram insertion for crowded bins (the keys of a sample or of a
+// candidate list sit in a narrow range, so a whole wave's plain LDS atomics
+// would queue on one address): a thread counts its first two distinct bins in
+// registers and sends only other bins to LDS; each register count then goes
+// out with one atomic, or with one atomic per wave when every lane of the
+// wave holds the same bin.  flush() must be called by all 64 lanes of a wave.
+struct HotBins {
+  uint32_t b0 = 0u, c0 = 0u, b1 = 0u, c1 = 0u;
+  __device__ __forceinline__ void add(uint32_t bin, uint32_t* h) {
+    if (c0 != 0u && bin == b0) {
+      ++c0;
+    } else if (c1 != 0u && bin == b1) {
+      ++c1;
+    } else if (c0 == 0u) {
+      b0 = bin;
+      c0 = 1u;
+    } else if (c1 == 0u) {
+      b1 = bin;
+      c1 = 1u;
+    } else {
+      atomicAdd(&h[bin], 1u);
     }
-    hs[b] = s;
   }
-  __syncthreads();
-}
-
-// Shared memory of the three segment steps.
-struct SegSmem {
-  uint32_t h[HB];
-  uint32_t hs[HB];
-  uint32_t sbuf[TK_WAVES];
-  uint32_t s_res[2];
+  __device__ __forceinline__ static void flush_one(uint32_t b, uint32_t c, uint32_t* h) {
+    const uint32_t bl = __builtin_amdgcn_readfirstlane(b);
+    if (__ballot(c == 0u || b == bl) == ~0ull) {
+      const uint32_t t = wave_sum(c);
+      if ((threadIdx.x & 63) == 0 && t != 0u) atomicAdd(&h[bl], t);
+    } else if (c != 0u) {
+      atomicAdd(&h[b], c);
+    }
+  }
+  __device__ __forceinline__ void flush(uint32_t* h) const {
+    flush_one(b0, c0, h);
+    flush_one(b1, c1, h);
+  }
 };
 
-// Step 1: histogram of key bits 31..21 of this segment.
-__device__ void seg_hist1(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t n, uint32_t* __restrict__ dst,
-                          SegSmem& sm) {
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) sm.h[b] = 0;
-  __syncthreads();
-  const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u)
-    if (i0 + u < n) atomicAdd(&sm.h[k[u] >> 21], 1u);
-  __syncthreads();
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) dst[b] = sm.h[b];
-}
+constexpr int FB = 4096;                   // bins of the range-adaptive histograms
+constexpr int FB_PER_T = FB / TK_THREADS;  // bins per thread when scanning them
+constexpr int FB_BITS = 12;
 
-// Step 2: digit 31..21 of T from the row's step-1 histograms, then a
-// histogram of bits 20..10 of this segment's keys that share it.
-__device__ void seg_hist2(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t n, int K, int nseg,
-                          const uint32_t* __restrict__ row_hist1, uint32_t* __restrict__ dst,
-                          uint32_t* __restrict__ row_d1, bool first, SegSmem& sm) {
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) sm.h[b] = 0;
-  sum_hist(row_hist1, nseg, sm.hs);
-  uint32_t above;
-  const uint32_t d1 = find_digit(sm.hs, HB, (uint32_t)K, above, sm.sbuf, sm.s_res);
-  if (first && threadIdx.x == 0) {  // every segment finds the same digit; the first records it for step 3
-    row_d1[0] = d1;
-    row_d1[1] = above;
-  }
-  const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u)
-    if (i0 + u < n && (k[u] >> 21) == d1) atomicAdd(&sm.h[(k[u] >> 10) & (HB - 1)], 1u);
-  __syncthreads();
-  for (int b = threadIdx.x; b < HB; b += TK_THREADS) dst[b] = sm.h[b];
-}
+// Number of bits needed for x (0 for x == 0).
+__device__ __forceinline__ int bit_width(uint32_t x) { return x == 0u ? 0 : 32 - __clz(x); }
 
-// Step 3: bits 31..10 of T, then this segment's keys above that prefix
-// (definite) and on it (candidates), in index order.
-__device__ void seg_classify(const uint32_t (&k)[SEG_PER_T], int64_t seg0, int64_t n, int K, int nseg,
-                             const uint32_t* __restrict__ row_d1, const uint32_t* __restrict__ row_hist2,
-                             const LongWs& ws, size_t sidx, SegSmem& sm) {
-  uint32_t above;
-  const uint32_t d1 = row_d1[0];
-  const uint32_t kk1 = (uint32_t)K - row_d1[1];
-  sum_hist(row_hist2, nseg, sm.hs);
-  const uint32_t d2 = find_digit(sm.hs, HB, kk1, above, sm.sbuf, sm.s_res);
-  const uint32_t p22 = (d1 << 11) | d2;
-
-  int32_t* defi = ws.defi + sidx * K;
-  uint2* cand = ws.cand + sidx * CAND_CAP;
-  const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
-  uint32_t nd = 0, nc = 0;
+// Given a histogram h of FB bins, find for each of two descending ranks
+// ra, rb (1-based, at most the histogram total) the bin that holds it;
+// *_above receives how many counted keys lie in higher bins.
+__device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, uint32_t rb, uint32_t& ba,
+                                              uint32_t& above_a, uint32_t& bb, uint32_t& above_b, uint32_t* sbuf,
+                                              uint32_t* s_res) {
+  const int tid = threadIdx.x;
+  uint32_t c[FB_PER_T], t = 0;
 #pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u) {
-    const bool valid = i0 + u < n;
-    nd += valid && (k[u] >> 10) > p22;
-    nc += valid && (k[u] >> 10) == p22;
+  for (int u = 0; u < FB_PER_T; ++u) {  // thread t owns bins FB-1-FB_PER_T*t-u, descending
+    c[u] = h[FB - 1 - FB_PER_T * tid - u];
+    t += c[u];
   }
   uint32_t tot;
-  const uint32_t ex = block_excl_scan((nc << 16) | nd, tot, sm.sbuf);
-  uint32_t pd = ex & 0xffffu, pc = ex >> 16;
+  uint32_t run = block_excl_scan(t, tot, sbuf);
 #pragma unroll
-  for (int u = 0; u < SEG_PER_T; ++u) {
-    if (i0 + u >= n) break;
-    const uint32_t top = k[u] >> 10;
-    if (top > p22) defi[pd++] = (int32_t)(i0 + u);
-    else if (top == p22) {
-      if (pc < CAND_CAP) cand[pc] = make_uint2(k[u] & 1023u, (uint32_t)(i0 + u));
-      ++pc;
+  for (int u = 0; u < FB_PER_T; ++u) {
+    const uint32_t b = (uint32_t)(FB - 1 - FB_PER_T * tid - u);
+    if (run < ra && ra <= run + c[u]) {
+      s_res[0] = b;
+      s_res[1] = run;
+    }
+    if (run < rb && rb <= run + c[u]) {
+      s_res[2] = b;
+      s_res[3] = run;
+    }
+    run += c[u];
+  }
+  __syncthreads();
+  ba = s_res[0];
+  above_a = s_res[1];
+  bb = s_res[2];
+  above_b = s_res[3];
+  __syncthreads();
+}
+
+// Smallest and largest of the valid keys held PER per thread (block-wide).
+template <int PER>
+__device__ __forceinline__ void block_min_max(const uint32_t (&k)[PER], const bool (&valid)[PER], uint32_t& kmin,
+                                              uint32_t& kmax, uint32_t* sbuf2) {
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (valid[u]) {
+      mn = min(mn, k[u]);
+      mx = max(mx, k[u]);
+    }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sbuf2[2 * wave] = mn;
+    sbuf2[2 * wave + 1] = mx;
+  }
+  __syncthreads();
+  mn = 0xffffffffu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < TK_WAVES; ++w) {
+    mn = min(mn, sbuf2[2 * w]);
+    mx = max(mx, sbuf2[2 * w + 1]);
+  }
+  kmin = mn;
+  kmax = mx;
+  __syncthreads();
+}
+
+// Histogram of the valid keys in [lo, lo + (FB << shift)) on FB bins of
+// (key - lo) >> shift; keys outside are not counted.
+template <int PER>
+__device__ __forceinline__ void range_hist(const uint32_t (&k)[PER], const bool (&valid)[PER], uint32_t lo,
+                                           uint32_t hi, int shift, uint32_t* h) {
+  for (int b = threadIdx.x; b < FB; b += TK_THREADS) h[b] = 0;
+  __syncthreads();
+  HotBins hb;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (valid[u] && k[u] >= lo && k[u] <= hi) hb.add((k[u] - lo) >> shift, h);
+  hb.flush(h);
+  __syncthreads();
+}
+
+// Exact select among the valid keys in [lo, hi] held PER per thread: the key
+// value at descending rank r (1 <= r <= their number), and in `above` how
+// many of them exceed it.  Each round splits the remaining key range into FB
+// bins and keeps the bin holding rank r, so a range of b bits takes
+// ceil(b / 12) rounds.
+template <int PER>
+__device__ uint32_t select_rank(const uint32_t (&k)[PER], const bool (&valid)[PER], uint32_t lo, uint32_t hi,
+                                uint32_t r, uint32_t& above, uint32_t* h, uint32_t* sbuf, uint32_t* s_res) {
+  above = 0;
+#pragma unroll 1
+  while (true) {
+    const int shift = max(0, bit_width(hi - lo) - FB_BITS);
+    range_hist<PER>(k, valid, lo, hi, shift, h);
+    uint32_t b, ab, b2, ab2;
+    find_two_bins(h, r, r, b, ab, b2, ab2, sbuf, s_res);
+    above += ab;
+    r -= ab;
+    const uint32_t nlo = lo + (b << shift);
+    const uint32_t nhi = (uint32_t)min((uint64_t)hi, (uint64_t)nlo + ((uint64_t)1 << shift) - 1);
+    lo = nlo;
+    hi = nhi;
+    if (shift == 0) return lo;
+  }
+}
+
+// Bounds on the row's threshold from a sample of its keys: SAMPLE_BLOCKS runs
+// of SAMPLE_RUN consecutive keys spread evenly over the row (the whole row
+// when it has at most SAMPLES keys).  With e = K * S / n the expected sample
+// rank of the K-th largest key, r_hi ~ e - 4 sqrt(e) and r_lo ~ e + 4 sqrt(e);
+// one histogram over the sample's key range gives the bins holding those
+// ranks, and t_hi is the top of the first, t_lo the bottom of the second (at
+// most r_hi - 1 sample keys lie above t_hi, at least r_lo lie at or above
+// t_lo).  Any two keys would keep the method exact (the final step checks
+// them); these make the checks pass with overwhelming probability unless the
+// scores are strongly ordered by position, and keep the candidate list short.
+__device__ void sample_bounds(const float* __restrict__ src, int64_t n, int K, uint32_t& t_hi, uint32_t& t_lo,
+                              uint32_t* h, uint32_t* sbuf, uint32_t* s_res) {
+  uint32_t k[SAMPLE_PER_T];
+  bool valid[SAMPLE_PER_T];
+  int S;
+  if (n <= SAMPLES) {
+    S = (int)n;
+#pragma unroll
+    for (int u = 0; u < SAMPLE_PER_T; ++u) {
+      const int j = (int)threadIdx.x + TK_THREADS * u;
+      valid[u] = j < S;
+      k[u] = valid[u] ? float_order_key(src[j]) : 0u;
+    }
+  } else {
+    S = SAMPLES;
+    const int j0 = SAMPLE_PER_T * (int)threadIdx.x;  // a thread's samples lie in one run
+    const int64_t blk = j0 / SAMPLE_RUN;
+    const int64_t start = blk * (n - SAMPLE_RUN) / (SAMPLE_BLOCKS - 1);
+#pragma unroll
+    for (int u = 0; u < SAMPLE_PER_T; ++u) {
+      valid[u] = true;
+      k[u] = float_order_key(src[start + (j0 % SAMPLE_RUN) + u]);
     }
   }
-  if (threadIdx.x == 0) {
-    ws.defc[sidx] = tot & 0xffffu;
-    ws.candc[sidx] = tot >> 16;
-  }
+  const float e = (float)K * (float)S / (float)n;
+  const float sd = 4.f * sqrtf(e) + 2.f;
+  int r_hi = (int)floorf(e - sd), r_lo = (int)ceilf(e + sd);
+  r_hi = max(1, min(r_hi, S));
+  r_lo = max(r_hi, min(r_lo, S));
+  uint32_t kmin, kmax;
+  block_min_max<SAMPLE_PER_T>(k, valid, kmin, kmax, sbuf + TK_WAVES);
+  const int shift = max(0, bit_width(kmax - kmin) - FB_BITS);
+  range_hist<SAMPLE_PER_T>(k, valid, kmin, kmax, shift, h);
+  uint32_t b_hi, ab_hi, b_lo, ab_lo;
+  find_two_bins(h, (uint32_t)r_hi, (uint32_t)r_lo, b_hi, ab_hi, b_lo, ab_lo, sbuf, s_res);
+  t_hi = (uint32_t)min((uint64_t)kmax, (uint64_t)kmin + ((uint64_t)(b_hi + 1) << shift) - 1);
+  t_lo = kmin + (b_lo << shift);
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_seg_hist1(const float* __restrict__ scores, LongWs ws,
-                                                             int64_t Tq, int64_t N, int64_t q_pos0, int K, int G) {
-  __shared__ SegSmem sm;
-  const int64_t row = blockIdx.y;
-  const int g = blockIdx.x;
-  const int64_t n = n_visible(row, Tq, N, q_pos0);
-  const int64_t seg0 = (int64_t)g * SEG;
-  if (n <= K || seg0 >= n) return;
-  uint32_t k[SEG_PER_T];
-  load_segment(scores + row * N, seg0, n, k);
-  seg_hist1(k, seg0, n, ws.hist1 + ((size_t)row * G + g) * HB, sm);
-}
+// Shared memory of the segment step.
+struct SegSmem {
+  uint32_t h[FB];
+  uint32_t sbuf[3 * TK_WAVES];
+  uint32_t s_res[4];
+};
 
-__global__ __launch_bounds__(TK_THREADS) void topk_seg_hist2(const float* __restrict__ scores, LongWs ws,
-                                                             int64_t Tq, int64_t N, int64_t q_pos0, int K, int G) {
-  __shared__ SegSmem sm;
-  const int64_t row = blockIdx.y;
-  const int g = blockIdx.x;
-  const int64_t n = n_visible(row, Tq, N, q_pos0);
-  const int64_t seg0 = (int64_t)g * SEG;
-  if (n <= K || seg0 >= n) return;
-  uint32_t k[SEG_PER_T];
-  load_segment(scores + row * N, seg0, n, k);
-  seg_hist2(k, seg0, n, K, (int)((n + SEG - 1) / SEG), ws.hist1 + (size_t)row * G * HB,
-            ws.hist2 + ((size_t)row * G + g) * HB, ws.rowd1 + 2 * row, g == 0, sm);
-}
-
+// Step 1, one workgroup per segment: the row's bounds t_lo <= t_hi from its
+// sample (every segment of a row computes the same ones), then this
+// segment's keys above t_hi ("definite", index order) and its keys in
+// [t_lo, t_hi] ("candidates", key and index, index order).
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __restrict__ scores, LongWs ws,
                                                                 int64_t Tq, int64_t N, int64_t q_pos0, int K,
                                                                 int G) {
@@ -399,36 +477,63 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __r
   const int64_t n = n_visible(row, Tq, N, q_pos0);
   const int64_t seg0 = (int64_t)g * SEG;
   if (n <= K || seg0 >= n) return;
+  const float* src = scores + row * N;
   uint32_t k[SEG_PER_T];
-  load_segment(scores + row * N, seg0, n, k);
-  seg_classify(k, seg0, n, K, (int)((n + SEG - 1) / SEG), ws.rowd1 + 2 * row,
-               ws.hist2 + (size_t)row * G * HB, ws, (size_t)row * G + g, sm);
+  load_segment(src, seg0, n, k);
+  uint32_t t_hi, t_lo;
+  sample_bounds(src, n, K, t_hi, t_lo, sm.h, sm.sbuf, sm.s_res);
+
+  const size_t sidx = (size_t)row * G + g;
+  int32_t* defi = ws.defi + sidx * K;
+  uint2* cand = ws.cand + sidx * CAND_CAP;
+  const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
+  uint32_t nd = 0, nc = 0;
+#pragma unroll
+  for (int u = 0; u < SEG_PER_T; ++u) {
+    const bool v = i0 + u < n;
+    nd += v && k[u] > t_hi;
+    nc += v && k[u] >= t_lo && k[u] <= t_hi;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan((nc << 16) | nd, tot, sm.sbuf);
+  uint32_t pd = ex & 0xffffu, pc = ex >> 16;
+#pragma unroll
+  for (int u = 0; u < SEG_PER_T; ++u) {
+    if (i0 + u >= n) break;
+    if (k[u] > t_hi) {
+      if (pd < (uint32_t)K) defi[pd] = (int32_t)(i0 + u);
+      ++pd;
+    } else if (k[u] >= t_lo) {
+      if (pc < CAND_CAP) cand[pc] = make_uint2(k[u], (uint32_t)(i0 + u));
+      ++pc;
+    }
+  }
+  if (threadIdx.x == 0) {
+    ws.defc[sidx] = tot & 0xffffu;
+    ws.candc[sidx] = tot >> 16;
+  }
 }
 
 // Shared memory of the final step.
 struct FinalSmem {
-  uint32_t ck[ROW_CAND_CAP];   // candidate low key bits, index order
+  uint32_t ck[ROW_CAND_CAP];   // candidate keys, index order
   int32_t ci[ROW_CAND_CAP];    // candidate indices
   int32_t dl[LONG_MAX_K];      // definite indices, ascending
   int32_t sl[LONG_MAX_K];      // kept candidate indices, ascending
-  uint32_t h[HB];              // 1024 bins here; 2048 in the fallback
-  uint32_t sbuf[TK_WAVES];
-  uint32_t s_res[2];
+  uint32_t h[FB];               // FB >= HB: also the fallback's histogram
+  uint32_t sbuf[3 * TK_WAVES];
+  uint32_t s_res[4];
   uint32_t s_doff[LONG_MAX_G + 1];
   uint32_t s_coff[LONG_MAX_G + 1];
 };
 
+// Step 2, one workgroup per row: check the bounds (the definite keys are at
+// most K and, with the candidates, at least K; no list overflowed), keep the
+// K - #definite best candidates (exact select on their full keys), and merge
+// the two ascending lists into the output.  If a check fails, the exact
+// one-workgroup method runs over the row from global memory instead.
 __device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws, int32_t* __restrict__ idx,
                               int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, int K, int G, FinalSmem& sm) {
-  uint32_t* ck = sm.ck;
-  int32_t* ci = sm.ci;
-  int32_t* dl = sm.dl;
-  int32_t* sl = sm.sl;
-  uint32_t* h = sm.h;
-  uint32_t* sbuf = sm.sbuf;
-  uint32_t* s_res = sm.s_res;
-  uint32_t* s_doff = sm.s_doff;
-  uint32_t* s_coff = sm.s_coff;
   const int tid = threadIdx.x;
   const int64_t n = n_visible(row, Tq, N, q_pos0);
   int32_t* out = idx + row * K;
@@ -439,29 +544,30 @@ __device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws
   const int nseg = (int)((n + SEG - 1) / SEG);
   const size_t s0 = (size_t)row * G;
   // per-segment list offsets: exclusive prefix sums of the counts (nseg <= TK_THREADS)
+  bool ok;
   {
     const uint32_t dc = tid < nseg ? ws.defc[s0 + tid] : 0u;
     const uint32_t cc = tid < nseg ? ws.candc[s0 + tid] : 0u;
     uint32_t dtot, ctot, otot;
-    const uint32_t dex = block_excl_scan(dc, dtot, sbuf);
-    const uint32_t cex = block_excl_scan(cc, ctot, sbuf);
-    block_excl_scan(cc > CAND_CAP ? 1u : 0u, otot, sbuf);
+    const uint32_t dex = block_excl_scan(dc, dtot, sm.sbuf);
+    const uint32_t cex = block_excl_scan(cc, ctot, sm.sbuf);
+    block_excl_scan(cc > CAND_CAP ? 1u : 0u, otot, sm.sbuf);
     if (tid < nseg) {
-      s_doff[tid] = dex;
-      s_coff[tid] = cex;
+      sm.s_doff[tid] = dex;
+      sm.s_coff[tid] = cex;
     }
     if (tid == 0) {
-      s_doff[nseg] = dtot;
-      s_coff[nseg] = otot ? 0xffffffffu : ctot;
+      sm.s_doff[nseg] = dtot;
+      sm.s_coff[nseg] = ctot;
     }
+    ok = otot == 0 && dtot <= (uint32_t)K && ctot <= (uint32_t)ROW_CAND_CAP && dtot + ctot >= (uint32_t)K;
     __syncthreads();
   }
-  const uint32_t ndef = s_doff[nseg], ncand = s_coff[nseg];
-  if (ncand > ROW_CAND_CAP) {
-    // many equal keys at the boundary: exact one-workgroup method over the whole row
-    select_row(scores + row * N, n, K, out, nullptr, h, sbuf, s_res);
+  if (!ok) {
+    select_row(scores + row * N, n, K, out, nullptr, sm.h, sm.sbuf, sm.s_res);
     return;
   }
+  const uint32_t ndef = sm.s_doff[nseg], ncand = sm.s_coff[nseg];
   // gather both lists in segment order (ascending index); every load independent
   auto seg_of = [&](const uint32_t* off, uint32_t j) {
     int lo = 0, hi = nseg;  // largest g with off[g] <= j
@@ -473,37 +579,48 @@ __device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws
     return lo;
   };
   for (uint32_t j = tid; j < ndef; j += TK_THREADS) {
-    const int g = seg_of(s_doff, j);
-    dl[j] = ws.defi[(s0 + g) * K + (j - s_doff[g])];
+    const int g = seg_of(sm.s_doff, j);
+    sm.dl[j] = ws.defi[(s0 + g) * K + (j - sm.s_doff[g])];
   }
-  for (uint32_t j = tid; j < ncand; j += TK_THREADS) {
-    const int g = seg_of(s_coff, j);
-    const uint2 v = ws.cand[(s0 + g) * CAND_CAP + (j - s_coff[g])];
-    ck[j] = v.x;
-    ci[j] = (int32_t)v.y;
+  constexpr int CPT = ROW_CAND_CAP / TK_THREADS;  // candidates per thread
+  uint32_t ck[CPT];
+  bool cv[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const uint32_t j = tid + TK_THREADS * u;
+    cv[u] = j < ncand;
+    ck[u] = 0u;
+    if (cv[u]) {
+      const int g = seg_of(sm.s_coff, j);
+      const uint2 v = ws.cand[(s0 + g) * CAND_CAP + (j - sm.s_coff[g])];
+      ck[u] = v.x;
+      sm.ck[j] = v.x;
+      sm.ci[j] = (int32_t)v.y;
+    }
   }
-  for (int b = tid; b < 1024; b += TK_THREADS) h[b] = 0;
+  const uint32_t kk = (uint32_t)K - ndef;  // candidates to keep (0 <= kk <= ncand)
+  uint32_t T = 0xffffffffu, keq = 0;
+  if (kk > 0) {  // candidates lie in [t_lo, t_hi]; their own range is found first
+    uint32_t cmin, cmax, above;
+    block_min_max<CPT>(ck, cv, cmin, cmax, sm.sbuf + TK_WAVES);
+    T = select_rank<CPT>(ck, cv, cmin, cmax, kk, above, sm.h, sm.sbuf, sm.s_res);
+    keq = kk - above;
+  }
   __syncthreads();
-  for (uint32_t j = tid; j < ncand; j += TK_THREADS) atomicAdd(&h[ck[j]], 1u);
-  __syncthreads();
-  const uint32_t kk = (uint32_t)K - ndef;  // candidates to keep (1 <= kk <= ncand)
-  uint32_t above;
-  const uint32_t d3 = find_digit(h, 1024, kk, above, sbuf, s_res);
-  const uint32_t keq = kk - above;
   // kept candidates, in index order
   uint32_t run_sel = 0, run_eq = 0;
   for (uint32_t base = 0; base < ncand; base += TK_THREADS) {
     const uint32_t j = base + tid;
     uint32_t gt = 0, eq = 0;
-    if (j < ncand) {
-      gt = ck[j] > d3;
-      eq = ck[j] == d3;
+    if (j < ncand && kk > 0) {
+      gt = sm.ck[j] > T;
+      eq = sm.ck[j] == T;
     }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sbuf);
+    const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sm.sbuf);
     const uint32_t gb = run_sel + (ex & 0xffffu), eb = run_eq + (ex >> 16);
-    if (gt) sl[gb + min(eb, keq)] = ci[j];
-    else if (eq && eb < keq) sl[gb + eb] = ci[j];
+    if (gt) sm.sl[gb + min(eb, keq)] = sm.ci[j];
+    else if (eq && eb < keq) sm.sl[gb + eb] = sm.ci[j];
     run_sel += tot & 0xffffu;
     run_eq += tot >> 16;
   }
@@ -518,8 +635,8 @@ __device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws
     }
     return lo;
   };
-  for (uint32_t j = tid; j < ndef; j += TK_THREADS) out[j + lower(sl, kk, dl[j])] = dl[j];
-  for (uint32_t j = tid; j < kk; j += TK_THREADS) out[j + lower(dl, ndef, sl[j])] = sl[j];
+  for (uint32_t j = tid; j < ndef; j += TK_THREADS) out[j + lower(sm.sl, kk, sm.dl[j])] = sm.dl[j];
+  for (uint32_t j = tid; j < kk; j += TK_THREADS) out[j + lower(sm.dl, ndef, sm.sl[j])] = sm.sl[j];
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __restrict__ scores, LongWs ws,
@@ -554,8 +671,6 @@ hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq,
   const int G = long_segments(N);
   const LongWs ws = long_ws(workspace, R, G, K);
   const dim3 grid((unsigned)G, (unsigned)R);
-  hipLaunchKernelGGL(topk_seg_hist1, grid, dim3(TK_THREADS), 0, stream, scores, ws, Tq, N, q_pos0, K, G);
-  hipLaunchKernelGGL(topk_seg_hist2, grid, dim3(TK_THREADS), 0, stream, scores, ws, Tq, N, q_pos0, K, G);
   hipLaunchKernelGGL(topk_seg_classify, grid, dim3(TK_THREADS), 0, stream, scores, ws, Tq, N, q_pos0, K, G);
   hipLaunchKernelGGL(topk_seg_final, dim3((unsigned)R), dim3(TK_THREADS), 0, stream, scores, ws, idx, Tq, N,
                      q_pos0, K, G);

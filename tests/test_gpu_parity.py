@@ -165,6 +165,29 @@ def test_topk_long_rows_heavy_ties(kind):
         assert np.array_equal(idx[0, t], exp), f"{kind} row {t}"
 
 
+def test_topk_long_rows_sample_bounds_miss():
+    """The segmented method bounds the threshold from 64 evenly spaced runs of
+    64 keys.  Here every large score lies outside those runs, so the bounds
+    let through more than K definite keys and the row must fall back to the
+    exact one-workgroup method."""
+    dsa = _dsa()
+    rng = np.random.default_rng(21)
+    N, K = 70000, 2048
+    vals = (rng.random((1, 2, N)) * 0.5).astype(np.float32)
+    sampled = np.zeros(N, dtype=bool)
+    for b in range(64):
+        s0 = b * (N - 64) // 63
+        sampled[s0:s0 + 64] = True
+    outside = np.flatnonzero(~sampled)
+    for t in range(2):
+        big = rng.choice(outside, 5000, replace=False)
+        vals[0, t, big] = (1.0 + rng.random(5000)).astype(np.float32)
+    idx = dsa.topk(torch.from_numpy(vals).cuda(), K, N - 1).cpu().numpy()
+    for t in range(2):
+        exp = oracle.topk_row(vals[0, t, :oracle.n_valid_keys(t, N - 1, N)], K)
+        assert np.array_equal(idx[0, t], exp), f"row {t}"
+
+
 def test_topk_long_rows_many_rows():
     """More segment workgroups than fit on the GPU at once (160 rows x 2 segments):
     the segmented method runs as separate kernels instead of one cooperative one."""
