@@ -17,8 +17,10 @@
 //
 // Two schedules:
 //  * rows of up to 16384 keys (prefill): one 1024-thread workgroup per row,
-//    the row staged once in LDS, three histogram passes (11, 11 and 10 bits),
-//    then an in-order compaction with one block prefix sum per 16384 keys;
+//    the row staged once in LDS with its key range, then exact select rounds
+//    that each split the remaining range into 2048 bins (ceil(bits / 11)
+//    rounds for a range of that many bits), then an in-order compaction with
+//    one block prefix sum per 16384 keys;
 //  * long rows (decode at long context): each row is cut into 16384-key
 //    segments, and two kernels replace the serial passes:
 //      1. one workgroup per segment holds its keys in registers, finds bounds
@@ -81,29 +83,141 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total,
   return before + x - v;
 }
 
-// Given a histogram `h` of `nb` bins (nb <= 2*TK_THREADS) over the keys that
-// share the prefix found so far, find the digit holding the kk-th largest key.
-// Returns the digit; `above` receives how many counted keys lie in higher bins.
-__device__ __forceinline__ uint32_t find_digit(const uint32_t* h, int nb, uint32_t kk, uint32_t& above,
-                                               uint32_t* sbuf, uint32_t* s_res) {
+// ------------------------------------------------- range-adaptive select
+
+// Histogram insertion for crowded bins (a row's keys, a sample or a candidate
+// list often sit in a narrow range, so a whole wave's plain LDS atomics would
+// queue on one address): a thread counts its first two distinct bins in
+// registers and sends only other bins to LDS; each register count then goes
+// out with one atomic, or with one atomic per wave when every lane of the
+// wave holds the same bin.  flush() must be called by all 64 lanes of a wave.
+struct HotBins {
+  uint32_t b0 = 0u, c0 = 0u, b1 = 0u, c1 = 0u;
+  __device__ __forceinline__ void add(uint32_t bin, uint32_t* h) {
+    if (c0 != 0u && bin == b0) {
+      ++c0;
+    } else if (c1 != 0u && bin == b1) {
+      ++c1;
+    } else if (c0 == 0u) {
+      b0 = bin;
+      c0 = 1u;
+    } else if (c1 == 0u) {
+      b1 = bin;
+      c1 = 1u;
+    } else {
+      atomicAdd(&h[bin], 1u);
+    }
+  }
+  __device__ __forceinline__ static void flush_one(uint32_t b, uint32_t c, uint32_t* h) {
+    const uint32_t bl = __builtin_amdgcn_readfirstlane(b);
+    if (__ballot(c == 0u || b == bl) == ~0ull) {
+      const uint32_t t = wave_sum(c);
+      if ((threadIdx.x & 63) == 0 && t != 0u) atomicAdd(&h[bl], t);
+    } else if (c != 0u) {
+      atomicAdd(&h[b], c);
+    }
+  }
+  __device__ __forceinline__ void flush(uint32_t* h) const {
+    flush_one(b0, c0, h);
+    flush_one(b1, c1, h);
+  }
+};
+
+// Number of bits needed for x (0 for x == 0).
+__device__ __forceinline__ int bit_width(uint32_t x) { return x == 0u ? 0 : 32 - __clz(x); }
+
+// Given a histogram h of 2^FBITS bins, find for each of two descending ranks
+// ra, rb (1-based, at most the histogram total) the bin that holds it;
+// *_above receives how many counted keys lie in higher bins.  s_res: 4 words.
+template <int FBITS>
+__device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, uint32_t rb, uint32_t& ba,
+                                              uint32_t& above_a, uint32_t& bb, uint32_t& above_b, uint32_t* sbuf,
+                                              uint32_t* s_res) {
+  constexpr int NB = 1 << FBITS, PER_T = NB / TK_THREADS;
+  static_assert(PER_T * TK_THREADS == NB, "whole bins per thread");
   const int tid = threadIdx.x;
-  // thread t owns bins nb-1-2t and nb-2-2t (descending order)
-  const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
-  const uint32_t c0 = b0 >= 0 ? h[b0] : 0u, c1 = b1 >= 0 ? h[b1] : 0u;
+  uint32_t c[PER_T], t = 0;
+#pragma unroll
+  for (int u = 0; u < PER_T; ++u) {  // thread t owns bins NB-1-PER_T*t-u, descending
+    c[u] = h[NB - 1 - PER_T * tid - u];
+    t += c[u];
+  }
   uint32_t tot;
-  const uint32_t ex = block_excl_scan(c0 + c1, tot, sbuf);
-  if (b0 >= 0 && ex < kk && kk <= ex + c0) {
-    s_res[0] = (uint32_t)b0;
-    s_res[1] = ex;
-  } else if (b1 >= 0 && ex + c0 < kk && kk <= ex + c0 + c1) {
-    s_res[0] = (uint32_t)b1;
-    s_res[1] = ex + c0;
+  uint32_t run = block_excl_scan(t, tot, sbuf);
+#pragma unroll
+  for (int u = 0; u < PER_T; ++u) {
+    const uint32_t b = (uint32_t)(NB - 1 - PER_T * tid - u);
+    if (run < ra && ra <= run + c[u]) {
+      s_res[0] = b;
+      s_res[1] = run;
+    }
+    if (run < rb && rb <= run + c[u]) {
+      s_res[2] = b;
+      s_res[3] = run;
+    }
+    run += c[u];
   }
   __syncthreads();
-  above = s_res[1];
-  const uint32_t d = s_res[0];
+  ba = s_res[0];
+  above_a = s_res[1];
+  bb = s_res[2];
+  above_b = s_res[3];
   __syncthreads();
-  return d;
+}
+
+// Block-wide smallest and largest of per-thread values (mn, mx).
+// sbuf2: 2 * TK_WAVES words.
+__device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t& kmin, uint32_t& kmax,
+                                              uint32_t* sbuf2) {
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sbuf2[2 * wave] = mn;
+    sbuf2[2 * wave + 1] = mx;
+  }
+  __syncthreads();
+  mn = 0xffffffffu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < TK_WAVES; ++w) {
+    mn = min(mn, sbuf2[2 * w]);
+    mx = max(mx, sbuf2[2 * w + 1]);
+  }
+  kmin = mn;
+  kmax = mx;
+  __syncthreads();
+}
+
+// Exact select among the keys in [lo, hi] of a key set: the key value at
+// descending rank r (1 <= r <= their number), and in `above` how many of them
+// exceed it.  Each round splits the remaining key range into 2^FBITS bins of
+// (key - lo) >> shift and keeps the bin holding rank r, so a range of b bits
+// takes ceil(b / FBITS) rounds.  add_keys(hb, lo, hi, shift) must pass every
+// key of the set in [lo, hi] to hb.add((key - lo) >> shift, h).
+template <int FBITS, typename AddKeys>
+__device__ uint32_t select_rank(AddKeys add_keys, uint32_t lo, uint32_t hi, uint32_t r, uint32_t& above,
+                                uint32_t* h, uint32_t* sbuf, uint32_t* s_res) {
+  above = 0;
+#pragma unroll 1
+  while (true) {
+    const int shift = max(0, bit_width(hi - lo) - FBITS);
+    for (int b = threadIdx.x; b < (1 << FBITS); b += TK_THREADS) h[b] = 0;
+    __syncthreads();
+    HotBins hb;
+    add_keys(hb, lo, hi, shift);
+    hb.flush(h);
+    __syncthreads();
+    uint32_t b, ab, b2, ab2;
+    find_two_bins<FBITS>(h, r, r, b, ab, b2, ab2, sbuf, s_res);
+    above += ab;
+    r -= ab;
+    const uint32_t nlo = lo + (b << shift);
+    const uint32_t nhi = (uint32_t)min((uint64_t)hi, (uint64_t)nlo + ((uint64_t)1 << shift) - 1);
+    lo = nlo;
+    hi = nhi;
+    if (shift == 0) return lo;
+  }
 }
 
 // Writes the kept keys of the run [i0, i0 + RUN) (clipped to n) of one chunk:
@@ -126,7 +240,8 @@ __device__ __forceinline__ void emit_run(KeyAt key_at, int64_t i0, int64_t n, ui
 }
 
 // The one-workgroup method for one row.  skey: LDS stage of TK_CAP keys, or
-// nullptr to read the row from global memory on every pass.
+// nullptr to read the row from global memory on every pass.  hist: 2048 bins;
+// sbuf: 3 * TK_WAVES words; s_res: 4 words.
 __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int32_t* __restrict__ out,
                            uint32_t* skey, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res) {
   const int tid = threadIdx.x;
@@ -134,20 +249,32 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
     for (int64_t i = tid; i < K; i += TK_THREADS) out[i] = i < n ? (int32_t)i : -1;
     return;
   }
-  if (skey != nullptr) {
-    for (int64_t i = tid; i < n; i += TK_THREADS) skey[i] = float_order_key(src[i]);
-    __syncthreads();
+  // keys (staged in LDS when skey is given) and their range; eight loads in
+  // flight per thread
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int64_t base = tid; base < n; base += 8 * TK_THREADS) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = base + (int64_t)u * TK_THREADS;
+      v[u] = i < n ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = base + (int64_t)u * TK_THREADS;
+      if (i < n) {
+        const uint32_t k = float_order_key(v[u]);
+        if (skey != nullptr) skey[i] = k;
+        mn = min(mn, k);
+        mx = max(mx, k);
+      }
+    }
   }
+  uint32_t kmin, kmax;
+  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);  // its barriers also publish skey
   auto key_at = [&](int64_t i) -> uint32_t { return skey != nullptr ? skey[i] : float_order_key(src[i]); };
-
-  // three passes: key bits 31..21, 20..10, 9..0
-  uint32_t prefix = 0, mask = 0, kk = (uint32_t)K;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : HB;
-    for (int b = tid; b < nb; b += TK_THREADS) hist[b] = 0;
-    __syncthreads();
+  // (the bins span the keys' own range, so plain atomics rarely collide)
+  auto add_row = [&](HotBins&, uint32_t lo, uint32_t hi, int shift) {
     for (int64_t base = tid; base < n; base += 8 * TK_THREADS) {
       uint32_t k[8];
 #pragma unroll
@@ -158,19 +285,13 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t i = base + (int64_t)u * TK_THREADS;
-        const bool hit = i < n && (k[u] & mask) == prefix;
-        const uint32_t bin = (k[u] >> shift) & (uint32_t)(nb - 1);
-        if (hit) atomicAdd(&hist[bin], 1u);
+        if (i < n && k[u] >= lo && k[u] <= hi) atomicAdd(&hist[(k[u] - lo) >> shift], 1u);
       }
     }
-    __syncthreads();
-    uint32_t above;
-    const uint32_t d = find_digit(hist, nb, kk, above, sbuf, s_res);
-    prefix |= d << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
-    kk -= above;
-  }
-  const uint32_t T = prefix, keq = kk;
+  };
+  uint32_t above;
+  const uint32_t T = select_rank<11>(add_row, kmin, kmax, (uint32_t)K, above, hist, sbuf, s_res);
+  const uint32_t keq = (uint32_t)K - above;
 
   // in-order compaction: thread t owns keys [base + RUN*t, base + RUN*t + RUN)
   uint32_t run_gt = 0, run_eq = 0;
@@ -197,8 +318,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(const float* __re
                                                                int64_t N, int64_t q_pos0, int K) {
   __shared__ uint32_t skey[TK_CAP];
   __shared__ uint32_t hist[HB];
-  __shared__ uint32_t sbuf[TK_WAVES];
-  __shared__ uint32_t s_res[2];
+  __shared__ uint32_t sbuf[3 * TK_WAVES];
+  __shared__ uint32_t s_res[4];
   const int64_t row = blockIdx.x;
   const int64_t n = n_visible(row, Tq, N, q_pos0);
   select_row(scores + row * N, n, K, idx + row * K, n <= TK_CAP ? skey : nullptr, hist, sbuf, s_res);
@@ -211,6 +332,9 @@ constexpr int SAMPLE_RUN = 64;                           // keys per run
 constexpr int SAMPLES = SAMPLE_BLOCKS * SAMPLE_RUN;      // 4096
 constexpr int SAMPLE_PER_T = SAMPLES / TK_THREADS;       // 4
 static_assert(SAMPLE_PER_T * TK_THREADS == SAMPLES && SAMPLE_RUN % SAMPLE_PER_T == 0, "sample geometry");
+
+constexpr int FB_BITS = 12;               // bins of the long-row histograms: 4096
+constexpr int FB = 1 << FB_BITS;
 
 struct LongWs {
   uint32_t* defc;   // [R][G] definite keys per segment (may exceed K: the bounds missed)
@@ -256,158 +380,6 @@ __device__ __forceinline__ void load_segment(const float* __restrict__ src, int6
   }
 }
 
-// Histogram insertion for crowded bins (the keys of a sample or of a
-// candidate list sit in a narrow range, so a whole wave's plain LDS atomics
-// would queue on one address): a thread counts its first two distinct bins in
-// registers and sends only other bins to LDS; each register count then goes
-// out with one atomic, or with one atomic per wave when every lane of the
-// wave holds the same bin.  flush() must be called by all 64 lanes of a wave.
-struct HotBins {
-  uint32_t b0 = 0u, c0 = 0u, b1 = 0u, c1 = 0u;
-  __device__ __forceinline__ void add(uint32_t bin, uint32_t* h) {
-    if (c0 != 0u && bin == b0) {
-      ++c0;
-    } else if (c1 != 0u && bin == b1) {
-      ++c1;
-    } else if (c0 == 0u) {
-      b0 = bin;
-      c0 = 1u;
-    } else if (c1 == 0u) {
-      b1 = bin;
-      c1 = 1u;
-    } else {
-      atomicAdd(&h[bin], 1u);
-    }
-  }
-  __device__ __forceinline__ static void flush_one(uint32_t b, uint32_t c, uint32_t* h) {
-    const uint32_t bl = __builtin_amdgcn_readfirstlane(b);
-    if (__ballot(c == 0u || b == bl) == ~0ull) {
-      const uint32_t t = wave_sum(c);
-      if ((threadIdx.x & 63) == 0 && t != 0u) atomicAdd(&h[bl], t);
-    } else if (c != 0u) {
-      atomicAdd(&h[b], c);
-    }
-  }
-  __device__ __forceinline__ void flush(uint32_t* h) const {
-    flush_one(b0, c0, h);
-    flush_one(b1, c1, h);
-  }
-};
-
-constexpr int FB = 4096;                   // bins of the range-adaptive histograms
-constexpr int FB_PER_T = FB / TK_THREADS;  // bins per thread when scanning them
-constexpr int FB_BITS = 12;
-
-// Number of bits needed for x (0 for x == 0).
-__device__ __forceinline__ int bit_width(uint32_t x) { return x == 0u ? 0 : 32 - __clz(x); }
-
-// Given a histogram h of FB bins, find for each of two descending ranks
-// ra, rb (1-based, at most the histogram total) the bin that holds it;
-// *_above receives how many counted keys lie in higher bins.
-__device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, uint32_t rb, uint32_t& ba,
-                                              uint32_t& above_a, uint32_t& bb, uint32_t& above_b, uint32_t* sbuf,
-                                              uint32_t* s_res) {
-  const int tid = threadIdx.x;
-  uint32_t c[FB_PER_T], t = 0;
-#pragma unroll
-  for (int u = 0; u < FB_PER_T; ++u) {  // thread t owns bins FB-1-FB_PER_T*t-u, descending
-    c[u] = h[FB - 1 - FB_PER_T * tid - u];
-    t += c[u];
-  }
-  uint32_t tot;
-  uint32_t run = block_excl_scan(t, tot, sbuf);
-#pragma unroll
-  for (int u = 0; u < FB_PER_T; ++u) {
-    const uint32_t b = (uint32_t)(FB - 1 - FB_PER_T * tid - u);
-    if (run < ra && ra <= run + c[u]) {
-      s_res[0] = b;
-      s_res[1] = run;
-    }
-    if (run < rb && rb <= run + c[u]) {
-      s_res[2] = b;
-      s_res[3] = run;
-    }
-    run += c[u];
-  }
-  __syncthreads();
-  ba = s_res[0];
-  above_a = s_res[1];
-  bb = s_res[2];
-  above_b = s_res[3];
-  __syncthreads();
-}
-
-// Smallest and largest of the valid keys held PER per thread (block-wide).
-template <int PER>
-__device__ __forceinline__ void block_min_max(const uint32_t (&k)[PER], const bool (&valid)[PER], uint32_t& kmin,
-                                              uint32_t& kmax, uint32_t* sbuf2) {
-  uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-  for (int u = 0; u < PER; ++u)
-    if (valid[u]) {
-      mn = min(mn, k[u]);
-      mx = max(mx, k[u]);
-    }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    sbuf2[2 * wave] = mn;
-    sbuf2[2 * wave + 1] = mx;
-  }
-  __syncthreads();
-  mn = 0xffffffffu;
-  mx = 0u;
-#pragma unroll
-  for (int w = 0; w < TK_WAVES; ++w) {
-    mn = min(mn, sbuf2[2 * w]);
-    mx = max(mx, sbuf2[2 * w + 1]);
-  }
-  kmin = mn;
-  kmax = mx;
-  __syncthreads();
-}
-
-// Histogram of the valid keys in [lo, lo + (FB << shift)) on FB bins of
-// (key - lo) >> shift; keys outside are not counted.
-template <int PER>
-__device__ __forceinline__ void range_hist(const uint32_t (&k)[PER], const bool (&valid)[PER], uint32_t lo,
-                                           uint32_t hi, int shift, uint32_t* h) {
-  for (int b = threadIdx.x; b < FB; b += TK_THREADS) h[b] = 0;
-  __syncthreads();
-  HotBins hb;
-#pragma unroll
-  for (int u = 0; u < PER; ++u)
-    if (valid[u] && k[u] >= lo && k[u] <= hi) hb.add((k[u] - lo) >> shift, h);
-  hb.flush(h);
-  __syncthreads();
-}
-
-// Exact select among the valid keys in [lo, hi] held PER per thread: the key
-// value at descending rank r (1 <= r <= their number), and in `above` how
-// many of them exceed it.  Each round splits the remaining key range into FB
-// bins and keeps the bin holding rank r, so a range of b bits takes
-// ceil(b / 12) rounds.
-template <int PER>
-__device__ uint32_t select_rank(const uint32_t (&k)[PER], const bool (&valid)[PER], uint32_t lo, uint32_t hi,
-                                uint32_t r, uint32_t& above, uint32_t* h, uint32_t* sbuf, uint32_t* s_res) {
-  above = 0;
-#pragma unroll 1
-  while (true) {
-    const int shift = max(0, bit_width(hi - lo) - FB_BITS);
-    range_hist<PER>(k, valid, lo, hi, shift, h);
-    uint32_t b, ab, b2, ab2;
-    find_two_bins(h, r, r, b, ab, b2, ab2, sbuf, s_res);
-    above += ab;
-    r -= ab;
-    const uint32_t nlo = lo + (b << shift);
-    const uint32_t nhi = (uint32_t)min((uint64_t)hi, (uint64_t)nlo + ((uint64_t)1 << shift) - 1);
-    lo = nlo;
-    hi = nhi;
-    if (shift == 0) return lo;
-  }
-}
-
 // Bounds on the row's threshold from a sample of its keys: SAMPLE_BLOCKS runs
 // of SAMPLE_RUN consecutive keys spread evenly over the row (the whole row
 // when it has at most SAMPLES keys).  With e = K * S / n the expected sample
@@ -447,12 +419,27 @@ __device__ void sample_bounds(const float* __restrict__ src, int64_t n, int K, u
   int r_hi = (int)floorf(e - sd), r_lo = (int)ceilf(e + sd);
   r_hi = max(1, min(r_hi, S));
   r_lo = max(r_hi, min(r_lo, S));
-  uint32_t kmin, kmax;
-  block_min_max<SAMPLE_PER_T>(k, valid, kmin, kmax, sbuf + TK_WAVES);
+  uint32_t mn = 0xffffffffu, mx = 0u, kmin, kmax;
+#pragma unroll
+  for (int u = 0; u < SAMPLE_PER_T; ++u)
+    if (valid[u]) {
+      mn = min(mn, k[u]);
+      mx = max(mx, k[u]);
+    }
+  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);
   const int shift = max(0, bit_width(kmax - kmin) - FB_BITS);
-  range_hist<SAMPLE_PER_T>(k, valid, kmin, kmax, shift, h);
+  for (int b = threadIdx.x; b < FB; b += TK_THREADS) h[b] = 0;
+  __syncthreads();
+  {
+    HotBins hb;
+#pragma unroll
+    for (int u = 0; u < SAMPLE_PER_T; ++u)
+      if (valid[u]) hb.add((k[u] - kmin) >> shift, h);
+    hb.flush(h);
+  }
+  __syncthreads();
   uint32_t b_hi, ab_hi, b_lo, ab_lo;
-  find_two_bins(h, (uint32_t)r_hi, (uint32_t)r_lo, b_hi, ab_hi, b_lo, ab_lo, sbuf, s_res);
+  find_two_bins<FB_BITS>(h, (uint32_t)r_hi, (uint32_t)r_lo, b_hi, ab_hi, b_lo, ab_lo, sbuf, s_res);
   t_hi = (uint32_t)min((uint64_t)kmax, (uint64_t)kmin + ((uint64_t)(b_hi + 1) << shift) - 1);
   t_lo = kmin + (b_lo << shift);
 }
@@ -601,9 +588,20 @@ __device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws
   const uint32_t kk = (uint32_t)K - ndef;  // candidates to keep (0 <= kk <= ncand)
   uint32_t T = 0xffffffffu, keq = 0;
   if (kk > 0) {  // candidates lie in [t_lo, t_hi]; their own range is found first
-    uint32_t cmin, cmax, above;
-    block_min_max<CPT>(ck, cv, cmin, cmax, sm.sbuf + TK_WAVES);
-    T = select_rank<CPT>(ck, cv, cmin, cmax, kk, above, sm.h, sm.sbuf, sm.s_res);
+    uint32_t mn = 0xffffffffu, mx = 0u, cmin, cmax, above;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+      if (cv[u]) {
+        mn = min(mn, ck[u]);
+        mx = max(mx, ck[u]);
+      }
+    block_min_max(mn, mx, cmin, cmax, sm.sbuf + TK_WAVES);
+    auto add_cand = [&](HotBins& hb, uint32_t lo, uint32_t hi, int shift) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u)
+        if (cv[u] && ck[u] >= lo && ck[u] <= hi) hb.add((ck[u] - lo) >> shift, sm.h);
+    };
+    T = select_rank<FB_BITS>(add_cand, cmin, cmax, kk, above, sm.h, sm.sbuf, sm.s_res);
     keq = kk - above;
   }
   __syncthreads();
