@@ -292,42 +292,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // PV of tile tV interleaved with QK^T of the next tile tS: three k-step
-  // pairs per PV step, so the matrix cores always have independent work while
-  // the LDS serves both operand streams, and the logits are complete two PV
-  // steps before the end: the softmax that follows issues while those last
-  // PV MFMAs still run.
-  // The gather of tile gt (if gt >= 0) is spread over the first nine k-step
-  // pairs: an instruction waits at issue until the memory pipeline takes it,
-  // and the MFMAs already issued keep the matrix cores busy meanwhile.
-  auto tile_pv_s = [&](const uint16_t* tV, const uint16_t* pbuf, const uint16_t* tS, int gt) {
-    uint32_t g_lds0 = 0, g_voff = 0;
-    if (gt >= 0) g_voff = gather_begin(gt, g_lds0);
-    bf16x8 ring[SLOOK], pb[4], vring[PVLOOK];
-#pragma unroll
-    for (int s = 0; s < SLOOK; ++s) ring[s] = aop(tS, s);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) pb[nb] = pbop(pbuf, 0, nb);
-#pragma unroll
-    for (int st = 0; st < PVLOOK; ++st) vring[st] = vop(tV, st);
-    f32x16 sacc;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-#pragma unroll
-      for (int rep = 0; rep < 3; ++rep) {
-        const int g = 3 * st + rep;
-        if (g < KS / 2) s_pair(tS, 2 * g, ring, sacc);
-        if (g < GU && gt >= 0) gather_line(g_voff, g_lds0, g);
-        __builtin_amdgcn_sched_barrier(0);  // keep the ring
-      }
-      pv_step(tV, st, vring, pb);
-      if (st == 3)  // second half of the tile's keys: the P operands of ks = 1
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) pb[nb] = pbop(pbuf, 1, nb);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return sacc;
-  };
   bool overflow = false;
   // Online softmax of tile `t` in log2 units; writes its bf16 P to pbuf.  This
   // lane holds head 32*wave+col for keys mfma_row(i, half); lane j^32 holds
@@ -379,9 +343,118 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     }
   };
 
+  // PV of tile tV, QK^T of tile tS (= tile ts) and the softmax of tile ts,
+  // with the softmax's vector work spread between the matrix instructions:
+  // the 36 QK^T k-steps run in the first three PV steps (six pairs each), so
+  // the logits are complete with 20 PV MFMAs still to issue, and the 16
+  // softmax pieces go one after each of the middle 16 of those (a wave
+  // issues vector instructions while its own MFMA runs only when they sit
+  // right behind it).  The gather of tile gt
+  // (if gt >= 0) rides on the first nine k-step pairs.  Writes P of tile ts to
+  // pout.
+  auto tile_fused = [&](const uint16_t* tV, const uint16_t* pbuf, const uint16_t* tS, int ts, uint16_t* pout,
+                        int gt) {
+    uint32_t g_lds0 = 0, g_voff = 0;
+    if (gt >= 0) g_voff = gather_begin(gt, g_lds0);
+    bf16x8 ring[SLOOK], pb[4], vring[PVLOOK];
+#pragma unroll
+    for (int s = 0; s < SLOOK; ++s) ring[s] = aop(tS, s);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) pb[nb] = pbop(pbuf, 0, nb);
+#pragma unroll
+    for (int st = 0; st < PVLOOK; ++st) vring[st] = vop(tV, st);
+    const int4 tf = *reinterpret_cast<const int4*>(&tfull[ts % NBUF][0]);
+    f32x16 sacc;
+    constexpr int PAIRS_AT[4] = {0, 6, 12, 18};  // k-step pairs before PV step st = 0..3
+    int g = 0;
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+#pragma unroll
+      for (int q2 = PAIRS_AT[st]; q2 < PAIRS_AT[st + 1]; ++q2) {
+        s_pair(tS, 2 * q2, ring, sacc);
+        if (g < GU && gt >= 0) gather_line(g_voff, g_lds0, g);
+        ++g;
+        __builtin_amdgcn_sched_barrier(0);  // keep the ring
+      }
+      pv_step(tV, st, vring, pb);
+      if (st == 3)  // second half of the tile's keys: the P operands of ks = 1
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) pb[nb] = pbop(pbuf, 1, nb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // softmax pieces (same arithmetic as softmax_p), one after each PV MFMA
+    float mh = 0.f, mt = 0.f, lsum = 0.f;
+    float x[16];
+    uint16_t* pp = &pout[(32 * wave + col) * PP + 4 * half];
+    auto piece = [&](int k) {
+      if (k == 0) {
+        if (!__builtin_amdgcn_readfirstlane(tf.x && tf.y && tf.z && tf.w)) {
+          const int32_t* vcur = vflag[ts % NBUF];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int4 vf = *reinterpret_cast<const int4*>(&vcur[8 * a + 4 * half]);
+            const int fl[4] = {vf.x, vf.y, vf.z, vf.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (!fl[c]) sacc[4 * a + c] = -INFINITY;
+          }
+        }
+        mh = sacc[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mh = fmaxf(mh, sacc[i]);
+      } else if (k == 1) {
+#pragma unroll
+        for (int i = 8; i < 16; ++i) mh = fmaxf(mh, sacc[i]);
+      } else if (k == 2) {
+        mt = max_halves(mh * scale_log2);  // this head's largest scaled logit in the tile
+      } else if (k == 3) {
+        m_max = fmaxf(m_max, mt);
+        if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated yet: start the reference here
+        overflow |= mt > m_ref + 64.f;
+      } else if (k >= 4 && k < 12) {
+        // arguments are at most 64 here (else the split is redone); exp2(-inf) = 0;
+        // no reference yet (every logit so far masked): weight 0
+        const int i0 = 2 * (k - 4);
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -m_ref));
+          x[i] = m_ref == -INFINITY ? 0.f : e;
+          lsum += x[i];
+        }
+      } else if (k >= 12 && k < 16) {
+        const int a = k - 12;
+        u32x2 pk;
+        pk.x = pack_bf16x2(x[4 * a + 0], x[4 * a + 1]);
+        pk.y = pack_bf16x2(x[4 * a + 2], x[4 * a + 3]);
+        *reinterpret_cast<u32x2*>(pp + 8 * a) = pk;
+        if (k == 15) l_run += lsum;  // this half's keys; the halves are added at the end
+      }
+    };
+    bf16x8 av;
+#pragma unroll
+    for (int st = 3; st < 8; ++st) {
+      const int mb = st & 3;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if (nb == 0) {
+          av = vring[st % PVLOOK];
+          if (st + PVLOOK < 8) vring[st % PVLOOK] = vop(tV, st + PVLOOK);
+        }
+        o[mb][nb] = mfma32x32x16(av, pb[nb], o[mb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int slot = 4 * (st - 3) + nb;  // 20 slots for 16 pieces
+        if (slot >= 2 && slot < 18) piece(slot - 2);
+        if (st == 3 && nb == 3)
+#pragma unroll
+          for (int b2 = 0; b2 < 4; ++b2) pb[b2] = pbop(pbuf, 1, b2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // ---- the tile pipeline ----
-  // Iteration it runs PV(it) together with QK^T(it+1) and the gather of tile
-  // it+2, then the softmax of tile it+1, then one barrier.  Tile it+2 goes into
+  // Iteration it runs PV(it) together with QK^T(it+1), the softmax of tile
+  // it+1 and the gather of tile it+2, then one barrier.  Tile it+2 goes into
   // the buffer of tile it-1, which every wave finished before that barrier; P
   // alternates between two LDS buffers.
   for (int pass = 0; pass < 2; ++pass) {
@@ -411,16 +484,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     }
     // (the iteration without a gather is peeled, so the loop body has no branch)
     for (int it = 0; it + 2 < ntiles; ++it) {
-      const f32x16 sacc = tile_pv_s(kvs[it % NBUF], ps[it & 1], kvs[(it + 1) % NBUF], it + 2);
-      softmax_p(sacc, it + 1, ps[(it + 1) & 1]);
+      tile_fused(kvs[it % NBUF], ps[it & 1], kvs[(it + 1) % NBUF], it + 1, ps[(it + 1) & 1], it + 2);
       // tile it+2 (the only gather in flight) must have landed
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       sync_lds();  // P(it+1) and tile it+2 visible; every wave is done with tile it and P(it)
     }
     if (ntiles > 1) {
       const int it = ntiles - 2;
-      const f32x16 sacc = tile_pv_s(kvs[it % NBUF], ps[it & 1], kvs[(it + 1) % NBUF], -1);
-      softmax_p(sacc, it + 1, ps[(it + 1) & 1]);
+      tile_fused(kvs[it % NBUF], ps[it & 1], kvs[(it + 1) % NBUF], it + 1, ps[(it + 1) & 1], -1);
       sync_lds();
     }
     if (ntiles > 0) tile_pv(kvs[(ntiles - 1) % NBUF], ps[(ntiles - 1) & 1]);  // the last tile has no successor
