@@ -169,6 +169,55 @@ dsa_status dsa_forward(const void* q_idx, const void* k_idx, const void* w, cons
                        int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype,
                        void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Per-sequence cache lengths ("varlen"): the three steps and the fused call
+ * for a batch whose sequences hold different numbers of tokens.
+ * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)":
+ * each query is scored against all of its sequence's preceding keys; in a
+ * batch those counts differ per sequence.)
+ *
+ * seq_lens: device memory, int64 [B], 8-byte aligned; sequence b holds
+ * seq_lens[b] valid rows of its caches (expected 0 <= seq_lens[b] <= N; the
+ * kernels clamp to N).  Its Tq queries are its last Tq tokens: query t sits at
+ * position seq_lens[b] - Tq + t and sees keys s < seq_lens[b] - Tq + t + 1 (a
+ * query at a negative position sees none: its top-k row is all -1 and its
+ * attention output is 0 with lse = -inf).  Everything else, including the
+ * workspaces and their sizes (dsa_topk_workspace_size,
+ * dsa_forward_workspace_size with the same B, Tq, N), is as for the entry
+ * points above with q_pos0 replaced by seq_lens[b] - Tq per sequence.  The
+ * host cannot see seq_lens, so no length is validated.
+ */
+dsa_status dsa_index_scores_varlen(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                                   const int64_t* seq_lens, int64_t B, int64_t Tq, int64_t N, int32_t H_I,
+                                   int32_t D_I, int32_t dtype, void* stream);
+dsa_status dsa_topk_varlen(const float* scores, int32_t* idx, const int64_t* seq_lens, int64_t B, int64_t Tq,
+                           int64_t N, int32_t K, void* workspace, size_t ws_bytes, void* stream);
+dsa_status dsa_forward_varlen(const void* q_idx, const void* k_idx, const void* w, const void* q, const void* kv,
+                              void* out, float* lse, int32_t* idx_out, const int64_t* seq_lens, int64_t B,
+                              int64_t Tq, int64_t N, int32_t H_I, int32_t D_I, int32_t H, int32_t D, int32_t DV,
+                              int32_t K, float scale, int32_t dtype, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * Cache append: one new token per sequence.
+ * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)",
+ *  paragraph on the indexer's key cache: a per-token, single-head key cache
+ *  kept next to the main key/value cache and updated as tokens arrive.)
+ *
+ * Static-cache layout (the caches of the entry points above):
+ *   k_idx [B, N, D_I] and kv [B, N, D] (dtype), updated in place;
+ *   new_k_idx [B, D_I], new_kv [B, D] (dtype): the new token's rows;
+ *   pos: device memory, int64 [B], 8-byte aligned.
+ * For every b with 0 <= pos[b] < N: k_idx[b, pos[b], :] = new_k_idx[b, :] and
+ * kv[b, pos[b], :] = new_kv[b, :]; other entries of pos write nothing (the
+ * host cannot see pos).  A cache and its new rows are given together or both
+ * NULL (that cache is then left alone); at least one cache is required.
+ * Appending then running the steps with seq_lens[b] = pos[b] + 1 equals
+ * running them on caches built with that row in place.
+ */
+dsa_status dsa_cache_append(void* k_idx, void* kv, const void* new_k_idx, const void* new_kv, const int64_t* pos,
+                            int64_t B, int64_t N, int32_t D_I, int32_t D, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,10 @@ Functions mirror the C entry points:
   topk(scores, K, q_pos0=0)                               -> idx [B,Tq,K] int32
   sparse_mla(q, kv, idx, scale, DV=512)                   -> (out [B,Tq,H,DV], lse [B,Tq,H])
   forward(q_idx, k_idx, w, q, kv, K, scale, q_pos0=0, DV=512, return_idx=False)
+  index_scores_varlen(q_idx, k_idx, w, seq_lens)          -> scores (per-sequence cache lengths)
+  topk_varlen(scores, K, seq_lens)                        -> idx
+  forward_varlen(q_idx, k_idx, w, q, kv, K, scale, seq_lens, ...)
+  cache_append(k_idx, kv, new_k_idx, new_kv, pos)         (in place; either cache may be None)
 """
 from __future__ import annotations
 
@@ -57,6 +61,11 @@ _SIGNATURES = {
     "dsa_forward_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),
     "dsa_forward": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
                                    _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "dsa_index_scores_varlen": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
+    "dsa_topk_varlen": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]),
+    "dsa_forward_varlen": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "dsa_cache_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
 }
 
 
@@ -219,3 +228,108 @@ def forward(q_idx, k_idx, w, q, kv, K: int, scale: float, q_pos0: int = 0, DV: i
     _check(lib.dsa_forward(pqi, pki, pw, pq, pkv, po, pl, pi, B, Tq, N, q_pos0, H_I, D_I, H, D, DV, K, scale,
                            code, ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
     return out, lse_t, idx_out
+
+
+def _seq_lens(seq_lens, B: int) -> int:
+    p = _dev(seq_lens, "seq_lens", 1, torch.int64)
+    if seq_lens.shape[0] != B:
+        raise ValueError(f"seq_lens must have B={B} entries")
+    return p
+
+
+def index_scores_varlen(q_idx, k_idx, w, seq_lens, scores=None, stream=None) -> torch.Tensor:
+    """Indexer scores with per-sequence cache lengths: sequence b's queries are
+    its last Tq tokens (positions seq_lens[b] - Tq + t)."""
+    B, Tq, H_I, D_I = q_idx.shape
+    N = k_idx.shape[1]
+    dt = q_idx.dtype
+    pq = _dev(q_idx, "q_idx", 4)
+    pk = _dev(k_idx, "k_idx", 3, dt)
+    pw = _dev(w, "w", 3, dt)
+    if tuple(k_idx.shape) != (B, N, D_I) or tuple(w.shape) != (B, Tq, H_I):
+        raise ValueError("k_idx must be [B,N,D_I] and w [B,Tq,H_I]")
+    pl = _seq_lens(seq_lens, B)
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q_idx.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if tuple(scores.shape) != (B, Tq, N):
+        raise ValueError("scores must be [B,Tq,N]")
+    _check(library().dsa_index_scores_varlen(pq, pk, pw, ps, pl, B, Tq, N, H_I, D_I, _dtype_code(q_idx),
+                                             _stream(stream)))
+    return scores
+
+
+def topk_varlen(scores, K: int, seq_lens, idx=None, workspace=None, stream=None) -> torch.Tensor:
+    B, Tq, N = scores.shape
+    ps = _dev(scores, "scores", 3, torch.float32)
+    pl = _seq_lens(seq_lens, B)
+    if idx is None:
+        idx = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+    pi = _dev(idx, "idx", 3, torch.int32)
+    if tuple(idx.shape) != (B, Tq, K):
+        raise ValueError("idx must be [B,Tq,K]")
+    lib = library()
+    ws, nbytes = _workspace(lib.dsa_topk_workspace_size(B, Tq, N, K), scores.device, workspace)
+    _check(lib.dsa_topk_varlen(ps, pi, pl, B, Tq, N, K, ws.data_ptr() if ws is not None else None, nbytes,
+                               _stream(stream)))
+    return idx
+
+
+def forward_varlen(q_idx, k_idx, w, q, kv, K: int, scale: float, seq_lens, DV: int = 512, out=None, lse=True,
+                   idx_out=None, return_idx: bool = False, workspace=None, stream=None):
+    """forward() with per-sequence cache lengths.  Returns (out, lse, idx or None)."""
+    B, Tq, H_I, D_I = q_idx.shape
+    N = k_idx.shape[1]
+    H, D = q.shape[2], q.shape[3]
+    dt = q.dtype
+    pqi = _dev(q_idx, "q_idx", 4, dt)
+    pki = _dev(k_idx, "k_idx", 3, dt)
+    pw = _dev(w, "w", 3, dt)
+    pq = _dev(q, "q", 4, dt)
+    pkv = _dev(kv, "kv", 3, dt)
+    if tuple(q.shape[:2]) != (B, Tq) or tuple(kv.shape) != (B, N, D):
+        raise ValueError("q must be [B,Tq,H,D] and kv [B,N,D]")
+    pls = _seq_lens(seq_lens, B)
+    if out is None:
+        out = torch.empty((B, Tq, H, DV), dtype=dt, device=q.device)
+    po = _dev(out, "out", 4, dt)
+    lse_t = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if lse is True else (
+        lse if isinstance(lse, torch.Tensor) else None)
+    pl = _dev(lse_t, "lse", 3, torch.float32) if lse_t is not None else None
+    if return_idx and idx_out is None:
+        idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=q.device)
+    pi = _dev(idx_out, "idx_out", 3, torch.int32) if idx_out is not None else None
+    lib = library()
+    code = _dtype_code(q)
+    ws, nbytes = _workspace(lib.dsa_forward_workspace_size(B, Tq, N, H, DV, K, code), q.device, workspace)
+    _check(lib.dsa_forward_varlen(pqi, pki, pw, pq, pkv, po, pl, pi, pls, B, Tq, N, H_I, D_I, H, D, DV, K, scale,
+                                  code, ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    return out, lse_t, idx_out
+
+
+def cache_append(k_idx, kv, new_k_idx, new_kv, pos, stream=None):
+    """Writes new_k_idx[b] to k_idx[b, pos[b]] and new_kv[b] to kv[b, pos[b]] in place
+    (entries of pos outside [0, N) are skipped).  Either cache may be None."""
+    ref = k_idx if k_idx is not None else kv
+    if ref is None:
+        raise ValueError("no cache to append to")
+    B, N = ref.shape[0], ref.shape[1]
+    dt = ref.dtype
+    D_I = D = 0
+    pk = pnk = pv = pnv = None
+    if k_idx is not None:
+        pk = _dev(k_idx, "k_idx", 3, dt)
+        pnk = _dev(new_k_idx, "new_k_idx", 2, dt)
+        D_I = k_idx.shape[2]
+        if tuple(k_idx.shape[:2]) != (B, N) or tuple(new_k_idx.shape) != (B, D_I):
+            raise ValueError("k_idx must be [B,N,D_I] and new_k_idx [B,D_I]")
+    if kv is not None:
+        pv = _dev(kv, "kv", 3, dt)
+        pnv = _dev(new_kv, "new_kv", 2, dt)
+        D = kv.shape[2]
+        if tuple(kv.shape[:2]) != (B, N) or tuple(new_kv.shape) != (B, D):
+            raise ValueError("kv must be [B,N,D] and new_kv [B,D]")
+    pp = _dev(pos, "pos", 1, torch.int64)
+    if pos.shape[0] != B:
+        raise ValueError(f"pos must have B={B} entries")
+    _check(library().dsa_cache_append(pk, pv, pnk, pnv, pp, B, N, D_I, D, _dtype_code(ref), _stream(stream)))

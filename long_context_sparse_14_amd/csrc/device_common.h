@@ -88,6 +88,18 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p));
 }
 
+// Position of query 0 of sequence b: q_pos0, or, with per-sequence lengths,
+// seq_lens[b] - Tq (the queries are the sequence's last Tq tokens).
+__device__ __forceinline__ int64_t seq_q0(const int64_t* seq_lens, int64_t b, int64_t Tq, int64_t q_pos0) {
+  return seq_lens != nullptr ? seq_lens[b] - Tq : q_pos0;
+}
+
+// Keys query t of a sequence may see: positions 0 .. q0 + t, at most N (none
+// for a query at a negative position).
+__device__ __forceinline__ int64_t visible_keys(int64_t q0, int64_t t, int64_t N) {
+  return max((int64_t)0, min(N, q0 + t + 1));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves
 // (row shifts within each row of 16 lanes, then the row broadcasts of lanes
 // 15 and 31): six vector adds, no LDS traffic.  All 64 lanes must be active.

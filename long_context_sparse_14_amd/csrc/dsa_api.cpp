@@ -136,6 +136,14 @@ ForwardLayout forward_layout(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_
   return L;
 }
 
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+dsa_status check_seq_lens(const int64_t* seq_lens) {
+  if (!seq_lens) return fail(DSA_ERR_INVALID_ARG, "seq_lens must not be null");
+  if (!aligned8(seq_lens)) return fail(DSA_ERR_INVALID_ARG, "seq_lens must be 8-byte aligned");
+  return DSA_OK;
+}
+
 dsa_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -254,6 +262,99 @@ dsa_status dsa_forward(const void* q_idx, const void* k_idx, const void* w, cons
     e = dsa::launch_sparse_mla_f32(static_cast<const float*>(q), static_cast<const float*>(kv), idx,
                                    static_cast<float*>(out), lse, B, Tq, N, H, D, DV, K, scale, s);
   return hip_status(e, "sparse MLA launch");
+}
+
+dsa_status dsa_index_scores_varlen(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                                   const int64_t* seq_lens, int64_t B, int64_t Tq, int64_t N, int32_t H_I,
+                                   int32_t D_I, int32_t dtype, void* stream) {
+  dsa_status st = check_index_scores(q_idx, k_idx, w, scores, B, Tq, N, 0, H_I, D_I, dtype, true);
+  if (st != DSA_OK) return st;
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  if (dtype == DSA_F32 && B * Tq * ((N + 255) / 256) > kMaxGrid)
+    return fail(DSA_ERR_UNSUPPORTED, "fp32 indexer problem too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == DSA_BF16)
+    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, 0, s, seq_lens);
+  else
+    e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
+                                     static_cast<const float*>(w), scores, B, Tq, N, 0, H_I, D_I, s, seq_lens);
+  return hip_status(e, "index scores launch");
+}
+
+dsa_status dsa_topk_varlen(const float* scores, int32_t* idx, const int64_t* seq_lens, int64_t B, int64_t Tq,
+                           int64_t N, int32_t K, void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_topk(scores, idx, B, Tq, N, 0, K, workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  return hip_status(dsa::launch_topk(scores, idx, B, Tq, N, 0, K, workspace, static_cast<hipStream_t>(stream),
+                                     seq_lens),
+                    "top-k launch");
+}
+
+dsa_status dsa_forward_varlen(const void* q_idx, const void* k_idx, const void* w, const void* q, const void* kv,
+                              void* out, float* lse, int32_t* idx_out, const int64_t* seq_lens, int64_t B,
+                              int64_t Tq, int64_t N, int32_t H_I, int32_t D_I, int32_t H, int32_t D, int32_t DV,
+                              int32_t K, float scale, int32_t dtype, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  dsa_status st = check_index_scores(q_idx, k_idx, w, nullptr, B, Tq, N, 0, H_I, D_I, dtype, false);
+  if (st != DSA_OK) return st;
+  if (dtype == DSA_F32 && B * Tq * ((N + 255) / 256) > kMaxGrid)
+    return fail(DSA_ERR_UNSUPPORTED, "fp32 indexer problem too large");
+  st = check_mla(q, kv, nullptr, out, lse, B, Tq, N, H, D, DV, K, scale, dtype, nullptr, 0, false);
+  if (st != DSA_OK) return st;
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  if (idx_out && !aligned16(idx_out)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 16-byte aligned");
+  const ForwardLayout L = forward_layout(B, Tq, N, H, DV, K, dtype);
+  if (!workspace || ws_bytes < L.total)
+    return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  void* mla_ws = ws + L.mla;
+  void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  if (dtype == DSA_BF16)
+    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, 0, s, seq_lens);
+  else
+    e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
+                                     static_cast<const float*>(w), scores, B, Tq, N, 0, H_I, D_I, s, seq_lens);
+  if (e != hipSuccess) return hip_status(e, "index scores launch");
+  e = dsa::launch_topk(scores, idx, B, Tq, N, 0, K, topk_ws, s, seq_lens);
+  if (e != hipSuccess) return hip_status(e, "top-k launch");
+  if (dtype == DSA_BF16)
+    e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
+                                    static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, mla_ws, s);
+  else
+    e = dsa::launch_sparse_mla_f32(static_cast<const float*>(q), static_cast<const float*>(kv), idx,
+                                   static_cast<float*>(out), lse, B, Tq, N, H, D, DV, K, scale, s);
+  return hip_status(e, "sparse MLA launch");
+}
+
+dsa_status dsa_cache_append(void* k_idx, void* kv, const void* new_k_idx, const void* new_kv, const int64_t* pos,
+                            int64_t B, int64_t N, int32_t D_I, int32_t D, int32_t dtype, void* stream) {
+  if (B < 1 || N < 1) return fail(DSA_ERR_INVALID_ARG, "B and N must be >= 1 (got %lld, %lld)", (long long)B,
+                                  (long long)N);
+  if (N > kMaxN) return fail(DSA_ERR_INVALID_ARG, "N must be < 2^31 (got %lld)", (long long)N);
+  if (B > kMaxGrid) return fail(DSA_ERR_INVALID_ARG, "B must be < 2^31");
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!pos) return fail(DSA_ERR_INVALID_ARG, "pos must not be null");
+  if (!aligned8(pos)) return fail(DSA_ERR_INVALID_ARG, "pos must be 8-byte aligned");
+  if ((k_idx == nullptr) != (new_k_idx == nullptr) || (kv == nullptr) != (new_kv == nullptr))
+    return fail(DSA_ERR_INVALID_ARG, "a cache and its new rows must be given together");
+  if (!k_idx && !kv) return fail(DSA_ERR_INVALID_ARG, "no cache to append to");
+  if ((k_idx && (!aligned16(k_idx) || !aligned16(new_k_idx))) || (kv && (!aligned16(kv) || !aligned16(new_kv))))
+    return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if ((k_idx && D_I < 1) || (kv && D < 1)) return fail(DSA_ERR_INVALID_ARG, "row widths must be >= 1");
+  return hip_status(dsa::launch_cache_append(k_idx, kv, new_k_idx, new_kv, pos, B, N, k_idx ? D_I : 0, kv ? D : 0,
+                                             dtype == DSA_BF16 ? 2 : 4, static_cast<hipStream_t>(stream)),
+                    "cache append launch");
 }
 
 }  // extern "C"

@@ -7,16 +7,25 @@
 
 namespace dsa {
 
+// seq_lens (device, [B], may be null): per-sequence cache lengths; when given,
+// the queries of sequence b sit at positions seq_lens[b] - Tq + t and q_pos0
+// is ignored.
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                                    hipStream_t stream);
+                                    hipStream_t stream, const int64_t* seq_lens = nullptr);
 hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const float* w, float* scores,
                                    int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int H_I, int D_I,
-                                   hipStream_t stream);
+                                   hipStream_t stream, const int64_t* seq_lens = nullptr);
 
 size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
 hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                       int K, void* workspace, hipStream_t stream);
+                       int K, void* workspace, hipStream_t stream, const int64_t* seq_lens = nullptr);
+
+// Writes row pos[b] of each sequence's caches (rows of D_I and D elements of
+// esize bytes); entries of pos outside [0, N) are skipped.  Either cache may
+// be null.
+hipError_t launch_cache_append(void* k_idx, void* kv, const void* new_k_idx, const void* new_kv, const int64_t* pos,
+                               int64_t B, int64_t N, int D_I, int D, int esize, hipStream_t stream);
 
 int mla_num_splits(int64_t rows, int K);
 size_t mla_workspace_bytes(int64_t rows, int H, int DV, int K, int is_bf16);

@@ -107,3 +107,35 @@ def test_python_binding_refuses_host_tensors():
     x = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         dsa.index_scores(x, torch.zeros(1, 4, 128, dtype=torch.bfloat16), torch.zeros(1, 1, 64, dtype=torch.bfloat16))
+
+
+def test_varlen_validation():
+    L = lib()
+    s = 0.07
+    # seq_lens is required and 8-byte aligned; everything else as for the uniform entry points
+    assert L.dsa_index_scores_varlen(P, P, P, P, None, 2, 1, 100, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert "seq_lens" in last()
+    assert L.dsa_index_scores_varlen(P, P, P, P, P + 4, 2, 1, 100, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_scores_varlen(P, P, P, P, P, 2, 1, 100, 32, 128, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_topk_varlen(P, P, None, 2, 1, 100, 16, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_varlen(P, P, P, 2, 1, 100, 0, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    B, Tq, N, K = 32, 1, 131072, 2048
+    need = L.dsa_forward_workspace_size(B, Tq, N, 128, 512, K, BF16)
+    args = [P, P, P, P, P, P, None, None, P, B, Tq, N, 64, 128, 128, 576, 512, K, s, BF16]
+    assert L.dsa_forward_varlen(*args, P, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    bad = list(args)
+    bad[8] = None  # seq_lens
+    assert L.dsa_forward_varlen(*bad, P, need, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_cache_append_validation():
+    L = lib()
+    assert L.dsa_cache_append(None, None, None, None, P, 2, 10, 128, 576, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert "no cache" in last()
+    assert L.dsa_cache_append(P, None, None, None, P, 2, 10, 128, 576, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert "together" in last()
+    assert L.dsa_cache_append(P, P, P, P, None, 2, 10, 128, 576, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_cache_append(P, P, P, P, P + 4, 2, 10, 128, 576, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_cache_append(P, P, P, P, P, 0, 10, 128, 576, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_cache_append(P, P, P, P, P, 2, 10, 128, 576, 9, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_cache_append(P + 2, P, P, P, P, 2, 10, 128, 576, BF16, None) == dsa.DSA_ERR_INVALID_ARG
