@@ -26,7 +26,10 @@ reader can check it against the pages by eye:
   kv_lora_rank = 512, qk_rope_head_dim = 64, qk_nope_head_dim = 128,
   num_attention_heads = 128.
   DeepSeek-V4 model documentation, section on the attention mask layout: an
-  indexer entry of -1 means "no selection" and reaches the mask unchanged.
+  indexer entry of -1 means "no selection" and reaches the mask unchanged;
+  a compressed entry w (positions m*w .. m*w + m - 1) becomes visible to the
+  query at position p once its window has closed, w < (p + 1) // m, so
+  queries before the first window closes (p < m - 1) select nothing.
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes of the repository):
@@ -67,9 +70,15 @@ def as_f64(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def n_valid_keys(t: int, q_pos0: int, N: int) -> int:
-    """Number of keys query t may see: positions 0..q_pos0+t, capped by the cache length."""
-    return max(0, min(N, q_pos0 + t + 1))
+def n_valid_keys(t: int, q_pos0: int, N: int, m: int = 1) -> int:
+    """Number of keys query t may see: positions 0..q_pos0+t, capped by the cache length.
+
+    With a key axis compressed at rate m (entry w summarises positions
+    m*w .. m*w+m-1), entry w is visible once its window has closed:
+    w < (q_pos0 + t + 1) // m.  m = 1 is the plain causal rule.
+    """
+    p1 = q_pos0 + t + 1
+    return 0 if p1 <= 0 else min(N, p1 // m)
 
 
 # ----------------------------------------------------------------------------
@@ -77,18 +86,18 @@ def n_valid_keys(t: int, q_pos0: int, N: int) -> int:
 # ----------------------------------------------------------------------------
 
 def index_scores_rows(q_idx_b: np.ndarray, k_idx_b: np.ndarray, w_b: np.ndarray,
-                      ts, q_pos0: int) -> list:
+                      ts, q_pos0: int, m: int = 1) -> list:
     """Index scores of queries `ts` of one sequence against their visible keys.
 
     q_idx_b [Tq, H_I, D_I], k_idx_b [N, D_I], w_b [Tq, H_I] (any storage dtype).
-    Returns one float64 vector per query t, of length n_valid_keys(t):
+    Returns one float64 vector per query t, of length n_valid_keys(t, q_pos0, N, m):
         I[s] = sum_h w[t,h] * max(0, sum_d qI[t,h,d] * kI[s,d]).
     """
     kI = as_f64(k_idx_b)
     N = kI.shape[0]
     out = []
     for t in ts:
-        n = n_valid_keys(int(t), q_pos0, N)
+        n = n_valid_keys(int(t), q_pos0, N, m)
         qI = as_f64(q_idx_b[t])            # [H_I, D_I]
         w = as_f64(w_b[t])                 # [H_I]
         dots = kI[:n] @ qI.T               # [n, H_I]: per-head dot product q_h . k_s
@@ -96,13 +105,13 @@ def index_scores_rows(q_idx_b: np.ndarray, k_idx_b: np.ndarray, w_b: np.ndarray,
     return out
 
 
-def index_scores(q_idx: np.ndarray, k_idx: np.ndarray, w: np.ndarray, q_pos0: int) -> np.ndarray:
+def index_scores(q_idx: np.ndarray, k_idx: np.ndarray, w: np.ndarray, q_pos0: int, m: int = 1) -> np.ndarray:
     """Full score tensor [B, Tq, N] (float64); entries a query may not see are NaN."""
     B, Tq = q_idx.shape[:2]
     N = k_idx.shape[1]
     out = np.full((B, Tq, N), np.nan)
     for b in range(B):
-        rows = index_scores_rows(q_idx[b], k_idx[b], w[b], range(Tq), q_pos0)
+        rows = index_scores_rows(q_idx[b], k_idx[b], w[b], range(Tq), q_pos0, m)
         for t, r in enumerate(rows):
             out[b, t, :len(r)] = r
     return out
@@ -133,13 +142,13 @@ def topk_row(scores: np.ndarray, K: int) -> np.ndarray:
     return out
 
 
-def topk(scores: np.ndarray, K: int, q_pos0: int) -> np.ndarray:
+def topk(scores: np.ndarray, K: int, q_pos0: int, m: int = 1) -> np.ndarray:
     """scores [B, Tq, N] -> idx [B, Tq, K] int32 (row t uses its visible keys only)."""
     B, Tq, N = scores.shape
     out = np.empty((B, Tq, K), dtype=np.int32)
     for b in range(B):
         for t in range(Tq):
-            n = n_valid_keys(t, q_pos0, N)
+            n = n_valid_keys(t, q_pos0, N, m)
             out[b, t] = topk_row(scores[b, t, :n], K)
     return out
 

@@ -123,6 +123,61 @@ def pin_indexer_heads(index_scores_rows) -> bool:
             and all(not np.any(x) for x in e))
 
 
+def windows_closed(t, q_pos0, N, m):
+    """Independent count: entry w of a key axis compressed at rate m summarises
+    positions m*w .. m*w+m-1 and is visible to the query at position q_pos0+t
+    once the last of them has arrived.  Counted entry by entry."""
+    pos = q_pos0 + t
+    return sum(1 for w in range(N) if m * w + m - 1 <= pos)
+
+
+def pin_compressed_visibility(n_valid_keys) -> bool:
+    """The visible-entry count follows the worked 16-token example and, on a
+    grid of positions, rates and cache lengths, the closed-window count."""
+    g = load_golden("compressed_visibility.json")
+    hca = g["hca"]
+    if [n_valid_keys(t, 0, g["tokens"], hca["m"]) for t in range(g["tokens"])] != hca["visible_entries_per_t"]:
+        return False
+    csa = g["csa"]
+    for t in range(g["tokens"]):
+        if (n_valid_keys(t, 0, g["tokens"], csa["m"]) == 0) != (t < csa["empty_rows_below_t"]):
+            return False
+    for m in (1, 2, 3, 4, 8, 128):
+        for N in (0, 1, 5, 40):
+            for p0 in (-3, 0, 5, 33):
+                for t in range(12):
+                    if n_valid_keys(t, p0, N, m) != windows_closed(t, p0, N, m):
+                        return False
+    return True
+
+
+def pin_compressed_pipeline(index_scores, topk) -> bool:
+    """Indexer and top-k over a compressed axis on the worked example: rows of
+    queries whose first window is still open are all -1, and a row's scores are
+    the prefix of the uncompressed row (compression only hides entries)."""
+    g = load_golden("compressed_visibility.json")
+    r = _rng(15)
+    T, HI, DI, m, K = g["tokens"], 2, 4, g["csa"]["m"], g["csa"]["K"]
+    nent = T // m
+    q = r.integers(-3, 4, size=(1, T, HI, DI)).astype(np.float64)
+    k = r.integers(-3, 4, size=(1, nent, DI)).astype(np.float64)
+    w = r.choice([0.5, 1.0, 2.0], size=(1, T, HI))
+    sc = index_scores(q, k, w, 0, m)
+    sc1 = index_scores(q, k, w, 0, 1)
+    idx = topk(np.nan_to_num(sc, nan=-np.inf).astype(np.float32), K, 0, m)
+    for t in range(T):
+        n = windows_closed(t, 0, nent, m)
+        if not np.array_equal(sc[0, t, :n], sc1[0, t, :n]) or not np.all(np.isnan(sc[0, t, n:])):
+            return False
+        row = idx[0, t]
+        if t < g["csa"]["empty_rows_below_t"] and not np.all(row == -1):
+            return False
+        kept = row[row >= 0]
+        if len(kept) != min(n, K) or (len(kept) and kept.max() >= n):
+            return False
+    return True
+
+
 # ------------------------------------------------------------------ top-k ---
 
 def rank_count_topk(v, K):

@@ -197,3 +197,38 @@ def test_mla_pins_catch_planted_mistakes(mutant):
     checks = [pins.pin_mla_golden(mutant), pins.pin_mla_single_key(mutant), pins.pin_mla_uniform(mutant),
               pins.pin_mla_permutation_and_mask(mutant)]
     assert not all(checks)
+
+
+def test_compressed_visibility():
+    assert pins.pin_compressed_visibility(oracle.n_valid_keys)
+
+
+def test_compressed_pipeline():
+    assert pins.pin_compressed_pipeline(oracle.index_scores, oracle.topk)
+
+
+def _mut_vis_open_window(t, q_pos0, N, m=1):
+    """an entry counted as soon as its window opens"""
+    p = q_pos0 + t
+    return 0 if p < 0 else min(N, p // m + 1)
+
+
+def _mut_vis_off_by_one(t, q_pos0, N, m=1):
+    """own position left out of the closing test"""
+    p = q_pos0 + t
+    return 0 if p <= 0 else min(N, p // m)
+
+
+def _mut_vis_rate_ignored(t, q_pos0, N, m=1):
+    return oracle.n_valid_keys(t, q_pos0, N, 1)
+
+
+def _mut_vis_no_cap(t, q_pos0, N, m=1):
+    p1 = q_pos0 + t + 1
+    return 0 if p1 <= 0 else p1 // m
+
+
+@pytest.mark.parametrize("mutant", [_mut_vis_open_window, _mut_vis_off_by_one, _mut_vis_rate_ignored,
+                                    _mut_vis_no_cap])
+def test_compressed_pins_catch_planted_mistakes(mutant):
+    assert not pins.pin_compressed_visibility(mutant)
