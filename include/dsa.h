@@ -199,6 +199,32 @@ dsa_status dsa_forward_varlen(const void* q_idx, const void* k_idx, const void* 
                               void* stream);
 
 /*
+ * Indexer and top-k over a compressed key axis (the DeepSeek-V4 compressed
+ * sparse attention layer: the lightning indexer scores each query against
+ * compressed cache entries and keeps index_topk of them).
+ * (DeepSeek-V4 documentation, hybrid attention section for the compression
+ *  rate m of the compressed sparse layer (default 4) and index_topk (default
+ *  512); attention mask layout section for the visibility rule: entry w,
+ *  which summarises positions m*w .. m*w + m - 1, becomes visible to the query
+ *  at position p once that window has closed, i.e. when w < (p + 1) / m, so
+ *  queries before the first window closes select nothing and get only -1.)
+ *
+ * k_idx [B, N, D_I] holds N compressed entries per sequence (the indexer's
+ * compressed key cache); query t sits at position p = q_pos0 + t and sees
+ * entries w < min(N, (p + 1) / m) (integer division).  m = 1 is
+ * dsa_index_scores / dsa_topk.  m < 1 returns DSA_ERR_INVALID_ARG and
+ * launches nothing.  Arguments, layouts, workspace and the other errors are
+ * those of dsa_index_scores / dsa_topk.  When no query sees an entry the
+ * indexer launches nothing and leaves scores untouched.
+ */
+dsa_status dsa_index_scores_compressed(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                                       int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t m, int32_t H_I,
+                                       int32_t D_I, int32_t dtype, void* stream);
+dsa_status dsa_topk_compressed(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N,
+                               int64_t q_pos0, int32_t m, int32_t K, void* workspace, size_t ws_bytes,
+                               void* stream);
+
+/*
  * Cache append: one new token per sequence.
  * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)",
  *  paragraph on the indexer's key cache: a per-token, single-head key cache

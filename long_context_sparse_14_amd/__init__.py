@@ -16,6 +16,8 @@ Functions mirror the C entry points:
   topk_varlen(scores, K, seq_lens)                        -> idx
   forward_varlen(q_idx, k_idx, w, q, kv, K, scale, seq_lens, ...)
   cache_append(k_idx, kv, new_k_idx, new_kv, pos)         (in place; either cache may be None)
+  index_scores_compressed(q_idx, k_idx, w, m, q_pos0=0)   -> scores over m-compressed entries
+  topk_compressed(scores, K, m, q_pos0=0)                 -> idx
 """
 from __future__ import annotations
 
@@ -66,6 +68,9 @@ _SIGNATURES = {
     "dsa_forward_varlen": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32,
                                           _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "dsa_cache_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
+    "dsa_index_scores_compressed": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
+                                                   _p]),
+    "dsa_topk_compressed": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _p, _sz, _p]),
 }
 
 
@@ -333,3 +338,40 @@ def cache_append(k_idx, kv, new_k_idx, new_kv, pos, stream=None):
     if pos.shape[0] != B:
         raise ValueError(f"pos must have B={B} entries")
     _check(library().dsa_cache_append(pk, pv, pnk, pnv, pp, B, N, D_I, D, _dtype_code(ref), _stream(stream)))
+
+
+def index_scores_compressed(q_idx, k_idx, w, m: int, q_pos0: int = 0, scores=None, stream=None) -> torch.Tensor:
+    """Indexer scores against N compressed entries (entry w visible to the query at
+    position p when w < (p + 1) // m)."""
+    B, Tq, H_I, D_I = q_idx.shape
+    N = k_idx.shape[1]
+    dt = q_idx.dtype
+    pq = _dev(q_idx, "q_idx", 4)
+    pk = _dev(k_idx, "k_idx", 3, dt)
+    pw = _dev(w, "w", 3, dt)
+    if tuple(k_idx.shape) != (B, N, D_I) or tuple(w.shape) != (B, Tq, H_I):
+        raise ValueError("k_idx must be [B,N,D_I] and w [B,Tq,H_I]")
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q_idx.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if tuple(scores.shape) != (B, Tq, N):
+        raise ValueError("scores must be [B,Tq,N]")
+    _check(library().dsa_index_scores_compressed(pq, pk, pw, ps, B, Tq, N, q_pos0, m, H_I, D_I,
+                                                 _dtype_code(q_idx), _stream(stream)))
+    return scores
+
+
+def topk_compressed(scores, K: int, m: int, q_pos0: int = 0, idx=None, workspace=None, stream=None) -> torch.Tensor:
+    """Top-K over N compressed entries; row t keeps only entries w < (q_pos0 + t + 1) // m."""
+    B, Tq, N = scores.shape
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if idx is None:
+        idx = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+    pi = _dev(idx, "idx", 3, torch.int32)
+    if tuple(idx.shape) != (B, Tq, K):
+        raise ValueError("idx must be [B,Tq,K]")
+    lib = library()
+    ws, nbytes = _workspace(lib.dsa_topk_workspace_size(B, Tq, N, K), scores.device, workspace)
+    _check(lib.dsa_topk_compressed(ps, pi, B, Tq, N, q_pos0, m, K, ws.data_ptr() if ws is not None else None, nbytes,
+                                   _stream(stream)))
+    return idx

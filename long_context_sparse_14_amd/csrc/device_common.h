@@ -88,16 +88,26 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p));
 }
 
-// Position of query 0 of sequence b: q_pos0, or, with per-sequence lengths,
-// seq_lens[b] - Tq (the queries are the sequence's last Tq tokens).
-__device__ __forceinline__ int64_t seq_q0(const int64_t* seq_lens, int64_t b, int64_t Tq, int64_t q_pos0) {
-  return seq_lens != nullptr ? seq_lens[b] - Tq : q_pos0;
+// Which cache rows a query sees.  seq_lens (device, [B], may be null):
+// per-sequence lengths in tokens; with them the queries of sequence b are its
+// last Tq tokens, else query t sits at position q_pos0 + t.  m: compression
+// rate of the key axis: row w summarises positions m*w .. m*w + m - 1 and
+// becomes visible once that window has closed (m = 1: row w is position w).
+struct Vis {
+  const int64_t* seq_lens;
+  int32_t m;
+};
+
+// Position of query 0 of sequence b.
+__device__ __forceinline__ int64_t seq_q0(const Vis& v, int64_t b, int64_t Tq, int64_t q_pos0) {
+  return v.seq_lens != nullptr ? v.seq_lens[b] - Tq : q_pos0;
 }
 
-// Keys query t of a sequence may see: positions 0 .. q0 + t, at most N (none
+// Rows query t of a sequence may see: w < (q0 + t + 1) / m, at most N (none
 // for a query at a negative position).
-__device__ __forceinline__ int64_t visible_keys(int64_t q0, int64_t t, int64_t N) {
-  return max((int64_t)0, min(N, q0 + t + 1));
+__device__ __forceinline__ int64_t visible_keys(const Vis& v, int64_t q0, int64_t t, int64_t N) {
+  const int64_t p1 = q0 + t + 1;
+  return p1 <= 0 ? 0 : min(N, p1 / v.m);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves

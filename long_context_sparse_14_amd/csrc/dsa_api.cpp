@@ -337,6 +337,35 @@ dsa_status dsa_forward_varlen(const void* q_idx, const void* k_idx, const void* 
   return hip_status(e, "sparse MLA launch");
 }
 
+dsa_status dsa_index_scores_compressed(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                                       int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t m, int32_t H_I,
+                                       int32_t D_I, int32_t dtype, void* stream) {
+  dsa_status st = check_index_scores(q_idx, k_idx, w, scores, B, Tq, N, q_pos0, H_I, D_I, dtype, true);
+  if (st != DSA_OK) return st;
+  if (m < 1) return fail(DSA_ERR_INVALID_ARG, "the compression rate m must be >= 1 (got %d)", m);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == DSA_BF16)
+    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s, nullptr, m);
+  else
+    e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
+                                     static_cast<const float*>(w), scores, B, Tq, N, q_pos0, H_I, D_I, s, nullptr,
+                                     m);
+  return hip_status(e, "index scores launch");
+}
+
+dsa_status dsa_topk_compressed(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N,
+                               int64_t q_pos0, int32_t m, int32_t K, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  dsa_status st = check_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  if (m < 1) return fail(DSA_ERR_INVALID_ARG, "the compression rate m must be >= 1 (got %d)", m);
+  return hip_status(dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, static_cast<hipStream_t>(stream),
+                                     nullptr, m),
+                    "top-k launch");
+}
+
 dsa_status dsa_cache_append(void* k_idx, void* kv, const void* new_k_idx, const void* new_kv, const int64_t* pos,
                             int64_t B, int64_t N, int32_t D_I, int32_t D, int32_t dtype, void* stream) {
   if (B < 1 || N < 1) return fail(DSA_ERR_INVALID_ARG, "B and N must be >= 1 (got %lld, %lld)", (long long)B,

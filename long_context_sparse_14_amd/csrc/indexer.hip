@@ -86,8 +86,7 @@ __device__ __forceinline__ float weighted_relu_sum(const QFrags& f, const f32x16
 template <int WAVES, int NBUF, int SCAP>
 __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
-    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, const int64_t* __restrict__ seq_lens,
-    int64_t keys_per_wg) {
+    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, Vis vis, int64_t keys_per_wg) {
   constexpr int TILE_BYTES = 32 * ID * 2;
   static_assert(NBUF >= 2 && NBUF <= 5, "the vmcnt waits below cover up to four tiles in flight");
   static_assert(WAVES * NBUF * TILE_BYTES + SCAP * 4 <= 160 * 1024, "LDS budget");
@@ -98,7 +97,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
   const int half = lane >> 5, col = lane & 31;
   const int64_t t = blockIdx.y, b = blockIdx.z;
   const int64_t row = b * Tq + t;
-  const int64_t n_valid = visible_keys(seq_q0(seq_lens, b, Tq, q_pos0), t, N);
+  const int64_t n_valid = visible_keys(vis, seq_q0(vis, b, Tq, q_pos0), t, N);
   const int64_t k_begin = (int64_t)blockIdx.x * keys_per_wg;  // a multiple of 32
   const int64_t k_end = min(n_valid, k_begin + keys_per_wg);
   if (k_begin >= k_end) return;
@@ -185,8 +184,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
 template <int WAVES, int TK, int PRIO>
 __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
-    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, const int64_t* __restrict__ seq_lens,
-    int64_t nqb) {
+    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, Vis vis, int64_t nqb) {
   // TK keys per LDS tile
   constexpr int PITCH = ID + 8;   // bf16 per LDS row (272 B): spreads rows over the banks
   constexpr int CHUNKS = TK * ID / 8;
@@ -202,9 +200,9 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
   const int64_t t_last = min(Tq, t0 + WAVES) - 1;
   const int64_t t = t0 + wave;
   const bool active = t < Tq;
-  const int64_t q0 = seq_q0(seq_lens, b, Tq, q_pos0);
-  const int64_t n_valid = active ? visible_keys(q0, t, N) : 0;
-  const int64_t n_blk = visible_keys(q0, t_last, N);
+  const int64_t q0 = seq_q0(vis, b, Tq, q_pos0);
+  const int64_t n_valid = active ? visible_keys(vis, q0, t, N) : 0;
+  const int64_t n_blk = visible_keys(vis, q0, t_last, N);
   const int64_t row = b * Tq + (active ? t : t_last);
 
   QFrags f;
@@ -282,14 +280,13 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
 
 __global__ __launch_bounds__(256) void indexer_f32(const float* __restrict__ q, const float* __restrict__ k,
                                                    const float* __restrict__ w, float* __restrict__ scores,
-                                                   int64_t Tq, int64_t N, int64_t q_pos0,
-                                                   const int64_t* __restrict__ seq_lens, int H_I, int D_I,
-                                                   int64_t chunks) {
+                                                   int64_t Tq, int64_t N, int64_t q_pos0, Vis vis, int H_I,
+                                                   int D_I, int64_t chunks) {
   const int64_t blk = blockIdx.x;
   const int64_t rowi = blk / chunks;
   const int64_t s = (blk % chunks) * 256 + threadIdx.x;
   const int64_t t = rowi % Tq, b = rowi / Tq;
-  const int64_t n_valid = visible_keys(seq_q0(seq_lens, b, Tq, q_pos0), t, N);
+  const int64_t n_valid = visible_keys(vis, seq_q0(vis, b, Tq, q_pos0), t, N);
   if (s >= n_valid) return;
   const float* qr = q + rowi * H_I * D_I;
   const float* kr = k + (b * N + s) * D_I;
@@ -307,9 +304,11 @@ __global__ __launch_bounds__(256) void indexer_f32(const float* __restrict__ q, 
 
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                                    hipStream_t stream, const int64_t* seq_lens) {
+                                    hipStream_t stream, const int64_t* seq_lens, int m) {
+  const Vis vis{seq_lens, m};
   // longest visible row: with per-sequence lengths only N is known on the host
-  const int64_t nmax = seq_lens != nullptr ? N : min(N, q_pos0 + Tq);
+  const int64_t nmax = seq_lens != nullptr ? N : min(N, (q_pos0 + Tq) / m);
+  if (nmax <= 0) return hipSuccess;  // no query sees a row
   if (Tq <= 4) {
     // Roughly two workgroups per compute unit over the launch (one fits at a
     // time: it holds all of LDS), whole tiles for every wave, at most SCAP keys.
@@ -320,24 +319,26 @@ hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx
     if (kpw < 32 * WAVES) kpw = 32 * WAVES;
     dim3 grid((unsigned)((nmax + kpw - 1) / kpw), (unsigned)Tq, (unsigned)B);
     hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w,
-                       scores, Tq, N, q_pos0, seq_lens, kpw);
+                       scores, Tq, N, q_pos0, vis, kpw);
   } else {
     constexpr int WAVES = 8;
     const int64_t nqb = (Tq + WAVES - 1) / WAVES;
     dim3 grid((unsigned)nqb, (unsigned)B);
     hipLaunchKernelGGL((indexer_tiled_bf16<WAVES, 128, 1>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w, scores,
-                       Tq, N, q_pos0, seq_lens, nqb);
+                       Tq, N, q_pos0, vis, nqb);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const float* w, float* scores,
                                    int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int H_I, int D_I,
-                                   hipStream_t stream, const int64_t* seq_lens) {
-  const int64_t chunks = ((seq_lens != nullptr ? N : min(N, q_pos0 + Tq)) + 255) / 256;
+                                   hipStream_t stream, const int64_t* seq_lens, int m) {
+  const Vis vis{seq_lens, m};
+  const int64_t chunks = ((seq_lens != nullptr ? N : min(N, (q_pos0 + Tq) / m)) + 255) / 256;
   dim3 grid((unsigned)(B * Tq * chunks));
-  hipLaunchKernelGGL(indexer_f32, grid, dim3(256), 0, stream, q_idx, k_idx, w, scores, Tq, N, q_pos0, seq_lens, H_I,
-                     D_I, chunks);
+  if (chunks == 0) return hipSuccess;  // no query sees a row
+  hipLaunchKernelGGL(indexer_f32, grid, dim3(256), 0, stream, q_idx, k_idx, w, scores, Tq, N, q_pos0, vis, H_I, D_I,
+                     chunks);
   return hipGetLastError();
 }
 

@@ -7,19 +7,21 @@
 
 namespace dsa {
 
-// seq_lens (device, [B], may be null): per-sequence cache lengths; when given,
-// the queries of sequence b sit at positions seq_lens[b] - Tq + t and q_pos0
-// is ignored.
+// seq_lens (device, [B], may be null): per-sequence lengths in tokens; when
+// given, the queries of sequence b sit at positions seq_lens[b] - Tq + t and
+// q_pos0 is ignored.  m: compression rate of the key axis (row w becomes
+// visible to the query at position p when w < (p + 1) / m; m = 1: causal).
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                                    hipStream_t stream, const int64_t* seq_lens = nullptr);
+                                    hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1);
 hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const float* w, float* scores,
                                    int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int H_I, int D_I,
-                                   hipStream_t stream, const int64_t* seq_lens = nullptr);
+                                   hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1);
 
 size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
 hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                       int K, void* workspace, hipStream_t stream, const int64_t* seq_lens = nullptr);
+                       int K, void* workspace, hipStream_t stream, const int64_t* seq_lens = nullptr,
+                       int m = 1);
 
 // Writes row pos[b] of each sequence's caches (rows of D_I and D elements of
 // esize bytes); entries of pos outside [0, N) are skipped.  Either cache may

@@ -61,9 +61,8 @@ constexpr int LONG_MAX_G = TK_THREADS;   // bound on segments per row (one threa
 constexpr int RUN = 16;                  // consecutive keys per thread in a chunk
 constexpr int CHUNK = RUN * TK_THREADS;  // keys ordered by one block prefix sum
 
-__device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N, int64_t q_pos0,
-                                             const int64_t* seq_lens) {
-  return visible_keys(seq_q0(seq_lens, row / Tq, Tq, q_pos0), row % Tq, N);
+__device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, const Vis& vis) {
+  return visible_keys(vis, seq_q0(vis, row / Tq, Tq, q_pos0), row % Tq, N);
 }
 
 // Exclusive block-wide prefix sum of v; `total` receives the block sum.
@@ -316,14 +315,13 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
 
 __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(const float* __restrict__ scores,
                                                                int32_t* __restrict__ idx, int64_t Tq,
-                                                               int64_t N, int64_t q_pos0,
-                                                               const int64_t* __restrict__ seq_lens, int K) {
+                                                               int64_t N, int64_t q_pos0, Vis vis, int K) {
   __shared__ uint32_t skey[TK_CAP];
   __shared__ uint32_t hist[HB];
   __shared__ uint32_t sbuf[3 * TK_WAVES];
   __shared__ uint32_t s_res[4];
   const int64_t row = blockIdx.x;
-  const int64_t n = n_visible(row, Tq, N, q_pos0, seq_lens);
+  const int64_t n = n_visible(row, Tq, N, q_pos0, vis);
   select_row(scores + row * N, n, K, idx + row * K, n <= TK_CAP ? skey : nullptr, hist, sbuf, s_res);
 }
 
@@ -458,13 +456,13 @@ struct SegSmem {
 // segment's keys above t_hi ("definite", index order) and its keys in
 // [t_lo, t_hi] ("candidates", key and index, index order).
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __restrict__ scores, LongWs ws,
-                                                                int64_t Tq, int64_t N, int64_t q_pos0,
-                                                                const int64_t* __restrict__ seq_lens, int K,
+                                                                int64_t Tq, int64_t N, int64_t q_pos0, Vis vis,
+                                                                int K,
                                                                 int G) {
   __shared__ SegSmem sm;
   const int64_t row = blockIdx.y;
   const int g = blockIdx.x;
-  const int64_t n = n_visible(row, Tq, N, q_pos0, seq_lens);
+  const int64_t n = n_visible(row, Tq, N, q_pos0, vis);
   const int64_t seg0 = (int64_t)g * SEG;
   if (n <= K || seg0 >= n) return;
   const float* src = scores + row * N;
@@ -523,10 +521,10 @@ struct FinalSmem {
 // the two ascending lists into the output.  If a check fails, the exact
 // one-workgroup method runs over the row from global memory instead.
 __device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws, int32_t* __restrict__ idx,
-                              int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, const int64_t* seq_lens, int K,
-                              int G, FinalSmem& sm) {
+                              int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, const Vis& vis, int K, int G,
+                              FinalSmem& sm) {
   const int tid = threadIdx.x;
-  const int64_t n = n_visible(row, Tq, N, q_pos0, seq_lens);
+  const int64_t n = n_visible(row, Tq, N, q_pos0, vis);
   int32_t* out = idx + row * K;
   if (n <= K) {
     for (int64_t i = tid; i < K; i += TK_THREADS) out[i] = i < n ? (int32_t)i : -1;
@@ -643,10 +641,9 @@ __device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws
 
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __restrict__ scores, LongWs ws,
                                                              int32_t* __restrict__ idx, int64_t Tq, int64_t N,
-                                                             int64_t q_pos0, const int64_t* __restrict__ seq_lens,
-                                                             int K, int G) {
+                                                             int64_t q_pos0, Vis vis, int K, int G) {
   __shared__ FinalSmem sm;
-  seg_final_row(scores, ws, idx, blockIdx.x, Tq, N, q_pos0, seq_lens, K, G, sm);
+  seg_final_row(scores, ws, idx, blockIdx.x, Tq, N, q_pos0, vis, K, G, sm);
 }
 
 int long_segments(int64_t N) { return (int)((N + SEG - 1) / SEG); }
@@ -663,22 +660,22 @@ size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K) {
 }
 
 hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                       int K, void* workspace, hipStream_t stream, const int64_t* seq_lens) {
+                       int K, void* workspace, hipStream_t stream, const int64_t* seq_lens, int m) {
+  const Vis vis{seq_lens, m};
   const int64_t R = B * Tq;
   // longest visible row: with per-sequence lengths only N is known on the host
-  const int64_t nmax = seq_lens != nullptr ? N : min(N, q_pos0 + Tq);
+  const int64_t nmax = seq_lens != nullptr ? N : min(N, (q_pos0 + Tq) / m);
   if (nmax <= TK_CAP || !use_long_path(B, Tq, N, K)) {
     hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)R), dim3(TK_THREADS), 0, stream, scores, idx, Tq, N, q_pos0,
-                       seq_lens, K);
+                       vis, K);
     return hipGetLastError();
   }
   const int G = long_segments(N);
   const LongWs ws = long_ws(workspace, R, G, K);
   const dim3 grid((unsigned)G, (unsigned)R);
-  hipLaunchKernelGGL(topk_seg_classify, grid, dim3(TK_THREADS), 0, stream, scores, ws, Tq, N, q_pos0, seq_lens, K,
-                     G);
+  hipLaunchKernelGGL(topk_seg_classify, grid, dim3(TK_THREADS), 0, stream, scores, ws, Tq, N, q_pos0, vis, K, G);
   hipLaunchKernelGGL(topk_seg_final, dim3((unsigned)R), dim3(TK_THREADS), 0, stream, scores, ws, idx, Tq, N,
-                     q_pos0, seq_lens, K, G);
+                     q_pos0, vis, K, G);
   return hipGetLastError();
 }
 

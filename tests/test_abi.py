@@ -139,3 +139,16 @@ def test_cache_append_validation():
     assert L.dsa_cache_append(P, P, P, P, P, 0, 10, 128, 576, BF16, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_cache_append(P, P, P, P, P, 2, 10, 128, 576, 9, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_cache_append(P + 2, P, P, P, P, 2, 10, 128, 576, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_compressed_validation():
+    L = lib()
+    # the compression rate must be at least one; the other checks are those of the plain entry points
+    assert L.dsa_index_scores_compressed(P, P, P, P, 2, 1, 100, 64, 0, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert "compression rate" in last()
+    assert L.dsa_index_scores_compressed(P, P, P, P, 2, 1, 100, 64, -4, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_scores_compressed(None, P, P, P, 2, 1, 100, 64, 4, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_compressed(P, P, 2, 1, 100, 64, 0, 16, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert "compression rate" in last()
+    assert L.dsa_topk_compressed(P, P, 2, 1, 100, 64, 4, 0, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_compressed(P, None, 2, 1, 100, 64, 4, 16, None, 0, None) == dsa.DSA_ERR_INVALID_ARG

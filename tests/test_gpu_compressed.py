@@ -1,0 +1,92 @@
+"""GPU parity for the indexer and top-k over a compressed key axis.
+
+With compression rate m, key row w of the cache is one compressed entry that
+summarises positions m*w .. m*w+m-1; the query at position p sees entry w once
+that window has closed, w < (p + 1) // m.  Each case runs the HIP kernels
+through the C-ABI and compares with the oracle at the same rate: scores and
+indices bit-exact (the integer-valued inputs make every fp32 sum exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import causal_scores_equal, dev
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.WORKLOADS
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _dsa():
+    import long_context_sparse_14_amd as dsa
+    dsa.library()
+    return dsa
+
+
+@pytest.mark.parametrize("name,Tq,N,m,q_pos0", [
+    ("indexer_topk_prefill_8k", 1, 32768, 4, 131071),   # decode kernel, every entry closed
+    ("indexer_topk_prefill_8k", 4, 40000, 4, 100000),   # decode kernel, part of the cache visible
+    ("indexer_topk_prefill_8k", 70, 600, 4, 0),         # tiled kernel: the first three rows see nothing
+    ("indexer_topk_prefill_8k", 5, 300, 128, 1000),     # large rate, few visible entries
+    ("tiny_prefill_f32", 64, 32, 8, 0),                 # fp32 kernel
+    ("indexer_topk_prefill_8k", 2, 64, 4, 0),           # no query sees an entry: nothing is launched
+])
+def test_indexer_compressed_exact(name, Tq, N, m, q_pos0):
+    dsa = _dsa()
+    wl = WL[name].replace(B=2, Tq=Tq, N=N, q_pos0=q_pos0)
+    x = synth.make_inputs(wl)
+    scores = dsa.index_scores_compressed(dev(x["q_idx"]), dev(x["k_idx"]), dev(x["w"]), m,
+                                         q_pos0=q_pos0).cpu().numpy()
+    ts = sorted({0, 1, 2, 3, m - 1, m, Tq // 2, Tq - 1} & set(range(Tq)))
+    if max(oracle.n_valid_keys(t, q_pos0, N, m) for t in range(Tq)) == 0:
+        # the call must leave the score buffer alone
+        buf = torch.full((2, Tq, N), 7.0, device="cuda")
+        dsa.index_scores_compressed(dev(x["q_idx"]), dev(x["k_idx"]), dev(x["w"]), m, q_pos0=q_pos0, scores=buf)
+        assert torch.all(buf == 7.0)
+    for b in range(2):
+        ref = oracle.index_scores_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], ts, q_pos0, m)
+        causal_scores_equal(scores[b], ref, ts, f"scores b={b} m={m}")
+
+
+@pytest.mark.parametrize("B,Tq,N,K,m,q_pos0", [
+    (2, 1, 32768, 512, 4, 131071),   # 32768 visible entries: segmented long-row method
+    (1, 4, 40000, 2048, 2, 79990),   # long-row method, rows of 39995..39997 entries
+    (2, 20, 3000, 64, 8, 0),         # one-workgroup method, rows 0..6 see nothing
+    (1, 16, 4, 2, 4, 0),             # the 16-token example of the attention mask layout, CSA m=4
+    (2, 2, 64, 8, 4, 0),             # no row sees an entry: every slot -1
+])
+def test_topk_compressed_exact(B, Tq, N, K, m, q_pos0):
+    dsa = _dsa()
+    rng = np.random.default_rng(N + K + m)
+    vals = (rng.integers(0, 3000, size=(B, Tq, N)) / 8).astype(np.float32)
+    idx = dsa.topk_compressed(torch.from_numpy(vals).cuda(), K, m, q_pos0=q_pos0).cpu().numpy()
+    ref = oracle.topk(vals, K, q_pos0, m)
+    for b in range(B):
+        for t in range(Tq):
+            n = oracle.n_valid_keys(t, q_pos0, N, m)
+            assert np.array_equal(idx[b, t], ref[b, t]), f"row {b},{t} (n={n})"
+
+
+def test_compressed_index_then_topk_example():
+    """Indexer then top-2 over 4 entries of rate 4 for 16 queries: queries 0..2
+    select nothing (all -1), queries 3..6 select entry 0 only, later ones two."""
+    dsa = _dsa()
+    wl = WL["indexer_topk_prefill_8k"].replace(B=1, Tq=16, N=4, q_pos0=0)
+    x = synth.make_inputs(wl, seed=3)
+    sc = dsa.index_scores_compressed(dev(x["q_idx"]), dev(x["k_idx"]), dev(x["w"]), 4)
+    idx = dsa.topk_compressed(sc, 2, 4).cpu().numpy()[0]
+    ref_sc = oracle.index_scores(x["q_idx"], x["k_idx"], x["w"], 0, 4)
+    ref = oracle.topk(np.nan_to_num(ref_sc, nan=-np.inf).astype(np.float32), 2, 0, 4)[0]
+    assert np.array_equal(idx, ref)
+    assert np.all(idx[:3] == -1)
+    assert np.all(idx[3:7, 0] == 0) and np.all(idx[3:7, 1] == -1)
+    assert np.all(idx[7:] >= 0)
