@@ -43,7 +43,11 @@ the design notes of the repository):
     D-wide latent row shared by all heads; the value is the row's first DV
     entries; logits are scale * q.kv; negative indices are masked (additive
     -inf); a row with no valid index gives o = 0 and lse = -inf;
-  * lse is the natural-log sum of exp(logits).
+  * lse is the natural-log sum of exp(logits);
+  * absorbed and naive MLA: head h's key up-projection W_UK[h] [d_nope, d_c]
+    folds into its query (mla_absorb_query) and its value up-projection
+    W_UV[h] [d_v, d_c] applies to the latent output (mla_output_projection);
+    mla_naive_rows is the per-head form with explicit keys and values.
 
 Every function works on float64 copies of its inputs.  bf16 inputs arrive as
 uint16 bit patterns and are widened exactly by ``as_f64``.
@@ -55,7 +59,7 @@ import numpy as np
 __all__ = [
     "as_f64", "bf16_bits_to_f64", "n_valid_keys", "index_scores", "index_scores_rows",
     "topk_row", "topk", "sparse_mla", "sparse_mla_rows", "dense_masked_mla", "forward_rows",
-    "sylvester_hadamard",
+    "mla_naive_rows", "mla_absorb_query", "mla_output_projection", "sylvester_hadamard",
 ]
 
 
@@ -232,6 +236,63 @@ def dense_masked_mla(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, scale: floa
             o[b, t] = (p @ kvb[:n, :DV]) / l
             lse[b, t] = (m + np.log(l))[:, 0]
     return o, lse
+
+
+# ----------------------------------------------------------------------------
+# MLA projections around the absorbed form, and the naive per-head form
+# ----------------------------------------------------------------------------
+#
+# DeepSeek-V3 documentation, "DeepseekV3Config": keys and values come from a
+# kv_lora_rank-wide latent through low-rank (LoRA) projections; each head has
+# a qk_nope_head_dim part without rotary embedding, a qk_rope_head_dim part
+# with it, and a v_head_dim-wide value.  Its section on limitations notes
+# that the port computes attention the "naive" way (per-head keys and values,
+# not strictly MLA).  Reading: the key up-projection of head h is a matrix
+# W_UK[h] [d_nope, d_c] and the value up-projection W_UV[h] [d_v, d_c], both
+# applied to the latent c; the rope part of the key is one d_rope vector per
+# token shared by all heads.  One latent cache row is [c (d_c) | k_rope
+# (d_rope)].
+
+def mla_naive_rows(q_head: np.ndarray, c_kv: np.ndarray, k_rope: np.ndarray, idx_row: np.ndarray,
+                   W_UK: np.ndarray, W_UV: np.ndarray, scale: float):
+    """Naive MLA for one query over its selected tokens, head by head.
+
+    q_head [H, d_nope + d_rope]; c_kv [N, d_c]; k_rope [N, d_rope];
+    W_UK [H, d_nope, d_c]; W_UV [H, d_v, d_c].  Head h builds explicit keys
+    k_j = [W_UK[h] c_j, k_rope_j] and values v_j = W_UV[h] c_j for the selected
+    tokens j (indices < 0 are masked), then runs softmax(scale * q.k) v.
+    Returns (o [H, d_v], lse [H]).
+    """
+    q_head, c_kv, k_rope = as_f64(q_head), as_f64(c_kv), as_f64(k_rope)
+    W_UK, W_UV = as_f64(W_UK), as_f64(W_UV)
+    H = q_head.shape[0]
+    sel = [int(i) for i in np.asarray(idx_row).reshape(-1) if int(i) >= 0]
+    o = np.zeros((H, W_UV.shape[1]))
+    lse = np.full(H, -np.inf)
+    for h in range(H):
+        keys = np.concatenate([c_kv[sel] @ W_UK[h].T, k_rope[sel]], axis=1)   # [n, d_nope + d_rope]
+        values = c_kv[sel] @ W_UV[h].T                                         # [n, d_v]
+        oh, lh = _softmax_attend(scale * (q_head[h][None, :] @ keys.T), values)
+        o[h], lse[h] = oh[0], lh[0]
+    return o, lse
+
+
+def mla_absorb_query(q_head: np.ndarray, W_UK: np.ndarray) -> np.ndarray:
+    """Fold the key up-projection into the query: [..., H, d_nope + d_rope] -> [..., H, d_c + d_rope].
+
+    q_lat[h] = [W_UK[h]^T q_nope[h], q_rope[h]], so that q_lat[h] . [c | k_rope]
+    equals the naive head's q[h] . [W_UK[h] c | k_rope].
+    """
+    q_head, W_UK = as_f64(q_head), as_f64(W_UK)
+    d_nope = W_UK.shape[1]
+    q_nope, q_rope = q_head[..., :d_nope], q_head[..., d_nope:]
+    q_c = np.einsum("...hn,hnc->...hc", q_nope, W_UK)
+    return np.concatenate([q_c, q_rope], axis=-1)
+
+
+def mla_output_projection(o_lat: np.ndarray, W_UV: np.ndarray) -> np.ndarray:
+    """Apply the value up-projection to the latent output: [..., H, d_c] -> [..., H, d_v], o[h] = W_UV[h] o_lat[h]."""
+    return np.einsum("...hc,hvc->...hv", as_f64(o_lat), as_f64(W_UV))
 
 
 # ----------------------------------------------------------------------------

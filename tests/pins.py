@@ -335,3 +335,68 @@ def pin_mla_sparse_equals_dense(sparse_mla, dense_masked_mla) -> bool:
     o, lse = sparse_mla(q, kv, idx, 0.5, DV)
     od, lsed = dense_masked_mla(q, kv, idx, 0.5, DV, 0)
     return np.allclose(o, od, atol=1e-13) and np.allclose(lse, lsed, atol=1e-13)
+
+
+# ------------------------------------------------- MLA projections (absorbed) ---
+
+def _mla_proj_case(seed, H=3, d_nope=4, d_rope=2, d_c=6, d_v=5, N=11):
+    r = _rng(seed)
+    return dict(q=r.standard_normal((H, d_nope + d_rope)), c=r.standard_normal((N, d_c)),
+                kr=r.standard_normal((N, d_rope)), W_UK=r.standard_normal((H, d_nope, d_c)),
+                W_UV=r.standard_normal((H, d_v, d_c)))
+
+
+def _safe(fn, *a):
+    try:
+        return fn(*a)
+    except Exception:
+        return None
+
+
+def pin_mla_naive_sdpa(mla_naive_rows) -> bool:
+    """The naive per-head form is plain attention with per-head keys [W_UK c | k_rope]
+    and values W_UV c: compare against torch's scaled_dot_product_attention (CPU,
+    float64) over the selected tokens, and check lse against logsumexp."""
+    import torch
+    x = _mla_proj_case(41)
+    H = x["q"].shape[0]
+    idx = np.array([7, 2, -1, 9, 0, -1])
+    sel = [int(i) for i in idx if i >= 0]
+    out = _safe(mla_naive_rows, x["q"], x["c"], x["kr"], idx, x["W_UK"], x["W_UV"], 0.45)
+    if out is None:
+        return False
+    o, lse = out
+    c = torch.from_numpy(x["c"][sel])
+    keys = torch.stack([torch.cat([c @ torch.from_numpy(x["W_UK"][h]).T, torch.from_numpy(x["kr"][sel])], 1)
+                        for h in range(H)])                                  # [H, n, d_nope + d_rope]
+    vals = torch.stack([c @ torch.from_numpy(x["W_UV"][h]).T for h in range(H)])  # [H, n, d_v]
+    tq = torch.from_numpy(x["q"])[:, None, :]                                  # [H, 1, d]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, keys, vals, scale=0.45)[:, 0].numpy()
+    ref_lse = torch.logsumexp((tq @ keys.transpose(1, 2))[:, 0] * 0.45, dim=-1).numpy()
+    # no selected token: zero output, lse -inf
+    o0, l0 = mla_naive_rows(x["q"], x["c"], x["kr"], np.array([-1, -1]), x["W_UK"], x["W_UV"], 0.45)
+    return (o.shape == ref.shape and np.allclose(o, ref, atol=1e-12) and np.allclose(lse, ref_lse, atol=1e-12)
+            and not np.any(o0) and np.all(np.isneginf(l0)))
+
+
+def pin_mla_absorbed_equals_naive(mla_absorb_query, sparse_mla_rows, mla_output_projection, mla_naive_rows) -> bool:
+    """Absorbed latent attention (query folded through W_UK, attention over the
+    [c | k_rope] rows with value c, then W_UV) equals naive per-head attention
+    with the same weights, on several index rows including masked and empty ones."""
+    for seed, dims in ((42, {}), (43, dict(H=2, d_nope=3, d_rope=3, d_c=8, d_v=2, N=7))):
+        x = _mla_proj_case(seed, **dims)
+        d_c = x["c"].shape[1]
+        rows = np.concatenate([x["c"], x["kr"]], axis=1)
+        N = rows.shape[0]
+        for idx in (np.arange(N), np.array([3, -1, 0, 5]), np.array([N - 1]), np.array([-1, -1])):
+            q_lat = _safe(mla_absorb_query, x["q"], x["W_UK"])
+            if q_lat is None or q_lat.shape != (x["q"].shape[0], rows.shape[1]):
+                return False
+            o_lat, lse = sparse_mla_rows(q_lat, rows, idx, 0.3, d_c)
+            o = _safe(mla_output_projection, o_lat, x["W_UV"])
+            on, ln = mla_naive_rows(x["q"], x["c"], x["kr"], idx, x["W_UK"], x["W_UV"], 0.3)
+            if o is None or o.shape != on.shape or not np.allclose(o, on, atol=1e-12):
+                return False
+            if not np.allclose(lse, ln, atol=1e-12) and not (np.all(np.isneginf(lse)) and np.all(np.isneginf(ln))):
+                return False
+    return True

@@ -232,3 +232,68 @@ def _mut_vis_no_cap(t, q_pos0, N, m=1):
                                     _mut_vis_no_cap])
 def test_compressed_pins_catch_planted_mistakes(mutant):
     assert not pins.pin_compressed_visibility(mutant)
+
+
+def test_mla_naive_sdpa():
+    assert pins.pin_mla_naive_sdpa(oracle.mla_naive_rows)
+
+
+def test_mla_absorbed_equals_naive():
+    assert pins.pin_mla_absorbed_equals_naive(oracle.mla_absorb_query, oracle.sparse_mla_rows,
+                                              oracle.mla_output_projection, oracle.mla_naive_rows)
+
+
+def _mut_absorb_no_rope(q, W_UK):
+    out = oracle.mla_absorb_query(q, W_UK)
+    out[..., W_UK.shape[2]:] = 0.0
+    return out
+
+
+def _mut_absorb_transposed(q, W_UK):
+    """W_UK used as if stored [d_c, d_nope] (only runs where the shapes allow)"""
+    d_nope = W_UK.shape[1]
+    q = np.asarray(q, dtype=np.float64)
+    return np.concatenate([np.einsum("hn,hcn->hc", q[:, :d_nope], W_UK.transpose(0, 2, 1).reshape(
+        W_UK.shape[0], W_UK.shape[2], d_nope)[:, :, ::-1]), q[:, d_nope:]], axis=-1)
+
+
+def _mut_out_proj_transposed(o_lat, W_UV):
+    return np.einsum("hc,hvc->hv", np.asarray(o_lat)[:, ::-1], W_UV)
+
+
+def _mut_naive_value_from_key(q, c, kr, idx, W_UK, W_UV, scale):
+    """values read through the key projection padded to d_v columns"""
+    H, d_nope, d_c = W_UK.shape
+    W = np.zeros_like(W_UV)
+    n = min(d_nope, W_UV.shape[1])
+    W[:, :n] = W_UK[:, :n]
+    return oracle.mla_naive_rows(q, c, kr, idx, W_UK, W, scale)
+
+
+def _mut_naive_no_rope(q, c, kr, idx, W_UK, W_UV, scale):
+    return oracle.mla_naive_rows(q, c, np.zeros_like(kr), idx, W_UK, W_UV, scale)
+
+
+@pytest.mark.parametrize("mutant", [_mut_absorb_no_rope, _mut_absorb_transposed])
+def test_absorb_pin_catches_planted_mistakes(mutant):
+    assert not pins.pin_mla_absorbed_equals_naive(mutant, oracle.sparse_mla_rows, oracle.mla_output_projection,
+                                                  oracle.mla_naive_rows)
+
+
+def test_out_proj_pin_catches_planted_mistake():
+    assert not pins.pin_mla_absorbed_equals_naive(oracle.mla_absorb_query, oracle.sparse_mla_rows,
+                                                  _mut_out_proj_transposed, oracle.mla_naive_rows)
+
+
+@pytest.mark.parametrize("mutant", [_mut_naive_value_from_key, _mut_naive_no_rope])
+def test_naive_pin_catches_planted_mistakes(mutant):
+    assert not pins.pin_mla_naive_sdpa(mutant)
+
+
+def test_absorbed_pin_catches_value_from_rope():
+    """the value read from the wrong end of the latent row breaks absorbed == naive"""
+    def mla_rows_mut(q, kv, idx, scale, DV):
+        kv = np.asarray(kv, dtype=np.float64)
+        return oracle.sparse_mla_rows(q, kv[:, ::-1], idx, scale, DV)
+    assert not pins.pin_mla_absorbed_equals_naive(oracle.mla_absorb_query, mla_rows_mut,
+                                                  oracle.mla_output_projection, oracle.mla_naive_rows)
