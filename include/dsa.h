@@ -244,6 +244,49 @@ dsa_status dsa_topk_compressed(const float* scores, int32_t* idx, int64_t B, int
 dsa_status dsa_cache_append(void* k_idx, void* kv, const void* new_k_idx, const void* new_kv, const int64_t* pos,
                             int64_t B, int64_t N, int32_t D_I, int32_t D, int32_t dtype, void* stream);
 
+/*
+ * Projections on either side of the sparse MLA (bf16 only; fp32 accumulation,
+ * outputs rounded to nearest even).
+ * (DeepSeek-V3 documentation, "DeepseekV3Config": keys and values are
+ *  low-rank projections of a kv_lora_rank-wide latent, with qk_nope_head_dim,
+ *  qk_rope_head_dim and v_head_dim per head; its limitations note describes the
+ *  naive per-head form these projections turn into the absorbed one.
+ *  DeepSeek-V3.2 documentation, "DeepSeek Sparse Attention (DSA)": the
+ *  indexer's queries come from the low-rank query latent through wq_b.)
+ *
+ * dsa_mla_absorb_q: folds the key up-projection into the query.
+ *   q     [M, H, d_nope + d_rope]  per-head queries, the part without rotary
+ *                                  embedding first (M = B*Tq rows);
+ *   w_uk  [H, d_nope, d_c]         key up-projection of each head (key_h = w_uk[h] c);
+ *   q_lat [M, H, d_c + d_rope]     out: q_lat[m,h,:d_c] = w_uk[h]^T q[m,h,:d_nope],
+ *                                  q_lat[m,h,d_c:] = q[m,h,d_nope:] (copied).
+ *   q_lat is the query dsa_sparse_mla_fwd takes (d_c = 512, d_rope = 64).
+ *   Requires d_nope a positive multiple of 32, d_c a positive multiple of 8,
+ *   d_rope a multiple of 8 (0 allowed).
+ *
+ * dsa_mla_out_proj: applies the value up-projection to the latent output.
+ *   o_lat [M, H, d_c]   the output of dsa_sparse_mla_fwd;
+ *   w_uv  [H, d_v, d_c] value up-projection of each head (value_h = w_uv[h] c);
+ *   o     [M, H, d_v]   out: o[m,h,:] = w_uv[h] o_lat[m,h,:].
+ *   Requires d_c a positive multiple of 32, d_v >= 1.
+ *
+ * dsa_linear: y [M, N] = x [M, K] w^T, w [N, K] (a linear layer's weight, as
+ *   the indexer's wq_b [H_I*D_I, q_lora_rank] and its head-weight projection).
+ *   Requires K a positive multiple of 32, N >= 1.
+ *
+ * All tensors are dense, row-major, 16-byte aligned device memory owned by the
+ * caller; inputs and outputs must not overlap.  M = 0 launches nothing.
+ * M <= 65535*64 and H <= 65535.  Errors: DSA_ERR_INVALID_ARG (null or
+ * misaligned pointers, negative sizes, unknown dtype), DSA_ERR_UNSUPPORTED
+ * (fp32, or sizes outside the requirements above); nothing is launched then.
+ */
+dsa_status dsa_mla_absorb_q(const void* q, const void* w_uk, void* q_lat, int64_t M, int32_t H, int32_t d_nope,
+                            int32_t d_rope, int32_t d_c, int32_t dtype, void* stream);
+dsa_status dsa_mla_out_proj(const void* o_lat, const void* w_uv, void* o, int64_t M, int32_t H, int32_t d_c,
+                            int32_t d_v, int32_t dtype, void* stream);
+dsa_status dsa_linear(const void* x, const void* w, void* y, int64_t M, int32_t N, int32_t K, int32_t dtype,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

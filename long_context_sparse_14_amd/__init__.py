@@ -18,6 +18,9 @@ Functions mirror the C entry points:
   cache_append(k_idx, kv, new_k_idx, new_kv, pos)         (in place; either cache may be None)
   index_scores_compressed(q_idx, k_idx, w, m, q_pos0=0)   -> scores over m-compressed entries
   topk_compressed(scores, K, m, q_pos0=0)                 -> idx
+  mla_absorb_q(q, w_uk)                                   -> q_lat [..., H, d_c + d_rope] (query absorption)
+  mla_out_proj(o_lat, w_uv)                               -> o [..., H, d_v] (value up-projection)
+  linear(x, w)                                            -> x w^T (indexer projections)
 """
 from __future__ import annotations
 
@@ -71,6 +74,9 @@ _SIGNATURES = {
     "dsa_index_scores_compressed": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
                                                    _p]),
     "dsa_topk_compressed": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _p, _sz, _p]),
+    "dsa_mla_absorb_q": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _p]),
+    "dsa_mla_out_proj": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p]),
+    "dsa_linear": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _p]),
 }
 
 
@@ -375,3 +381,55 @@ def topk_compressed(scores, K: int, m: int, q_pos0: int = 0, idx=None, workspace
     _check(lib.dsa_topk_compressed(ps, pi, B, Tq, N, q_pos0, m, K, ws.data_ptr() if ws is not None else None, nbytes,
                                    _stream(stream)))
     return idx
+
+
+def mla_absorb_q(q, w_uk, q_lat=None, stream=None) -> torch.Tensor:
+    """q [..., H, d_nope + d_rope], w_uk [H, d_nope, d_c] -> q_lat [..., H, d_c + d_rope]."""
+    H, d_nope, d_c = w_uk.shape
+    if q.dim() < 2 or q.shape[-2] != H or q.shape[-1] < d_nope:
+        raise ValueError("q must be [..., H, d_nope + d_rope] with the H and d_nope of w_uk")
+    d_rope = q.shape[-1] - d_nope
+    M = q.numel() // (H * (d_nope + d_rope))
+    pq = _dev(q, "q", q.dim())
+    pw = _dev(w_uk, "w_uk", 3, q.dtype)
+    if q_lat is None:
+        q_lat = torch.empty(tuple(q.shape[:-1]) + (d_c + d_rope,), dtype=q.dtype, device=q.device)
+    pl = _dev(q_lat, "q_lat", q.dim(), q.dtype)
+    if tuple(q_lat.shape) != tuple(q.shape[:-1]) + (d_c + d_rope,):
+        raise ValueError("q_lat must be [..., H, d_c + d_rope]")
+    _check(library().dsa_mla_absorb_q(pq, pw, pl, M, H, d_nope, d_rope, d_c, _dtype_code(q), _stream(stream)))
+    return q_lat
+
+
+def mla_out_proj(o_lat, w_uv, o=None, stream=None) -> torch.Tensor:
+    """o_lat [..., H, d_c], w_uv [H, d_v, d_c] -> o [..., H, d_v]."""
+    H, d_v, d_c = w_uv.shape
+    if o_lat.dim() < 2 or tuple(o_lat.shape[-2:]) != (H, d_c):
+        raise ValueError("o_lat must be [..., H, d_c] with the H and d_c of w_uv")
+    M = o_lat.numel() // (H * d_c)
+    pi = _dev(o_lat, "o_lat", o_lat.dim())
+    pw = _dev(w_uv, "w_uv", 3, o_lat.dtype)
+    if o is None:
+        o = torch.empty(tuple(o_lat.shape[:-1]) + (d_v,), dtype=o_lat.dtype, device=o_lat.device)
+    po = _dev(o, "o", o_lat.dim(), o_lat.dtype)
+    if tuple(o.shape) != tuple(o_lat.shape[:-1]) + (d_v,):
+        raise ValueError("o must be [..., H, d_v]")
+    _check(library().dsa_mla_out_proj(pi, pw, po, M, H, d_c, d_v, _dtype_code(o_lat), _stream(stream)))
+    return o
+
+
+def linear(x, w, y=None, stream=None) -> torch.Tensor:
+    """x [..., K], w [N, K] -> y [..., N] = x w^T."""
+    N, K = w.shape
+    if x.shape[-1] != K:
+        raise ValueError("x must be [..., K] with the K of w")
+    M = x.numel() // K
+    px = _dev(x, "x", x.dim())
+    pw = _dev(w, "w", 2, x.dtype)
+    if y is None:
+        y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=x.device)
+    py = _dev(y, "y", x.dim(), x.dtype)
+    if tuple(y.shape) != tuple(x.shape[:-1]) + (N,):
+        raise ValueError("y must be [..., N]")
+    _check(library().dsa_linear(px, pw, py, M, N, K, _dtype_code(x), _stream(stream)))
+    return y

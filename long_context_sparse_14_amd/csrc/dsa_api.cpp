@@ -149,6 +149,19 @@ dsa_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+constexpr int64_t kMaxGemmRows = 65535LL * 64;
+
+dsa_status check_proj_common(const void* a, const void* b, const void* c, int64_t M, int32_t dtype) {
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "the projections are built for bf16 only");
+  if (!a || !b || !c) return fail(DSA_ERR_INVALID_ARG, "tensor pointers must not be null");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c))
+    return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (M < 0) return fail(DSA_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+  if (M > kMaxGemmRows) return fail(DSA_ERR_UNSUPPORTED, "M must be <= %lld", (long long)kMaxGemmRows);
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +397,47 @@ dsa_status dsa_cache_append(void* k_idx, void* kv, const void* new_k_idx, const 
   return hip_status(dsa::launch_cache_append(k_idx, kv, new_k_idx, new_kv, pos, B, N, k_idx ? D_I : 0, kv ? D : 0,
                                              dtype == DSA_BF16 ? 2 : 4, static_cast<hipStream_t>(stream)),
                     "cache append launch");
+}
+
+dsa_status dsa_mla_absorb_q(const void* q, const void* w_uk, void* q_lat, int64_t M, int32_t H, int32_t d_nope,
+                            int32_t d_rope, int32_t d_c, int32_t dtype, void* stream) {
+  dsa_status st = check_proj_common(q, w_uk, q_lat, M, dtype);
+  if (st != DSA_OK) return st;
+  if (H < 1 || H > 65535) return fail(DSA_ERR_INVALID_ARG, "H must be in [1, 65535] (got %d)", H);
+  if (d_nope < 32 || d_nope % 32) return fail(DSA_ERR_UNSUPPORTED, "d_nope must be a positive multiple of 32");
+  if (d_c < 8 || d_c % 8) return fail(DSA_ERR_UNSUPPORTED, "d_c must be a positive multiple of 8");
+  if (d_rope < 0 || d_rope % 8) return fail(DSA_ERR_UNSUPPORTED, "d_rope must be a multiple of 8 (0 allowed)");
+  const int64_t dq = (int64_t)d_nope + d_rope, dl = (int64_t)d_c + d_rope;
+  const uint16_t* qp = static_cast<const uint16_t*>(q);
+  uint16_t* lp = static_cast<uint16_t*>(q_lat);
+  dsa::GemmArgs g{qp, H * dq, dq, static_cast<const uint16_t*>(w_uk), d_c, (int64_t)d_nope * d_c, lp, H * dl, dl,
+                  M, d_c, d_nope, d_rope ? qp + d_nope : nullptr, H * dq, dq, d_rope ? lp + d_c : nullptr, H * dl,
+                  dl, d_rope};
+  return hip_status(dsa::launch_gemm_bf16(g, false, H, static_cast<hipStream_t>(stream)), "absorption launch");
+}
+
+dsa_status dsa_mla_out_proj(const void* o_lat, const void* w_uv, void* o, int64_t M, int32_t H, int32_t d_c,
+                            int32_t d_v, int32_t dtype, void* stream) {
+  dsa_status st = check_proj_common(o_lat, w_uv, o, M, dtype);
+  if (st != DSA_OK) return st;
+  if (H < 1 || H > 65535) return fail(DSA_ERR_INVALID_ARG, "H must be in [1, 65535] (got %d)", H);
+  if (d_c < 32 || d_c % 32) return fail(DSA_ERR_UNSUPPORTED, "d_c must be a positive multiple of 32");
+  if (d_v < 1) return fail(DSA_ERR_INVALID_ARG, "d_v must be >= 1");
+  dsa::GemmArgs g{static_cast<const uint16_t*>(o_lat), (int64_t)H * d_c, d_c, static_cast<const uint16_t*>(w_uv),
+                  d_c, (int64_t)d_v * d_c, static_cast<uint16_t*>(o), (int64_t)H * d_v, d_v, M, d_v, d_c,
+                  nullptr, 0, 0, nullptr, 0, 0, 0};
+  return hip_status(dsa::launch_gemm_bf16(g, true, H, static_cast<hipStream_t>(stream)), "output projection launch");
+}
+
+dsa_status dsa_linear(const void* x, const void* w, void* y, int64_t M, int32_t N, int32_t K, int32_t dtype,
+                      void* stream) {
+  dsa_status st = check_proj_common(x, w, y, M, dtype);
+  if (st != DSA_OK) return st;
+  if (N < 1) return fail(DSA_ERR_INVALID_ARG, "N must be >= 1");
+  if (K < 32 || K % 32) return fail(DSA_ERR_UNSUPPORTED, "K must be a positive multiple of 32");
+  dsa::GemmArgs g{static_cast<const uint16_t*>(x), K, 0, static_cast<const uint16_t*>(w), K, 0,
+                  static_cast<uint16_t*>(y), N, 0, M, N, K, nullptr, 0, 0, nullptr, 0, 0, 0};
+  return hip_status(dsa::launch_gemm_bf16(g, true, 1, static_cast<hipStream_t>(stream)), "linear launch");
 }
 
 }  // extern "C"

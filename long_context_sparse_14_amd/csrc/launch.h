@@ -38,4 +38,30 @@ hipError_t launch_sparse_mla_f32(const float* q, const float* kv, const int32_t*
                                  int64_t B, int64_t Tq, int64_t N, int H, int D, int DV, int K, float scale,
                                  hipStream_t stream);
 
+// Batched bf16 GEMM: C[z][m, n] = sum_k A[z][m, k] * B[z](k, n) for z < batch,
+// fp32 accumulation, bf16 (round to nearest even) output.  A: row m at
+// A + z*sA + m*lda, k contiguous.  B: b_nk ? element (k, n) at B + z*sB +
+// n*ldb + k : at B + z*sB + k*ldb + n.  C: element (m, n) at C + z*sC + m*ldc +
+// n.  Requires K % 32 == 0, 16-byte aligned rows of A and B (lda, ldb, sA, sB
+// multiples of 8, and N % 8 == 0 when !b_nk), M <= 65535*64, batch <= 65535.
+// When cp_dst is set, the first column block also copies cp_w (a multiple of
+// 8) elements of each row m: cp_src + z*cp_ss + m*cp_lds -> cp_dst + z*cp_sd +
+// m*cp_ldd (16-byte aligned rows).
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t lda, sA;
+  const uint16_t* B;
+  int64_t ldb, sB;
+  uint16_t* C;
+  int64_t ldc, sC;
+  int64_t M;
+  int N, K;
+  const uint16_t* cp_src;
+  int64_t cp_lds, cp_ss;
+  uint16_t* cp_dst;
+  int64_t cp_ldd, cp_sd;
+  int cp_w;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& g, bool b_nk, int64_t batch, hipStream_t stream);
+
 }  // namespace dsa

@@ -1,0 +1,327 @@
+// Projections on either side of the sparse MLA, as one batched bf16 GEMM on
+// the matrix cores:
+//   * query absorption: q_lat[m, h, :d_c] = W_UK[h]^T q[m, h, :d_nope], with the
+//     rope part q[m, h, d_nope:] copied behind it (the key up-projection folded
+//     into the query, so that the attention runs over the shared latent rows);
+//   * output projection: o[m, h, :] = W_UV[h] o_lat[m, h, :] (the value
+//     up-projection applied to the latent attention output);
+//   * a plain linear layer y = x W^T (the indexer's query projection wq_b from
+//     the query latent, and its per-head weight projection).
+// DeepSeek-V3 documentation, "DeepseekV3Config" (kv_lora_rank, qk_nope_head_dim,
+// qk_rope_head_dim, v_head_dim: keys and values are low-rank projections of one
+// latent); DeepSeek-V3.2 documentation, "DeepSeek Sparse Attention (DSA)" (the
+// indexer's queries come from the low-rank query latent through wq_b).
+//
+// C[z][m, n] = sum_k A[z][m, k] * B[z](k, n), fp32 accumulation, bf16 output
+// rounded to nearest even.  A is row-major with k contiguous.  B is either
+// [N][K] (k contiguous, as a linear layer's weight) or [K][N] (n contiguous,
+// as W_UK[h] [d_nope, d_c] is read by the absorption).
+//
+// Tiling for many rows: a 256-thread workgroup (4 waves) owns a 128 x 128
+// tile of C; each wave a 64 x 64 block, four 32x32x16 MFMA chains fed by two A
+// and two B operand reads per k-step (few rows take the split-K kernel below).
+// K advances 32 at a time through double-buffered LDS tiles,
+// and global loads run two tiles ahead through registers.  A and a [N][K] B
+// sit in LDS row-major with k contiguous (80-byte pitch), so an operand is
+// one 16-byte read.  A [K][N] B keeps its global layout in LDS (n contiguous,
+// 288-byte pitch) and reaches the MFMA through the gfx950 transposing read
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i & 3) of the 8 bytes addressed by lane 4c + (i >> 2), c = 0..3, so lanes
+// that address four consecutive k-rows of four consecutive columns hand every
+// lane four k-values of its own column.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int GK = 32;            // k per LDS tile
+constexpr int APITCH = GK + 8;    // bf16 per LDS row of A and of a [N][K] B
+constexpr int GN = 128;           // columns of C per workgroup
+constexpr int KNPITCH = GN + 16;  // bf16 per LDS k-row of a [K][N] B
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
+}
+
+// WM x WN MFMA tiles per wave, WAVES_M x WAVES_N waves (4 in all).
+template <int WM, int WN, int WAVES_M, bool B_NK>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int BM = 32 * WM * WAVES_M;
+  static_assert(32 * WN * WAVES_N == GN, "a workgroup covers 128 columns");
+  constexpr int A_CHUNKS = BM * GK / 8;                   // 16-byte chunks of an A tile
+  constexpr int A_PER = (A_CHUNKS + 255) / 256;
+  constexpr int B_PER = GN * GK / 8 / 256;                // 2
+  constexpr int B_LDS = B_NK ? GN * APITCH : GK * KNPITCH;
+  __shared__ __align__(16) uint16_t As[2][BM * APITCH];
+  __shared__ __align__(16) uint16_t Bs[2][B_LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int half = lane >> 5, col = lane & 31;
+  const int64_t z = blockIdx.z;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int n0 = blockIdx.x * GN;
+  const uint16_t* A = g.A + z * g.sA;
+  const uint16_t* B = g.B + z * g.sB;
+  uint16_t* C = g.C + z * g.sC;
+
+  // Chunk c of an A tile: row c >> 2, k-chunk c & 3.  Of a [N][K] B tile: the
+  // same with n for the row.  Of a [K][N] B tile: k-row c >> 4, n-chunk c & 15.
+  typedef u32x4 Stage[A_PER + B_PER];
+  auto gload = [&](Stage& r, int k0) {
+#pragma unroll
+    for (int u = 0; u < A_PER; ++u) {
+      const int c = tid + 256 * u;
+      const int64_t m = m0 + (c >> 2);
+      r[u] = (c < A_CHUNKS && m < g.M) ? *reinterpret_cast<const u32x4*>(A + m * g.lda + k0 + 8 * (c & 3))
+                                       : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < B_PER; ++u) {
+      const int c = tid + 256 * u;
+      if (B_NK) {
+        const int n = n0 + (c >> 2);
+        r[A_PER + u] = n < g.N ? *reinterpret_cast<const u32x4*>(B + (int64_t)n * g.ldb + k0 + 8 * (c & 3))
+                               : u32x4{0, 0, 0, 0};
+      } else {
+        const int n = n0 + 8 * (c & 15);
+        r[A_PER + u] = n < g.N ? *reinterpret_cast<const u32x4*>(B + (int64_t)(k0 + (c >> 4)) * g.ldb + n)
+                               : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](const Stage& r, int buf) {
+#pragma unroll
+    for (int u = 0; u < A_PER; ++u) {
+      const int c = tid + 256 * u;
+      if (c < A_CHUNKS) *reinterpret_cast<u32x4*>(&As[buf][(c >> 2) * APITCH + 8 * (c & 3)]) = r[u];
+    }
+#pragma unroll
+    for (int u = 0; u < B_PER; ++u) {
+      const int c = tid + 256 * u;
+      if (B_NK)
+        *reinterpret_cast<u32x4*>(&Bs[buf][(c >> 2) * APITCH + 8 * (c & 3)]) = r[A_PER + u];
+      else
+        *reinterpret_cast<u32x4*>(&Bs[buf][(c >> 4) * KNPITCH + 8 * (c & 15)]) = r[A_PER + u];
+    }
+  };
+  // B operand of MFMA column block j (32 columns) at k-step ks.
+  const int g16 = lane >> 4, i16 = lane & 15;
+  auto bop = [&](int buf, int j, int ks) -> bf16x8 {
+    const int nb = 32 * (WN * wn + j);
+    if (B_NK) return *reinterpret_cast<const bf16x8*>(&Bs[buf][(nb + col) * APITCH + 16 * ks + 8 * half]);
+    // lane (group g16, c = i16 >> 2, r = i16 & 3) addresses k-row 8*(g16>>1) + c (+4 for the upper four)
+    // at columns nb + 16*(g16&1) + 4r .. +3
+    const uint16_t* p = &Bs[buf][(16 * ks + 8 * (g16 >> 1) + (i16 >> 2)) * KNPITCH + nb + 16 * (g16 & 1) +
+                                 4 * (i16 & 3)];
+    const s16x4 lo = lds_read_tr16(p);
+    const s16x4 hi = lds_read_tr16(p + 4 * KNPITCH);
+    return __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+  };
+
+  f32x16 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x16{};
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < GK / 16; ++ks) {
+      bf16x8 a[WM], b[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(32 * (WM * wm + i) + col) * APITCH + 16 * ks + 8 * half]);
+#pragma unroll
+      for (int j = 0; j < WN; ++j) b[j] = bop(buf, j, ks);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+    }
+  };
+
+  // Global loads run two tiles ahead: r0 and r1 alternate between tiles.
+  const int nt = g.K / GK;
+  Stage r0, r1;
+  gload(r0, 0);
+  if (nt > 1) gload(r1, GK);
+  lstore(r0, 0);
+  __syncthreads();
+  for (int it = 0; it < nt; it += 2) {
+    if (it + 2 < nt) gload(r0, (it + 2) * GK);
+    compute(0);
+    if (it + 1 < nt) lstore(r1, 1);
+    __syncthreads();
+    if (it + 1 >= nt) break;
+    if (it + 3 < nt) gload(r1, (it + 3) * GK);
+    compute(1);
+    if (it + 2 < nt) lstore(r0, 0);
+    __syncthreads();
+  }
+
+  // Epilogue: lanes 0..31 of a register hold 32 consecutive columns of one row.
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int n = n0 + 32 * (WN * wn + j) + col;
+    if (n >= g.N) continue;
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + 32 * (WM * wm + i) + mfma_row(e, half);
+        if (m < g.M) C[m * g.ldc + n] = (uint16_t)float_to_bf16_bits(acc[i][j][e]);
+      }
+  }
+
+  // Optional row copy riding on the first column block (the rope part of an
+  // absorbed query): cp_w bf16 per row, in 16-byte chunks.
+  if (g.cp_dst != nullptr && blockIdx.x == 0) {
+    const int chunks = g.cp_w / 8;
+    for (int c = tid; c < BM * chunks; c += 256) {
+      const int64_t m = m0 + c / chunks;
+      if (m >= g.M) break;
+      const int off = 8 * (c % chunks);
+      *reinterpret_cast<u32x4*>(g.cp_dst + z * g.cp_sd + m * g.cp_ldd + off) =
+          *reinterpret_cast<const u32x4*>(g.cp_src + z * g.cp_ss + m * g.cp_lds + off);
+    }
+  }
+}
+
+// Few rows (M <= 64), where the weights' bytes bound the time: a workgroup
+// owns a 32 x 32 tile of C over the whole of K, its WAVES waves take every
+// WAVES-th k-step of 16 each, and each wave keeps U k-steps of operand loads
+// in flight.  A and a [N][K] B go from global memory straight into the MFMA
+// operand registers (lane j: row or column j % 32, eight k from 8 * (j / 32)).
+// A [K][N] B is staged per wave through LDS ([16 k][32 n] per k-step) and read
+// back with the transposing read.  The WAVES partial tiles are summed in LDS
+// in a fixed order, so the result does not depend on timing.
+template <bool B_NK, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(GemmArgs g) {
+  constexpr int U = 4;            // k-steps per wave in flight
+  constexpr int KP = 48;          // bf16 per staging row (96 B: four rows fall on distinct banks)
+  constexpr int STAGE = B_NK ? 1 : WAVES * U * 16 * KP;
+  __shared__ __align__(16) uint16_t stage[STAGE];
+  __shared__ float red[WAVES][16][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int64_t z = blockIdx.z;
+  const int64_t m0 = (int64_t)blockIdx.y * 32;
+  const int n0 = blockIdx.x * 32;
+  const uint16_t* A = g.A + z * g.sA;
+  const uint16_t* B = g.B + z * g.sB;
+  uint16_t* C = g.C + z * g.sC;
+
+  const int64_t m = m0 + col;
+  const bool m_ok = m < g.M;
+  const uint16_t* a_ptr = A + (m_ok ? m : 0) * g.lda + 8 * half;
+  // [N][K]: column n0 + col, k from 8 * half.  [K][N]: k-row lane >> 2 of the
+  // step, columns n0 + 8 * (lane & 3) .. +7.
+  const int n_nk = n0 + col;
+  const int n_kn = n0 + 8 * (lane & 3);
+  const bool b_ok = B_NK ? n_nk < g.N : n_kn < g.N;
+  const uint16_t* b_ptr = B_NK ? B + (int64_t)(b_ok ? n_nk : 0) * g.ldb + 8 * half
+                               : B + (int64_t)(lane >> 2) * g.ldb + (b_ok ? n_kn : 0);
+  const int64_t b_step = B_NK ? 16 : 16 * g.ldb;
+
+  f32x16 acc{};
+  const int S = g.K / 16;
+  for (int s0 = wave; s0 < S; s0 += WAVES * U) {
+    u32x4 ra[U], rb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + WAVES * u;
+      if (s < S) {
+        ra[u] = m_ok ? *reinterpret_cast<const u32x4*>(a_ptr + 16 * s) : u32x4{0, 0, 0, 0};
+        rb[u] = b_ok ? *reinterpret_cast<const u32x4*>(b_ptr + b_step * s) : u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + WAVES * u;
+      if (s >= S) break;
+      bf16x8 bv;
+      if (B_NK) {
+        bv = __builtin_bit_cast(bf16x8, rb[u]);
+      } else {
+        uint16_t* st = &stage[(wave * U + u) * 16 * KP];
+        *reinterpret_cast<u32x4*>(&st[(lane >> 2) * KP + 8 * (lane & 3)]) = rb[u];
+        // the wave's own LDS writes are performed before its later reads
+        __builtin_amdgcn_wave_barrier();
+        const uint16_t* p = &st[(8 * (g16 >> 1) + (i16 >> 2)) * KP + 16 * (g16 & 1) + 4 * (i16 & 3)];
+        const s16x4 lo = lds_read_tr16(p);
+        const s16x4 hi = lds_read_tr16(p + 4 * KP);
+        bv = __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+      }
+      acc = mfma32x32x16(__builtin_bit_cast(bf16x8, ra[u]), bv, acc);
+    }
+  }
+
+#pragma unroll
+  for (int e = 0; e < 16; ++e) red[wave][e][lane] = acc[e];
+  __syncthreads();
+  constexpr int PER = 16 / WAVES;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int e = PER * wave + q;
+    float v = red[0][e][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) v += red[w][e][lane];
+    const int64_t mm = m0 + mfma_row(e, half);
+    const int nn = n0 + col;
+    if (mm < g.M && nn < g.N) C[mm * g.ldc + nn] = (uint16_t)float_to_bf16_bits(v);
+  }
+
+  if (g.cp_dst != nullptr && blockIdx.x == 0) {
+    const int chunks = g.cp_w / 8;
+    for (int c = tid; c < 32 * chunks; c += 64 * WAVES) {
+      const int64_t mr = m0 + c / chunks;
+      if (mr >= g.M) break;
+      const int off = 8 * (c % chunks);
+      *reinterpret_cast<u32x4*>(g.cp_dst + z * g.cp_sd + mr * g.cp_ldd + off) =
+          *reinterpret_cast<const u32x4*>(g.cp_src + z * g.cp_ss + mr * g.cp_lds + off);
+    }
+  }
+}
+
+template <int WM, int WN, int WAVES_M>
+hipError_t launch_tiles(const GemmArgs& g, bool b_nk, int64_t batch, hipStream_t stream) {
+  constexpr int BM = 32 * WM * WAVES_M;
+  const dim3 grid((unsigned)((g.N + GN - 1) / GN), (unsigned)((g.M + BM - 1) / BM), (unsigned)batch);
+  if (b_nk)
+    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, WAVES_M, true>), grid, dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, WAVES_M, false>), grid, dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, bool b_nk, int64_t batch, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
+  if (g.M <= 64) {
+    // 32 x 32 tiles over the whole of K; sixteen waves per workgroup when the
+    // grid alone would leave most compute units idle
+    const dim3 grid((unsigned)((g.N + 31) / 32), (unsigned)((g.M + 31) / 32), (unsigned)batch);
+    const bool few = (int64_t)grid.x * grid.y * grid.z < 256;
+    if (b_nk && few)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, 16>), grid, dim3(1024), 0, stream, g);
+    else if (b_nk)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, 4>), grid, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, 4>), grid, dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
+  return launch_tiles<2, 2, 2>(g, b_nk, batch, stream);                  // 128 x 128 tiles
+}
+
+}  // namespace dsa

@@ -59,7 +59,7 @@ import numpy as np
 __all__ = [
     "as_f64", "bf16_bits_to_f64", "n_valid_keys", "index_scores", "index_scores_rows",
     "topk_row", "topk", "sparse_mla", "sparse_mla_rows", "dense_masked_mla", "forward_rows",
-    "mla_naive_rows", "mla_absorb_query", "mla_output_projection", "sylvester_hadamard",
+    "mla_naive_rows", "mla_absorb_query", "mla_output_projection", "linear", "sylvester_hadamard",
 ]
 
 
@@ -293,6 +293,14 @@ def mla_absorb_query(q_head: np.ndarray, W_UK: np.ndarray) -> np.ndarray:
 def mla_output_projection(o_lat: np.ndarray, W_UV: np.ndarray) -> np.ndarray:
     """Apply the value up-projection to the latent output: [..., H, d_c] -> [..., H, d_v], o[h] = W_UV[h] o_lat[h]."""
     return np.einsum("...hc,hvc->...hv", as_f64(o_lat), as_f64(W_UV))
+
+
+def linear(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """A linear layer without bias, y = x W^T with W [N, K] (out, in): the
+    indexer's query projection wq_b from the low-rank query latent (DeepSeek-V3.2
+    documentation, "DeepSeek Sparse Attention (DSA)", note on the query LoRA
+    path) and its per-head weight projection."""
+    return as_f64(x) @ as_f64(W).T
 
 
 # ----------------------------------------------------------------------------

@@ -400,3 +400,19 @@ def pin_mla_absorbed_equals_naive(mla_absorb_query, sparse_mla_rows, mla_output_
             if not np.allclose(lse, ln, atol=1e-12) and not (np.all(np.isneginf(lse)) and np.all(np.isneginf(ln))):
                 return False
     return True
+
+
+def pin_linear(linear) -> bool:
+    """y = x W^T with W [out, in]: the identity weight returns x, a one-hot input
+    row picks the matching column of W, and a one-hot weight row picks one input
+    feature (fixes the orientation of W)."""
+    r = _rng(44)
+    x = r.standard_normal((3, 5))
+    W = r.standard_normal((4, 5))
+    e = np.zeros((1, 5))
+    e[0, 2] = 1.0
+    sel = np.zeros((1, 5))
+    sel[0, 4] = 1.0
+    y = _safe(linear, x, W)
+    return (y is not None and y.shape == (3, 4) and np.array_equal(linear(x, np.eye(5)), x)
+            and np.array_equal(linear(e, W)[0], W[:, 2]) and np.array_equal(linear(x, sel)[:, 0], x[:, 4]))

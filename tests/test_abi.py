@@ -152,3 +152,27 @@ def test_compressed_validation():
     assert "compression rate" in last()
     assert L.dsa_topk_compressed(P, P, 2, 1, 100, 64, 4, 0, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_topk_compressed(P, None, 2, 1, 100, 64, 4, 16, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_projection_validation():
+    L = lib()
+    # absorption: bf16 only, aligned pointers, d_nope a multiple of 32, d_c and d_rope multiples of 8
+    assert L.dsa_mla_absorb_q(P, P, P, 4, 128, 128, 64, 512, dsa.DSA_F32, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_mla_absorb_q(None, P, P, 4, 128, 128, 64, 512, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_mla_absorb_q(P + 2, P, P, 4, 128, 128, 64, 512, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_mla_absorb_q(P, P, P, -1, 128, 128, 64, 512, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_mla_absorb_q(P, P, P, 4, 0, 128, 64, 512, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_mla_absorb_q(P, P, P, 4, 128, 100, 64, 512, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_mla_absorb_q(P, P, P, 4, 128, 128, 60, 512, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_mla_absorb_q(P, P, P, 4, 128, 128, 64, 500, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_mla_absorb_q(P, P, P, 65535 * 64 + 1, 128, 128, 64, 512, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    # output projection: d_c a multiple of 32
+    assert L.dsa_mla_out_proj(P, P, P, 4, 128, 500, 128, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_mla_out_proj(P, P, P, 4, 128, 512, 0, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_mla_out_proj(P, None, P, 4, 128, 512, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    # linear: K a multiple of 32
+    assert L.dsa_linear(P, P, P, 4, 64, 100, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_linear(P, P, P, 4, 0, 1536, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_linear(P, P, None, 4, 64, 1536, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    # nothing to do is not an error
+    assert L.dsa_linear(P, P, P, 0, 64, 1536, BF16, None) == dsa.DSA_OK

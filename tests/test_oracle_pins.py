@@ -297,3 +297,13 @@ def test_absorbed_pin_catches_value_from_rope():
         return oracle.sparse_mla_rows(q, kv[:, ::-1], idx, scale, DV)
     assert not pins.pin_mla_absorbed_equals_naive(oracle.mla_absorb_query, mla_rows_mut,
                                                   oracle.mla_output_projection, oracle.mla_naive_rows)
+
+
+def test_linear():
+    assert pins.pin_linear(oracle.linear)
+
+
+@pytest.mark.parametrize("mutant", [lambda x, W: np.asarray(x) @ np.asarray(W),
+                                    lambda x, W: np.asarray(x)[:, ::-1] @ np.asarray(W).T])
+def test_linear_pin_catches_planted_mistakes(mutant):
+    assert not pins.pin_linear(mutant)
