@@ -54,12 +54,15 @@ uint16 bit patterns and are widened exactly by ``as_f64``.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
     "as_f64", "bf16_bits_to_f64", "n_valid_keys", "index_scores", "index_scores_rows",
     "topk_row", "topk", "sparse_mla", "sparse_mla_rows", "dense_masked_mla", "forward_rows",
-    "mla_naive_rows", "mla_absorb_query", "mla_output_projection", "linear", "sylvester_hadamard",
+    "mla_naive_rows", "mla_absorb_query", "mla_output_projection", "linear", "fwht_f32", "e4m3_decode",
+    "e4m3_encode_rne", "pow2_scale_exp", "quantize_fp8_rows", "index_scores_fp8_rows", "sylvester_hadamard",
 ]
 
 
@@ -327,6 +330,113 @@ def forward_rows(q_idx_b, k_idx_b, w_b, q_b, kv_b, ts, q_pos0: int, K: int, scal
         o, lse = sparse_mla_rows(q_b[t], rows, idx, scale, DV)
         res.append({"t": int(t), "scores": s, "idx": idx, "o": o, "lse": lse})
     return res
+
+
+# ----------------------------------------------------------------------------
+# FP8 indexer: Hadamard rotation, e4m3 rows with power-of-two scales, scores
+# ----------------------------------------------------------------------------
+#
+# DeepSeek-V3.2 documentation, "DeepSeek Sparse Attention (DSA)": the
+# reference implementation runs the indexer in FP8 after a Hadamard rotation
+# of queries and keys; the rotation is orthogonal (Hq . Hk = q . k) and FP8 is
+# only a precision optimisation.  Readings (the pages give no format details):
+#   * FP8 is OCP E4M3 (bias 7, largest finite 448, no infinities);
+#   * the rotation is the unnormalised Sylvester matrix H (entries +-1, so
+#     H H^T = D I), applied by the fast Walsh-Hadamard transform in float32
+#     with pair distance 1, 2, 4, ... (a + b on the lower, a - b on the upper
+#     element); the factor D is taken out of the score;
+#   * each rotated row of D values (one key, or one head of one query) has
+#     one scale 2^e, the smallest power of two with max|y| <= 448 * 2^e
+#     (e = 0 for an all-zero row), and codes e4m3_rne(y / 2^e);
+#   * the score is I[t,s] = sum_h w[t,h] * max(0, qs[t,h] * ks[s] / D *
+#     sum_d dec(q8[t,h,d]) * dec(k8[s,d])), which is the bf16 score when
+#     quantisation is exact.
+
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform of the last axis (a power of two), in float32."""
+    y = np.array(x, dtype=np.float32)
+    n = y.shape[-1]
+    d = 1
+    while d < n:
+        blocks = y.reshape(y.shape[:-1] + (n // (2 * d), 2, d))
+        a, b = blocks[..., 0, :], blocks[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2).reshape(y.shape)
+        d *= 2
+    return y
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3 codes -> float64 (S.EEEE.MMM, bias 7, subnormals M * 2^-9, S.1111.111 is NaN)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    E = (c >> 3) & 15
+    M = (c & 7).astype(np.float64)
+    mag = np.where(E == 0, M * 2.0 ** -9, (1.0 + M / 8.0) * np.exp2(E - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode_rne(v: np.ndarray) -> np.ndarray:
+    """float32 values with |v| <= 448 -> OCP E4M3 codes, rounded to nearest, ties to even."""
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)   # exact widening
+    if np.any(np.abs(v) > 448.0) or np.any(np.isnan(v)):
+        raise ValueError("e4m3_encode_rne: |v| must be <= 448")
+    a = np.abs(v)
+    out = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal range: a multiple of 2^-9 (a code of 8 is the smallest normal, 0x08)
+    out[sub] = np.rint(a[sub] * 512.0).astype(np.int64)
+    nrm = ~sub
+    if np.any(nrm):
+        e = np.floor(np.log2(a[nrm])).astype(np.int64)
+        # log2 of a float can land one off at exact powers of two: fix up
+        e = np.where(np.exp2(e.astype(np.float64)) > a[nrm], e - 1, e)
+        e = np.where(np.exp2((e + 1).astype(np.float64)) <= a[nrm], e + 1, e)
+        q = np.rint((a[nrm] / np.exp2(e.astype(np.float64)) - 1.0) * 8.0).astype(np.int64)
+        e = np.where(q == 8, e + 1, e)
+        q = np.where(q == 8, 0, q)
+        out[nrm] = ((e + 7) << 3) | q
+    out = np.where(np.signbit(v), out | 0x80, out)
+    return out.astype(np.uint8)
+
+
+def pow2_scale_exp(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e (0 for amax == 0)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    m, E = math.frexp(amax)          # amax = m * 2^E, 0.5 <= m < 1; 448 = 0.875 * 2^9
+    return E - 9 if m <= 0.875 else E - 8
+
+
+def quantize_fp8_rows(x: np.ndarray):
+    """Rows of the last axis -> (codes uint8 [..., D], scales float32 [...]): rotate, scale, round."""
+    y = fwht_f32(as_f64(x).astype(np.float32))
+    amax = np.max(np.abs(y), axis=-1)
+    flat_e = np.array([pow2_scale_exp(a) for a in amax.reshape(-1)], dtype=np.int64)
+    e = flat_e.reshape(amax.shape)
+    v = (y.astype(np.float64) * np.exp2(-e.astype(np.float64))[..., None]).astype(np.float32)  # exact
+    return e4m3_encode_rne(v), np.exp2(e.astype(np.float64)).astype(np.float32)
+
+
+def index_scores_fp8_rows(q8_b, qs_b, k8_b, ks_b, w_b, ts, q_pos0: int) -> list:
+    """FP8 index scores of queries `ts` of one sequence (float64 from the codes).
+
+    q8_b [Tq, H_I, D] codes, qs_b [Tq, H_I] scales, k8_b [N, D] codes, ks_b [N]
+    scales, w_b [Tq, H_I] head weights.  Query t sees keys s < n_valid_keys(t).
+    """
+    k = e4m3_decode(k8_b)
+    ks = np.asarray(ks_b, dtype=np.float64)
+    N, D = k.shape
+    out = []
+    for t in ts:
+        n = n_valid_keys(int(t), q_pos0, N)
+        q = e4m3_decode(q8_b[t])                                   # [H_I, D]
+        qs = np.asarray(qs_b[t], dtype=np.float64)
+        w = as_f64(w_b[t])
+        dots = (k[:n] @ q.T) * ks[:n, None] * qs[None, :] / D      # [n, H_I]
+        out.append(np.maximum(dots, 0.0) @ w)
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -416,3 +416,105 @@ def pin_linear(linear) -> bool:
     y = _safe(linear, x, W)
     return (y is not None and y.shape == (3, 4) and np.array_equal(linear(x, np.eye(5)), x)
             and np.array_equal(linear(e, W)[0], W[:, 2]) and np.array_equal(linear(x, sel)[:, 0], x[:, 4]))
+
+
+# ------------------------------------------------------------- FP8 indexer ---
+
+def pin_e4m3(e4m3_decode, e4m3_encode_rne) -> bool:
+    """The E4M3 table facts and rounding midpoints of tests/golden/e4m3_codes.json,
+    the round trip of every finite code, and monotone encoding."""
+    g = load_golden("e4m3_codes.json")
+    for c in g["decode"]:
+        v = _safe(e4m3_decode, np.array([int(c["code"], 16)], dtype=np.uint8))
+        if v is None or v[0] != c["value"]:
+            return False
+    if not all(np.isnan(e4m3_decode(np.array([int(c, 16)], dtype=np.uint8))[0]) for c in g["nan_codes"]):
+        return False
+    for c in g["encode_rne"]:
+        got = _safe(e4m3_encode_rne, np.array([c["value"]], dtype=np.float32))
+        if got is None or int(got[0]) != int(c["code"], 16):
+            return False
+    codes = np.arange(256, dtype=np.uint8)
+    vals = e4m3_decode(codes)
+    fin = ~np.isnan(vals)
+    if not np.array_equal(e4m3_encode_rne(vals[fin].astype(np.float32)), codes[fin]):
+        return False
+    sweep = np.linspace(-448.0, 448.0, 20001).astype(np.float32)
+    dec = e4m3_decode(e4m3_encode_rne(sweep))
+    return bool(np.all(np.diff(dec) >= 0))
+
+
+def pin_fwht(fwht_f32, hadamard) -> bool:
+    """The transform is the Sylvester matrix product (exact on integer rows), and
+    applying it twice multiplies by the length."""
+    r = _rng(51)
+    x = r.integers(-4, 5, size=(6, 128)).astype(np.float32)
+    y = _safe(fwht_f32, x)
+    if y is None:
+        return False
+    H = hadamard(128)
+    return np.array_equal(y.astype(np.float64), x.astype(np.float64) @ H.T) and \
+        np.array_equal(fwht_f32(y).astype(np.float64), 128.0 * x)
+
+
+def pin_pow2_scale(pow2_scale_exp) -> bool:
+    """e is the smallest integer with amax <= 448 * 2^e."""
+    cases = [448.0, 448.0001, 224.0, 224.0001, 1.0, 3.5, 1e-3, 7e5, 2.0 ** -40]
+    for a in cases:
+        e = _safe(pow2_scale_exp, a)
+        if e is None or not (a <= 448.0 * 2.0 ** e and a > 448.0 * 2.0 ** (e - 1)):
+            return False
+    return pow2_scale_exp(448.0) == 0 and pow2_scale_exp(224.0) == -1 and pow2_scale_exp(0.0) == 0
+
+
+def pin_quantize_fp8(quantize_fp8_rows, fwht_f32, e4m3_decode) -> bool:
+    """Dequantised rows equal the rotated rows within the e4m3 rounding bound
+    (2^-4 relative in the normal range, half of 2^-9 * scale below it), and each
+    row's largest value lands in [224, 448] after scaling."""
+    r = _rng(52)
+    x = np.concatenate([r.integers(-4, 5, size=(20, 128)).astype(np.float32),
+                        r.standard_normal((20, 128)).astype(np.float32),
+                        np.zeros((1, 128), dtype=np.float32)])
+    out = _safe(quantize_fp8_rows, x)
+    if out is None:
+        return False
+    codes, scales = out
+    y = fwht_f32(x).astype(np.float64)
+    deq = e4m3_decode(codes) * scales[:, None].astype(np.float64)
+    v = np.abs(y) / scales[:, None]
+    bound = np.where(v >= 2.0 ** -6, 2.0 ** -4 * np.abs(y), 2.0 ** -10 * scales[:, None])
+    if not np.all(np.abs(deq - y) <= bound):
+        return False
+    top = np.max(np.abs(e4m3_decode(codes[:-1])), axis=-1)
+    return bool(np.all((top >= 224.0) & (top <= 448.0)) and not np.any(codes[-1] & 0x7F))
+
+
+def pin_fp8_scores_near_bf16(quantize_fp8_rows, index_scores_fp8_rows, index_scores_rows, fwht_f32,
+                             e4m3_decode) -> bool:
+    """Through the orthogonality H^T H = D I, the FP8 score equals the bf16 score
+    up to the quantisation error of the rotated rows:
+        |I_fp8 - I| <= sum_h |w_h| / D * sum_d (|dq||yk| + |yq||dk| + |dq||dk|)."""
+    r = _rng(53)
+    T, HI, D, N = 4, 3, 128, 40
+    q = r.integers(-4, 5, size=(T, HI, D)).astype(np.float32)
+    k = r.integers(-4, 5, size=(N, D)).astype(np.float32)
+    w = r.choice([0.25, 0.5, 1.0, 2.0], size=(T, HI))
+    q8, qs = quantize_fp8_rows(q)
+    k8, ks = quantize_fp8_rows(k)
+    got = _safe(index_scores_fp8_rows, q8, qs, k8, ks, w, range(T), 20)
+    if got is None:
+        return False
+    ref = index_scores_rows(q, k, w, range(T), 20)
+    yq, yk = fwht_f32(q).astype(np.float64), fwht_f32(k).astype(np.float64)
+    dq = e4m3_decode(q8) * qs[..., None] - yq
+    dk = e4m3_decode(k8) * ks[..., None] - yk
+    for t in range(T):
+        n = len(ref[t])
+        if len(got[t]) != n:
+            return False
+        per_head = (np.abs(dq[t]) @ np.abs(yk[:n]).T + np.abs(yq[t]) @ np.abs(dk[:n]).T
+                    + np.abs(dq[t]) @ np.abs(dk[:n]).T) / D                  # [H_I, n]
+        bound = np.abs(w[t]) @ per_head
+        if not np.all(np.abs(got[t] - ref[t]) <= bound + 1e-9):
+            return False
+    return True

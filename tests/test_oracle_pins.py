@@ -307,3 +307,62 @@ def test_linear():
                                     lambda x, W: np.asarray(x)[:, ::-1] @ np.asarray(W).T])
 def test_linear_pin_catches_planted_mistakes(mutant):
     assert not pins.pin_linear(mutant)
+
+
+def test_e4m3():
+    assert pins.pin_e4m3(oracle.e4m3_decode, oracle.e4m3_encode_rne)
+
+
+def test_fwht():
+    assert pins.pin_fwht(oracle.fwht_f32, oracle.sylvester_hadamard)
+
+
+def test_pow2_scale():
+    assert pins.pin_pow2_scale(oracle.pow2_scale_exp)
+
+
+def test_quantize_fp8():
+    assert pins.pin_quantize_fp8(oracle.quantize_fp8_rows, oracle.fwht_f32, oracle.e4m3_decode)
+
+
+def test_fp8_scores_near_bf16():
+    assert pins.pin_fp8_scores_near_bf16(oracle.quantize_fp8_rows, oracle.index_scores_fp8_rows,
+                                         oracle.index_scores_rows, oracle.fwht_f32, oracle.e4m3_decode)
+
+
+def _mut_e4m3_fnuz(codes):
+    """bias 8 instead of 7"""
+    return oracle.e4m3_decode(codes) / 2.0
+
+
+def _mut_e4m3_truncate(v):
+    v = np.asarray(v, dtype=np.float32)
+    d = oracle.e4m3_decode(oracle.e4m3_encode_rne(v))
+    over = np.abs(d) > np.abs(v.astype(np.float64))
+    out = oracle.e4m3_encode_rne(v).astype(np.int64)
+    return np.where(over, out - 1, out).astype(np.uint8)
+
+
+def test_e4m3_pin_catches_planted_mistakes():
+    assert not pins.pin_e4m3(_mut_e4m3_fnuz, oracle.e4m3_encode_rne)
+    assert not pins.pin_e4m3(oracle.e4m3_decode, _mut_e4m3_truncate)
+
+
+def test_fwht_pin_catches_planted_mistake():
+    assert not pins.pin_fwht(lambda x: oracle.fwht_f32(x)[..., ::-1], oracle.sylvester_hadamard)
+
+
+def test_pow2_pin_catches_planted_mistake():
+    assert not pins.pin_pow2_scale(lambda a: oracle.pow2_scale_exp(a) + 1)
+
+
+def test_fp8_score_pin_catches_planted_mistakes():
+    def no_div(q8, qs, k8, ks, w, ts, p0):
+        return [r * 128.0 for r in oracle.index_scores_fp8_rows(q8, qs, k8, ks, w, ts, p0)]
+
+    def no_key_scale(q8, qs, k8, ks, w, ts, p0):
+        return oracle.index_scores_fp8_rows(q8, qs, k8, np.ones_like(ks), w, ts, p0)
+
+    for mut in (no_div, no_key_scale):
+        assert not pins.pin_fp8_scores_near_bf16(oracle.quantize_fp8_rows, mut, oracle.index_scores_rows,
+                                                 oracle.fwht_f32, oracle.e4m3_decode)
