@@ -11,7 +11,7 @@ resident in HBM), the roofline position of the dominant kernel measured with
 HIP events on the launch stream, and the CPU oracle timed on a bounded sample
 of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--fp8-indexer]
   python bench.py --calib-copy     (plain 1 GiB device copy, for counter scaling)
   python bench.py --record-traffic --workload NAME --pmc-fetch F.csv --pmc-write W.csv
                   --calib-fetch CF.csv --calib-write CW.csv --commands "..."
@@ -46,6 +46,9 @@ def _parse():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--fused", action="store_true",
                     help="time the single dsa_forward call (no per-stage events)")
+    ap.add_argument("--fp8-indexer", action="store_true",
+                    help="decode workloads: the FP8 indexer (key cache held as E4M3 codes; each step quantises "
+                         "its queries, then scores)")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--record-traffic", action="store_true",
                     help="store the dominant kernel's HBM traffic from four rocprofv3 -f csv counter files")
@@ -62,6 +65,7 @@ def _parse():
 KERNEL_SOURCES = {
     "indexer_dma_bf16": ["indexer.hip", "device_common.h"],
     "indexer_tiled_bf16": ["indexer.hip", "device_common.h"],
+    "indexer_dma_fp8": ["indexer.hip", "device_common.h"],
     "sparse_mla_bf16_kernel": ["sparse_mla.hip", "device_common.h"],
 }
 
@@ -119,7 +123,7 @@ def record_traffic(args):
     traffic of the dominant kernel."""
     import synth
     wl = synth.WORKLOADS[args.workload]
-    _, kname, _, work, wunit = dominant_stage(wl)
+    _, kname, _, work, wunit = dominant_stage(wl, args.fp8_indexer)
     calib_bytes = 1 << 30
 
     def per_dispatch(csv_path, counter, name_part):
@@ -155,12 +159,17 @@ def record_traffic(args):
     print(json.dumps(rec))
 
 
-def dominant_stage(wl):
+def dominant_stage(wl, fp8=False):
     """Stage that bounds the workload, its roofline and its algorithmic work per launch."""
     B, Tq, N, q0, K = wl.B, wl.Tq, wl.N, wl.q_pos0, wl.K
     vis = [min(N, q0 + t + 1) for t in range(Tq)]
     keys = B * sum(vis)                                  # (query, visible key) pairs
     sel = B * sum(min(v, K) for v in vis)                # (query, selected key) pairs
+    if fp8:
+        # FP8 decode indexer: each key's 128 code bytes and 4-byte scale read once, its fp32 score
+        # written once, plus the query codes, scales and head weights
+        nbytes = B * N * (wl.D_I + 4) + keys * 4 + B * Tq * wl.H_I * (wl.D_I + 4 + 2)
+        return "index", "indexer_dma_fp8", "hbm", nbytes, "B"
     if "mla" in wl.stages and Tq > 4:
         # prefill: the sparse MLA (K selected rows x 128 heads x 1088 MACs each) dominates
         flops = 2 * wl.H * (wl.D + wl.DV) * sel
@@ -222,6 +231,40 @@ def cpu_baseline(wl, x, budget_s: float):
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {len(rows)} queries of {wl.name} (whole path per query), {el:.1f} s"}
+
+
+def cpu_baseline_fp8(wl, x, budget_s: float, max_seqs: int = 4):
+    """The oracle's FP8 path on whole decode queries: the sequence's key cache is quantised
+    first (untimed: the cache is held as codes), then the query is quantised, scored,
+    selected and attended (timed)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    done, timed = 0, 0.0
+    for b in rng.permutation(wl.B)[:max_seqs]:
+        k8, ks = oracle.quantize_fp8_rows(x["k_idx"][b])
+        for t in range(wl.Tq):
+            t0 = time.perf_counter()
+            q8, qs = oracle.quantize_fp8_rows(x["q_idx"][b, t])
+            sc = oracle.index_scores_fp8_rows(q8[None], qs[None], k8, ks, x["w"][b, t][None], [0], wl.q_pos0 + t)[0]
+            idx = oracle.topk_row(sc.astype(np.float32), wl.K)
+            sel = idx[idx >= 0]
+            rows = {int(j): r for j, r in zip(sel, x["kv"][b][sel])}
+            oracle.sparse_mla_rows(x["q"][b, t], rows, idx, wl.scale, wl.DV)
+            timed += time.perf_counter() - t0
+            done += 1
+        if timed > budget_s:
+            break
+    return {"value": done / timed, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {wl.B * wl.Tq} queries of {wl.name} with the FP8 indexer (whole path per query; "
+                      f"each sequence's key cache quantised beforehand, untimed), {timed:.1f} s"}
 
 
 def main():
@@ -292,6 +335,30 @@ def main():
                                             ptr(out), ptr(lse), None, B, Tq, N, wl.q_pos0, wl.H_I, wl.D_I, wl.H,
                                             wl.D, wl.DV, wl.K, wl.scale, code, ptr(fwd_ws), fwd_ws.numel(), sp))
 
+    fp8 = args.fp8_indexer
+    if fp8:
+        if not (has_idx and Tq <= 4 and dtt == torch.bfloat16):
+            raise SystemExit("--fp8-indexer applies to bf16 decode workloads with an indexer stage")
+        # the key cache is held as codes: quantised once, before timing (appended tokens are quantised as
+        # they arrive); each step quantises its own queries
+        k8 = torch.empty((B, N, wl.D_I), dtype=torch.uint8, device="cuda")
+        ks = torch.empty((B, N), dtype=torch.float32, device="cuda")
+        q8 = torch.empty((B, Tq, wl.H_I, wl.D_I), dtype=torch.uint8, device="cuda")
+        qs = torch.empty((B, Tq, wl.H_I), dtype=torch.float32, device="cuda")
+        rc = lib.dsa_indexer_quantize_fp8(ptr(d["k_idx"]), ptr(k8), ptr(ks), B * N, wl.D_I, code, sp)
+        if rc != 0:
+            raise RuntimeError(lib.dsa_last_error().decode())
+        del d["k_idx"]
+        calls["quant_q"] = (lib.dsa_indexer_quantize_fp8, (ptr(d["q_idx"]), ptr(q8), ptr(qs), B * Tq * wl.H_I,
+                                                           wl.D_I, code, sp))
+        calls["index"] = (lib.dsa_index_scores_fp8, (ptr(q8), ptr(qs), ptr(k8), ptr(ks), ptr(d["w"]), ptr(scores),
+                                                     B, Tq, N, wl.q_pos0, wl.H_I, wl.D_I, code, sp))
+        if has_mla:
+            calls["fused"] = (lib.dsa_forward_fp8, (ptr(q8), ptr(qs), ptr(k8), ptr(ks), ptr(d["w"]), ptr(d["q"]),
+                                                    ptr(d["kv"]), ptr(out), ptr(lse), None, B, Tq, N, wl.q_pos0,
+                                                    wl.H_I, wl.D_I, wl.H, wl.D, wl.DV, wl.K, wl.scale, code,
+                                                    ptr(fwd_ws), fwd_ws.numel(), sp))
+
     def run(name):
         fn, a = calls[name]
         rc = fn(*a)
@@ -299,6 +366,10 @@ def main():
             raise RuntimeError(f"{name}: {lib.dsa_last_error().decode()}")
 
     def step(evs=None):
+        if fp8:
+            if evs is not None:
+                evs[4].record(stream)
+            run("quant_q")
         if evs is not None:
             evs[0].record(stream)
         if has_idx:
@@ -314,6 +385,8 @@ def main():
             evs[3].record(stream)
 
     def fused_step():
+        if fp8:
+            run("quant_q")
         run("fused")
 
     use_fused = args.fused and has_idx and has_mla
@@ -321,7 +394,7 @@ def main():
         fused_step() if use_fused else step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -339,10 +412,12 @@ def main():
             if (name != "mla" and not has_idx) or (name == "mla" and not has_mla):
                 continue
             stage_ms[name] = float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+        if fp8:
+            stage_ms["quantize_q"] = float(np.mean([e[4].elapsed_time(e[0]) for e in events]))
 
     queries = B * Tq
     value = queries / (ms_per_step / 1e3)
-    stage, kname, bound, work, wunit = dominant_stage(wl)
+    stage, kname, bound, work, wunit = dominant_stage(wl, fp8)
     roof = None
     if stage in stage_ms:
         sec = stage_ms[stage] / 1e3
@@ -370,11 +445,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dtt == torch.bfloat16 else "f32",
+        "dtype": ("bf16 (indexer: fp8-e4m3 codes widened to bf16)" if fp8 else "bf16") if dtt == torch.bfloat16
+        else "f32",
         "data": "synthetic (seeded generator; integer-valued indexer inputs, N(0,1) latents)",
         "config": {"workload": wl.name, "batch": B, "queries_per_seq": Tq, "context": N, "index_topk": wl.K,
                    "indexer_heads": wl.H_I, "indexer_dim": wl.D_I, "mla_heads": wl.H, "latent_dim": wl.D,
                    "value_dim": wl.DV, "timed": "fused dsa_forward" if use_fused else "staged C-ABI calls",
+                   "indexer": "fp8 (Hadamard-rotated E4M3 key cache, power-of-two row scales)" if fp8 else "bf16",
                    "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "tokens_per_s": round(value, 1),
@@ -382,7 +459,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_budget_s)
+        res["cpu_baseline"] = cpu_baseline_fp8(wl, x, args.cpu_budget_s) if fp8 else \
+            cpu_baseline(wl, x, args.cpu_budget_s)
     print(json.dumps(res), flush=True)
 
 

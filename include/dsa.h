@@ -287,6 +287,50 @@ dsa_status dsa_mla_out_proj(const void* o_lat, const void* w_uv, void* o, int64_
 dsa_status dsa_linear(const void* x, const void* w, void* y, int64_t M, int32_t N, int32_t K, int32_t dtype,
                       void* stream);
 
+/*
+ * FP8 indexer.
+ * (DeepSeek-V3.2 documentation, "DeepSeek Sparse Attention (DSA)": the
+ *  reference implementation runs the lightning indexer in FP8 after a
+ *  Hadamard rotation of queries and keys; the rotation is orthogonal,
+ *  Hq . Hk = q . k, and FP8 is a precision optimisation only.)
+ * Format (the pages give none; readings of this library): OCP E4M3 codes
+ * (bias 7, largest finite 448), rows of D = 128 rotated by the unnormalised
+ * Sylvester Hadamard matrix (entries +-1, H H^T = 128 I; fast Walsh-Hadamard
+ * transform in float32, pair distance 1, 2, 4, ...), one power-of-two scale
+ * per row: scale = 2^e, the smallest with max|Hx| <= 448 * 2^e (1 for an
+ * all-zero row), codes = E4M3 round-to-nearest-even of Hx / scale.
+ *
+ * dsa_indexer_quantize_fp8: x bf16 [R, D] -> codes uint8 [R, D], scales
+ *   float [R].  Used for the indexer key cache (R = B*N rows, or the rows
+ *   being appended) and for the indexer queries (R = B*Tq*H_I rows).
+ *   dtype must be DSA_BF16 and D = 128.
+ *
+ * dsa_index_scores_fp8: scores [B, Tq, N] float32 =
+ *   ks[b,s] * sum_h (w[b,t,h] * qs[b,t,h] / 128) * max(0, sum_d q8[b,t,h,d] k8[b,s,d])
+ *   (codes read as their E4M3 values), for s < min(N, q_pos0 + t + 1); other
+ *   entries are not written.  q8 [B, Tq, H_I, D_I], q_scale [B, Tq, H_I],
+ *   k8 [B, N, D_I], k_scale [B, N], w bf16 [B, Tq, H_I] (dtype DSA_BF16);
+ *   compiled for H_I = 64, D_I = 128.  The key cache is streamed once per
+ *   query (the decode shape); prefill works but re-reads the cache per query.
+ *
+ * dsa_forward_fp8: dsa_forward with the FP8 indexer in place of the bf16 one
+ *   (same outputs, workspace size from dsa_forward_workspace_size).
+ *
+ * All pointers: device memory, 16-byte aligned, owned by the caller.  Errors
+ * as for dsa_index_scores / dsa_forward; fp32 head weights or other shapes
+ * return DSA_ERR_UNSUPPORTED.
+ */
+dsa_status dsa_indexer_quantize_fp8(const void* x, uint8_t* codes, float* scales, int64_t R, int32_t D,
+                                    int32_t dtype, void* stream);
+dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                                const void* w, float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                                int32_t H_I, int32_t D_I, int32_t dtype, void* stream);
+dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                           const void* w, const void* q, const void* kv, void* out, float* lse, int32_t* idx_out,
+                           int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t H,
+                           int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype, void* workspace,
+                           size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

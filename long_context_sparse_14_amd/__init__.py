@@ -21,6 +21,9 @@ Functions mirror the C entry points:
   mla_absorb_q(q, w_uk)                                   -> q_lat [..., H, d_c + d_rope] (query absorption)
   mla_out_proj(o_lat, w_uv)                               -> o [..., H, d_v] (value up-projection)
   linear(x, w)                                            -> x w^T (indexer projections)
+  indexer_quantize_fp8(x)                                 -> (codes uint8 [..., 128], scales float32 [...])
+  index_scores_fp8(q8, q_scale, k8, k_scale, w, q_pos0=0) -> scores [B,Tq,N] float32
+  forward_fp8(q8, q_scale, k8, k_scale, w, q, kv, K, scale, q_pos0=0, DV=512, return_idx=False)
 """
 from __future__ import annotations
 
@@ -77,6 +80,10 @@ _SIGNATURES = {
     "dsa_mla_absorb_q": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _p]),
     "dsa_mla_out_proj": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p]),
     "dsa_linear": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _p]),
+    "dsa_indexer_quantize_fp8": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _p]),
+    "dsa_index_scores_fp8": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
+    "dsa_forward_fp8": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32,
+                                       _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
 }
 
 
@@ -433,3 +440,67 @@ def linear(x, w, y=None, stream=None) -> torch.Tensor:
         raise ValueError("y must be [..., N]")
     _check(library().dsa_linear(px, pw, py, M, N, K, _dtype_code(x), _stream(stream)))
     return y
+
+
+def indexer_quantize_fp8(x, codes=None, scales=None, stream=None):
+    """bf16 rows [..., 128] -> (Hadamard-rotated E4M3 codes uint8 [..., 128], power-of-two scales float32 [...])."""
+    D = x.shape[-1]
+    R = x.numel() // D
+    px = _dev(x, "x", x.dim(), torch.bfloat16)
+    if codes is None:
+        codes = torch.empty(tuple(x.shape), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(tuple(x.shape[:-1]), dtype=torch.float32, device=x.device)
+    pc = _dev(codes, "codes", x.dim(), torch.uint8)
+    ps = _dev(scales, "scales", x.dim() - 1, torch.float32)
+    if tuple(codes.shape) != tuple(x.shape) or tuple(scales.shape) != tuple(x.shape[:-1]):
+        raise ValueError("codes must be shaped like x and scales like x without its last axis")
+    _check(library().dsa_indexer_quantize_fp8(px, pc, ps, R, D, DSA_BF16, _stream(stream)))
+    return codes, scales
+
+
+def _fp8_indexer_args(q8, q_scale, k8, k_scale, w):
+    B, Tq, H_I, D_I = q8.shape
+    N = k8.shape[1]
+    ptrs = (_dev(q8, "q8", 4, torch.uint8), _dev(q_scale, "q_scale", 3, torch.float32),
+            _dev(k8, "k8", 3, torch.uint8), _dev(k_scale, "k_scale", 2, torch.float32),
+            _dev(w, "w", 3, torch.bfloat16))
+    if (tuple(q_scale.shape) != (B, Tq, H_I) or tuple(k8.shape) != (B, N, D_I) or tuple(k_scale.shape) != (B, N)
+            or tuple(w.shape) != (B, Tq, H_I)):
+        raise ValueError("expected q8 [B,Tq,H_I,D_I], q_scale [B,Tq,H_I], k8 [B,N,D_I], k_scale [B,N], w [B,Tq,H_I]")
+    return ptrs, (B, Tq, N, H_I, D_I)
+
+
+def index_scores_fp8(q8, q_scale, k8, k_scale, w, q_pos0: int = 0, scores=None, stream=None) -> torch.Tensor:
+    ptrs, (B, Tq, N, H_I, D_I) = _fp8_indexer_args(q8, q_scale, k8, k_scale, w)
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q8.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if tuple(scores.shape) != (B, Tq, N):
+        raise ValueError("scores must be [B,Tq,N]")
+    _check(library().dsa_index_scores_fp8(*ptrs, ps, B, Tq, N, q_pos0, H_I, D_I, DSA_BF16, _stream(stream)))
+    return scores
+
+
+def forward_fp8(q8, q_scale, k8, k_scale, w, q, kv, K: int, scale: float, q_pos0: int = 0, DV: int = 512,
+                out=None, lse=True, workspace=None, return_idx=False, stream=None):
+    """dsa_forward with the FP8 indexer: returns (out, lse) or (out, lse, idx)."""
+    ptrs, (B, Tq, N, H_I, D_I) = _fp8_indexer_args(q8, q_scale, k8, k_scale, w)
+    H, D = q.shape[2], q.shape[3]
+    pq = _dev(q, "q", 4, torch.bfloat16)
+    pkv = _dev(kv, "kv", 3, torch.bfloat16)
+    if tuple(q.shape[:2]) != (B, Tq) or tuple(kv.shape) != (B, N, D):
+        raise ValueError("q must be [B,Tq,H,D] and kv [B,N,D]")
+    if out is None:
+        out = torch.empty((B, Tq, H, DV), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", 4, q.dtype)
+    lse_t = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if lse is True else (
+        lse if isinstance(lse, torch.Tensor) else None)
+    pl = _dev(lse_t, "lse", 3, torch.float32) if lse_t is not None else None
+    idx = torch.empty((B, Tq, K), dtype=torch.int32, device=q.device) if return_idx else None
+    lib = library()
+    ws, nbytes = _workspace(lib.dsa_forward_workspace_size(B, Tq, N, H, DV, K, DSA_BF16), q.device, workspace)
+    _check(lib.dsa_forward_fp8(*ptrs, pq, pkv, po, pl, idx.data_ptr() if idx is not None else None, B, Tq, N,
+                               q_pos0, H_I, D_I, H, D, DV, K, scale, DSA_BF16,
+                               ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    return (out, lse_t, idx) if return_idx else (out, lse_t)

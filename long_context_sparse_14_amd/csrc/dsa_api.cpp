@@ -149,6 +149,22 @@ dsa_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Checks the FP8 indexer inputs (codes, scales, bf16 head weights).
+dsa_status check_index_scores_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
+                                  const void* w, const float* scores, int64_t B, int64_t Tq, int64_t N,
+                                  int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t dtype, bool check_scores) {
+  dsa_status st = check_common(B, Tq, N, q_pos0, dtype);
+  if (st != DSA_OK) return st;
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "the FP8 indexer takes bf16 head weights");
+  if (!q8 || !qs || !k8 || !ks || !w || (check_scores && !scores)) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(q8) || !aligned16(qs) || !aligned16(k8) || !aligned16(ks) || !aligned16(w) ||
+      (check_scores && !aligned16(scores)))
+    return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (H_I != 64 || D_I != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "the FP8 indexer is compiled for H_I=64, D_I=128 (got %d, %d)", H_I, D_I);
+  return DSA_OK;
+}
+
 constexpr int64_t kMaxGemmRows = 65535LL * 64;
 
 dsa_status check_proj_common(const void* a, const void* b, const void* c, int64_t M, int32_t dtype) {
@@ -438,6 +454,60 @@ dsa_status dsa_linear(const void* x, const void* w, void* y, int64_t M, int32_t 
   dsa::GemmArgs g{static_cast<const uint16_t*>(x), K, 0, static_cast<const uint16_t*>(w), K, 0,
                   static_cast<uint16_t*>(y), N, 0, M, N, K, nullptr, 0, 0, nullptr, 0, 0, 0};
   return hip_status(dsa::launch_gemm_bf16(g, true, 1, static_cast<hipStream_t>(stream)), "linear launch");
+}
+
+dsa_status dsa_indexer_quantize_fp8(const void* x, uint8_t* codes, float* scales, int64_t R, int32_t D,
+                                    int32_t dtype, void* stream) {
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "FP8 quantisation takes bf16 rows");
+  if (D != 128) return fail(DSA_ERR_UNSUPPORTED, "FP8 quantisation is compiled for rows of 128 (got %d)", D);
+  if (R < 0) return fail(DSA_ERR_INVALID_ARG, "R must be >= 0 (got %lld)", (long long)R);
+  if (!x || !codes || !scales) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  return hip_status(dsa::launch_quantize_fp8(static_cast<const uint16_t*>(x), codes, scales, R,
+                                             static_cast<hipStream_t>(stream)),
+                    "FP8 quantisation launch");
+}
+
+dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                                const void* w, float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                                int32_t H_I, int32_t D_I, int32_t dtype, void* stream) {
+  dsa_status st = check_index_scores_fp8(q8, q_scale, k8, k_scale, w, scores, B, Tq, N, q_pos0, H_I, D_I, dtype, true);
+  if (st != DSA_OK) return st;
+  return hip_status(dsa::launch_index_scores_fp8(q8, q_scale, k8, k_scale, static_cast<const uint16_t*>(w), scores,
+                                                 B, Tq, N, q_pos0, static_cast<hipStream_t>(stream)),
+                    "FP8 index scores launch");
+}
+
+dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                           const void* w, const void* q, const void* kv, void* out, float* lse, int32_t* idx_out,
+                           int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t H,
+                           int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  dsa_status st =
+      check_index_scores_fp8(q8, q_scale, k8, k_scale, w, nullptr, B, Tq, N, q_pos0, H_I, D_I, dtype, false);
+  if (st != DSA_OK) return st;
+  st = check_mla(q, kv, nullptr, out, lse, B, Tq, N, H, D, DV, K, scale, dtype, nullptr, 0, false);
+  if (st != DSA_OK) return st;
+  if (idx_out && !aligned16(idx_out)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 16-byte aligned");
+  const ForwardLayout L = forward_layout(B, Tq, N, H, DV, K, dtype);
+  if (!workspace || ws_bytes < L.total)
+    return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dsa::launch_index_scores_fp8(q8, q_scale, k8, k_scale, static_cast<const uint16_t*>(w), scores, B,
+                                              Tq, N, q_pos0, s);
+  if (e != hipSuccess) return hip_status(e, "FP8 index scores launch");
+  e = dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
+  if (e != hipSuccess) return hip_status(e, "top-k launch");
+  e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
+                                  static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, ws + L.mla, s);
+  return hip_status(e, "sparse MLA launch");
 }
 
 }  // extern "C"

@@ -300,6 +300,208 @@ __global__ __launch_bounds__(256) void indexer_f32(const float* __restrict__ q, 
   scores[rowi * N + s] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// FP8 indexer (DeepSeek-V3.2 documentation, "DeepSeek Sparse Attention (DSA)":
+// the reference indexer runs in FP8 after a Hadamard rotation of queries and
+// keys; the rotation is orthogonal, so the scores are those of the bf16 path
+// up to the quantisation).  Rows of 128 are rotated by the unnormalised
+// Sylvester matrix (fast Walsh-Hadamard transform in float32, pair distance
+// 1, 2, 4, ...), scaled by one power of two per row (the smallest 2^e with
+// max|y| <= 448 * 2^e, so the scaling is exact) and rounded to OCP E4M3,
+// nearest even.  The score divides by 128, the squared norm of the rotation:
+//   I[t,s] = ks[s] * sum_h (w[t,h] * qs[t,h] / 128) * max(0, q8[t,h] . k8[s]).
+// The key cache is read as codes, half the bytes of bf16.  The codes are
+// widened to bf16 in registers (exact: E4M3 values have four significant
+// bits) for the bf16 MFMA, whose products and sums of such values were exact
+// when measured, whereas the fp8 MFMA rounded its dot products to about
+// 2^-13 of the largest product.
+// ---------------------------------------------------------------------------
+
+// OCP E4M3 code of v (|v| <= 448), round to nearest even.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);  // multiples of 2^-9; 8 is 0x08
+  const uint32_t au = __float_as_uint(a);
+  int e = (int)(au >> 23) - 127;
+  uint32_t q = (au >> 20) & 7u;
+  const uint32_t rem = au & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+  if (q == 8u) {
+    q = 0u;
+    ++e;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | q;
+}
+
+// One wave per row of 128: lane l holds elements 2l and 2l+1.
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                                           float* __restrict__ scales, int64_t R) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += nw) {
+    const uint32_t pair = *reinterpret_cast<const uint32_t*>(x + r * ID + 2 * lane);
+    const float a = bf16_bits_to_float(pair & 0xffffu), b = bf16_bits_to_float(pair >> 16);
+    float y0 = a + b, y1 = a - b;  // pair distance 1, inside the lane
+    // distance 2m: the partner element sits in lane l ^ m; the lane with bit m
+    // clear holds the lower element (sum), the other the upper (difference)
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float p0 = __shfl_xor(y0, m), p1 = __shfl_xor(y1, m);
+      const bool upper = (lane & m) != 0;
+      y0 = upper ? p0 - y0 : y0 + p0;
+      y1 = upper ? p1 - y1 : y1 + p1;
+    }
+    const uint32_t ab = wave_max(max(__float_as_uint(fabsf(y0)), __float_as_uint(fabsf(y1))));
+    int e = 0;
+    if (ab != 0u) {
+      int E;
+      const float m = frexpf(__uint_as_float(ab), &E);  // amax = m * 2^E, 0.5 <= m < 1; 448 = 0.875 * 2^9
+      e = m <= 0.875f ? E - 9 : E - 8;
+    }
+    const uint32_t c0 = e4m3_rne(ldexpf(y0, -e)), c1 = e4m3_rne(ldexpf(y1, -e));
+    *reinterpret_cast<uint16_t*>(codes + r * ID + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+    if (lane == 0) scales[r] = ldexpf(1.0f, e);
+  }
+}
+
+// Eight E4M3 codes (bytes of lo, then hi) -> eight bf16 values (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  const u32x4 v{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]), pack_bf16x2(d[0], d[1])};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Query codes of one row as bf16 MFMA operands (same layout as load_query),
+// with each head's weight folded with its scale and the rotation's 1/128.
+__device__ __forceinline__ void load_query_fp8(QFrags& f, const uint8_t* __restrict__ q8, const float* __restrict__ qs,
+                                               const uint16_t* __restrict__ w, int64_t row, int half, int col) {
+  const uint8_t* qr = q8 + row * (IH * ID) + 64 * half;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(qr + col * ID + 16 * v);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(qr + (32 + col) * ID + 16 * v);
+    f.a0[2 * v] = fp8x8_to_bf16(x0[0], x0[1]);
+    f.a0[2 * v + 1] = fp8x8_to_bf16(x0[2], x0[3]);
+    f.a1[2 * v] = fp8x8_to_bf16(x1[0], x1[1]);
+    f.a1[2 * v + 1] = fp8x8_to_bf16(x1[2], x1[3]);
+  }
+  const uint16_t* wr = w + row * IH;
+  const float* sr = qs + row * IH;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int h0 = mfma_row(i, half), h1 = 32 + h0;
+    f.w0[i] = bf16_bits_to_float(wr[h0]) * sr[h0] * 0.0078125f;
+    f.w1[i] = bf16_bits_to_float(wr[h1]) * sr[h1] * 0.0078125f;
+  }
+}
+
+// Decode kernel over an FP8 key cache: the bf16 decode kernel's structure
+// with 128-byte key rows.  A tile of 32 keys is 4 KiB, fetched by four
+// direct-to-LDS loads of eight keys each; lane L of a load fetches chunk
+// (L & 7) ^ (L >> 3) of key L >> 3 and lands at slot L, so chunk c of tile key
+// r sits at slot 8r + (c ^ (r & 7)).  The key scales are applied when the
+// workgroup's scores leave LDS.
+template <int WAVES, int NBUF, int SCAP>
+__global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
+    const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
+    const float* __restrict__ ks, const uint16_t* __restrict__ w, float* __restrict__ scores, int64_t Tq, int64_t N,
+    int64_t q_pos0, Vis vis, int64_t keys_per_wg) {
+  constexpr int TILE_BYTES = 32 * ID;
+  static_assert(NBUF >= 2 && NBUF <= 8, "the vmcnt waits below cover up to seven tiles in flight");
+  static_assert(WAVES * NBUF * TILE_BYTES + SCAP * 4 <= 160 * 1024, "LDS budget");
+  __shared__ __align__(16) uint8_t kt[WAVES][NBUF][TILE_BYTES];
+  __shared__ __align__(16) float sl[SCAP];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int64_t t = blockIdx.y, b = blockIdx.z;
+  const int64_t row = b * Tq + t;
+  const int64_t n_valid = visible_keys(vis, seq_q0(vis, b, Tq, q_pos0), t, N);
+  const int64_t k_begin = (int64_t)blockIdx.x * keys_per_wg;  // a multiple of 32
+  const int64_t k_end = min(n_valid, k_begin + keys_per_wg);
+  if (k_begin >= k_end) return;
+  const int total_tiles = (int)((k_end - k_begin + 31) / 32);
+  const int nt = total_tiles > wave ? (total_tiles - wave + WAVES - 1) / WAVES : 0;
+
+  const uint8_t* kb = k8 + b * N * ID;
+  const uint32_t ring = lds_address(&kt[wave][0][0]);
+  const uint32_t voff = 128u * (uint32_t)(lane >> 3) + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+  auto key0_of = [&](int it) { return k_begin + 32 * (int64_t)(it * WAVES + wave); };
+  auto dma_tile = [&](int it) {
+    const int64_t key0 = key0_of(it);
+    const uint32_t dst = ring + (uint32_t)((it % NBUF) * TILE_BYTES);
+    if (key0 + 32 <= N) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dma16(kb + (key0 + 8 * u) * ID, voff, dst + 1024u * u);
+    } else {
+      // last rows of the cache: clamp to a real row (those keys are never scored)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t kbase = min(key0 + 8 * u, N - 1);
+        const int64_t key = min(key0 + 8 * u + (lane >> 3), N - 1);
+        const uint32_t off = (uint32_t)(key - kbase) * 128u + (voff & 127u);
+        dma16(kb + kbase * ID, off, dst + 1024u * u);
+      }
+    }
+  };
+  QFrags f;
+  load_query_fp8(f, q8, qs, w, row, half, col);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nt) dma_tile(p);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // operand of k-step s: channels 64*half + 8s .. +7 = chunk 4*half + s/2, bytes 8*(s&1)
+  const uint32_t rbase = 128u * col;
+  for (int it = 0; it < nt; ++it) {
+    if (it + NBUF - 1 < nt) dma_tile(it + NBUF - 1);
+    const int after = min(NBUF - 1, nt - 1 - it);
+    switch (after) {
+      case 7: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+      case 6: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+    const uint8_t* tile = &kt[wave][it % NBUF][0];
+    f32x16 c0 = {}, c1 = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int c = 4 * half + (s >> 1);
+      const u32x2 kv = *reinterpret_cast<const u32x2*>(tile + rbase + 16u * (uint32_t)(c ^ (col & 7)) + 8u * (s & 1));
+      const bf16x8 bv = fp8x8_to_bf16(kv[0], kv[1]);
+      c0 = mfma32x32x16(f.a0[s], bv, c0);
+      c1 = mfma32x32x16(f.a1[s], bv, c1);
+    }
+    const float sc = weighted_relu_sum(f, c0, c1);
+    if (half == 0) sl[key0_of(it) - k_begin + col] = sc;
+  }
+  __syncthreads();
+  const int n = (int)(k_end - k_begin);
+  float* dst = scores + row * N + k_begin;
+  const float* ksr = ks + b * N + k_begin;
+  if (((row * N) & 3) == 0 && ((b * N) & 3) == 0) {
+    for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * WAVES * 64) {
+      if (i + 4 <= n) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sl[i]) * *reinterpret_cast<const f32x4*>(ksr + i);
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + i));
+      } else {
+        for (int e = i; e < n; ++e) dst[e] = sl[e] * ksr[e];
+      }
+    }
+  } else {
+    for (int i = (int)threadIdx.x; i < n; i += WAVES * 64) dst[i] = sl[i] * ksr[i];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
@@ -339,6 +541,34 @@ hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const
   if (chunks == 0) return hipSuccess;  // no query sees a row
   hipLaunchKernelGGL(indexer_f32, grid, dim3(256), 0, stream, q_idx, k_idx, w, scores, Tq, N, q_pos0, vis, H_I, D_I,
                      chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* codes, float* scales, int64_t R, hipStream_t stream) {
+  if (R <= 0) return hipSuccess;
+  const int64_t blocks = (R + 3) / 4 < 16384 ? (R + 3) / 4 : 16384;
+  hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, codes, scales, R);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
+                                   const uint16_t* w, float* scores, int64_t B, int64_t Tq, int64_t N,
+                                   int64_t q_pos0, hipStream_t stream) {
+  const Vis vis{nullptr, 1};
+  const int64_t nmax = min(N, q_pos0 + Tq);
+  if (nmax <= 0) return hipSuccess;  // no query sees a key
+  // About eight workgroups per compute unit over the launch, two resident at
+  // a time (72 KiB of LDS each), three 4 KiB tiles in flight per wave: the
+  // best of a sweep over waves (2, 4, 8), ring depth (2..8) and keys per
+  // workgroup (1024..8192) at the 128K decode batch.
+  constexpr int WAVES = 4, NBUF = 4, SCAP = 2048;
+  int64_t kpw = (nmax * B * Tq + 2047) / 2048;
+  kpw = (kpw + 32 * WAVES - 1) / (32 * WAVES) * (32 * WAVES);
+  if (kpw > SCAP) kpw = SCAP;
+  if (kpw < 32 * WAVES) kpw = 32 * WAVES;
+  dim3 grid((unsigned)((nmax + kpw - 1) / kpw), (unsigned)Tq, (unsigned)B);
+  hipLaunchKernelGGL((indexer_dma_fp8<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q8, qs, k8, ks, w, scores,
+                     Tq, N, q_pos0, vis, kpw);
   return hipGetLastError();
 }
 

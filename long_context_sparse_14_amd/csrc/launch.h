@@ -18,6 +18,14 @@ hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const
                                    int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int H_I, int D_I,
                                    hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1);
 
+// FP8 indexer: rows of 128 bf16 -> Hadamard-rotated OCP E4M3 codes and one
+// power-of-two scale per row; scores from codes and scales (decode kernel,
+// any Tq, causal with q_pos0).
+hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* codes, float* scales, int64_t R, hipStream_t stream);
+hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
+                                   const uint16_t* w, float* scores, int64_t B, int64_t Tq, int64_t N,
+                                   int64_t q_pos0, hipStream_t stream);
+
 size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
 hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
                        int K, void* workspace, hipStream_t stream, const int64_t* seq_lens = nullptr,

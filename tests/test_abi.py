@@ -176,3 +176,28 @@ def test_projection_validation():
     assert L.dsa_linear(P, P, None, 4, 64, 1536, BF16, None) == dsa.DSA_ERR_INVALID_ARG
     # nothing to do is not an error
     assert L.dsa_linear(P, P, P, 0, 64, 1536, BF16, None) == dsa.DSA_OK
+
+
+def test_fp8_validation():
+    L = lib()
+    F32 = dsa.DSA_F32
+    # quantisation: bf16 rows of 128 only
+    assert L.dsa_indexer_quantize_fp8(P, P, P, 10, 128, F32, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_indexer_quantize_fp8(P, P, P, 10, 64, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_indexer_quantize_fp8(P, None, P, 10, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_indexer_quantize_fp8(P, P, P + 4, 10, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_indexer_quantize_fp8(P, P, P, -1, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_indexer_quantize_fp8(P, P, P, 0, 128, BF16, None) == dsa.DSA_OK
+    # scores: 64 x 128, bf16 weights, aligned scales
+    assert L.dsa_index_scores_fp8(P, P, P, P, P, P, 2, 1, 100, 64, 64, 128, F32, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_index_scores_fp8(P, P, P, P, P, P, 2, 1, 100, 64, 32, 128, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_index_scores_fp8(P, P, P, P + 4, P, P, 2, 1, 100, 64, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_scores_fp8(P, None, P, P, P, P, 2, 1, 100, 64, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    # forward: the workspace of dsa_forward
+    B, Tq, N, K = 32, 1, 131072, 2048
+    need = L.dsa_forward_workspace_size(B, Tq, N, 128, 512, K, BF16)
+    args = [P, P, P, P, P, P, P, P, P, None, B, Tq, N, N - 1, 64, 128, 128, 576, 512, K, 0.07, BF16]
+    assert L.dsa_forward_fp8(*args, P, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    bad = list(args)
+    bad[5] = None  # q
+    assert L.dsa_forward_fp8(*bad, P, need, None) == dsa.DSA_ERR_INVALID_ARG
