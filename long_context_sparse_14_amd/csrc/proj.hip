@@ -51,7 +51,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
 
 // WM x WN MFMA tiles per wave, WAVES_M x WAVES_N waves (4 in all).
 template <int WM, int WN, int WAVES_M, bool B_NK>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int BM = 32 * WM * WAVES_M;
   static_assert(32 * WN * WAVES_N == GN, "a workgroup covers 128 columns");
@@ -59,15 +59,26 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int A_PER = (A_CHUNKS + 255) / 256;
   constexpr int B_PER = GN * GK / 8 / 256;                // 2
   constexpr int B_LDS = B_NK ? GN * APITCH : GK * KNPITCH;
-  __shared__ __align__(16) uint16_t As[2][BM * APITCH];
-  __shared__ __align__(16) uint16_t Bs[2][B_LDS];
+  constexpr int CPITCH = GN + 8;                          // bf16 per staged output row
+  constexpr int LDS_ELEMS = 2 * BM * APITCH + 2 * B_LDS;
+  static_assert(BM * CPITCH <= LDS_ELEMS, "the output tile is staged in the operand buffers");
+  __shared__ __align__(16) uint16_t lds[LDS_ELEMS];
+  uint16_t(*As)[BM * APITCH] = reinterpret_cast<uint16_t(*)[BM * APITCH]>(lds);
+  uint16_t(*Bs)[B_LDS] = reinterpret_cast<uint16_t(*)[B_LDS]>(lds + 2 * BM * APITCH);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int half = lane >> 5, col = lane & 31;
-  const int64_t z = blockIdx.z;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int n0 = blockIdx.x * GN;
+  // Workgroups are dealt to the 8 XCDs round-robin by launch order; renumber
+  // them so that each XCD runs a contiguous range of tiles, and the column
+  // blocks that share rows of A run on one XCD and find them in its L2.
+  const int64_t gx = gridDim.x, gy = gridDim.y;
+  const int64_t total = gx * gy * gridDim.z;
+  int64_t P = blockIdx.x + gx * (blockIdx.y + gy * (int64_t)blockIdx.z);
+  if ((total & 7) == 0) P = (P & 7) * (total >> 3) + (P >> 3);
+  const int64_t z = P / (gx * gy);
+  const int64_t m0 = ((P / gx) % gy) * BM;
+  const int n0 = (int)(P % gx) * GN;
   const uint16_t* A = g.A + z * g.sA;
   const uint16_t* B = g.B + z * g.sB;
   uint16_t* C = g.C + z * g.sC;
@@ -167,23 +178,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // Epilogue: lanes 0..31 of a register hold 32 consecutive columns of one row.
+  // Epilogue: the tile is staged in LDS as bf16 (the loop's last barrier has
+  // freed the operand buffers), then leaves in 16-byte row chunks.
 #pragma unroll
-  for (int j = 0; j < WN; ++j) {
-    const int n = n0 + 32 * (WN * wn + j) + col;
-    if (n >= g.N) continue;
+  for (int j = 0; j < WN; ++j)
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + 32 * (WM * wm + i) + mfma_row(e, half);
-        if (m < g.M) C[m * g.ldc + n] = (uint16_t)float_to_bf16_bits(acc[i][j][e]);
-      }
+      for (int e = 0; e < 16; ++e)
+        lds[(32 * (WM * wm + i) + mfma_row(e, half)) * CPITCH + 32 * (WN * wn + j) + col] =
+            (uint16_t)float_to_bf16_bits(acc[i][j][e]);
+  __syncthreads();
+  const bool vec = ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && (g.ldc % 8) == 0;
+  for (int c = tid; c < BM * (GN / 8); c += 256) {
+    const int r = c / (GN / 8), ch = c % (GN / 8);
+    const int64_t m = m0 + r;
+    const int n = n0 + 8 * ch;
+    if (m >= g.M || n >= g.N) continue;
+    const uint16_t* src = &lds[r * CPITCH + 8 * ch];
+    if (vec && n + 8 <= g.N) {
+      *reinterpret_cast<u32x4*>(C + m * g.ldc + n) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int e = 0; e < 8 && n + e < g.N; ++e) C[m * g.ldc + n + e] = src[e];
+    }
   }
 
   // Optional row copy riding on the first column block (the rope part of an
   // absorbed query): cp_w bf16 per row, in 16-byte chunks.
-  if (g.cp_dst != nullptr && blockIdx.x == 0) {
+  if (g.cp_dst != nullptr && n0 == 0) {
     const int chunks = g.cp_w / 8;
     for (int c = tid; c < BM * chunks; c += 256) {
       const int64_t m = m0 + c / chunks;
@@ -195,28 +217,31 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-// Few rows (M <= 64), where the weights' bytes bound the time: a workgroup
-// owns a 32 x 32 tile of C over the whole of K, its WAVES waves take every
-// WAVES-th k-step of 16 each, and each wave keeps U k-steps of operand loads
-// in flight.  A and a [N][K] B go from global memory straight into the MFMA
-// operand registers (lane j: row or column j % 32, eight k from 8 * (j / 32)).
-// A [K][N] B is staged per wave through LDS ([16 k][32 n] per k-step) and read
-// back with the transposing read.  The WAVES partial tiles are summed in LDS
-// in a fixed order, so the result does not depend on timing.
-template <bool B_NK, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(GemmArgs g) {
-  constexpr int U = 4;            // k-steps per wave in flight
+// Few rows (M <= 64), where the weights' bytes bound the time.  A workgroup
+// of WK x WN waves owns a 32 x 32*WN tile of C over the whole of K: wave
+// (wk, wn) computes columns 32*wn .. +32 from every WK-th k-step of 16
+// (starting at wk), keeping U k-steps of operand loads in flight.  A and a
+// [N][K] B go from global memory straight into the MFMA operand registers
+// (lane j: row or column j % 32, eight k from 8 * (j / 32)).  A [K][N] B is
+// staged per wave through LDS ([16 k][32 n] per k-step) and read back with the
+// transposing read.  With WK > 1 the partial tiles are summed in LDS in a
+// fixed order, so the result does not depend on timing.
+template <bool B_NK, int WK, int WN, int U>
+__global__ __launch_bounds__(64 * WK * WN) void gemm_skinny_kernel(GemmArgs g) {
+  constexpr int WAVES = WK * WN;
   constexpr int KP = 48;          // bf16 per staging row (96 B: four rows fall on distinct banks)
   constexpr int STAGE = B_NK ? 1 : WAVES * U * 16 * KP;
+  constexpr int RED = WK > 1 ? WAVES * 16 * 64 : 1;
   __shared__ __align__(16) uint16_t stage[STAGE];
-  __shared__ float red[WAVES][16][64];
+  __shared__ float red[RED];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wk = wave % WK, wn = wave / WK;
   const int half = lane >> 5, col = lane & 31;
   const int g16 = lane >> 4, i16 = lane & 15;
   const int64_t z = blockIdx.z;
   const int64_t m0 = (int64_t)blockIdx.y * 32;
-  const int n0 = blockIdx.x * 32;
+  const int n0 = blockIdx.x * 32 * WN + 32 * wn;
   const uint16_t* A = g.A + z * g.sA;
   const uint16_t* B = g.B + z * g.sB;
   uint16_t* C = g.C + z * g.sC;
@@ -235,11 +260,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(GemmArgs g) {
 
   f32x16 acc{};
   const int S = g.K / 16;
-  for (int s0 = wave; s0 < S; s0 += WAVES * U) {
+  for (int s0 = wk; s0 < S; s0 += WK * U) {
     u32x4 ra[U], rb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = s0 + WAVES * u;
+      const int s = s0 + WK * u;
       if (s < S) {
         ra[u] = m_ok ? *reinterpret_cast<const u32x4*>(a_ptr + 16 * s) : u32x4{0, 0, 0, 0};
         rb[u] = b_ok ? *reinterpret_cast<const u32x4*>(b_ptr + b_step * s) : u32x4{0, 0, 0, 0};
@@ -247,7 +272,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = s0 + WAVES * u;
+      const int s = s0 + WK * u;
       if (s >= S) break;
       bf16x8 bv;
       if (B_NK) {
@@ -266,19 +291,27 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(GemmArgs g) {
     }
   }
 
+  const int nn = n0 + col;
+  if (WK == 1) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) red[wave][e][lane] = acc[e];
-  __syncthreads();
-  constexpr int PER = 16 / WAVES;
+    for (int e = 0; e < 16; ++e) {
+      const int64_t mm = m0 + mfma_row(e, half);
+      if (mm < g.M && nn < g.N) C[mm * g.ldc + nn] = (uint16_t)float_to_bf16_bits(acc[e]);
+    }
+  } else {
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int e = PER * wave + q;
-    float v = red[0][e][lane];
+    for (int e = 0; e < 16; ++e) red[(wave * 16 + e) * 64 + lane] = acc[e];
+    __syncthreads();
+    constexpr int PER = 16 / WK;
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) v += red[w][e][lane];
-    const int64_t mm = m0 + mfma_row(e, half);
-    const int nn = n0 + col;
-    if (mm < g.M && nn < g.N) C[mm * g.ldc + nn] = (uint16_t)float_to_bf16_bits(v);
+    for (int q = 0; q < PER; ++q) {
+      const int e = PER * wk + q;
+      float v = red[((WK * wn) * 16 + e) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < WK; ++w) v += red[((WK * wn + w) * 16 + e) * 64 + lane];
+      const int64_t mm = m0 + mfma_row(e, half);
+      if (mm < g.M && nn < g.N) C[mm * g.ldc + nn] = (uint16_t)float_to_bf16_bits(v);
+    }
   }
 
   if (g.cp_dst != nullptr && blockIdx.x == 0) {
@@ -291,6 +324,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(GemmArgs g) {
           *reinterpret_cast<const u32x4*>(g.cp_src + z * g.cp_ss + mr * g.cp_lds + off);
     }
   }
+}
+
+template <bool B_NK, int WK, int WN, int U>
+hipError_t launch_skinny(const GemmArgs& g, int64_t batch, hipStream_t stream) {
+  const dim3 grid((unsigned)((g.N + 32 * WN - 1) / (32 * WN)), (unsigned)((g.M + 31) / 32), (unsigned)batch);
+  hipLaunchKernelGGL((gemm_skinny_kernel<B_NK, WK, WN, U>), grid, dim3(64 * WK * WN), 0, stream, g);
+  return hipGetLastError();
 }
 
 template <int WM, int WN, int WAVES_M>
@@ -309,17 +349,15 @@ hipError_t launch_tiles(const GemmArgs& g, bool b_nk, int64_t batch, hipStream_t
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool b_nk, int64_t batch, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
   if (g.M <= 64) {
-    // 32 x 32 tiles over the whole of K; sixteen waves per workgroup when the
-    // grid alone would leave most compute units idle
-    const dim3 grid((unsigned)((g.N + 31) / 32), (unsigned)((g.M + 31) / 32), (unsigned)batch);
-    const bool few = (int64_t)grid.x * grid.y * grid.z < 256;
-    if (b_nk && few)
-      hipLaunchKernelGGL((gemm_skinny_kernel<true, 16>), grid, dim3(1024), 0, stream, g);
-    else if (b_nk)
-      hipLaunchKernelGGL((gemm_skinny_kernel<true, 4>), grid, dim3(256), 0, stream, g);
-    else
-      hipLaunchKernelGGL((gemm_skinny_kernel<false, 4>), grid, dim3(256), 0, stream, g);
-    return hipGetLastError();
+    // Shapes from a sweep at the decode batch (M = 32): [N][K] weights take 8
+    // waves over K per 32 columns (16 when the grid alone would leave most
+    // compute units idle); the [K][N] absorption weight takes 2 waves over K
+    // times 4 over N per 128 columns (6.5 us for 128 heads, against 10.4 us
+    // with 4 waves over K per 32 columns).
+    const bool few = (int64_t)((g.N + 31) / 32) * ((g.M + 31) / 32) * batch < 256;
+    if (b_nk && few) return launch_skinny<true, 16, 1, 4>(g, batch, stream);
+    if (b_nk) return launch_skinny<true, 8, 1, 4>(g, batch, stream);
+    return launch_skinny<false, 2, 4, 4>(g, batch, stream);
   }
   return launch_tiles<2, 2, 2>(g, b_nk, batch, stream);                  // 128 x 128 tiles
 }
