@@ -223,10 +223,10 @@ __device__ uint32_t select_rank(AddKeys add_keys, uint32_t lo, uint32_t hi, uint
 // Writes the kept keys of the run [i0, i0 + RUN) (clipped to n) of one chunk:
 // gt/eq are the per-thread counts before this thread within the whole row.
 template <typename KeyAt>
-__device__ __forceinline__ void emit_run(KeyAt key_at, int64_t i0, int64_t n, uint32_t T, uint32_t keq,
+__device__ __forceinline__ void emit_run(KeyAt key_at, int i0, int n, uint32_t T, uint32_t keq,
                                          uint32_t gt, uint32_t eq, int32_t* __restrict__ out) {
   for (int u = 0; u < RUN; ++u) {
-    const int64_t i = i0 + u;
+    const int i = i0 + u;
     if (i >= n) break;
     const uint32_t k = key_at(i);
     if (k > T) {
@@ -242,7 +242,7 @@ __device__ __forceinline__ void emit_run(KeyAt key_at, int64_t i0, int64_t n, ui
 // The one-workgroup method for one row.  skey: LDS stage of TK_CAP keys, or
 // nullptr to read the row from global memory on every pass.  hist: 2048 bins;
 // sbuf: 3 * TK_WAVES words; s_res: 4 words.
-__device__ void select_row(const float* __restrict__ src, int64_t n, int K, int32_t* __restrict__ out,
+__device__ __forceinline__ void select_row(const float* __restrict__ src, int64_t n, int K, int32_t* __restrict__ out,
                            uint32_t* skey, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res) {
   const int tid = threadIdx.x;
   if (n <= K) {
@@ -251,18 +251,20 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
   }
   // keys (staged in LDS when skey is given) and their range; eight loads in
   // flight per thread
+  // (row offsets fit 32 bits: N < 2^31)
+  const int n32 = (int)n;
   uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int64_t base = tid; base < n; base += 8 * TK_THREADS) {
+  for (int base = tid; base < n32; base += 8 * TK_THREADS) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t i = base + (int64_t)u * TK_THREADS;
-      v[u] = i < n ? src[i] : 0.f;
+      const int i = base + u * TK_THREADS;
+      v[u] = i < n32 ? src[i] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t i = base + (int64_t)u * TK_THREADS;
-      if (i < n) {
+      const int i = base + u * TK_THREADS;
+      if (i < n32) {
         const uint32_t k = float_order_key(v[u]);
         if (skey != nullptr) skey[i] = k;
         mn = min(mn, k);
@@ -272,20 +274,20 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
   }
   uint32_t kmin, kmax;
   block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);  // its barriers also publish skey
-  auto key_at = [&](int64_t i) -> uint32_t { return skey != nullptr ? skey[i] : float_order_key(src[i]); };
+  auto key_at = [&](int i) -> uint32_t { return skey != nullptr ? skey[i] : float_order_key(src[i]); };
   // (the bins span the keys' own range, so plain atomics rarely collide)
   auto add_row = [&](HotBins&, uint32_t lo, uint32_t hi, int shift) {
-    for (int64_t base = tid; base < n; base += 8 * TK_THREADS) {
+    for (int base = tid; base < n32; base += 8 * TK_THREADS) {
       uint32_t k[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t i = base + (int64_t)u * TK_THREADS;
-        k[u] = i < n ? key_at(i) : 0u;
+        const int i = base + u * TK_THREADS;
+        k[u] = i < n32 ? key_at(i) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t i = base + (int64_t)u * TK_THREADS;
-        if (i < n && k[u] >= lo && k[u] <= hi) atomicAdd(&hist[(k[u] - lo) >> shift], 1u);
+        const int i = base + u * TK_THREADS;
+        if (i < n32 && k[u] >= lo && k[u] <= hi) atomicAdd(&hist[(k[u] - lo) >> shift], 1u);
       }
     }
   };
@@ -295,19 +297,19 @@ __device__ void select_row(const float* __restrict__ src, int64_t n, int K, int3
 
   // in-order compaction: thread t owns keys [base + RUN*t, base + RUN*t + RUN)
   uint32_t run_gt = 0, run_eq = 0;
-  for (int64_t base = 0; base < n; base += CHUNK) {
-    const int64_t i0 = base + (int64_t)RUN * tid;
+  for (int base = 0; base < n32; base += CHUNK) {
+    const int i0 = base + RUN * tid;
     uint32_t gt = 0, eq = 0;
     for (int u = 0; u < RUN; ++u) {
-      const int64_t i = i0 + u;
-      if (i >= n) break;
+      const int i = i0 + u;
+      if (i >= n32) break;
       const uint32_t k = key_at(i);
       gt += k > T;
       eq += k == T;
     }
     uint32_t tot;
     const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sbuf);
-    emit_run(key_at, i0, n, T, keq, run_gt + (ex & 0xffffu), run_eq + (ex >> 16), out);
+    emit_run(key_at, i0, n32, T, keq, run_gt + (ex & 0xffffu), run_eq + (ex >> 16), out);
     run_gt += tot & 0xffffu;
     run_eq += tot >> 16;
   }
@@ -390,7 +392,7 @@ __device__ __forceinline__ void load_segment(const float* __restrict__ src, int6
 // t_lo).  Any two keys would keep the method exact (the final step checks
 // them); these make the checks pass with overwhelming probability unless the
 // scores are strongly ordered by position, and keep the candidate list short.
-__device__ void sample_bounds(const float* __restrict__ src, int64_t n, int K, uint32_t& t_hi, uint32_t& t_lo,
+__device__ __forceinline__ void sample_bounds(const float* __restrict__ src, int64_t n, int K, uint32_t& t_hi, uint32_t& t_lo,
                               uint32_t* h, uint32_t* sbuf, uint32_t* s_res) {
   uint32_t k[SAMPLE_PER_T];
   bool valid[SAMPLE_PER_T];
@@ -520,7 +522,7 @@ struct FinalSmem {
 // K - #definite best candidates (exact select on their full keys), and merge
 // the two ascending lists into the output.  If a check fails, the exact
 // one-workgroup method runs over the row from global memory instead.
-__device__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws, int32_t* __restrict__ idx,
+__device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws, int32_t* __restrict__ idx,
                               int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, const Vis& vis, int K, int G,
                               FinalSmem& sm) {
   const int tid = threadIdx.x;
