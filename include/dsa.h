@@ -331,6 +331,68 @@ dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_
                            int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/*
+ * Paged caches (decode shapes, bf16).
+ * (DeepSeek-V3.2 documentation, "DeepSeek Sparse Attention (DSA)": the
+ *  indexer key cache lives beside the main key/value cache in static or
+ *  growing cache layers and is updated as tokens arrive.  Reading of this
+ *  library: a paged layer keeps each cache as a pool of fixed-size blocks
+ *  with one block table per sequence.)
+ *
+ * Layout: k_pool [num_blocks * block_size, D_I] (bf16 indexer keys, or E4M3
+ * codes with k_scale_pool [num_blocks * block_size] for the FP8 indexer) and
+ * kv_pool [num_blocks * block_size, D] (bf16 latent rows); block_table int32
+ * [B, max_blocks] (device, 4-byte aligned): logical row r of sequence b is
+ * pool row block_table[b, r / block_size] * block_size + r % block_size.
+ * block_size is a power of two in [64, 2^20]; max_blocks * block_size and
+ * num_blocks * block_size are below 2^31.  seq_lens int64 [B] (device) gives
+ * each sequence's length; its Tq queries are its last Tq tokens, exactly as
+ * for the varlen entry points, and only table entries of blocks that hold
+ * rows < seq_lens[b] are read.  An entry outside [0, num_blocks) is read as
+ * block 0 (caller error: wrong results, never an access outside the pool).
+ * Every paged call equals the matching static-cache call on the caches
+ * gathered through the table (scores over the logical axis of length
+ * max_blocks * block_size, indices logical).
+ *
+ * dsa_index_scores_paged / dsa_index_scores_fp8_paged: scores [B, Tq,
+ *   max_blocks * block_size]; Tq <= 4 (DSA_ERR_UNSUPPORTED otherwise).
+ *   Select with dsa_topk_varlen.
+ * dsa_sparse_mla_fwd_paged: idx [B, Tq, K] logical; the pool is gathered as
+ *   one array, so num_blocks * block_size * D * 2 bytes must stay below
+ *   4 GiB (DSA_ERR_UNSUPPORTED otherwise).  Workspace:
+ *   dsa_paged_workspace_size(...) bytes (covers this call and the next).
+ * dsa_forward_paged: indexer -> top-k -> sparse MLA over paged caches;
+ *   workspace dsa_paged_workspace_size(...) bytes; idx_out (optional)
+ *   receives the logical indices.
+ * dsa_cache_append_paged: as dsa_cache_append, pos[b] logical; entries of pos
+ *   outside [0, max_blocks * block_size) write nothing.
+ */
+size_t dsa_paged_workspace_size(int64_t B, int64_t Tq, int64_t max_blocks, int32_t block_size, int32_t H,
+                                int32_t DV, int32_t K, int32_t dtype);
+dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const void* w, float* scores,
+                                  const int64_t* seq_lens, const int32_t* block_table, int64_t B, int64_t Tq,
+                                  int64_t max_blocks, int32_t block_size, int64_t num_blocks, int32_t H_I,
+                                  int32_t D_I, int32_t dtype, void* stream);
+dsa_status dsa_index_scores_fp8_paged(const uint8_t* q8, const float* q_scale, const uint8_t* k8_pool,
+                                      const float* k_scale_pool, const void* w, float* scores,
+                                      const int64_t* seq_lens, const int32_t* block_table, int64_t B, int64_t Tq,
+                                      int64_t max_blocks, int32_t block_size, int64_t num_blocks, int32_t H_I,
+                                      int32_t D_I, int32_t dtype, void* stream);
+dsa_status dsa_sparse_mla_fwd_paged(const void* q, const void* kv_pool, const int32_t* idx, const int32_t* block_table,
+                                    void* out, float* lse, int64_t B, int64_t Tq, int64_t max_blocks,
+                                    int32_t block_size, int64_t num_blocks, int32_t H, int32_t D, int32_t DV, int32_t K,
+                                    float scale, int32_t dtype, void* workspace, size_t ws_bytes, void* stream);
+dsa_status dsa_forward_paged(const void* q_idx, const void* k_pool, const void* w, const void* q, const void* kv_pool,
+                             void* out, float* lse, int32_t* idx_out, const int64_t* seq_lens,
+                             const int32_t* block_table, int64_t B, int64_t Tq, int64_t max_blocks,
+                             int32_t block_size, int64_t num_blocks, int32_t H_I, int32_t D_I, int32_t H, int32_t D,
+                             int32_t DV, int32_t K, float scale, int32_t dtype, void* workspace, size_t ws_bytes,
+                             void* stream);
+dsa_status dsa_cache_append_paged(void* k_pool, void* kv_pool, const void* new_k_idx, const void* new_kv,
+                                  const int64_t* pos, const int32_t* block_table, int64_t B, int64_t max_blocks,
+                                  int32_t block_size, int64_t num_blocks, int32_t D_I, int32_t D, int32_t dtype,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

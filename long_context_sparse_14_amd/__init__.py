@@ -24,6 +24,11 @@ Functions mirror the C entry points:
   indexer_quantize_fp8(x)                                 -> (codes uint8 [..., 128], scales float32 [...])
   index_scores_fp8(q8, q_scale, k8, k_scale, w, q_pos0=0) -> scores [B,Tq,N] float32
   forward_fp8(q8, q_scale, k8, k_scale, w, q, kv, K, scale, q_pos0=0, DV=512, return_idx=False)
+  index_scores_paged(q_idx, k_pool, w, seq_lens, block_table)     -> scores over the logical axis
+  index_scores_fp8_paged(q8, q_scale, k8_pool, k_scale_pool, w, seq_lens, block_table)
+  sparse_mla_paged(q, kv_pool, idx, block_table, scale, DV=512)   -> (out, lse)
+  forward_paged(q_idx, k_pool, w, q, kv_pool, K, scale, seq_lens, block_table, ...)
+  cache_append_paged(k_pool, kv_pool, new_k_idx, new_kv, pos, block_table)
 """
 from __future__ import annotations
 
@@ -84,6 +89,17 @@ _SIGNATURES = {
     "dsa_index_scores_fp8": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "dsa_forward_fp8": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "dsa_paged_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32]),
+    "dsa_index_scores_paged": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i32, _i32,
+                                              _i32, _p]),
+    "dsa_index_scores_fp8_paged": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i64,
+                                                  _i32, _i32, _i32, _p]),
+    "dsa_sparse_mla_fwd_paged": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i32, _i32,
+                                                _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "dsa_forward_paged": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i64,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "dsa_cache_append_paged": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i64, _i32, _i32, _i32,
+                                              _p]),
 }
 
 
@@ -504,3 +520,118 @@ def forward_fp8(q8, q_scale, k8, k_scale, w, q, kv, K: int, scale: float, q_pos0
                                q_pos0, H_I, D_I, H, D, DV, K, scale, DSA_BF16,
                                ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
     return (out, lse_t, idx) if return_idx else (out, lse_t)
+
+
+def _paged(block_table, pool_rows: int, B: int):
+    """(table pointer, max_blocks, block_size, num_blocks) of a paged cache."""
+    pt = _dev(block_table, "block_table", 2, torch.int32)
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table must have B={B} rows")
+    return pt, block_table.shape[1]
+
+
+def index_scores_paged(q_idx, k_pool, w, seq_lens, block_table, block_size: int, scores=None, stream=None):
+    """Scores [B, Tq, max_blocks * block_size] over a paged indexer key pool [rows, D_I]."""
+    B, Tq, H_I, D_I = q_idx.shape
+    pt, max_blocks = _paged(block_table, k_pool.shape[0], B)
+    num_blocks = k_pool.shape[0] // block_size
+    N = max_blocks * block_size
+    pq = _dev(q_idx, "q_idx", 4)
+    pk = _dev(k_pool, "k_pool", 2, q_idx.dtype)
+    pw = _dev(w, "w", 3, q_idx.dtype)
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q_idx.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    _check(library().dsa_index_scores_paged(pq, pk, pw, ps, _seq_lens(seq_lens, B), pt, B, Tq, max_blocks, block_size,
+                                            num_blocks, H_I, D_I, _dtype_code(q_idx), _stream(stream)))
+    return scores
+
+
+def index_scores_fp8_paged(q8, q_scale, k8_pool, k_scale_pool, w, seq_lens, block_table, block_size: int,
+                           scores=None, stream=None):
+    B, Tq, H_I, D_I = q8.shape
+    pt, max_blocks = _paged(block_table, k8_pool.shape[0], B)
+    num_blocks = k8_pool.shape[0] // block_size
+    N = max_blocks * block_size
+    ptrs = (_dev(q8, "q8", 4, torch.uint8), _dev(q_scale, "q_scale", 3, torch.float32),
+            _dev(k8_pool, "k8_pool", 2, torch.uint8), _dev(k_scale_pool, "k_scale_pool", 1, torch.float32),
+            _dev(w, "w", 3, torch.bfloat16))
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q8.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    _check(library().dsa_index_scores_fp8_paged(*ptrs, ps, _seq_lens(seq_lens, B), pt, B, Tq, max_blocks, block_size,
+                                                num_blocks, H_I, D_I, DSA_BF16, _stream(stream)))
+    return scores
+
+
+def paged_workspace_size(B, Tq, max_blocks, block_size, H, DV, K, dtype=None) -> int:
+    return library().dsa_paged_workspace_size(B, Tq, max_blocks, block_size, H, DV, K,
+                                              DSA_BF16 if dtype is None else dtype)
+
+
+def sparse_mla_paged(q, kv_pool, idx, block_table, block_size: int, scale: float, DV: int = 512, out=None, lse=True,
+                     workspace=None, stream=None):
+    B, Tq, H, D = q.shape
+    K = idx.shape[2]
+    pt, max_blocks = _paged(block_table, kv_pool.shape[0], B)
+    num_blocks = kv_pool.shape[0] // block_size
+    pq = _dev(q, "q", 4)
+    pkv = _dev(kv_pool, "kv_pool", 2, q.dtype)
+    pi = _dev(idx, "idx", 3, torch.int32)
+    if out is None:
+        out = torch.empty((B, Tq, H, DV), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", 4, q.dtype)
+    lse_t = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if lse is True else (
+        lse if isinstance(lse, torch.Tensor) else None)
+    pl = _dev(lse_t, "lse", 3, torch.float32) if lse_t is not None else None
+    lib = library()
+    ws, nbytes = _workspace(paged_workspace_size(B, Tq, max_blocks, block_size, H, DV, K), q.device, workspace)
+    _check(lib.dsa_sparse_mla_fwd_paged(pq, pkv, pi, pt, po, pl, B, Tq, max_blocks, block_size, num_blocks, H, D, DV,
+                                        K, scale, _dtype_code(q), ws.data_ptr() if ws is not None else None, nbytes,
+                                        _stream(stream)))
+    return out, lse_t
+
+
+def forward_paged(q_idx, k_pool, w, q, kv_pool, K: int, scale: float, seq_lens, block_table, block_size: int,
+                  DV: int = 512, out=None, lse=True, workspace=None, return_idx=False, stream=None):
+    B, Tq, H_I, D_I = q_idx.shape
+    H, D = q.shape[2], q.shape[3]
+    pt, max_blocks = _paged(block_table, kv_pool.shape[0], B)
+    num_blocks = kv_pool.shape[0] // block_size
+    if k_pool.shape[0] != kv_pool.shape[0]:
+        raise ValueError("k_pool and kv_pool must hold the same number of rows")
+    pq = _dev(q_idx, "q_idx", 4)
+    pk = _dev(k_pool, "k_pool", 2, q_idx.dtype)
+    pw = _dev(w, "w", 3, q_idx.dtype)
+    pqq = _dev(q, "q", 4, q_idx.dtype)
+    pkv = _dev(kv_pool, "kv_pool", 2, q_idx.dtype)
+    if out is None:
+        out = torch.empty((B, Tq, H, DV), dtype=q.dtype, device=q.device)
+    po = _dev(out, "out", 4, q.dtype)
+    lse_t = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if lse is True else (
+        lse if isinstance(lse, torch.Tensor) else None)
+    pl = _dev(lse_t, "lse", 3, torch.float32) if lse_t is not None else None
+    idx = torch.empty((B, Tq, K), dtype=torch.int32, device=q.device) if return_idx else None
+    lib = library()
+    ws, nbytes = _workspace(paged_workspace_size(B, Tq, max_blocks, block_size, H, DV, K), q.device, workspace)
+    _check(lib.dsa_forward_paged(pq, pk, pw, pqq, pkv, po, pl, idx.data_ptr() if idx is not None else None,
+                                 _seq_lens(seq_lens, B), pt, B, Tq, max_blocks, block_size, num_blocks, H_I, D_I, H,
+                                 D, DV, K, scale, _dtype_code(q), ws.data_ptr() if ws is not None else None, nbytes,
+                                 _stream(stream)))
+    return (out, lse_t, idx) if return_idx else (out, lse_t)
+
+
+def cache_append_paged(k_pool, kv_pool, new_k_idx, new_kv, pos, block_table, block_size: int, stream=None):
+    ref = k_pool if k_pool is not None else kv_pool
+    B = (new_k_idx if new_k_idx is not None else new_kv).shape[0]
+    pt, max_blocks = _paged(block_table, ref.shape[0], B)
+    num_blocks = ref.shape[0] // block_size
+    pk = _dev(k_pool, "k_pool", 2, ref.dtype) if k_pool is not None else None
+    pv = _dev(kv_pool, "kv_pool", 2, ref.dtype) if kv_pool is not None else None
+    pnk = _dev(new_k_idx, "new_k_idx", 2, ref.dtype) if new_k_idx is not None else None
+    pnv = _dev(new_kv, "new_kv", 2, ref.dtype) if new_kv is not None else None
+    D_I = k_pool.shape[1] if k_pool is not None else 0
+    D = kv_pool.shape[1] if kv_pool is not None else 0
+    pp = _dev(pos, "pos", 1, torch.int64)
+    _check(library().dsa_cache_append_paged(pk, pv, pnk, pnv, pp, pt, B, max_blocks, block_size, num_blocks, D_I, D,
+                                            _dtype_code(ref), _stream(stream)))

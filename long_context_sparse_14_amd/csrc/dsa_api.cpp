@@ -165,6 +165,36 @@ dsa_status check_index_scores_fp8(const uint8_t* q8, const float* qs, const uint
   return DSA_OK;
 }
 
+// Checks a paged cache description and fills `pg`.
+dsa_status check_paged(const int32_t* block_table, int64_t max_blocks, int32_t block_size, int64_t num_blocks,
+                       dsa::Paged& pg) {
+  if (!block_table) return fail(DSA_ERR_INVALID_ARG, "block_table must not be null");
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
+    return fail(DSA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+  if (block_size < 64 || block_size > (1 << 20) || (block_size & (block_size - 1)) != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "block_size must be a power of two in [64, 2^20] (got %d)", block_size);
+  if (max_blocks < 1 || num_blocks < 1) return fail(DSA_ERR_INVALID_ARG, "max_blocks and num_blocks must be >= 1");
+  if (max_blocks * (int64_t)block_size > kMaxN || num_blocks * (int64_t)block_size > kMaxN)
+    return fail(DSA_ERR_INVALID_ARG, "max_blocks*block_size and num_blocks*block_size must be < 2^31");
+  int shift = 0;
+  while ((1 << shift) < block_size) ++shift;
+  pg = dsa::Paged{block_table, max_blocks, shift, (int32_t)num_blocks};
+  return DSA_OK;
+}
+
+// The paged sparse MLA: logical indices -> pool rows (into `phys`), then the
+// gather kernel over the pool as one sequence of num_blocks * block_size rows.
+dsa_status run_paged_mla(const void* q, const void* kv_pool, const int32_t* idx, int32_t* phys, void* out, float* lse,
+                         int64_t B, int64_t Tq, int32_t K, float scale, const dsa::Paged& pg, void* mla_ws,
+                         hipStream_t s) {
+  hipError_t e = dsa::launch_page_translate(idx, phys, B, Tq, K, pg, s);
+  if (e != hipSuccess) return hip_status(e, "page translate launch");
+  e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_pool), phys,
+                                  static_cast<uint16_t*>(out), lse, 1, B * Tq, (int64_t)pg.num_blocks << pg.shift, K,
+                                  scale, mla_ws, s);
+  return hip_status(e, "sparse MLA launch");
+}
+
 constexpr int64_t kMaxGemmRows = 65535LL * 64;
 
 dsa_status check_proj_common(const void* a, const void* b, const void* c, int64_t M, int32_t dtype) {
@@ -508,6 +538,140 @@ dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_
   e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
                                   static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, ws + L.mla, s);
   return hip_status(e, "sparse MLA launch");
+}
+
+size_t dsa_paged_workspace_size(int64_t B, int64_t Tq, int64_t max_blocks, int32_t block_size, int32_t H,
+                                int32_t DV, int32_t K, int32_t dtype) {
+  if (B < 1 || Tq < 1 || max_blocks < 1 || block_size < 1 || H < 1 || DV < 1 || K < 1) return 0;
+  return forward_layout(B, Tq, max_blocks * (int64_t)block_size, H, DV, K, dtype).total +
+         align256((size_t)B * Tq * K * sizeof(int32_t));
+}
+
+dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const void* w, float* scores,
+                                  const int64_t* seq_lens, const int32_t* block_table, int64_t B, int64_t Tq,
+                                  int64_t max_blocks, int32_t block_size, int64_t num_blocks, int32_t H_I,
+                                  int32_t D_I, int32_t dtype, void* stream) {
+  dsa::Paged pg;
+  dsa_status st = check_paged(block_table, max_blocks, block_size, num_blocks, pg);
+  if (st != DSA_OK) return st;
+  const int64_t N = max_blocks * (int64_t)block_size;
+  if ((st = check_index_scores(q_idx, k_pool, w, scores, B, Tq, N, 0, H_I, D_I, dtype, true)) != DSA_OK) return st;
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "paged caches are built for bf16 only");
+  if (Tq > 4) return fail(DSA_ERR_UNSUPPORTED, "paged caches are built for decode shapes (Tq <= 4, got %lld)",
+                          (long long)Tq);
+  return hip_status(dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx),
+                                                  static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(w),
+                                                  scores, B, Tq, N, 0, static_cast<hipStream_t>(stream), seq_lens, 1,
+                                                  &pg),
+                    "paged index scores launch");
+}
+
+dsa_status dsa_index_scores_fp8_paged(const uint8_t* q8, const float* q_scale, const uint8_t* k8_pool,
+                                      const float* k_scale_pool, const void* w, float* scores,
+                                      const int64_t* seq_lens, const int32_t* block_table, int64_t B, int64_t Tq,
+                                      int64_t max_blocks, int32_t block_size, int64_t num_blocks, int32_t H_I,
+                                      int32_t D_I, int32_t dtype, void* stream) {
+  dsa::Paged pg;
+  dsa_status st = check_paged(block_table, max_blocks, block_size, num_blocks, pg);
+  if (st != DSA_OK) return st;
+  const int64_t N = max_blocks * (int64_t)block_size;
+  st = check_index_scores_fp8(q8, q_scale, k8_pool, k_scale_pool, w, scores, B, Tq, N, 0, H_I, D_I, dtype, true);
+  if (st != DSA_OK) return st;
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  if (Tq > 4) return fail(DSA_ERR_UNSUPPORTED, "paged caches are built for decode shapes (Tq <= 4, got %lld)",
+                          (long long)Tq);
+  return hip_status(dsa::launch_index_scores_fp8(q8, q_scale, k8_pool, k_scale_pool, static_cast<const uint16_t*>(w),
+                                                 scores, B, Tq, N, 0, static_cast<hipStream_t>(stream), seq_lens, &pg),
+                    "paged FP8 index scores launch");
+}
+
+dsa_status dsa_sparse_mla_fwd_paged(const void* q, const void* kv_pool, const int32_t* idx, const int32_t* block_table,
+                                    void* out, float* lse, int64_t B, int64_t Tq, int64_t max_blocks,
+                                    int32_t block_size, int64_t num_blocks, int32_t H, int32_t D, int32_t DV, int32_t K,
+                                    float scale, int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
+  dsa::Paged pg;
+  dsa_status st = check_paged(block_table, max_blocks, block_size, num_blocks, pg);
+  if (st != DSA_OK) return st;
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "paged caches are built for bf16 only");
+  // the gather addresses the whole pool as one sequence
+  const int64_t pool_rows = num_blocks * (int64_t)block_size;
+  st = check_mla(q, kv_pool, idx, out, lse, 1, B * Tq, pool_rows, H, D, DV, K, scale, dtype, nullptr, 0, false);
+  if (st != DSA_OK) return st;
+  if ((st = check_common(B, Tq, 1, 0, dtype)) != DSA_OK) return st;
+  if (!idx || !aligned16(idx)) return fail(DSA_ERR_INVALID_ARG, "idx must be a 16-byte aligned device pointer");
+  const size_t mla = align256(dsa::mla_workspace_bytes(B * Tq, H, DV, K, 1));
+  const size_t need = mla + align256((size_t)B * Tq * K * sizeof(int32_t));
+  if (!workspace || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "paged sparse MLA workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  return run_paged_mla(q, kv_pool, idx, reinterpret_cast<int32_t*>(ws + mla), out, lse, B, Tq, K, scale, pg, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_forward_paged(const void* q_idx, const void* k_pool, const void* w, const void* q, const void* kv_pool,
+                             void* out, float* lse, int32_t* idx_out, const int64_t* seq_lens,
+                             const int32_t* block_table, int64_t B, int64_t Tq, int64_t max_blocks,
+                             int32_t block_size, int64_t num_blocks, int32_t H_I, int32_t D_I, int32_t H, int32_t D,
+                             int32_t DV, int32_t K, float scale, int32_t dtype, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  dsa::Paged pg;
+  dsa_status st = check_paged(block_table, max_blocks, block_size, num_blocks, pg);
+  if (st != DSA_OK) return st;
+  const int64_t N = max_blocks * (int64_t)block_size;
+  if ((st = check_index_scores(q_idx, k_pool, w, nullptr, B, Tq, N, 0, H_I, D_I, dtype, false)) != DSA_OK) return st;
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "paged caches are built for bf16 only");
+  if (Tq > 4) return fail(DSA_ERR_UNSUPPORTED, "paged caches are built for decode shapes (Tq <= 4, got %lld)",
+                          (long long)Tq);
+  st = check_mla(q, kv_pool, nullptr, out, lse, 1, B * Tq, num_blocks * (int64_t)block_size, H, D, DV, K, scale,
+                 dtype, nullptr, 0, false);
+  if (st != DSA_OK) return st;
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  if (idx_out && !aligned16(idx_out)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 16-byte aligned");
+  const ForwardLayout L = forward_layout(B, Tq, N, H, DV, K, dtype);
+  const size_t need = L.total + align256((size_t)B * Tq * K * sizeof(int32_t));
+  if (!workspace || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "paged forward workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
+  int32_t* phys = reinterpret_cast<int32_t*>(ws + L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_pool),
+                                               static_cast<const uint16_t*>(w), scores, B, Tq, N, 0, s, seq_lens, 1,
+                                               &pg);
+  if (e != hipSuccess) return hip_status(e, "paged index scores launch");
+  e = dsa::launch_topk(scores, idx, B, Tq, N, 0, K, topk_ws, s, seq_lens);
+  if (e != hipSuccess) return hip_status(e, "top-k launch");
+  return run_paged_mla(q, kv_pool, idx, phys, out, lse, B, Tq, K, scale, pg, ws + L.mla, s);
+}
+
+dsa_status dsa_cache_append_paged(void* k_pool, void* kv_pool, const void* new_k_idx, const void* new_kv,
+                                  const int64_t* pos, const int32_t* block_table, int64_t B, int64_t max_blocks,
+                                  int32_t block_size, int64_t num_blocks, int32_t D_I, int32_t D, int32_t dtype,
+                                  void* stream) {
+  dsa::Paged pg;
+  dsa_status st = check_paged(block_table, max_blocks, block_size, num_blocks, pg);
+  if (st != DSA_OK) return st;
+  if (B < 1) return fail(DSA_ERR_INVALID_ARG, "B must be >= 1 (got %lld)", (long long)B);
+  if (B > kMaxGrid) return fail(DSA_ERR_INVALID_ARG, "B must be < 2^31");
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!pos) return fail(DSA_ERR_INVALID_ARG, "pos must not be null");
+  if (!aligned8(pos)) return fail(DSA_ERR_INVALID_ARG, "pos must be 8-byte aligned");
+  if ((k_pool == nullptr) != (new_k_idx == nullptr) || (kv_pool == nullptr) != (new_kv == nullptr))
+    return fail(DSA_ERR_INVALID_ARG, "a cache and its new rows must be given together");
+  if (!k_pool && !kv_pool) return fail(DSA_ERR_INVALID_ARG, "no cache to append to");
+  if ((k_pool && (!aligned16(k_pool) || !aligned16(new_k_idx))) ||
+      (kv_pool && (!aligned16(kv_pool) || !aligned16(new_kv))))
+    return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if ((k_pool && D_I < 1) || (kv_pool && D < 1)) return fail(DSA_ERR_INVALID_ARG, "row widths must be >= 1");
+  return hip_status(dsa::launch_cache_append(k_pool, kv_pool, new_k_idx, new_kv, pos, B, 0, k_pool ? D_I : 0,
+                                             kv_pool ? D : 0, dtype == DSA_BF16 ? 2 : 4,
+                                             static_cast<hipStream_t>(stream), &pg),
+                    "paged cache append launch");
 }
 
 }  // extern "C"

@@ -67,6 +67,47 @@ __device__ __forceinline__ float weighted_relu_sum(const QFrags& f, const f32x16
   return sum_halves(part);
 }
 
+// Block-table entries of one workgroup's key range for a paged cache: lane j
+// holds entries j, j + 64 and j + 128 (at most 192: the host admits blocks of
+// at least 64 keys and at most 8192 keys per workgroup).  page_row() maps a
+// wave-uniform key to its pool row.
+template <bool PAGED>
+struct PageRows {
+  int32_t tbl[3] = {0, 0, 0};
+  int64_t blk0 = 0;
+  int32_t shift = 0;
+  __device__ __forceinline__ void load(const Paged& pg, int64_t b, int64_t k_begin, int64_t k_end, int lane) {
+    if (!PAGED) return;
+    shift = pg.shift;
+    blk0 = k_begin >> shift;
+    const int64_t nent = ((k_end - 1) >> shift) - blk0 + 1;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int64_t j = lane + 64 * u;
+      if (j < nent) {
+        const int32_t v = pg.table[b * pg.max_blocks + blk0 + j];
+        tbl[u] = (uint32_t)v < (uint32_t)pg.num_blocks ? v : 0;
+      }
+    }
+  }
+  __device__ __forceinline__ int64_t row(int64_t key) const {
+    if (!PAGED) return key;
+    const int64_t j = (key >> shift) - blk0;
+    const int32_t v = j < 64 ? tbl[0] : (j < 128 ? tbl[1] : tbl[2]);
+    const int32_t e = __builtin_amdgcn_readlane(v, (int)(j & 63));
+    return ((int64_t)e << shift) | (key & ((1 << shift) - 1));
+  }
+  // per-lane form (any key of the range; all lanes of the wave take part)
+  __device__ __forceinline__ int64_t row_any(int64_t key) const {
+    if (!PAGED) return key;
+    const int64_t j = (key >> shift) - blk0;
+    const int l = (int)(j & 63);
+    const int32_t v0 = __shfl(tbl[0], l), v1 = __shfl(tbl[1], l), v2 = __shfl(tbl[2], l);
+    const int32_t e = j < 64 ? v0 : (j < 128 ? v1 : v2);
+    return ((int64_t)e << shift) | (key & ((1 << shift) - 1));
+  }
+};
+
 // Decode kernel with the key tiles staged through LDS.  A wave owns a ring
 // of NBUF tiles of 32 keys (8 KiB) in LDS and keeps NBUF-1 of them in flight
 // with direct-to-LDS loads.  Each load instruction fetches 1 KiB of
@@ -83,10 +124,10 @@ __device__ __forceinline__ float weighted_relu_sum(const QFrags& f, const f32x16
 // chunk c of tile key r sits at slot 16r + (c ^ (r & 15)).  The operand read
 // of k-step s (chunk 8*half + s of key col) then spreads every 16 lanes over
 // all 64 banks.
-template <int WAVES, int NBUF, int SCAP>
+template <int WAVES, int NBUF, int SCAP, bool PAGED = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
-    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, Vis vis, int64_t keys_per_wg) {
+    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, Vis vis, int64_t keys_per_wg, Paged pg) {
   constexpr int TILE_BYTES = 32 * ID * 2;
   static_assert(NBUF >= 2 && NBUF <= 5, "the vmcnt waits below cover up to four tiles in flight");
   static_assert(WAVES * NBUF * TILE_BYTES + SCAP * 4 <= 160 * 1024, "LDS budget");
@@ -104,7 +145,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
   const int total_tiles = (int)((k_end - k_begin + 31) / 32);
   const int nt = total_tiles > wave ? (total_tiles - wave + WAVES - 1) / WAVES : 0;
 
-  const uint8_t* kb = reinterpret_cast<const uint8_t*>(k_idx + b * N * ID);
+  // a paged cache: tiles of 32 keys never cross a block (blocks hold a multiple of 32 keys)
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(k_idx + (PAGED ? 0 : b * N * ID));
+  PageRows<PAGED> pr;
+  pr.load(pg, b, k_begin, k_end, lane);
   const uint32_t ring = lds_address(&kt[wave][0][0]);
   // per-lane part of the source offset of load u, for u & 3 (the XOR term repeats every 4 loads)
   const int kk = lane >> 4, jj = lane & 15;
@@ -115,7 +159,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
   auto dma_tile = [&](int it) {
     const int64_t key0 = key0_of(it);
     const uint32_t dst = ring + (uint32_t)((it % NBUF) * TILE_BYTES);
-    if (key0 + 32 <= N) {
+    if (PAGED) {
+      const int64_t r0 = pr.row(key0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dma16(kb + (r0 + 4 * u) * (ID * 2), voff[u & 3], dst + 1024u * u);
+    } else if (key0 + 32 <= N) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) dma16(kb + (key0 + 4 * u) * (ID * 2), voff[u & 3], dst + 1024u * u);
     } else {
@@ -405,11 +453,11 @@ __device__ __forceinline__ void load_query_fp8(QFrags& f, const uint8_t* __restr
 // (L & 7) ^ (L >> 3) of key L >> 3 and lands at slot L, so chunk c of tile key
 // r sits at slot 8r + (c ^ (r & 7)).  The key scales are applied when the
 // workgroup's scores leave LDS.
-template <int WAVES, int NBUF, int SCAP>
+template <int WAVES, int NBUF, int SCAP, bool PAGED = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const uint16_t* __restrict__ w, float* __restrict__ scores, int64_t Tq, int64_t N,
-    int64_t q_pos0, Vis vis, int64_t keys_per_wg) {
+    int64_t q_pos0, Vis vis, int64_t keys_per_wg, Paged pg) {
   constexpr int TILE_BYTES = 32 * ID;
   static_assert(NBUF >= 2 && NBUF <= 8, "the vmcnt waits below cover up to seven tiles in flight");
   static_assert(WAVES * NBUF * TILE_BYTES + SCAP * 4 <= 160 * 1024, "LDS budget");
@@ -427,14 +475,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
   const int total_tiles = (int)((k_end - k_begin + 31) / 32);
   const int nt = total_tiles > wave ? (total_tiles - wave + WAVES - 1) / WAVES : 0;
 
-  const uint8_t* kb = k8 + b * N * ID;
+  const uint8_t* kb = k8 + (PAGED ? 0 : b * N * ID);
+  PageRows<PAGED> pr;
+  pr.load(pg, b, k_begin, k_end, lane);
   const uint32_t ring = lds_address(&kt[wave][0][0]);
   const uint32_t voff = 128u * (uint32_t)(lane >> 3) + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
   auto key0_of = [&](int it) { return k_begin + 32 * (int64_t)(it * WAVES + wave); };
   auto dma_tile = [&](int it) {
     const int64_t key0 = key0_of(it);
     const uint32_t dst = ring + (uint32_t)((it % NBUF) * TILE_BYTES);
-    if (key0 + 32 <= N) {
+    if (PAGED) {
+      const int64_t r0 = pr.row(key0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dma16(kb + (r0 + 8 * u) * ID, voff, dst + 1024u * u);
+    } else if (key0 + 32 <= N) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) dma16(kb + (key0 + 8 * u) * ID, voff, dst + 1024u * u);
     } else {
@@ -487,6 +541,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
   __syncthreads();
   const int n = (int)(k_end - k_begin);
   float* dst = scores + row * N + k_begin;
+  if (PAGED) {
+    // key scales through the block table: four consecutive keys share a block
+    for (int i0 = 0; i0 < n; i0 += 4 * WAVES * 64) {
+      const int i = i0 + 4 * (int)threadIdx.x;
+      const int64_t r = pr.row_any(k_begin + min(i, n - 1));  // every lane takes part in the exchange
+      for (int e = 0; e < 4; ++e)
+        if (i + e < n) dst[i + e] = sl[i + e] * ks[r + e];
+    }
+    return;
+  }
   const float* ksr = ks + b * N + k_begin;
   if (((row * N) & 3) == 0 && ((b * N) & 3) == 0) {
     for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * WAVES * 64) {
@@ -506,7 +570,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
 
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                                    hipStream_t stream, const int64_t* seq_lens, int m) {
+                                    hipStream_t stream, const int64_t* seq_lens, int m, const Paged* pg) {
   const Vis vis{seq_lens, m};
   // longest visible row: with per-sequence lengths only N is known on the host
   const int64_t nmax = seq_lens != nullptr ? N : min(N, (q_pos0 + Tq) / m);
@@ -520,9 +584,14 @@ hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx
     if (kpw > SCAP) kpw = SCAP;
     if (kpw < 32 * WAVES) kpw = 32 * WAVES;
     dim3 grid((unsigned)((nmax + kpw - 1) / kpw), (unsigned)Tq, (unsigned)B);
-    hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w,
-                       scores, Tq, N, q_pos0, vis, kpw);
+    if (pg != nullptr)
+      hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP, true>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx,
+                         w, scores, Tq, N, q_pos0, vis, kpw, *pg);
+    else
+      hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w,
+                         scores, Tq, N, q_pos0, vis, kpw, Paged{});
   } else {
+    if (pg != nullptr) return hipErrorInvalidValue;  // paged caches: decode shapes only
     constexpr int WAVES = 8;
     const int64_t nqb = (Tq + WAVES - 1) / WAVES;
     dim3 grid((unsigned)nqb, (unsigned)B);
@@ -553,9 +622,9 @@ hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* codes, float* scales,
 
 hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
                                    const uint16_t* w, float* scores, int64_t B, int64_t Tq, int64_t N,
-                                   int64_t q_pos0, hipStream_t stream) {
-  const Vis vis{nullptr, 1};
-  const int64_t nmax = min(N, q_pos0 + Tq);
+                                   int64_t q_pos0, hipStream_t stream, const int64_t* seq_lens, const Paged* pg) {
+  const Vis vis{seq_lens, 1};
+  const int64_t nmax = seq_lens != nullptr ? N : min(N, q_pos0 + Tq);
   if (nmax <= 0) return hipSuccess;  // no query sees a key
   // About eight workgroups per compute unit over the launch, two resident at
   // a time (72 KiB of LDS each), three 4 KiB tiles in flight per wave: the
@@ -567,8 +636,12 @@ hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uin
   if (kpw > SCAP) kpw = SCAP;
   if (kpw < 32 * WAVES) kpw = 32 * WAVES;
   dim3 grid((unsigned)((nmax + kpw - 1) / kpw), (unsigned)Tq, (unsigned)B);
-  hipLaunchKernelGGL((indexer_dma_fp8<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q8, qs, k8, ks, w, scores,
-                     Tq, N, q_pos0, vis, kpw);
+  if (pg != nullptr)
+    hipLaunchKernelGGL((indexer_dma_fp8<WAVES, NBUF, SCAP, true>), grid, dim3(WAVES * 64), 0, stream, q8, qs, k8, ks, w,
+                       scores, Tq, N, q_pos0, vis, kpw, *pg);
+  else
+    hipLaunchKernelGGL((indexer_dma_fp8<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q8, qs, k8, ks, w,
+                       scores, Tq, N, q_pos0, vis, kpw, Paged{});
   return hipGetLastError();
 }
 

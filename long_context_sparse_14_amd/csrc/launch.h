@@ -7,13 +7,27 @@
 
 namespace dsa {
 
+// A paged cache: rows live in a pool of num_blocks blocks of 2^shift rows;
+// row r of sequence b is pool row table[b * max_blocks + (r >> shift)] *
+// 2^shift + (r & (2^shift - 1)).  Table entries outside [0, num_blocks) are
+// read as block 0 (a caller error that must not become a wild access).
+struct Paged {
+  const int32_t* table;
+  int64_t max_blocks;
+  int32_t shift;
+  int32_t num_blocks;
+};
+
 // seq_lens (device, [B], may be null): per-sequence lengths in tokens; when
 // given, the queries of sequence b sit at positions seq_lens[b] - Tq + t and
 // q_pos0 is ignored.  m: compression rate of the key axis (row w becomes
 // visible to the query at position p when w < (p + 1) / m; m = 1: causal).
+// pg (may be null): the key cache is a paged pool (decode shapes, Tq <= 4;
+// seq_lens required); N is then the logical capacity max_blocks << shift.
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                                    hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1);
+                                    hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1,
+                                    const Paged* pg = nullptr);
 hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const float* w, float* scores,
                                    int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int H_I, int D_I,
                                    hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1);
@@ -24,7 +38,8 @@ hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const
 hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* codes, float* scales, int64_t R, hipStream_t stream);
 hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
                                    const uint16_t* w, float* scores, int64_t B, int64_t Tq, int64_t N,
-                                   int64_t q_pos0, hipStream_t stream);
+                                   int64_t q_pos0, hipStream_t stream, const int64_t* seq_lens = nullptr,
+                                   const Paged* pg = nullptr);
 
 size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
 hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
@@ -34,8 +49,13 @@ hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq,
 // Writes row pos[b] of each sequence's caches (rows of D_I and D elements of
 // esize bytes); entries of pos outside [0, N) are skipped.  Either cache may
 // be null.
+// pg (may be null): the caches are pools and pos[b] is a logical row.
 hipError_t launch_cache_append(void* k_idx, void* kv, const void* new_k_idx, const void* new_kv, const int64_t* pos,
-                               int64_t B, int64_t N, int D_I, int D, int esize, hipStream_t stream);
+                               int64_t B, int64_t N, int D_I, int D, int esize, hipStream_t stream,
+                               const Paged* pg = nullptr);
+// Logical key indices idx [B, Tq, K] -> pool rows in out (same shape).
+hipError_t launch_page_translate(const int32_t* idx, int32_t* out, int64_t B, int64_t Tq, int K, const Paged& pg,
+                                 hipStream_t stream);
 
 int mla_num_splits(int64_t rows, int K);
 size_t mla_workspace_bytes(int64_t rows, int H, int DV, int K, int is_bf16);

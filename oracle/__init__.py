@@ -59,7 +59,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "as_f64", "bf16_bits_to_f64", "n_valid_keys", "index_scores", "index_scores_rows",
+    "as_f64", "bf16_bits_to_f64", "n_valid_keys", "paged_gather", "index_scores", "index_scores_rows",
     "topk_row", "topk", "sparse_mla", "sparse_mla_rows", "dense_masked_mla", "forward_rows",
     "mla_naive_rows", "mla_absorb_query", "mla_output_projection", "linear", "fwht_f32", "e4m3_decode",
     "e4m3_encode_rne", "pow2_scale_exp", "quantize_fp8_rows", "index_scores_fp8_rows", "sylvester_hadamard",
@@ -86,6 +86,20 @@ def n_valid_keys(t: int, q_pos0: int, N: int, m: int = 1) -> int:
     """
     p1 = q_pos0 + t + 1
     return 0 if p1 <= 0 else min(N, p1 // m)
+
+
+def paged_gather(pool: np.ndarray, table_row, block_size: int, n_rows: int) -> np.ndarray:
+    """Rows 0..n_rows-1 of one sequence of a paged cache as a contiguous array.
+
+    A paged cache layer keeps its rows in a pool of blocks of block_size rows
+    and one block table per sequence (reading of the cache layers named in
+    the DeepSeek-V3.2 documentation, "DeepSeek Sparse Attention (DSA)"):
+    logical row r is pool row table_row[r // block_size] * block_size +
+    r % block_size.
+    """
+    table_row = np.asarray(table_row, dtype=np.int64)
+    r = np.arange(n_rows)
+    return np.asarray(pool)[table_row[r // block_size] * block_size + r % block_size]
 
 
 # ----------------------------------------------------------------------------

@@ -518,3 +518,23 @@ def pin_fp8_scores_near_bf16(quantize_fp8_rows, index_scores_fp8_rows, index_sco
         if not np.all(np.abs(got[t] - ref[t]) <= bound + 1e-9):
             return False
     return True
+
+
+# ------------------------------------------------------------------ paging ---
+
+def pin_paged_gather(paged_gather) -> bool:
+    """Scattering a contiguous cache into a pool by the table (written here row by
+    row) and gathering it back returns the cache; an identity table reads the
+    pool's prefix."""
+    r = _rng(61)
+    bs, n, width = 4, 13, 3
+    blocks = -(-n // bs)
+    table = r.permutation(10)[:blocks]
+    x = r.standard_normal((n, width))
+    pool = np.full((10 * bs, width), np.nan)
+    for row in range(n):
+        pool[table[row // bs] * bs + row % bs] = x[row]
+    got = _safe(paged_gather, pool, table, bs, n)
+    ident = _safe(paged_gather, pool, np.arange(10), bs, 10 * bs)
+    return got is not None and np.array_equal(got, x) and ident is not None and \
+        np.array_equal(ident, pool, equal_nan=True)

@@ -1,0 +1,181 @@
+"""GPU parity for paged caches (block tables).
+
+A paged call must equal the static-cache call on the caches gathered
+through the tables.  Each case scatters per-sequence caches into a pool in a
+random block order (unused table entries hold -1), then checks:
+
+* the paged scores against the oracle on the gathered caches (bit-exact,
+  integer-valued indexer inputs) and against the GPU's varlen scores;
+* the paged sparse MLA and the paged forward against the GPU's static-cache
+  results, bit for bit (same kernels, same gather order), and against the
+  oracle within the bf16 tolerance;
+* the FP8 paged scores against the FP8 static-cache scores, bit for bit;
+* the paged append: bytes in place, and append-then-attend equals attend
+  on a pool built with that row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_close, assert_lse_close, causal_scores_equal, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.WORKLOADS
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _dsa():
+    import long_context_sparse_14_amd as dsa
+    dsa.library()
+    return dsa
+
+
+def _layout(lens, bs, max_blocks, spare, seed):
+    """A random block assignment: table [B, max_blocks] (-1 where unused), pool size."""
+    rng = np.random.default_rng(seed)
+    need = [-(-n // bs) for n in lens]
+    num_blocks = sum(need) + spare
+    perm = rng.permutation(num_blocks)
+    table = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    k = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[k:k + nb]
+        k += nb
+    return table, num_blocks
+
+
+def _scatter(cache, table, lens, bs, num_blocks):
+    """Pool [num_blocks * bs, width] holding rows 0..lens[b]-1 of each sequence of cache [B, N, width]."""
+    width = cache.shape[-1]
+    pool = np.zeros((num_blocks * bs, width), dtype=cache.dtype)
+    for b, n in enumerate(lens):
+        r = np.arange(n)
+        pool[table[b, r // bs] * bs + r % bs] = cache[b, :n]
+    return pool
+
+
+def _case(lens, bs, K, seed=0):
+    B = len(lens)
+    N = max(lens)
+    max_blocks = -(-N // bs) + 2
+    wl = WL["dsa_decode_b32_128k"].replace(B=B, N=max_blocks * bs, q_pos0=0, K=K)
+    x = synth.make_inputs(wl, seed)
+    table, num_blocks = _layout(lens, bs, max_blocks, spare=5, seed=seed + 1)
+    pools = {name: _scatter(x[name], table, lens, bs, num_blocks) for name in ("k_idx", "kv")}
+    return wl, x, table, num_blocks, pools
+
+
+def _lens(v):
+    return torch.tensor(v, dtype=torch.int64, device="cuda")
+
+
+@pytest.mark.parametrize("lens,bs", [([5000, 1234, 300], 64), ([20000, 19000], 256), ([700, 64, 65], 128)])
+def test_index_scores_paged(lens, bs):
+    dsa = _dsa()
+    wl, x, table, num_blocks, pools = _case(lens, bs, 64)
+    scores = dsa.index_scores_paged(dev(x["q_idx"]), dev(pools["k_idx"]), dev(x["w"]), _lens(lens),
+                                    torch.from_numpy(table).cuda(), bs).cpu().numpy()
+    static = dsa.index_scores_varlen(dev(x["q_idx"]), dev(x["k_idx"]), dev(x["w"]), _lens(lens)).cpu().numpy()
+    for b, n in enumerate(lens):
+        k_b = oracle.paged_gather(pools["k_idx"], table[b], bs, n)
+        ref = oracle.index_scores_rows(x["q_idx"][b], k_b, x["w"][b], [0], n - 1)
+        causal_scores_equal(scores[b], ref, [0], f"paged scores b={b}")
+        assert np.array_equal(scores[b, 0, :n], static[b, 0, :n]), f"paged vs static b={b}"
+
+
+@pytest.mark.parametrize("lens,bs,K", [([5000, 1234, 300], 64, 2048), ([20000, 19000], 256, 2048)])
+def test_forward_paged(lens, bs, K):
+    dsa = _dsa()
+    wl, x, table, num_blocks, pools = _case(lens, bs, K, seed=2)
+    tt = torch.from_numpy(table).cuda()
+    d = {k: dev(v) for k, v in x.items()}
+    out, lse, idx = dsa.forward_paged(d["q_idx"], dev(pools["k_idx"]), d["w"], d["q"], dev(pools["kv"]), K, wl.scale,
+                                      _lens(lens), tt, bs, return_idx=True)
+    out_s, lse_s, idx_s = dsa.forward_varlen(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], K, wl.scale,
+                                             _lens(lens), return_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_s), "paged vs static indices"
+    assert torch.equal(out, out_s) and torch.equal(lse, lse_s), "paged vs static attention"
+    idx_h, out_h, lse_h = idx.cpu().numpy(), host64(out), host64(lse)
+    for b, n in enumerate(lens):
+        kv_b = oracle.as_f64(oracle.paged_gather(pools["kv"], table[b], bs, n))
+        k_b = oracle.paged_gather(pools["k_idx"], table[b], bs, n)
+        ref = oracle.forward_rows(x["q_idx"][b], k_b, x["w"][b], x["q"][b], kv_b, [0], n - 1, K, wl.scale, wl.DV)[0]
+        assert np.array_equal(idx_h[b, 0], ref["idx"]), f"indices b={b}"
+        assert_close(out_h[b, 0], ref["o"], "bf16", f"attention b={b}")
+        assert_lse_close(lse_h[b, 0], ref["lse"], f"lse b={b}")
+
+
+def test_sparse_mla_paged_given_indices():
+    """Caller-given logical indices (with -1 padding) through the tables."""
+    dsa = _dsa()
+    lens, bs, K = [3000, 900], 64, 512
+    wl, x, table, num_blocks, pools = _case(lens, bs, K, seed=4)
+    rng = np.random.default_rng(5)
+    idx = np.full((2, 1, K), -1, dtype=np.int32)
+    for b, n in enumerate(lens):
+        m = K - 37 * b
+        idx[b, 0, :m] = rng.choice(n, size=m, replace=False)
+    ti = torch.from_numpy(idx).cuda()
+    out, lse = dsa.sparse_mla_paged(dev(x["q"]), dev(pools["kv"]), ti, torch.from_numpy(table).cuda(), bs, wl.scale)
+    out_s, lse_s = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), ti, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_s) and torch.equal(lse, lse_s), "paged vs static attention"
+    for b in range(2):
+        o, l = oracle.sparse_mla_rows(x["q"][b, 0], oracle.as_f64(x["kv"][b]), idx[b, 0], wl.scale, wl.DV)
+        assert_close(host64(out[b, 0]), o, "bf16", f"attention b={b}")
+        assert_lse_close(host64(lse[b, 0]), l, f"lse b={b}")
+
+
+def test_index_scores_fp8_paged():
+    dsa = _dsa()
+    lens, bs = [6000, 2500, 130], 64
+    wl, x, table, num_blocks, pools = _case(lens, bs, 64, seed=6)
+    k8, ks = oracle.quantize_fp8_rows(x["k_idx"])                 # [B, N, 128], [B, N]
+    q8, qs = oracle.quantize_fp8_rows(x["q_idx"])
+    k8_pool = _scatter(k8, table, lens, bs, num_blocks)
+    ks_pool = _scatter(ks[..., None], table, lens, bs, num_blocks)[:, 0].copy()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    paged = dsa.index_scores_fp8_paged(t(q8), t(qs), t(k8_pool), t(ks_pool), dev(x["w"]), _lens(lens),
+                                       t(table), bs).cpu().numpy()
+    for b, n in enumerate(lens):
+        static = dsa.index_scores_fp8(t(q8[b:b + 1]), t(qs[b:b + 1]), t(k8[b:b + 1, :n]), t(ks[b:b + 1, :n]),
+                                      dev(x["w"][b:b + 1]), n - 1).cpu().numpy()
+        assert np.array_equal(paged[b, 0, :n], static[0, 0]), f"FP8 paged vs static b={b}"
+
+
+def test_cache_append_paged_then_attend():
+    dsa = _dsa()
+    lens, bs, K = [4000, 1000], 64, 2048
+    wl, x, table, num_blocks, pools = _case(lens, bs, K, seed=8)
+    pre = [n - 1 for n in lens]                                    # the last row arrives by append
+    tt = torch.from_numpy(table).cuda()
+    kp, vp = dev(pools["k_idx"]), dev(pools["kv"])
+    full = (dsa.forward_paged(dev(x["q_idx"]), kp, dev(x["w"]), dev(x["q"]), vp, K, wl.scale, _lens(lens), tt, bs,
+                              return_idx=True))
+    torch.cuda.synchronize()
+    full = [t.clone() for t in full]
+    # wipe the last row of each sequence in the pool, then append it back
+    rows = [table[b, p // bs] * bs + p % bs for b, p in enumerate(pre)]
+    for r in rows:
+        kp[r].zero_()
+        vp[r].zero_()
+    new_k = torch.stack([dev(x["k_idx"][b, p]) for b, p in enumerate(pre)])
+    new_kv = torch.stack([dev(x["kv"][b, p]) for b, p in enumerate(pre)])
+    dsa.cache_append_paged(kp, vp, new_k, new_kv, _lens(pre), tt, bs)
+    torch.cuda.synchronize()
+    assert torch.equal(kp.cpu(), dev(pools["k_idx"]).cpu()) and torch.equal(vp.cpu(), dev(pools["kv"]).cpu())
+    again = dsa.forward_paged(dev(x["q_idx"]), kp, dev(x["w"]), dev(x["q"]), vp, K, wl.scale, _lens(lens), tt, bs,
+                              return_idx=True)
+    torch.cuda.synchronize()
+    for a, b_ in zip(full, again):
+        assert torch.equal(a, b_)

@@ -366,3 +366,15 @@ def test_fp8_score_pin_catches_planted_mistakes():
     for mut in (no_div, no_key_scale):
         assert not pins.pin_fp8_scores_near_bf16(oracle.quantize_fp8_rows, mut, oracle.index_scores_rows,
                                                  oracle.fwht_f32, oracle.e4m3_decode)
+
+
+def test_paged_gather():
+    assert pins.pin_paged_gather(oracle.paged_gather)
+
+
+def test_paged_gather_pin_catches_planted_mistake():
+    def swapped(pool, table_row, bs, n):
+        t = np.asarray(table_row)
+        r = np.arange(n)
+        return np.asarray(pool)[t[r % len(t)] * bs + r // len(t)]
+    assert not pins.pin_paged_gather(swapped)
