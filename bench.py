@@ -13,6 +13,8 @@ of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--fp8-indexer]
   python bench.py --calib-copy     (plain 1 GiB device copy, for counter scaling)
+  python bench.py --next projections|paged|compressed
+                                   (the calls built beside the path, timed with HIP events)
   python bench.py --record-traffic --workload NAME --pmc-fetch F.csv --pmc-write W.csv
                   --calib-fetch CF.csv --calib-write CW.csv --commands "..."
                                    (store the dominant kernel's HBM bytes per launch)
@@ -50,6 +52,8 @@ def _parse():
                     help="decode workloads: the FP8 indexer (key cache held as E4M3 codes; each step quantises "
                          "its queries, then scores)")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--next", choices=["projections", "paged", "compressed"],
+                    help="time the calls built beside the path (one JSON line; not the headline)")
     ap.add_argument("--record-traffic", action="store_true",
                     help="store the dominant kernel's HBM traffic from four rocprofv3 -f csv counter files")
     ap.add_argument("--pmc-fetch")
@@ -267,6 +271,116 @@ def cpu_baseline_fp8(wl, x, budget_s: float, max_seqs: int = 4):
                       f"each sequence's key cache quantised beforehand, untimed), {timed:.1f} s"}
 
 
+def bench_next(args):
+    """Times the calls built beside the path, each with HIP events on the launch
+    stream over back-to-back launches of prebuilt C-ABI argument lists."""
+    import torch
+
+    import long_context_sparse_14_amd as dsa
+
+    lib = dsa.library()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    bf = torch.bfloat16
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    reps = max(5, args.steps)
+
+    def rnd(*shape, sc=1.0):
+        return (torch.randn(*shape, device="cuda", generator=g) * sc).to(bf)
+
+    def ints(lo, hi, *shape):
+        return torch.randint(lo, hi + 1, shape, device="cuda", generator=g).to(bf)
+
+    def timed(fn, a):
+        def once():
+            rc = fn(*a)
+            if rc != 0:
+                raise RuntimeError(lib.dsa_last_error().decode())
+        for _ in range(3):
+            once()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            once()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us per call
+
+    P = lambda t: t.data_ptr() if t is not None else None
+    rows = []
+    if args.next == "projections":
+        H = 128
+        w_uk, w_uv = rnd(H, 128, 512, sc=1 / 16), rnd(H, 128, 512, sc=1 / 16)
+        for M in (32, 16384):
+            q, ol = rnd(M, H, 192), rnd(M, H, 512)
+            ql = torch.empty(M, H, 576, dtype=bf, device="cuda")
+            o = torch.empty(M, H, 128, dtype=bf, device="cuda")
+            fl = 2.0 * M * H * 128 * 512
+            us = timed(lib.dsa_mla_absorb_q, (P(q), P(w_uk), P(ql), M, H, 128, 64, 512, dsa.DSA_BF16, sp))
+            nb = (w_uk.numel() + q.numel() + ql.numel()) * 2
+            rows.append({"call": "dsa_mla_absorb_q", "M": M, "heads": H, "us": round(us, 2),
+                         "GB_per_s": round(nb / us / 1e3, 1), "TFLOP_per_s": round(fl / us / 1e6, 1)})
+            us = timed(lib.dsa_mla_out_proj, (P(ol), P(w_uv), P(o), M, H, 512, 128, dsa.DSA_BF16, sp))
+            nb = (w_uv.numel() + ol.numel() + o.numel()) * 2
+            rows.append({"call": "dsa_mla_out_proj", "M": M, "heads": H, "us": round(us, 2),
+                         "GB_per_s": round(nb / us / 1e3, 1), "TFLOP_per_s": round(fl / us / 1e6, 1)})
+            x, wq = rnd(M, 1536), rnd(8192, 1536, sc=1 / 32)
+            y = torch.empty(M, 8192, dtype=bf, device="cuda")
+            us = timed(lib.dsa_linear, (P(x), P(wq), P(y), M, 8192, 1536, dsa.DSA_BF16, sp))
+            nb = (x.numel() + wq.numel() + y.numel()) * 2
+            rows.append({"call": "dsa_linear (wq_b)", "M": M, "N": 8192, "K": 1536, "us": round(us, 2),
+                         "GB_per_s": round(nb / us / 1e3, 1), "TFLOP_per_s": round(2.0 * M * 8192 * 1536 / us / 1e6, 1)})
+    elif args.next == "paged":
+        B, N, K, bs = 28, 131072, 2048, 64
+        q_idx, k_idx = ints(-4, 4, B, 1, 64, 128), ints(-4, 4, B, N, 128)
+        w = torch.pow(2.0, -torch.randint(0, 5, (B, 1, 64), device="cuda", generator=g).float()).to(bf)
+        q, kv = rnd(B, 1, 128, 576), rnd(B, N, 576)
+        lens = torch.full((B,), N, dtype=torch.int64, device="cuda")
+        mb = N // bs
+        table = torch.randperm(B * mb, device="cuda", generator=g).to(torch.int32).view(B, mb).contiguous()
+        prow = (table.long()[:, :, None] * bs + torch.arange(bs, device="cuda")).reshape(-1)
+        k_pool = torch.empty(B * N, 128, dtype=bf, device="cuda")
+        kv_pool = torch.empty(B * N, 576, dtype=bf, device="cuda")
+        k_pool[prow] = k_idx.reshape(-1, 128)
+        kv_pool[prow] = kv.reshape(-1, 576)
+        out = torch.empty(B, 1, 128, 512, dtype=bf, device="cuda")
+        lse = torch.empty(B, 1, 128, dtype=torch.float32, device="cuda")
+        wsp = torch.empty(lib.dsa_paged_workspace_size(B, 1, mb, bs, 128, 512, K, dsa.DSA_BF16), dtype=torch.uint8,
+                          device="cuda")
+        wss = torch.empty(lib.dsa_forward_workspace_size(B, 1, N, 128, 512, K, dsa.DSA_BF16), dtype=torch.uint8,
+                          device="cuda")
+        sc = 1.0 / 192 ** 0.5
+        us_s = timed(lib.dsa_forward_varlen, (P(q_idx), P(k_idx), P(w), P(q), P(kv), P(out), P(lse), None, P(lens), B,
+                                              1, N, 64, 128, 128, 576, 512, K, sc, dsa.DSA_BF16, P(wss), wss.numel(),
+                                              sp))
+        us_p = timed(lib.dsa_forward_paged, (P(q_idx), P(k_pool), P(w), P(q), P(kv_pool), P(out), P(lse), None, P(lens),
+                                             P(table), B, 1, mb, bs, B * mb, 64, 128, 128, 576, 512, K, sc,
+                                             dsa.DSA_BF16, P(wsp), wsp.numel(), sp))
+        rows.append({"call": "dsa_forward_varlen (static caches)", "batch": B, "context": N, "us": round(us_s, 2),
+                     "queries_per_s": round(B / us_s * 1e6, 1)})
+        rows.append({"call": "dsa_forward_paged", "batch": B, "context": N, "block_size": bs, "us": round(us_p, 2),
+                     "queries_per_s": round(B / us_p * 1e6, 1)})
+    else:
+        # V4 CSA: 128K tokens compressed at m = 4 into 32768 entries, index_topk = 512
+        B, T, m, K = 32, 131072, 4, 512
+        N = T // m
+        q_idx, k_idx = ints(-4, 4, B, 1, 64, 128), ints(-4, 4, B, N, 128)
+        w = torch.pow(2.0, -torch.randint(0, 5, (B, 1, 64), device="cuda", generator=g).float()).to(bf)
+        scores = torch.empty(B, 1, N, dtype=torch.float32, device="cuda")
+        idx = torch.empty(B, 1, K, dtype=torch.int32, device="cuda")
+        tws = torch.empty(max(256, lib.dsa_topk_workspace_size(B, 1, N, K)), dtype=torch.uint8, device="cuda")
+        us_i = timed(lib.dsa_index_scores_compressed, (P(q_idx), P(k_idx), P(w), P(scores), B, 1, N, T - 1, m, 64, 128,
+                                                       dsa.DSA_BF16, sp))
+        us_t = timed(lib.dsa_topk_compressed, (P(scores), P(idx), B, 1, N, T - 1, m, K, P(tws), tws.numel(), sp))
+        nb = B * N * 128 * 2 + B * N * 4
+        rows.append({"call": "dsa_index_scores_compressed", "batch": B, "tokens": T, "rate_m": m, "entries": N,
+                     "us": round(us_i, 2), "GB_per_s": round(nb / us_i / 1e3, 1)})
+        rows.append({"call": "dsa_topk_compressed", "batch": B, "entries": N, "K": K, "us": round(us_t, 2)})
+    print(json.dumps({"next": args.next, "launches_per_call": reps, "calls": rows}), flush=True)
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -281,6 +395,9 @@ def main():
 
     if args.calib_copy:
         calib_copy()
+        return
+    if args.next:
+        bench_next(args)
         return
 
     import long_context_sparse_14_amd as dsa

@@ -576,10 +576,13 @@ hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx
   const int64_t nmax = seq_lens != nullptr ? N : min(N, (q_pos0 + Tq) / m);
   if (nmax <= 0) return hipSuccess;  // no query sees a row
   if (Tq <= 4) {
-    // Roughly two workgroups per compute unit over the launch (one fits at a
-    // time: it holds all of LDS), whole tiles for every wave, at most SCAP keys.
+    // Two rounds of workgroups per compute unit (one fits at a time: it holds
+    // all of LDS): at most 512 workgroups, split evenly over the rows so that
+    // no third, partly filled round appears; whole tiles for every wave, at
+    // most SCAP keys.
     constexpr int WAVES = 4, NBUF = 4, SCAP = 8192;
-    int64_t kpw = (nmax * B * Tq + 511) / 512;
+    const int64_t per_row = 512 / (B * Tq) > 1 ? 512 / (B * Tq) : 1;
+    int64_t kpw = (nmax + per_row - 1) / per_row;
     kpw = (kpw + 32 * WAVES - 1) / (32 * WAVES) * (32 * WAVES);
     if (kpw > SCAP) kpw = SCAP;
     if (kpw < 32 * WAVES) kpw = 32 * WAVES;
@@ -631,7 +634,8 @@ hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uin
   // best of a sweep over waves (2, 4, 8), ring depth (2..8) and keys per
   // workgroup (1024..8192) at the 128K decode batch.
   constexpr int WAVES = 4, NBUF = 4, SCAP = 2048;
-  int64_t kpw = (nmax * B * Tq + 2047) / 2048;
+  const int64_t per_row = 2048 / (B * Tq) > 1 ? 2048 / (B * Tq) : 1;  // as many whole rounds
+  int64_t kpw = (nmax + per_row - 1) / per_row;
   kpw = (kpw + 32 * WAVES - 1) / (32 * WAVES) * (32 * WAVES);
   if (kpw > SCAP) kpw = SCAP;
   if (kpw < 32 * WAVES) kpw = 32 * WAVES;

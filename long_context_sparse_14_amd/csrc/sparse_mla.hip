@@ -683,12 +683,18 @@ __global__ __launch_bounds__(64) void sparse_mla_f32_kernel(const float* __restr
 
 int mla_num_splits(int64_t rows, int K) {
   const int tiles = (K + NT - 1) / NT;
-  int64_t want = (256 + rows - 1) / rows;  // about one workgroup per compute unit
+  // At most one workgroup per compute unit (256) over the launch: a second,
+  // partly filled round of workgroups would cost as much as the first.
+  int64_t want = 256 / rows;
+  if (want < 1) want = 1;
   if (want > 32) want = 32;
   if (want > tiles) want = tiles;
   // one workgroup stages at most MAX_SPLIT_KEYS indices
   const int64_t need = (K + MAX_SPLIT_KEYS - 1) / MAX_SPLIT_KEYS;
   if (want < need) want = need;
+  // drop splits that whole-tile shares would leave empty
+  const int64_t per = (tiles + want - 1) / want;
+  want = (tiles + per - 1) / per;
   return want < 1 ? 1 : (int)want;
 }
 
