@@ -9,7 +9,10 @@ sequence, 128-head MLA over its 2048 selected latent rows).
 Prints one JSON line: throughput in queries/s over the timed steps (inputs
 resident in HBM), the roofline position of the dominant kernel measured with
 HIP events on the launch stream, and the CPU oracle timed on a bounded sample
-of the same workload.
+of the same workload.  Timed steps call the fused entry point where the
+workload has one; every tenth step runs the stages as separate calls with
+events between them, which gives each kernel's duration inside the timed
+region.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--fp8-indexer]
   python bench.py --calib-copy     (plain 1 GiB device copy, for counter scaling)
@@ -46,8 +49,8 @@ def _parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--fused", action="store_true",
-                    help="time the single dsa_forward call (no per-stage events)")
+    ap.add_argument("--staged", action="store_true",
+                    help="run every timed step as separate stage calls with HIP events between them")
     ap.add_argument("--fp8-indexer", action="store_true",
                     help="decode workloads: the FP8 indexer (key cache held as E4M3 codes; each step quantises "
                          "its queries, then scores)")
@@ -506,31 +509,38 @@ def main():
             run("quant_q")
         run("fused")
 
-    use_fused = args.fused and has_idx and has_mla
+    # Steps run the fused entry point where the workload has one (one C-ABI
+    # call); every INSTR-th step of the timed region instead runs the stages as
+    # separate calls with HIP events between them, which measures each
+    # kernel's duration live on the launch stream (--staged: every step).
+    has_fused = has_idx and has_mla
+    INSTR = 1 if (args.staged or not has_fused) else 10
     for _ in range(args.warmup):
-        fused_step() if use_fused else step()
+        fused_step() if has_fused else step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    n_ev = (args.steps + INSTR - 1) // INSTR
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if use_fused:
-            fused_step()
+        if i % INSTR == 0:
+            step(events[i // INSTR])
         else:
-            step(events[i])
+            fused_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
     stage_ms = {}
-    if not use_fused:
-        for name, (a, b) in {"index": (0, 1), "topk": (1, 2), "mla": (2, 3)}.items():
-            if (name != "mla" and not has_idx) or (name == "mla" and not has_mla):
-                continue
-            stage_ms[name] = float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
-        if fp8:
-            stage_ms["quantize_q"] = float(np.mean([e[4].elapsed_time(e[0]) for e in events]))
+    for name, (a, b) in {"index": (0, 1), "topk": (1, 2), "mla": (2, 3)}.items():
+        if (name != "mla" and not has_idx) or (name == "mla" and not has_mla):
+            continue
+        stage_ms[name] = float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+    if fp8:
+        stage_ms["quantize_q"] = float(np.mean([e[4].elapsed_time(e[0]) for e in events]))
+    timed = ("fused C-ABI call per step; every %dth step staged with HIP events per kernel" % INSTR
+             if INSTR > 1 else "staged C-ABI calls with HIP events per kernel")
 
     queries = B * Tq
     value = queries / (ms_per_step / 1e3)
@@ -567,7 +577,7 @@ def main():
         "data": "synthetic (seeded generator; integer-valued indexer inputs, N(0,1) latents)",
         "config": {"workload": wl.name, "batch": B, "queries_per_seq": Tq, "context": N, "index_topk": wl.K,
                    "indexer_heads": wl.H_I, "indexer_dim": wl.D_I, "mla_heads": wl.H, "latent_dim": wl.D,
-                   "value_dim": wl.DV, "timed": "fused dsa_forward" if use_fused else "staged C-ABI calls",
+                   "value_dim": wl.DV, "timed": timed,
                    "indexer": "fp8 (Hadamard-rotated E4M3 key cache, power-of-two row scales)" if fp8 else "bf16",
                    "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
