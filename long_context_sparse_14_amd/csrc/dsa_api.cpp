@@ -162,6 +162,7 @@ dsa_status check_index_scores_fp8(const uint8_t* q8, const float* qs, const uint
     return fail(DSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (H_I != 64 || D_I != 128)
     return fail(DSA_ERR_UNSUPPORTED, "the FP8 indexer is compiled for H_I=64, D_I=128 (got %d, %d)", H_I, D_I);
+  if (Tq > 65535) return fail(DSA_ERR_UNSUPPORTED, "the FP8 indexer takes at most 65535 queries per sequence");
   return DSA_OK;
 }
 

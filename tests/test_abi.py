@@ -193,6 +193,7 @@ def test_fp8_validation():
     assert L.dsa_index_scores_fp8(P, P, P, P, P, P, 2, 1, 100, 64, 32, 128, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
     assert L.dsa_index_scores_fp8(P, P, P, P + 4, P, P, 2, 1, 100, 64, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_index_scores_fp8(P, None, P, P, P, P, 2, 1, 100, 64, 64, 128, BF16, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_scores_fp8(P, P, P, P, P, P, 2, 70000, 100, 64, 64, 128, BF16, None) == dsa.DSA_ERR_UNSUPPORTED
     # forward: the workspace of dsa_forward
     B, Tq, N, K = 32, 1, 131072, 2048
     need = L.dsa_forward_workspace_size(B, Tq, N, 128, 512, K, BF16)
