@@ -534,9 +534,29 @@ __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, 
   }
   const int nseg = (int)((n + SEG - 1) / SEG);
   const size_t s0 = (size_t)row * G;
-  // per-segment list offsets: exclusive prefix sums of the counts (nseg <= TK_THREADS)
+  // per-segment list offsets: exclusive prefix sums of the counts (nseg <= TK_THREADS);
+  // up to 64 segments (rows up to 2^20 keys) one wave scans them without barriers
   bool ok;
-  {
+  if (nseg <= 64) {
+    if (tid < 64) {
+      const uint32_t dc = tid < nseg ? ws.defc[s0 + tid] : 0u;
+      const uint32_t cc = tid < nseg ? ws.candc[s0 + tid] : 0u;
+      const uint32_t ov = cc > CAND_CAP ? 1u : 0u;
+      const uint32_t di = wave_incl_scan(dc), ci = wave_incl_scan(cc), oi = wave_incl_scan(ov);
+      if (tid < nseg) {
+        sm.s_doff[tid] = di - dc;
+        sm.s_coff[tid] = ci - cc;
+      }
+      if (tid == 63) {  // lanes past nseg add nothing: lane 63 holds the totals
+        sm.s_doff[nseg] = di;
+        sm.s_coff[nseg] = ci;
+        sm.s_res[0] = oi;
+      }
+    }
+    __syncthreads();
+    const uint32_t dtot = sm.s_doff[nseg], ctot = sm.s_coff[nseg];
+    ok = sm.s_res[0] == 0 && dtot <= (uint32_t)K && ctot <= (uint32_t)ROW_CAND_CAP && dtot + ctot >= (uint32_t)K;
+  } else {
     const uint32_t dc = tid < nseg ? ws.defc[s0 + tid] : 0u;
     const uint32_t cc = tid < nseg ? ws.candc[s0 + tid] : 0u;
     uint32_t dtot, ctot, otot;
@@ -609,22 +629,32 @@ __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, 
     keq = kk - above;
   }
   __syncthreads();
-  // kept candidates, in index order
-  uint32_t run_sel = 0, run_eq = 0;
-  for (uint32_t base = 0; base < ncand; base += TK_THREADS) {
-    const uint32_t j = base + tid;
+  // kept candidates, in index order: thread t owns the run [c*t, c*t + c) of
+  // the list, so one block prefix sum orders them all
+  {
+    const uint32_t c = (ncand + TK_THREADS - 1) / TK_THREADS;
+    const uint32_t j0 = c * (uint32_t)tid;
     uint32_t gt = 0, eq = 0;
-    if (j < ncand && kk > 0) {
-      gt = sm.ck[j] > T;
-      eq = sm.ck[j] == T;
-    }
+    if (kk > 0)
+      for (uint32_t u = 0; u < c && j0 + u < ncand; ++u) {
+        const uint32_t k = sm.ck[j0 + u];
+        gt += k > T;
+        eq += k == T;
+      }
     uint32_t tot;
     const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sm.sbuf);
-    const uint32_t gb = run_sel + (ex & 0xffffu), eb = run_eq + (ex >> 16);
-    if (gt) sm.sl[gb + min(eb, keq)] = sm.ci[j];
-    else if (eq && eb < keq) sm.sl[gb + eb] = sm.ci[j];
-    run_sel += tot & 0xffffu;
-    run_eq += tot >> 16;
+    uint32_t gb = ex & 0xffffu, eb = ex >> 16;
+    if (kk > 0)
+      for (uint32_t u = 0; u < c && j0 + u < ncand; ++u) {
+        const uint32_t k = sm.ck[j0 + u];
+        if (k > T) {
+          sm.sl[gb + min(eb, keq)] = sm.ci[j0 + u];
+          ++gb;
+        } else if (k == T) {
+          if (eb < keq) sm.sl[gb + eb] = sm.ci[j0 + u];
+          ++eb;
+        }
+      }
   }
   __syncthreads();
   // merge two ascending, disjoint lists: slot = own rank + rank in the other list
