@@ -427,3 +427,31 @@ def test_dsa_decode_b32_128k():
         causal_scores_equal(sc[b], ref, [0], f"scores b={b}")
     for b in range(wl.B):
         _check_selection_properties(scores[b], idx[b], wl.q_pos0, wl.K)
+
+
+@pytest.mark.parametrize("B,K", [
+    (28, 2048),   # 256 // 28 = 9 splits asked, 64 tiles: 8 splits of 8 tiles (an empty ninth dropped)
+    (100, 2048),  # 2 splits of 32 tiles
+    (7, 2048),    # 32 splits of 2 tiles
+    (5, 1000),    # 32 tiles (the last one ragged) over 32 splits
+])
+def test_sparse_mla_split_shapes(B, K):
+    dsa = _dsa()
+    wl, x = _mla_case(B, 1, 3000, K, seed=B + K, n_masked=5, empty_row=False)
+    out, lse = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), dev(x["idx"]), wl.scale, wl.DV)
+    torch.cuda.synchronize()
+    out, lse = host64(out), host64(lse)
+    for b in sorted({0, B // 2, B - 1}):
+        o, l = oracle.sparse_mla_rows(x["q"][b, 0], oracle.as_f64(x["kv"][b]), x["idx"][b, 0], wl.scale, wl.DV)
+        assert_close(out[b, 0], o, "bf16", f"out b={b}")
+        assert_lse_close(lse[b, 0], l, f"lse b={b}")
+
+
+def test_indexer_decode_batch_of_28_exact():
+    """28 rows: the launch divides two rounds of workgroups evenly over the rows."""
+    dsa = _dsa()
+    wl, x = _bf16_indexer_case(1, 5000, 4999, 28)
+    scores = dsa.index_scores(dev(x["q_idx"]), dev(x["k_idx"]), dev(x["w"]), 4999).cpu().numpy()
+    for b in (0, 13, 27):
+        ref = oracle.index_scores_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], [0], 4999)
+        causal_scores_equal(scores[b], ref, [0], f"scores b={b}")
