@@ -49,6 +49,9 @@ def _parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the fused step once in a HIP graph and replay it (workloads with a fused call)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size")
     ap.add_argument("--staged", action="store_true",
                     help="run every timed step as separate stage calls with HIP events between them")
     ap.add_argument("--fp8-indexer", action="store_true",
@@ -408,6 +411,8 @@ def main():
 
     dsa.library()
     wl = synth.WORKLOADS[args.workload]
+    if args.batch > 0:
+        wl = wl.replace(B=args.batch)
     x = synth.make_inputs(wl)
 
     def dev(a):
@@ -519,6 +524,31 @@ def main():
         fused_step() if has_fused else step()
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph and has_fused:
+        # the library launches only on the given stream and never allocates,
+        # synchronises or clears memory, so one fused step captures as is; the
+        # capture stream replaces the stream argument (the last one) of each call
+        cap = torch.cuda.Stream()
+        on_cap = {k: (fn, a[:-1] + (cap.cuda_stream,)) for k, (fn, a) in calls.items()}
+
+        def cap_step():
+            for name in (("quant_q", "fused") if fp8 else ("fused",)):
+                fn, a = on_cap[name]
+                if fn(*a) != 0:
+                    raise RuntimeError(f"{name}: {lib.dsa_last_error().decode()}")
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            cap_step()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            cap_step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
     n_ev = (args.steps + INSTR - 1) // INSTR
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
     torch.cuda.synchronize()
@@ -526,6 +556,8 @@ def main():
     for i in range(args.steps):
         if i % INSTR == 0:
             step(events[i // INSTR])
+        elif graph is not None:
+            graph.replay()
         else:
             fused_step()
     torch.cuda.synchronize()
@@ -539,7 +571,8 @@ def main():
         stage_ms[name] = float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
     if fp8:
         stage_ms["quantize_q"] = float(np.mean([e[4].elapsed_time(e[0]) for e in events]))
-    timed = ("fused C-ABI call per step; every %dth step staged with HIP events per kernel" % INSTR
+    timed = ("%s per step; every %dth step staged with HIP events per kernel"
+             % ("replay of a HIP graph of the fused call" if graph is not None else "fused C-ABI call", INSTR)
              if INSTR > 1 else "staged C-ABI calls with HIP events per kernel")
 
     queries = B * Tq
