@@ -27,12 +27,13 @@
 //         t_lo <= t_hi on T from a 4096-key sample of the row (exact selects
 //         at two sample ranks around the one expected to hold T; every
 //         segment of a row derives the same bounds), and writes, in index
-//         order, its keys above t_hi ("definite") and its keys in
-//         [t_lo, t_hi] ("candidates", key + index);
+//         order, key and index of its keys at or above t_lo: those above
+//         t_hi are "definite", those in [t_lo, t_hi] "candidates";
 //      2. one workgroup per row checks that at most K keys are definite and
-//         at least K are definite or candidates, selects the K - #definite
-//         best candidates exactly, and merges the two ascending lists into
-//         the output.
+//         at least K are definite or candidates, holds the row's list in
+//         registers, selects the K - #definite best candidates exactly, and
+//         compacts the kept entries, already in index order, into the
+//         output with one block prefix sum.
 //    The scores are read once (plus the sample).  A row whose bounds miss or
 //    whose candidates overflow their buffers (scores ordered by position, a
 //    large block of equal keys at the cut) falls back to the one-workgroup
@@ -338,11 +339,15 @@ static_assert(SAMPLE_PER_T * TK_THREADS == SAMPLES && SAMPLE_RUN % SAMPLE_PER_T 
 constexpr int FB_BITS = 12;               // bins of the long-row histograms: 4096
 constexpr int FB = 1 << FB_BITS;
 
+// A segment's list holds its keys at or above t_lo in index order, definite
+// and candidate keys together: at most K + CAND_CAP entries whenever the
+// final step's checks pass.
 struct LongWs {
   uint32_t* defc;   // [R][G] definite keys per segment (may exceed K: the bounds missed)
   uint32_t* candc;  // [R][G] candidates per segment (may exceed CAND_CAP: overflow)
-  int32_t* defi;    // [R][G][K] definite key indices, ascending within a segment
-  uint2* cand;      // [R][G][CAND_CAP] (key, index), ascending index within a segment
+  uint2* bounds;    // [R] (t_lo, t_hi), written by segment 0 of the row
+  uint2* list;      // [R][G][cap] (key, index) of keys >= t_lo, ascending index
+  int cap;          // K + CAND_CAP
 };
 
 __host__ __device__ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -353,13 +358,14 @@ __host__ __device__ inline LongWs long_ws(void* base, int64_t R, int G, int K) {
   const size_t cs = align_up((size_t)R * G * 8);
   w.defc = reinterpret_cast<uint32_t*>(p);
   w.candc = w.defc + (size_t)R * G;
-  w.defi = reinterpret_cast<int32_t*>(p + cs);
-  w.cand = reinterpret_cast<uint2*>(p + cs + align_up((size_t)R * G * K * 4));
+  w.bounds = reinterpret_cast<uint2*>(p + cs);
+  w.list = reinterpret_cast<uint2*>(p + cs + align_up((size_t)R * 8));
+  w.cap = K + CAND_CAP;
   return w;
 }
 
 size_t long_ws_bytes(int64_t R, int G, int K) {
-  return align_up((size_t)R * G * 8) + align_up((size_t)R * G * K * 4) + align_up((size_t)R * G * CAND_CAP * 8);
+  return align_up((size_t)R * G * 8) + align_up((size_t)R * 8) + align_up((size_t)R * G * (K + CAND_CAP) * 8);
 }
 
 // Keys of this workgroup's segment: thread t holds the run
@@ -455,8 +461,8 @@ struct SegSmem {
 
 // Step 1, one workgroup per segment: the row's bounds t_lo <= t_hi from its
 // sample (every segment of a row computes the same ones), then this
-// segment's keys above t_hi ("definite", index order) and its keys in
-// [t_lo, t_hi] ("candidates", key and index, index order).
+// segment's keys at or above t_lo, key and index, in index order: those above
+// t_hi are "definite", those in [t_lo, t_hi] "candidates"; both are counted.
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __restrict__ scores, LongWs ws,
                                                                 int64_t Tq, int64_t N, int64_t q_pos0, Vis vis,
                                                                 int K,
@@ -474,8 +480,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __r
   sample_bounds(src, n, K, t_hi, t_lo, sm.h, sm.sbuf, sm.s_res);
 
   const size_t sidx = (size_t)row * G + g;
-  int32_t* defi = ws.defi + sidx * K;
-  uint2* cand = ws.cand + sidx * CAND_CAP;
+  uint2* list = ws.list + sidx * ws.cap;
+  const uint32_t cap = (uint32_t)ws.cap;
   const int64_t i0 = seg0 + (int64_t)RUN * threadIdx.x;
   uint32_t nd = 0, nc = 0;
 #pragma unroll
@@ -486,42 +492,42 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __r
   }
   uint32_t tot;
   const uint32_t ex = block_excl_scan((nc << 16) | nd, tot, sm.sbuf);
-  uint32_t pd = ex & 0xffffu, pc = ex >> 16;
+  uint32_t pos = (ex & 0xffffu) + (ex >> 16);  // keys >= t_lo before this thread's run
 #pragma unroll
   for (int u = 0; u < SEG_PER_T; ++u) {
     if (i0 + u >= n) break;
-    if (k[u] > t_hi) {
-      if (pd < (uint32_t)K) defi[pd] = (int32_t)(i0 + u);
-      ++pd;
-    } else if (k[u] >= t_lo) {
-      if (pc < CAND_CAP) cand[pc] = make_uint2(k[u], (uint32_t)(i0 + u));
-      ++pc;
+    if (k[u] >= t_lo) {
+      if (pos < cap) list[pos] = make_uint2(k[u], (uint32_t)(i0 + u));
+      ++pos;
     }
   }
   if (threadIdx.x == 0) {
     ws.defc[sidx] = tot & 0xffffu;
     ws.candc[sidx] = tot >> 16;
+    if (g == 0) ws.bounds[row] = make_uint2(t_lo, t_hi);
   }
 }
 
 // Shared memory of the final step.
 struct FinalSmem {
-  uint32_t ck[ROW_CAND_CAP];   // candidate keys, index order
-  int32_t ci[ROW_CAND_CAP];    // candidate indices
-  int32_t dl[LONG_MAX_K];      // definite indices, ascending
-  int32_t sl[LONG_MAX_K];      // kept candidate indices, ascending
   uint32_t h[FB];               // FB >= HB: also the fallback's histogram
   uint32_t sbuf[3 * TK_WAVES];
   uint32_t s_res[4];
-  uint32_t s_doff[LONG_MAX_G + 1];
-  uint32_t s_coff[LONG_MAX_G + 1];
+  uint32_t s_loff[LONG_MAX_G + 1];  // list offsets of the segments in the row's list
 };
 
 // Step 2, one workgroup per row: check the bounds (the definite keys are at
-// most K and, with the candidates, at least K; no list overflowed), keep the
-// K - #definite best candidates (exact select on their full keys), and merge
-// the two ascending lists into the output.  If a check fails, the exact
+// most K and, with the candidates, at least K; no segment's candidates
+// overflowed), then treat the segments' lists, concatenated, as one list in
+// index order.  Thread t holds entries [LPT*t, LPT*t + LPT) in registers.  The
+// K - #definite best candidates are found by an exact select over the
+// candidates' keys (the range [t_lo, t_hi] holds every candidate and no
+// definite key), and one block prefix sum over the kept entries writes them,
+// in index order, straight to the output.  If a check fails, the exact
 // one-workgroup method runs over the row from global memory instead.
+constexpr int LPT = (LONG_MAX_K + ROW_CAND_CAP) / TK_THREADS;  // list entries per thread
+static_assert(LPT * TK_THREADS == LONG_MAX_K + ROW_CAND_CAP, "whole list entries per thread");
+
 __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, const LongWs& ws, int32_t* __restrict__ idx,
                               int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, const Vis& vis, int K, int G,
                               FinalSmem& sm) {
@@ -534,141 +540,110 @@ __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, 
   }
   const int nseg = (int)((n + SEG - 1) / SEG);
   const size_t s0 = (size_t)row * G;
-  // per-segment list offsets: exclusive prefix sums of the counts (nseg <= TK_THREADS);
-  // up to 64 segments (rows up to 2^20 keys) one wave scans them without barriers
+  // per-segment list offsets: exclusive prefix sums of the list lengths
+  // (nseg <= TK_THREADS); up to 64 segments (rows up to 2^20 keys) one wave
+  // scans them without barriers
   bool ok;
+  uint32_t ndef, ncand;
   if (nseg <= 64) {
     if (tid < 64) {
       const uint32_t dc = tid < nseg ? ws.defc[s0 + tid] : 0u;
       const uint32_t cc = tid < nseg ? ws.candc[s0 + tid] : 0u;
       const uint32_t ov = cc > CAND_CAP ? 1u : 0u;
       const uint32_t di = wave_incl_scan(dc), ci = wave_incl_scan(cc), oi = wave_incl_scan(ov);
-      if (tid < nseg) {
-        sm.s_doff[tid] = di - dc;
-        sm.s_coff[tid] = ci - cc;
-      }
+      if (tid < nseg) sm.s_loff[tid] = di - dc + ci - cc;
       if (tid == 63) {  // lanes past nseg add nothing: lane 63 holds the totals
-        sm.s_doff[nseg] = di;
-        sm.s_coff[nseg] = ci;
+        sm.s_loff[nseg] = di + ci;
         sm.s_res[0] = oi;
+        sm.s_res[1] = di;
+        sm.s_res[2] = ci;
       }
     }
     __syncthreads();
-    const uint32_t dtot = sm.s_doff[nseg], ctot = sm.s_coff[nseg];
-    ok = sm.s_res[0] == 0 && dtot <= (uint32_t)K && ctot <= (uint32_t)ROW_CAND_CAP && dtot + ctot >= (uint32_t)K;
+    ok = sm.s_res[0] == 0;
+    ndef = sm.s_res[1];
+    ncand = sm.s_res[2];
   } else {
     const uint32_t dc = tid < nseg ? ws.defc[s0 + tid] : 0u;
     const uint32_t cc = tid < nseg ? ws.candc[s0 + tid] : 0u;
-    uint32_t dtot, ctot, otot;
-    const uint32_t dex = block_excl_scan(dc, dtot, sm.sbuf);
-    const uint32_t cex = block_excl_scan(cc, ctot, sm.sbuf);
+    uint32_t otot;
+    const uint32_t dex = block_excl_scan(dc, ndef, sm.sbuf);
+    const uint32_t cex = block_excl_scan(cc, ncand, sm.sbuf);
     block_excl_scan(cc > CAND_CAP ? 1u : 0u, otot, sm.sbuf);
-    if (tid < nseg) {
-      sm.s_doff[tid] = dex;
-      sm.s_coff[tid] = cex;
-    }
-    if (tid == 0) {
-      sm.s_doff[nseg] = dtot;
-      sm.s_coff[nseg] = ctot;
-    }
-    ok = otot == 0 && dtot <= (uint32_t)K && ctot <= (uint32_t)ROW_CAND_CAP && dtot + ctot >= (uint32_t)K;
+    if (tid < nseg) sm.s_loff[tid] = dex + cex;
+    if (tid == 0) sm.s_loff[nseg] = ndef + ncand;
+    ok = otot == 0;
     __syncthreads();
   }
+  ok = ok && ndef <= (uint32_t)K && ncand <= (uint32_t)ROW_CAND_CAP && ndef + ncand >= (uint32_t)K;
   if (!ok) {
     select_row(scores + row * N, n, K, out, nullptr, sm.h, sm.sbuf, sm.s_res);
     return;
   }
-  const uint32_t ndef = sm.s_doff[nseg], ncand = sm.s_coff[nseg];
-  // gather both lists in segment order (ascending index); every load independent
-  auto seg_of = [&](const uint32_t* off, uint32_t j) {
-    int lo = 0, hi = nseg;  // largest g with off[g] <= j
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= j) lo = mid;
-      else hi = mid;
-    }
-    return lo;
-  };
-  for (uint32_t j = tid; j < ndef; j += TK_THREADS) {
-    const int g = seg_of(sm.s_doff, j);
-    sm.dl[j] = ws.defi[(s0 + g) * K + (j - sm.s_doff[g])];
-  }
-  constexpr int CPT = ROW_CAND_CAP / TK_THREADS;  // candidates per thread
-  uint32_t ck[CPT];
-  bool cv[CPT];
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    const uint32_t j = tid + TK_THREADS * u;
-    cv[u] = j < ncand;
-    ck[u] = 0u;
-    if (cv[u]) {
-      const int g = seg_of(sm.s_coff, j);
-      const uint2 v = ws.cand[(s0 + g) * CAND_CAP + (j - sm.s_coff[g])];
-      ck[u] = v.x;
-      sm.ck[j] = v.x;
-      sm.ci[j] = (int32_t)v.y;
-    }
-  }
-  const uint32_t kk = (uint32_t)K - ndef;  // candidates to keep (0 <= kk <= ncand)
-  uint32_t T = 0xffffffffu, keq = 0;
-  if (kk > 0) {  // candidates lie in [t_lo, t_hi]; their own range is found first
-    uint32_t mn = 0xffffffffu, mx = 0u, cmin, cmax, above;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u)
-      if (cv[u]) {
-        mn = min(mn, ck[u]);
-        mx = max(mx, ck[u]);
+  // this thread's entries of the row's list (every load independent)
+  const uint32_t len = ndef + ncand;
+  const uint32_t j0 = (uint32_t)LPT * (uint32_t)tid;
+  uint32_t ck[LPT];
+  int32_t ci[LPT];
+  {
+    int g = 0;  // segment of entry j0: the largest g with s_loff[g] <= j0
+    if (j0 < len) {
+      int lo = 0, hi = nseg;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm.s_loff[mid] <= j0) lo = mid;
+        else hi = mid;
       }
-    block_min_max(mn, mx, cmin, cmax, sm.sbuf + TK_WAVES);
+      g = lo;
+    }
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const uint32_t j = j0 + u;
+      ck[u] = 0u;
+      ci[u] = -1;
+      if (j < len) {
+        while (sm.s_loff[g + 1] <= j) ++g;
+        const uint2 v = ws.list[(s0 + g) * ws.cap + (j - sm.s_loff[g])];
+        ck[u] = v.x;
+        ci[u] = (int32_t)v.y;
+      }
+    }
+  }
+  const uint2 bnd = ws.bounds[row];
+  const uint32_t kk = (uint32_t)K - ndef;  // candidates to keep (0 <= kk <= ncand)
+  uint32_t T = bnd.y, keq = 0;             // kk == 0: exactly the definite keys (> t_hi)
+  if (kk > 0) {
     auto add_cand = [&](HotBins& hb, uint32_t lo, uint32_t hi, int shift) {
 #pragma unroll
-      for (int u = 0; u < CPT; ++u)
-        if (cv[u] && ck[u] >= lo && ck[u] <= hi) hb.add((ck[u] - lo) >> shift, sm.h);
+      for (int u = 0; u < LPT; ++u)
+        if (ci[u] >= 0 && ck[u] >= lo && ck[u] <= hi) hb.add((ck[u] - lo) >> shift, sm.h);
     };
-    T = select_rank<FB_BITS>(add_cand, cmin, cmax, kk, above, sm.h, sm.sbuf, sm.s_res);
+    uint32_t above;
+    T = select_rank<FB_BITS>(add_cand, bnd.x, bnd.y, kk, above, sm.h, sm.sbuf, sm.s_res);
     keq = kk - above;
   }
-  __syncthreads();
-  // kept candidates, in index order: thread t owns the run [c*t, c*t + c) of
-  // the list, so one block prefix sum orders them all
-  {
-    const uint32_t c = (ncand + TK_THREADS - 1) / TK_THREADS;
-    const uint32_t j0 = c * (uint32_t)tid;
-    uint32_t gt = 0, eq = 0;
-    if (kk > 0)
-      for (uint32_t u = 0; u < c && j0 + u < ncand; ++u) {
-        const uint32_t k = sm.ck[j0 + u];
-        gt += k > T;
-        eq += k == T;
-      }
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sm.sbuf);
-    uint32_t gb = ex & 0xffffu, eb = ex >> 16;
-    if (kk > 0)
-      for (uint32_t u = 0; u < c && j0 + u < ncand; ++u) {
-        const uint32_t k = sm.ck[j0 + u];
-        if (k > T) {
-          sm.sl[gb + min(eb, keq)] = sm.ci[j0 + u];
-          ++gb;
-        } else if (k == T) {
-          if (eb < keq) sm.sl[gb + eb] = sm.ci[j0 + u];
-          ++eb;
-        }
-      }
+  // kept entries in index order: key > T, or key == T among the first keq
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    gt += ci[u] >= 0 && ck[u] > T;
+    eq += ci[u] >= 0 && ck[u] == T;
   }
-  __syncthreads();
-  // merge two ascending, disjoint lists: slot = own rank + rank in the other list
-  auto lower = [](const int32_t* a, uint32_t len, int32_t v) {
-    uint32_t lo = 0, hi = len;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (a[mid] < v) lo = mid + 1;
-      else hi = mid;
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sm.sbuf);
+  gt = ex & 0xffffu;
+  eq = ex >> 16;
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    if (ci[u] < 0) continue;
+    if (ck[u] > T) {
+      out[gt + min(eq, keq)] = ci[u];
+      ++gt;
+    } else if (ck[u] == T) {
+      if (eq < keq) out[gt + eq] = ci[u];
+      ++eq;
     }
-    return lo;
-  };
-  for (uint32_t j = tid; j < ndef; j += TK_THREADS) out[j + lower(sm.sl, kk, sm.dl[j])] = sm.dl[j];
-  for (uint32_t j = tid; j < kk; j += TK_THREADS) out[j + lower(sm.dl, ndef, sm.sl[j])] = sm.sl[j];
+  }
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __restrict__ scores, LongWs ws,
