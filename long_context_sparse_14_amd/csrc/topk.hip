@@ -129,11 +129,12 @@ __device__ __forceinline__ int bit_width(uint32_t x) { return x == 0u ? 0 : 32 -
 
 // Given a histogram h of 2^FBITS bins, find for each of two descending ranks
 // ra, rb (1-based, at most the histogram total) the bin that holds it;
-// *_above receives how many counted keys lie in higher bins.  s_res: 4 words.
+// *_above receives how many counted keys lie in higher bins, count_a how many
+// lie in bin ba.  s_res: 8 words.
 template <int FBITS>
 __device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, uint32_t rb, uint32_t& ba,
-                                              uint32_t& above_a, uint32_t& bb, uint32_t& above_b, uint32_t* sbuf,
-                                              uint32_t* s_res) {
+                                              uint32_t& above_a, uint32_t& bb, uint32_t& above_b,
+                                              uint32_t& count_a, uint32_t* sbuf, uint32_t* s_res) {
   constexpr int NB = 1 << FBITS, PER_T = NB / TK_THREADS;
   static_assert(PER_T * TK_THREADS == NB, "whole bins per thread");
   const int tid = threadIdx.x;
@@ -151,6 +152,7 @@ __device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, ui
     if (run < ra && ra <= run + c[u]) {
       s_res[0] = b;
       s_res[1] = run;
+      s_res[4] = c[u];
     }
     if (run < rb && rb <= run + c[u]) {
       s_res[2] = b;
@@ -163,6 +165,7 @@ __device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, ui
   above_a = s_res[1];
   bb = s_res[2];
   above_b = s_res[3];
+  count_a = s_res[4];
   __syncthreads();
 }
 
@@ -194,23 +197,27 @@ __device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t
 // descending rank r (1 <= r <= their number), and in `above` how many of them
 // exceed it.  Each round splits the remaining key range into 2^FBITS bins of
 // (key - lo) >> shift and keeps the bin holding rank r, so a range of b bits
-// takes ceil(b / FBITS) rounds.  add_keys(hb, lo, hi, shift) must pass every
-// key of the set in [lo, hi] to hb.add((key - lo) >> shift, h).
-template <int FBITS, typename AddKeys>
-__device__ uint32_t select_rank(AddKeys add_keys, uint32_t lo, uint32_t hi, uint32_t r, uint32_t& above,
-                                uint32_t* h, uint32_t* sbuf, uint32_t* s_res) {
+// takes at most ceil(b / FBITS) rounds.  add_keys(hb, lo, hi, shift) must pass
+// every key of the set in [lo, hi] to hb.add((key - lo) >> shift, h), and
+// each_key(lo, hi, fn) must call fn(key) for the same keys.  Once the kept bin
+// holds at most 64 keys they are copied to `small` (65 words) and one wave
+// ranks them directly, in place of further histogram rounds.
+template <int FBITS, typename AddKeys, typename EachKey>
+__device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo, uint32_t hi, uint32_t r,
+                                uint32_t& above, uint32_t* h, uint32_t* sbuf, uint32_t* s_res, uint32_t* small) {
   above = 0;
 #pragma unroll 1
   while (true) {
     const int shift = max(0, bit_width(hi - lo) - FBITS);
     for (int b = threadIdx.x; b < (1 << FBITS); b += TK_THREADS) h[b] = 0;
+    if (threadIdx.x == 0) small[64] = 0u;
     __syncthreads();
     HotBins hb;
     add_keys(hb, lo, hi, shift);
     hb.flush(h);
     __syncthreads();
-    uint32_t b, ab, b2, ab2;
-    find_two_bins<FBITS>(h, r, r, b, ab, b2, ab2, sbuf, s_res);
+    uint32_t b, ab, b2, ab2, cnt;
+    find_two_bins<FBITS>(h, r, r, b, ab, b2, ab2, cnt, sbuf, s_res);
     above += ab;
     r -= ab;
     const uint32_t nlo = lo + (b << shift);
@@ -218,6 +225,32 @@ __device__ uint32_t select_rank(AddKeys add_keys, uint32_t lo, uint32_t hi, uint
     lo = nlo;
     hi = nhi;
     if (shift == 0) return lo;
+    if (cnt <= 64u) {
+      each_key(lo, hi, [&](uint32_t k) {
+        const uint32_t s = atomicAdd(&small[64], 1u);
+        if (s < 64u) small[s] = k;
+      });
+      __syncthreads();
+      if (threadIdx.x < 64) {  // lane i: how many of the bin's keys exceed / equal its own
+        const uint32_t i = threadIdx.x;
+        const uint32_t ki = i < cnt ? small[i] : 0u;
+        uint32_t gt = 0, eq = 0;
+        for (uint32_t j = 0; j < cnt; ++j) {
+          const uint32_t kj = small[j];
+          gt += kj > ki;
+          eq += kj == ki;
+        }
+        if (i < cnt && gt < r && r <= gt + eq) {  // lanes holding the key at rank r agree
+          s_res[5] = ki;
+          s_res[6] = gt;
+        }
+      }
+      __syncthreads();
+      const uint32_t T = s_res[5];
+      above += s_res[6];
+      __syncthreads();
+      return T;
+    }
   }
 }
 
@@ -242,9 +275,9 @@ __device__ __forceinline__ void emit_run(KeyAt key_at, int i0, int n, uint32_t T
 
 // The one-workgroup method for one row.  skey: LDS stage of TK_CAP keys, or
 // nullptr to read the row from global memory on every pass.  hist: 2048 bins;
-// sbuf: 3 * TK_WAVES words; s_res: 4 words.
+// sbuf: 3 * TK_WAVES words; s_res: 8 words; small: 65 words.
 __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_t n, int K, int32_t* __restrict__ out,
-                           uint32_t* skey, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res) {
+                           uint32_t* skey, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res, uint32_t* small) {
   const int tid = threadIdx.x;
   if (n <= K) {
     for (int64_t i = tid; i < K; i += TK_THREADS) out[i] = i < n ? (int32_t)i : -1;
@@ -292,8 +325,23 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_
       }
     }
   };
+  auto each_row = [&](uint32_t lo, uint32_t hi, auto fn) {
+    for (int base = tid; base < n32; base += 8 * TK_THREADS) {
+      uint32_t k[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * TK_THREADS;
+        k[u] = i < n32 ? key_at(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * TK_THREADS;
+        if (i < n32 && k[u] >= lo && k[u] <= hi) fn(k[u]);
+      }
+    }
+  };
   uint32_t above;
-  const uint32_t T = select_rank<11>(add_row, kmin, kmax, (uint32_t)K, above, hist, sbuf, s_res);
+  const uint32_t T = select_rank<11>(add_row, each_row, kmin, kmax, (uint32_t)K, above, hist, sbuf, s_res, small);
   const uint32_t keq = (uint32_t)K - above;
 
   // in-order compaction: thread t owns keys [base + RUN*t, base + RUN*t + RUN)
@@ -322,10 +370,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(const float* __re
   __shared__ uint32_t skey[TK_CAP];
   __shared__ uint32_t hist[HB];
   __shared__ uint32_t sbuf[3 * TK_WAVES];
-  __shared__ uint32_t s_res[4];
+  __shared__ uint32_t s_res[8];
+  __shared__ uint32_t small[65];
   const int64_t row = blockIdx.x;
   const int64_t n = n_visible(row, Tq, N, q_pos0, vis);
-  select_row(scores + row * N, n, K, idx + row * K, n <= TK_CAP ? skey : nullptr, hist, sbuf, s_res);
+  select_row(scores + row * N, n, K, idx + row * K, n <= TK_CAP ? skey : nullptr, hist, sbuf, s_res, small);
 }
 
 // ---------------------------------------------------------------- long rows
@@ -446,8 +495,8 @@ __device__ __forceinline__ void sample_bounds(const float* __restrict__ src, int
     hb.flush(h);
   }
   __syncthreads();
-  uint32_t b_hi, ab_hi, b_lo, ab_lo;
-  find_two_bins<FB_BITS>(h, (uint32_t)r_hi, (uint32_t)r_lo, b_hi, ab_hi, b_lo, ab_lo, sbuf, s_res);
+  uint32_t b_hi, ab_hi, b_lo, ab_lo, c_hi;
+  find_two_bins<FB_BITS>(h, (uint32_t)r_hi, (uint32_t)r_lo, b_hi, ab_hi, b_lo, ab_lo, c_hi, sbuf, s_res);
   t_hi = (uint32_t)min((uint64_t)kmax, (uint64_t)kmin + ((uint64_t)(b_hi + 1) << shift) - 1);
   t_lo = kmin + (b_lo << shift);
 }
@@ -456,7 +505,7 @@ __device__ __forceinline__ void sample_bounds(const float* __restrict__ src, int
 struct SegSmem {
   uint32_t h[FB];
   uint32_t sbuf[3 * TK_WAVES];
-  uint32_t s_res[4];
+  uint32_t s_res[8];
 };
 
 // Step 1, one workgroup per segment: the row's bounds t_lo <= t_hi from its
@@ -512,7 +561,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __r
 struct FinalSmem {
   uint32_t h[FB];               // FB >= HB: also the fallback's histogram
   uint32_t sbuf[3 * TK_WAVES];
-  uint32_t s_res[4];
+  uint32_t s_res[8];
+  uint32_t small[65];
   uint32_t s_loff[LONG_MAX_G + 1];  // list offsets of the segments in the row's list
 };
 
@@ -577,7 +627,7 @@ __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, 
   }
   ok = ok && ndef <= (uint32_t)K && ncand <= (uint32_t)ROW_CAND_CAP && ndef + ncand >= (uint32_t)K;
   if (!ok) {
-    select_row(scores + row * N, n, K, out, nullptr, sm.h, sm.sbuf, sm.s_res);
+    select_row(scores + row * N, n, K, out, nullptr, sm.h, sm.sbuf, sm.s_res, sm.small);
     return;
   }
   // this thread's entries of the row's list (every load independent)
@@ -618,8 +668,13 @@ __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, 
       for (int u = 0; u < LPT; ++u)
         if (ci[u] >= 0 && ck[u] >= lo && ck[u] <= hi) hb.add((ck[u] - lo) >> shift, sm.h);
     };
+    auto each_cand = [&](uint32_t lo, uint32_t hi, auto fn) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u)
+        if (ci[u] >= 0 && ck[u] >= lo && ck[u] <= hi) fn(ck[u]);
+    };
     uint32_t above;
-    T = select_rank<FB_BITS>(add_cand, bnd.x, bnd.y, kk, above, sm.h, sm.sbuf, sm.s_res);
+    T = select_rank<FB_BITS>(add_cand, each_cand, bnd.x, bnd.y, kk, above, sm.h, sm.sbuf, sm.s_res, sm.small);
     keq = kk - above;
   }
   // kept entries in index order: key > T, or key == T among the first keq
