@@ -558,16 +558,16 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) {  // four row reads in flight, then their four stores
       const uint16_t* sp4 = stage + (16 * wave + 4 * g) * EPITCH + 8 * elane;
-      const uint4 v0 = *reinterpret_cast<const uint4*>(sp4);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(sp4 + EPITCH);
-      const uint4 v2 = *reinterpret_cast<const uint4*>(sp4 + 2 * EPITCH);
-      const uint4 v3 = *reinterpret_cast<const uint4*>(sp4 + 3 * EPITCH);
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(sp4);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(sp4 + EPITCH);
+      const u32x4 v2 = *reinterpret_cast<const u32x4*>(sp4 + 2 * EPITCH);
+      const u32x4 v3 = *reinterpret_cast<const u32x4*>(sp4 + 3 * EPITCH);
       __builtin_amdgcn_sched_barrier(0);
       uint16_t* dp4 = dst + (64 * q + 16 * wave + 4 * g) * MDV + 8 * elane;
-      *reinterpret_cast<uint4*>(dp4) = v0;
-      *reinterpret_cast<uint4*>(dp4 + MDV) = v1;
-      *reinterpret_cast<uint4*>(dp4 + 2 * MDV) = v2;
-      *reinterpret_cast<uint4*>(dp4 + 3 * MDV) = v3;
+      __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(dp4));
+      __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(dp4 + MDV));
+      __builtin_nontemporal_store(v2, reinterpret_cast<u32x4*>(dp4 + 2 * MDV));
+      __builtin_nontemporal_store(v3, reinterpret_cast<u32x4*>(dp4 + 3 * MDV));
     }
   }
 }
@@ -616,12 +616,12 @@ __global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const u
       }
     }
   }
-  uint4 pk;
+  u32x4 pk;
   pk.x = pack_bf16x2(acc[0], acc[1]);
   pk.y = pack_bf16x2(acc[2], acc[3]);
   pk.z = pack_bf16x2(acc[4], acc[5]);
   pk.w = pack_bf16x2(acc[6], acc[7]);
-  *reinterpret_cast<uint4*>(out + rh * MDV + 8 * lane) = pk;
+  __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(out + rh * MDV + 8 * lane));
   if (lse != nullptr && lane == 0) lse[rh] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * LN2;
 }
 
