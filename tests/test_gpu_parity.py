@@ -174,11 +174,7 @@ def test_topk_long_rows_sample_bounds_miss():
     rng = np.random.default_rng(21)
     N, K = 70000, 2048
     vals = (rng.random((1, 2, N)) * 0.5).astype(np.float32)
-    sampled = np.zeros(N, dtype=bool)
-    for b in range(64):
-        s0 = b * (N - 64) // 63
-        sampled[s0:s0 + 64] = True
-    outside = np.flatnonzero(~sampled)
+    outside = np.flatnonzero(~_sampled_mask(N))
     for t in range(2):
         big = rng.choice(outside, 5000, replace=False)
         vals[0, t, big] = (1.0 + rng.random(5000)).astype(np.float32)
@@ -186,6 +182,56 @@ def test_topk_long_rows_sample_bounds_miss():
     for t in range(2):
         exp = oracle.topk_row(vals[0, t, :oracle.n_valid_keys(t, N - 1, N)], K)
         assert np.array_equal(idx[0, t], exp), f"row {t}"
+
+
+def _sampled_mask(n):
+    """Keys the segmented method samples from a row of n visible keys: 64 runs
+    of 64 consecutive keys spread evenly over the row."""
+    m = np.zeros(n, dtype=bool)
+    for b in range(64):
+        s0 = b * (n - 64) // 63
+        m[s0:s0 + 64] = True
+    return m
+
+
+def test_topk_long_rows_definite_keys_fill_k():
+    """Exactly K keys lie above the upper bound, so no candidate is kept.  The
+    sampled keys all hold one value (both bounds land on it), K larger keys sit
+    outside the sample and every other key lies below it: the K definite keys
+    are the answer and the 4096 sampled keys are candidates that all lose."""
+    dsa = _dsa()
+    rng = np.random.default_rng(33)
+    N, K = 70000, 2048
+    sampled = _sampled_mask(N)
+    vals = np.full((1, 1, N), 0.25, dtype=np.float32)
+    vals[0, 0, sampled] = 0.5
+    big = rng.choice(np.flatnonzero(~sampled), K, replace=False)
+    vals[0, 0, big] = (2.0 + rng.random(K)).astype(np.float32)
+    idx = dsa.topk(torch.from_numpy(vals).cuda(), K, N - 1).cpu().numpy()
+    exp = oracle.topk_row(vals[0, 0], K)
+    assert np.array_equal(exp, np.sort(big)), "the construction's answer"
+    assert np.array_equal(idx[0, 0], exp)
+
+
+@pytest.mark.parametrize("int_valued,K", [
+    (False, 256),    # a short candidate window: the list path
+    (True, 256),
+    (False, 2048),   # the window holds more than 4096 candidates: the fallback
+])
+def test_topk_rows_over_64_segments(int_valued, K):
+    """Rows longer than 2^20 keys (68 segments): the final step scans the
+    per-segment counts with block-wide prefix sums instead of one wave."""
+    dsa = _dsa()
+    rng = np.random.default_rng(41)
+    N, Tq = 1_100_000, 2
+    if int_valued:
+        vals = (rng.integers(0, 1 << 20, size=(1, Tq, N)) / 64).astype(np.float32)
+    else:
+        vals = rng.standard_normal((1, Tq, N)).astype(np.float32)
+    idx = dsa.topk(torch.from_numpy(vals).cuda(), K, N - Tq).cpu().numpy()
+    for t in range(Tq):
+        n = oracle.n_valid_keys(t, N - Tq, N)
+        assert np.array_equal(idx[0, t], oracle.topk_row(vals[0, t, :n], K)), f"row {t} (n={n})"
 
 
 def test_topk_long_rows_many_rows():
