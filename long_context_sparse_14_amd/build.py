@@ -18,6 +18,10 @@ LIB_PATH = os.path.join(PKG, "libdsa.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache.hip", "proj.hip", "dsa_api.cpp"]
 ARCH = "gfx950"
+# Per-source flags.  The decode indexers keep their two MFMA accumulator
+# blocks in ordinary vector registers rather than accumulation registers, so
+# the per-tile score epilogue reads them without a copy instruction each.
+EXTRA_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -34,7 +38,7 @@ def common_flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags()
+    cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, [])
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
