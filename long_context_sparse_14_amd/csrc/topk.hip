@@ -67,6 +67,9 @@ __device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N,
 }
 
 // Exclusive block-wide prefix sum of v; `total` receives the block sum.
+// Without TRAIL the closing barrier is left out, and the caller must pass
+// another barrier before sbuf[0 .. TK_WAVES) is written again.
+template <bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, uint32_t* sbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
@@ -79,7 +82,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total,
     tot += s;
     before += (w < wave) ? s : 0u;
   }
-  __syncthreads();
+  if (TRAIL) __syncthreads();
   total = tot;
   return before + x - v;
 }
@@ -130,9 +133,11 @@ __device__ __forceinline__ int bit_width(uint32_t x) { return x == 0u ? 0 : 32 -
 // Given a histogram h of 2^FBITS bins, find for each of two descending ranks
 // ra, rb (1-based, at most the histogram total) the bin that holds it;
 // *_above receives how many counted keys lie in higher bins, count_a how many
-// lie in bin ba.  s_res: 8 words.
-template <int FBITS>
-__device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, uint32_t rb, uint32_t& ba,
+// lie in bin ba.  s_res: 8 words; words 0..4 stay valid until the next call
+// (whose own barriers precede its writes).  With ZERO each thread clears the
+// bins it read, and the closing barrier publishes the cleared histogram.
+template <int FBITS, bool ZERO = false>
+__device__ __forceinline__ void find_two_bins(uint32_t* h, uint32_t ra, uint32_t rb, uint32_t& ba,
                                               uint32_t& above_a, uint32_t& bb, uint32_t& above_b,
                                               uint32_t& count_a, uint32_t* sbuf, uint32_t* s_res) {
   constexpr int NB = 1 << FBITS, PER_T = NB / TK_THREADS;
@@ -144,8 +149,11 @@ __device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, ui
     c[u] = h[NB - 1 - PER_T * tid - u];
     t += c[u];
   }
+  if (ZERO)
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) h[NB - 1 - PER_T * tid - u] = 0u;
   uint32_t tot;
-  uint32_t run = block_excl_scan(t, tot, sbuf);
+  uint32_t run = block_excl_scan<false>(t, tot, sbuf);  // the s_res barrier below closes it
 #pragma unroll
   for (int u = 0; u < PER_T; ++u) {
     const uint32_t b = (uint32_t)(NB - 1 - PER_T * tid - u);
@@ -166,11 +174,10 @@ __device__ __forceinline__ void find_two_bins(const uint32_t* h, uint32_t ra, ui
   bb = s_res[2];
   above_b = s_res[3];
   count_a = s_res[4];
-  __syncthreads();
 }
 
 // Block-wide smallest and largest of per-thread values (mn, mx).
-// sbuf2: 2 * TK_WAVES words.
+// sbuf2: 2 * TK_WAVES words, written once per workgroup (no closing barrier).
 __device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t& kmin, uint32_t& kmax,
                                               uint32_t* sbuf2) {
   mn = wave_min(mn);
@@ -190,7 +197,6 @@ __device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t
   }
   kmin = mn;
   kmax = mx;
-  __syncthreads();
 }
 
 // Exact select among the keys in [lo, hi] of a key set: the key value at
@@ -201,7 +207,9 @@ __device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t
 // every key of the set in [lo, hi] to hb.add((key - lo) >> shift, h), and
 // each_key(lo, hi, fn) must call fn(key) for the same keys.  Once the kept bin
 // holds at most 64 keys they are copied to `small` (65 words) and one wave
-// ranks them directly, in place of further histogram rounds.
+// ranks them directly, in place of further histogram rounds.  On entry all
+// 2^FBITS bins of h and the counter small[64] must be zero, made visible by a
+// barrier; each round's bin search clears the histogram for the next one.
 template <int FBITS, typename AddKeys, typename EachKey>
 __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo, uint32_t hi, uint32_t r,
                                 uint32_t& above, uint32_t* h, uint32_t* sbuf, uint32_t* s_res, uint32_t* small) {
@@ -209,15 +217,12 @@ __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo,
 #pragma unroll 1
   while (true) {
     const int shift = max(0, bit_width(hi - lo) - FBITS);
-    for (int b = threadIdx.x; b < (1 << FBITS); b += TK_THREADS) h[b] = 0;
-    if (threadIdx.x == 0) small[64] = 0u;
-    __syncthreads();
     HotBins hb;
     add_keys(hb, lo, hi, shift);
     hb.flush(h);
     __syncthreads();
     uint32_t b, ab, b2, ab2, cnt;
-    find_two_bins<FBITS>(h, r, r, b, ab, b2, ab2, cnt, sbuf, s_res);
+    find_two_bins<FBITS, true>(h, r, r, b, ab, b2, ab2, cnt, sbuf, s_res);
     above += ab;
     r -= ab;
     const uint32_t nlo = lo + (b << shift);
@@ -244,12 +249,11 @@ __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo,
           s_res[5] = ki;
           s_res[6] = gt;
         }
+        if (i == 0) small[64] = 0u;  // every append is done: reset the counter
       }
       __syncthreads();
-      const uint32_t T = s_res[5];
       above += s_res[6];
-      __syncthreads();
-      return T;
+      return s_res[5];
     }
   }
 }
@@ -306,8 +310,10 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_
       }
     }
   }
+  for (int b = tid; b < HB; b += TK_THREADS) hist[b] = 0u;  // the select starts from empty bins
+  if (tid == 0) small[64] = 0u;
   uint32_t kmin, kmax;
-  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);  // its barriers also publish skey
+  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);  // its barrier also publishes skey and the bins
   auto key_at = [&](int i) -> uint32_t { return skey != nullptr ? skey[i] : float_order_key(src[i]); };
   // (the bins span the keys' own range, so plain atomics rarely collide)
   auto add_row = [&](HotBins&, uint32_t lo, uint32_t hi, int shift) {
@@ -483,10 +489,9 @@ __device__ __forceinline__ void sample_bounds(const float* __restrict__ src, int
       mn = min(mn, k[u]);
       mx = max(mx, k[u]);
     }
-  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);
+  for (int b = threadIdx.x; b < FB; b += TK_THREADS) h[b] = 0u;
+  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);  // its barrier also publishes the cleared bins
   const int shift = max(0, bit_width(kmax - kmin) - FB_BITS);
-  for (int b = threadIdx.x; b < FB; b += TK_THREADS) h[b] = 0;
-  __syncthreads();
   {
     HotBins hb;
 #pragma unroll
@@ -590,6 +595,10 @@ __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, 
   }
   const int nseg = (int)((n + SEG - 1) / SEG);
   const size_t s0 = (size_t)row * G;
+  // the select's histogram and small-bin counter start empty (published by
+  // the barriers of the count scan below)
+  for (int b = tid; b < FB; b += TK_THREADS) sm.h[b] = 0u;
+  if (tid == 0) sm.small[64] = 0u;
   // per-segment list offsets: exclusive prefix sums of the list lengths
   // (nseg <= TK_THREADS); up to 64 segments (rows up to 2^20 keys) one wave
   // scans them without barriers
