@@ -81,12 +81,14 @@ KERNEL_SOURCES = {
 
 
 def kernel_sources_digest(kernel: str) -> str:
-    """Digest of the HIP sources of one kernel."""
+    """Digest of the HIP sources of one kernel and their per-file compile flags."""
+    from long_context_sparse_14_amd import build as _build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_sparse_14_amd", "csrc")
     for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
+        h.update(" ".join(_build.EXTRA_FLAGS.get(name, [])).encode())
     return h.hexdigest()[:16]
 
 
