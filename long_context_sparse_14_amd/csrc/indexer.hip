@@ -312,15 +312,51 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
       const float sc = weighted_relu_sum(f, cc[0], cc[1]);
       if (half == 0 && kk0 + col < n_valid) sr[kk0 + col] = sc;
     };
-    if (nbv > 0) mma_block(0, c[0]);
+    if (left >= TK) {
+      // Full tile (every key visible), branch-free: the scheduler is told to
+      // put four vector instructions of block nb-1's epilogue after each of
+      // block nb's MFMAs, so they issue while the matrix core runs instead of
+      // after it.  The scores leave after the last block.
+      float scv[NBK];
+      mma_block(0, c[0]);
 #pragma unroll
-    for (int nb = 1; nb < NBK; ++nb) {
-      if (nb < nbv) mma_block(nb, c[nb & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (nb - 1 < nbv) epi_block(nb - 1, c[(nb - 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int nb = 1; nb < NBK; ++nb) {
+        const uint16_t* lp = &ks[buf][(32 * nb + col) * PITCH + 64 * half];
+        bf16x8 bv[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) bv[s] = *reinterpret_cast<const bf16x8*>(lp + 8 * s);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16(&cc)[2] = c[nb & 1];
+        cc[0] = f32x16{};
+        cc[1] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          cc[0] = mfma32x32x16(f.a0[s], bv[s], cc[0]);
+          cc[1] = mfma32x32x16(f.a1[s], bv[s], cc[1]);
+        }
+        scv[nb - 1] = weighted_relu_sum(f, c[(nb - 1) & 1][0], c[(nb - 1) & 1][1]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four vector instructions
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      scv[NBK - 1] = weighted_relu_sum(f, c[(NBK - 1) & 1][0], c[(NBK - 1) & 1][1]);
+      if (half == 0)
+#pragma unroll
+        for (int nb = 0; nb < NBK; ++nb) sr[k0 + 32 * nb + col] = scv[nb];
+    } else {
+      if (nbv > 0) mma_block(0, c[0]);
+#pragma unroll
+      for (int nb = 1; nb < NBK; ++nb) {
+        if (nb < nbv) mma_block(nb, c[nb & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nb - 1 < nbv) epi_block(nb - 1, c[(nb - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (NBK - 1 < nbv) epi_block(NBK - 1, c[(NBK - 1) & 1]);
     }
-    if (NBK - 1 < nbv) epi_block(NBK - 1, c[(NBK - 1) & 1]);
     if (it + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();
   }

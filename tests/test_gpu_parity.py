@@ -110,6 +110,28 @@ def test_indexer_bf16_exact(B, Tq, N, q_pos0):
         causal_scores_equal(scores[b], ref, ts, f"scores b={b}")
 
 
+@pytest.mark.parametrize("B,Tq,N,q_pos0", [
+    (1, 300, 300, 0),        # prefill: rows end inside a tile, some inside its last 32-key block
+    (2, 77, 200, 50),        # chunked prefill: rows of 51..127 keys in a 200-row cache
+    (2, 1, 5000, 3000),      # decode kernel, keys past the row in the cache
+])
+def test_indexer_leaves_entries_past_the_row(B, Tq, N, q_pos0):
+    """Entries of a score row past its visible keys are not written, and the
+    visible ones stay exact."""
+    dsa = _dsa()
+    wl, x = _bf16_indexer_case(Tq, N, q_pos0, B)
+    out = torch.full((B, Tq, N), -7.25, dtype=torch.float32, device="cuda")
+    dsa.index_scores(dev(x["q_idx"]), dev(x["k_idx"]), dev(x["w"]), q_pos0, scores=out)
+    got = out.cpu().numpy()
+    for b in range(B):
+        ts = list(range(Tq))
+        causal_scores_equal(got[b], oracle.index_scores_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], ts, q_pos0),
+                            ts, f"scores b={b}")
+        for t in ts:
+            n = oracle.n_valid_keys(t, q_pos0, N)
+            assert np.all(got[b, t, n:] == -7.25), f"b={b} t={t}: entries past key {n} were written"
+
+
 def test_indexer_bf16_negative_weights_exact():
     dsa = _dsa()
     wl, x = _bf16_indexer_case(70, 70, 0, 1, synth.Dist("choice", values=(-1.0, 0.5, -0.25, 2.0)))
