@@ -90,6 +90,7 @@ def _tdev(a):
     (2, 1, 5000, 4999),     # decode: every key visible, a ragged last tile
     (3, 4, 3000, 1000),     # causal rows of 1001..1004 keys, cache longer than the rows
     (1, 2, 40, 0),          # rows of one and two keys
+    (1, 1, 131072, 131071), # one query over 128K keys: one round of 256-key workgroups
 ])
 def test_index_scores_fp8(B, Tq, N, q_pos0):
     dsa = _dsa()

@@ -98,6 +98,7 @@ def _bf16_indexer_case(Tq, N, q_pos0, B=1, dist_w=None):
     (2, 1, 40000, 39999),    # decode, several workgroups per row and a ragged last one
     (1, 4, 70, 10),          # decode queries seeing only part of the cache
     (1, 1, 1, 0),            # a single key
+    (1, 1, 131072, 131071),  # one query over 128K keys: one round of 512-key workgroups
     (1, 9, 9, 0),            # tiled path with a single short tile
 ])
 def test_indexer_bf16_exact(B, Tq, N, q_pos0):
