@@ -586,7 +586,7 @@ __global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const u
   const int64_t rh = (int64_t)blockIdx.x * COMBINE_WAVES + (threadIdx.x >> 6);
   const int64_t stride = R * MH;
   if (rh >= stride) return;  // whole waves only
-  // lane s < splits holds split s's log2-sum-exp (splits <= 32)
+  // lane s < splits holds split s's log2-sum-exp (splits <= 64, checked at launch)
   const float ls = lane < splits ? part_lse[lane * stride + rh] : -INFINITY;
   float M = ls;
 #pragma unroll
