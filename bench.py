@@ -213,72 +213,92 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}), flush=True)
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _host_cpus() -> int:
+    return os.cpu_count() or 1
+
+
 def cpu_baseline(wl, x, budget_s: float):
-    """The oracle, as it stands, on whole queries of the same workload, in seeded
-    random order and cycling over them, until the budget is spent."""
+    """The C++ oracle, as it stands, on whole queries of the same workload.
+
+    Queries are taken in seeded random order, cycling over the workload's
+    queries, in calls of one query per oracle thread (the oracle splits a
+    call's queries over its threads), until the budget is spent."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    nthreads = oracle.threads()
     rows = [(b, t) for b in range(wl.B) for t in range(wl.Tq)]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(len(rows))
-    done = 0
+    order = np.random.default_rng(0).permutation(len(rows))
+    done, calls = 0, 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 <= budget_s:
-        b, t = rows[order[done % len(rows)]]
+        sel = [rows[order[(done + i) % len(rows)]] for i in range(nthreads)]
         if "index" in wl.stages:
-            oracle.forward_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], x["q"][b],
-                                lambda sel, b=b: x["kv"][b][sel], [t], wl.q_pos0, wl.K, wl.scale, wl.DV)
+            oracle.forward_batch(x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"], sel, wl.q_pos0, wl.K, wl.scale,
+                                 wl.DV, want_scores=False)
         else:
-            rows_kv = {int(j): x["kv"][b, j] for j in x["idx"][b, t] if j >= 0}
-            oracle.sparse_mla_rows(x["q"][b, t], rows_kv, x["idx"][b, t], wl.scale, wl.DV)
-        done += 1
+            oracle.sparse_mla_batch(x["q"], x["kv"], x["idx"], sel, wl.scale, wl.DV)
+        done += len(sel)
+        calls += 1
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} queries of {wl.name} (whole path per query), cycling in seeded random order "
-                      f"over its {len(rows)}, {el:.1f} s"}
+    return {"value": done / el, "unit": "queries/s", "cores": int(nthreads), "kind": "oracle",
+            "host_cpus": _host_cpus(), "cpu_model": _cpu_model(),
+            "sample": f"{done} queries of {wl.name} (whole path per query: indexer, top-k, sparse MLA), in {calls} "
+                      f"calls of {nthreads}, cycling in seeded random order over its {len(rows)}, {el:.1f} s; "
+                      f"C++ oracle, double, {nthreads} threads"}
 
 
 def cpu_baseline_fp8(wl, x, budget_s: float, max_seqs: int = 4):
-    """The oracle's FP8 path on whole decode queries: the sequence's key cache is quantised
-    first (untimed: the cache is held as codes), then the query is quantised, scored,
-    selected and attended (timed)."""
+    """The C++ oracle's FP8 path on whole decode queries: the key caches of a few sequences are
+    quantised first (untimed: the cache is held as codes); each timed call quantises one query per
+    oracle thread, scores, selects and attends."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    rng = np.random.default_rng(0)
-    seqs = rng.permutation(wl.B)[:max_seqs]
-    cache = {int(b): oracle.quantize_fp8_rows(x["k_idx"][b]) for b in seqs}  # untimed
+    nthreads = oracle.threads()
+    seqs = np.sort(np.random.default_rng(0).permutation(wl.B)[:max_seqs])
+    k8, ks = oracle.quantize_fp8_rows(x["k_idx"][seqs])                      # untimed
+    q_idx, w, q = x["q_idx"][seqs], x["w"][seqs], x["q"][seqs]
+    kv = x["kv"][seqs]
+    rows = [(s, t) for s in range(len(seqs)) for t in range(wl.Tq)]
     done, timed = 0, 0.0
+    N = wl.N
     while timed <= budget_s:
-        b = int(seqs[(done // wl.Tq) % len(seqs)])
-        k8, ks = cache[b]
-        t = done % wl.Tq
+        sel = [rows[(done + i) % len(rows)] for i in range(nthreads)]
         t0 = time.perf_counter()
-        q8, qs = oracle.quantize_fp8_rows(x["q_idx"][b, t])
-        sc = oracle.index_scores_fp8_rows(q8[None], qs[None], k8, ks, x["w"][b, t][None], [0], wl.q_pos0 + t)[0]
-        idx = oracle.topk_row(sc.astype(np.float32), wl.K)
-        sel = idx[idx >= 0]
-        rows = {int(j): r for j, r in zip(sel, x["kv"][b][sel])}
-        oracle.sparse_mla_rows(x["q"][b, t], rows, idx, wl.scale, wl.DV)
+        q8, qs = oracle.quantize_fp8_rows(q_idx)
+        sc = np.full((len(sel), N), -np.inf, dtype=np.float32)
+        nvalid = []
+        for i, (s, t) in enumerate(sel):
+            r = oracle.index_scores_fp8_rows(q8[s], qs[s], k8[s], ks[s], w[s], [t], wl.q_pos0)[0]
+            sc[i, :len(r)] = r
+            nvalid.append(len(r))
+        idx = oracle.topk_rows(sc, nvalid, wl.K)
+        idx_full = np.full((len(seqs), wl.Tq, wl.K), -1, dtype=np.int32)
+        for i, (s, t) in enumerate(sel):
+            idx_full[s, t] = idx[i]
+            oracle.sparse_mla_batch(q, kv, idx_full, [(s, t)], wl.scale, wl.DV)
         timed += time.perf_counter() - t0
-        done += 1
-    return {"value": done / timed, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+        done += len(sel)
+    return {"value": done / timed, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "host_cpus": _host_cpus(), "cpu_model": _cpu_model(),
             "sample": f"{done} queries of {wl.name} with the FP8 indexer (whole path per query), cycling over the "
                       f"queries of {len(seqs)} sequences whose key caches were quantised beforehand (untimed), "
-                      f"{timed:.1f} s"}
+                      f"{timed:.1f} s; C++ oracle, double, one query at a time"}
 
 
 def bench_next(args):

@@ -538,3 +538,66 @@ def pin_paged_gather(paged_gather) -> bool:
     ident = _safe(paged_gather, pool, np.arange(10), bs, 10 * bs)
     return got is not None and np.array_equal(got, x) and ident is not None and \
         np.array_equal(ident, pool, equal_nan=True)
+
+
+# ------------------------------------------------------------- composition ---
+
+def pin_forward(forward_rows) -> bool:
+    """Indexer -> top-k -> sparse MLA, composed: on the hand-derived indexer
+    example the composition returns the fixture's scores and indices, and
+    with K >= L (every visible key selected) its attention is plain causal
+    attention, checked against torch's scaled_dot_product_attention (CPU,
+    float64) and logsumexp."""
+    import torch
+    g = load_golden("indexer_topk_tiny.json")
+    r = _rng(71)
+    T, H, D, DV = len(g["q_idx"]), 2, 5, 3
+    q = r.standard_normal((T, H, D))
+    kv = r.standard_normal((T, D))
+    res = _safe(forward_rows, np.array(g["q_idx"], dtype=np.float64), np.array(g["k_idx"], dtype=np.float64),
+                np.array(g["w"], dtype=np.float64), q, kv, range(T), g["q_pos0"], g["K"], 0.6, DV)
+    if res is None:
+        return False
+    for x, s, i in zip(res, g["scores"], g["idx"]):
+        if not (np.array_equal(x["scores"], np.array(s, dtype=np.float64)) and np.array_equal(x["idx"], np.array(i))):
+            return False
+    L, HI, DI = 11, 3, 4
+    qI = r.integers(-3, 4, size=(L, HI, DI)).astype(np.float64)
+    kI = r.integers(-3, 4, size=(L, DI)).astype(np.float64)
+    w = r.choice([0.5, 1.0, 2.0], size=(L, HI))
+    q = r.standard_normal((L, H, D))
+    kv = r.standard_normal((L, D))
+    res = forward_rows(qI, kI, w, q, kv, range(L), 0, L, 0.45, DV)
+    tq = torch.from_numpy(q).permute(1, 0, 2)                                   # [H, L, D]
+    tk = torch.from_numpy(kv)[None].expand(H, L, D)
+    tv = torch.from_numpy(kv[:, :DV])[None].expand(H, L, DV)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=0.45).permute(1, 0, 2)
+    logits = (tq @ tk.transpose(1, 2)) * 0.45
+    causal = torch.ones(L, L, dtype=torch.bool).tril()
+    ref_lse = torch.logsumexp(logits.masked_fill(~causal, float("-inf")), dim=-1).permute(1, 0).numpy()
+    for t, x in enumerate(res):
+        exp_idx = np.array(list(range(t + 1)) + [-1] * (L - t - 1), dtype=np.int32)
+        if not (np.array_equal(x["idx"], exp_idx) and np.allclose(x["o"], ref[t].numpy(), atol=1e-12)
+                and np.allclose(x["lse"], ref_lse[t], atol=1e-12)):
+            return False
+    return True
+
+
+def pin_topk_long_ties(topk_row) -> bool:
+    """Rows of a few hundred keys drawn from three values: the rank-count
+    definition fixes which of the tied keys are kept (the lower indices)."""
+    r = _rng(23)
+    for trial in range(20):
+        n = int(r.integers(100, 400))
+        K = int(r.integers(1, n))
+        v = r.integers(0, 3, size=n).astype(np.float32)
+        got = _safe(topk_row, v, K)
+        if got is None:
+            return False
+        # rank-count definition, vectorised: rank(s) = #{s' : v[s'] > v[s] or (v[s'] == v[s] and s' < s)}
+        i = np.arange(n)
+        rank = ((v[None, :] > v[:, None]) | ((v[None, :] == v[:, None]) & (i[None, :] < i[:, None]))).sum(1)
+        exp = np.flatnonzero(rank < K).astype(np.int32)
+        if not np.array_equal(got, exp):
+            return False
+    return True
