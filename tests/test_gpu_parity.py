@@ -1,10 +1,13 @@
-"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+"""GPU parity: the HIP path (through the C ABI) against the C++ CPU oracle.
 
 Indexer scores and top-k indices must match bit for bit (the inputs are
 integer-valued with power-of-two weights, so fp32 sums are exact); attention
 outputs must match within |d| <= 2e-2 + 1e-2|ref| (bf16) or
-|d| <= 1e-5|ref| + 1e-6 (fp32).  Small cases run whole; the full-size
-workloads compare sampled rows and check properties on every row.
+|d| <= 1e-5|ref| + 1e-6 (fp32).  Small cases run whole.  At full size, in the
+launch configuration the benchmark times: the 8192-token indexer + top-k is
+checked on every row, the 16384-token prefill on a fixed stratified set of
+512 query rows, and both decode batches on every query; each prints its
+largest attention error against the tighter internal target of 4e-3.
 """
 import math
 
@@ -35,9 +38,18 @@ def _dsa():
 
 
 def _forward_reference(wl, x, ts, b=0):
-    kv = oracle.as_f64(x["kv"][b])
-    return oracle.forward_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], x["q"][b], kv, ts, wl.q_pos0,
+    return oracle.forward_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], x["q"][b], x["kv"][b], ts, wl.q_pos0,
                                wl.K, wl.scale, wl.DV)
+
+
+INTERNAL_TARGET = 4e-3   # tighter regression target for bf16 attention outputs, reported (not the bar)
+
+
+def _report(what, got, ref):
+    err = np.abs(got - ref)
+    print(f"[parity] {what}: max|d| = {err.max():.3e} (internal target {INTERNAL_TARGET:.0e}), "
+          f"mean|d| = {err.mean():.3e}, max|ref| = {np.abs(ref).max():.3e}", flush=True)
+    return float(err.max())
 
 
 # ------------------------------------------------------------------ small
@@ -380,8 +392,13 @@ def test_causality_perturbation_bf16():
 
 # ------------------------------------------------------------- full sizes
 
+def _visible_mask(ts, q_pos0, N):
+    ts = np.asarray(ts)
+    return np.arange(N)[None, :] < np.minimum(N, ts + q_pos0 + 1)[:, None]
+
+
 def test_indexer_topk_prefill_8k():
-    """L=8192, 64x128 indexer, top-2048: sampled rows exact; selection properties on every row."""
+    """L=8192, 64x128 indexer, top-2048: every row's scores bit for bit and every row's indices."""
     dsa = _dsa()
     wl = WL["indexer_topk_prefill_8k"]
     x = synth.make_inputs(wl)
@@ -389,15 +406,22 @@ def test_indexer_topk_prefill_8k():
     scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], 0)
     idx = dsa.topk(scores, wl.K, 0)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    ts = sorted(set([0, 1, 2, 2046, 2047, 2048, 2049, 4095, 8191] + rng.integers(0, 8192, 23).tolist()))
-    ref = oracle.index_scores_rows(x["q_idx"][0], x["k_idx"][0], x["w"][0], ts, 0)
-    sc = scores[0].cpu().numpy()
-    causal_scores_equal(sc, ref, ts, "scores")
-    ix = idx[0].cpu().numpy()
-    for t, r in zip(ts, ref):
-        assert np.array_equal(ix[t], oracle.topk_row(r.astype(np.float32), wl.K)), f"idx row {t}"
     _check_selection_properties(scores[0], idx[0], 0, wl.K)
+    sc = scores[0].cpu().numpy()
+    ix = idx[0].cpu().numpy()
+    del scores, idx, d
+    N = wl.N
+    for r0 in range(0, wl.Tq, 1024):
+        ts = np.arange(r0, min(wl.Tq, r0 + 1024))
+        ref = oracle.index_scores_batch(x["q_idx"], x["k_idx"], x["w"], [(0, t) for t in ts], 0)
+        vis = _visible_mask(ts, 0, N)
+        ref32 = ref.astype(np.float32)
+        bad = (sc[ts] != ref32) & vis
+        assert not bad.any(), f"scores differ on rows {ts[bad.any(1)][:8]}"
+        ref_idx = oracle.topk_rows(np.where(vis, ref32, 0), np.minimum(N, ts + 1), wl.K)
+        rows_bad = ~(ix[ts] == ref_idx).all(1)
+        assert not rows_bad.any(), f"indices differ on rows {ts[rows_bad][:8]}"
+    print(f"[parity] indexer_topk_prefill_8k: all {wl.Tq} rows, scores and indices exact", flush=True)
 
 
 def _check_selection_properties(scores, idx, q_pos0, K):
@@ -433,44 +457,59 @@ def test_sparse_mla_decode_b64_32k():
     out, lse = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), dev(x["idx"]), wl.scale, wl.DV)
     o = host64(out)
     ls = host64(lse)
-    for b in range(wl.B):
-        rows = {int(i): x["kv"][b, i] for i in x["idx"][b, 0]}
-        o_ref, l_ref = oracle.sparse_mla_rows(x["q"][b, 0], rows, x["idx"][b, 0], wl.scale, wl.DV)
-        assert_close(o[b, 0], o_ref, "bf16", f"out b={b}")
-        assert_lse_close(ls[b, 0], l_ref, f"lse b={b}")
+    o_ref, l_ref = oracle.sparse_mla_batch(x["q"], x["kv"], x["idx"], [(b, 0) for b in range(wl.B)], wl.scale,
+                                           wl.DV)
+    assert_close(o[:, 0], o_ref, "bf16", "out")
+    assert_lse_close(ls[:, 0], l_ref, "lse")
+    _report("sparse_mla_decode_b64_32k out, all 64 queries", o[:, 0], o_ref)
+
+
+def c4_rows(T=16384, n=512, seed=4):
+    """The fixed stratified query rows of the 16384-token prefill check: the first rows, the rows around
+    index_topk (where a row first holds more keys than it keeps), the last row, and seeded rows."""
+    fixed = [0, 1, 2, 2046, 2047, 2048, 2049, T - 1]
+    rest = np.setdiff1d(np.arange(T), fixed)
+    more = np.random.default_rng(seed).choice(rest, n - len(fixed), replace=False)
+    return np.sort(np.concatenate([fixed, more]))
 
 
 def test_dsa_prefill_16k():
-    """L=16384 full forward: sampled rows exact (indices) and within tolerance (output);
-    the fused call equals the staged calls bit for bit."""
+    """L=16384 full forward: 512 stratified rows against the oracle (scores and indices bit for bit,
+    output within tolerance); the fused call equals the staged calls bit for bit."""
     dsa = _dsa()
     wl = WL["dsa_prefill_16k"]
     x = synth.make_inputs(wl)
     d = {k: dev(v) for k, v in x.items()}
     out, lse, idx = dsa.forward(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale, 0, wl.DV,
                                 return_idx=True)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(4)
-    ts = sorted(set([0, 1, 2047, 2048, 2049, 16383] + rng.integers(0, 16384, 10).tolist()))
-    ref = _forward_reference(wl, x, ts)
-    ix = idx[0].cpu().numpy()
-    o = host64(out[0])
-    ls = host64(lse[0])
-    for r in ref:
-        t = r["t"]
-        assert np.array_equal(ix[t], r["idx"]), f"idx row {t}"
-        assert_close(o[t], r["o"], "bf16", f"out row {t}")
-        assert_lse_close(ls[t], r["lse"], f"lse row {t}")
     scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], 0)
     idx2 = dsa.topk(scores, wl.K, 0)
     out2, lse2 = dsa.sparse_mla(d["q"], d["kv"], idx2, wl.scale, wl.DV)
+    torch.cuda.synchronize()
     assert torch.equal(idx2, idx) and torch.equal(out2, out) and torch.equal(lse2, lse)
     _check_selection_properties(scores[0], idx[0], 0, wl.K)
+    ts = c4_rows(wl.Tq)
+    sc = scores[0].cpu().numpy()[ts]
+    ix = idx[0].cpu().numpy()[ts]
+    o = host64(out[0, torch.from_numpy(ts).cuda()])
+    ls = host64(lse[0, torch.from_numpy(ts).cuda()])
+    del d, out, lse, idx, scores, idx2, out2, lse2
+    ref = oracle.forward_batch(x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"], [(0, t) for t in ts], 0, wl.K,
+                               wl.scale, wl.DV)
+    vis = _visible_mask(ts, 0, wl.N)
+    bad = (sc != ref["scores"].astype(np.float32)) & vis
+    assert not bad.any(), f"scores differ on rows {ts[bad.any(1)][:8]}"
+    rows_bad = ~(ix == ref["idx"]).all(1)
+    assert not rows_bad.any(), f"indices differ on rows {ts[rows_bad][:8]}"
+    assert_close(o, ref["o"], "bf16", "out")
+    assert_lse_close(ls, ref["lse"], "lse")
+    _report(f"dsa_prefill_16k out, {len(ts)} stratified rows", o, ref["o"])
 
 
 def test_dsa_decode_b32_128k():
-    """Batch-32 decode at 131072 context: sampled sequences against the oracle, properties on all;
-    two runs give identical bits."""
+    """Batch-32 decode at 131072 context: every sequence against the oracle -- its full 131072-key score
+    row bit for bit (staged indexer, the launch shape the benchmark times), its indices and its output (fused
+    call); two fused runs give identical bits."""
     dsa = _dsa()
     wl = WL["dsa_decode_b32_128k"]
     x = synth.make_inputs(wl)
@@ -479,23 +518,25 @@ def test_dsa_decode_b32_128k():
                                 wl.DV, return_idx=True)
     out_b, lse_b, idx_b = dsa.forward(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale,
                                       wl.q_pos0, wl.DV, return_idx=True)
+    scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], wl.q_pos0)
     torch.cuda.synchronize()
     assert torch.equal(out, out_b) and torch.equal(idx, idx_b) and torch.equal(lse, lse_b)
-    ix = idx.cpu().numpy()
-    o = host64(out)
-    ls = host64(lse)
-    for b in (0, 11, 31):
-        ref = _forward_reference(wl, x, [0], b)[0]
-        assert np.array_equal(ix[b, 0], ref["idx"]), f"idx b={b}"
-        assert_close(o[b, 0], ref["o"], "bf16", f"out b={b}")
-        assert_lse_close(ls[b, 0], ref["lse"], f"lse b={b}")
-    scores = dsa.index_scores(d["q_idx"], d["k_idx"], d["w"], wl.q_pos0)
-    sc = scores.cpu().numpy()
-    for b in (0, 31):  # full score rows, bit for bit, in the launch shape the benchmark times
-        ref = oracle.index_scores_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], [0], wl.q_pos0)
-        causal_scores_equal(sc[b], ref, [0], f"scores b={b}")
     for b in range(wl.B):
         _check_selection_properties(scores[b], idx[b], wl.q_pos0, wl.K)
+    sc = scores[:, 0].cpu().numpy()
+    ix = idx[:, 0].cpu().numpy()
+    o = host64(out[:, 0])
+    ls = host64(lse[:, 0])
+    del d, out, lse, idx, out_b, lse_b, idx_b, scores
+    ref = oracle.forward_batch(x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"], [(b, 0) for b in range(wl.B)],
+                               wl.q_pos0, wl.K, wl.scale, wl.DV)
+    bad = sc != ref["scores"].astype(np.float32)
+    assert not bad.any(), f"scores differ in sequences {np.flatnonzero(bad.any(1))[:8]}"
+    rows_bad = ~(ix == ref["idx"]).all(1)
+    assert not rows_bad.any(), f"indices differ in sequences {np.flatnonzero(rows_bad)[:8]}"
+    assert_close(o, ref["o"], "bf16", "out")
+    assert_lse_close(ls, ref["lse"], "lse")
+    _report("dsa_decode_b32_128k out, all 32 sequences", o, ref["o"])
 
 
 @pytest.mark.parametrize("B,K", [
