@@ -170,6 +170,32 @@ dsa_status dsa_forward(const void* q_idx, const void* k_idx, const void* w, cons
                        void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.
+ *
+ * Arguments, outputs and errors are those of dsa_forward; the result equals
+ * dsa_forward's bit for bit.  The workspace is instead a scratch array of
+ * DSA_NOALLOC_SCRATCH_BYTES bytes that the library holds in static device
+ * memory: one copy per GPU it runs on, set up on the first call on that GPU
+ * (the device `stream` belongs to; NULL = the current device) and kept until
+ * the process ends.  The call allocates nothing.  A problem whose
+ * dsa_forward_workspace_size exceeds DSA_NOALLOC_SCRATCH_BYTES returns
+ * DSA_ERR_WORKSPACE and launches nothing (64 MiB holds, for example, the
+ * 32-sequence decode at 131072-token context; a 16384-token prefill needs
+ * dsa_forward).  Every call on one GPU shares that GPU's scratch, which keeps
+ * the last call's contents (nothing in it needs to start at zero): calls
+ * that overlap on one GPU (on different streams, or from different threads
+ * without ordering) race and give undefined results.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+dsa_status dsa_forward_noalloc(const void* q_idx, const void* k_idx, const void* w, const void* q,
+                               const void* kv, void* out, float* lse, int32_t* idx_out, int64_t B,
+                               int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I,
+                               int32_t H, int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype,
+                               void* stream);
+
+/*
  * Per-sequence cache lengths ("varlen"): the three steps and the fused call
  * for a batch whose sequences hold different numbers of tokens.
  * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)":

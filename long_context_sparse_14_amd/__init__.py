@@ -12,6 +12,7 @@ Functions mirror the C entry points:
   topk(scores, K, q_pos0=0)                               -> idx [B,Tq,K] int32
   sparse_mla(q, kv, idx, scale, DV=512)                   -> (out [B,Tq,H,DV], lse [B,Tq,H])
   forward(q_idx, k_idx, w, q, kv, K, scale, q_pos0=0, DV=512, return_idx=False)
+  forward_noalloc(q_idx, k_idx, w, q, kv, K, scale, ...) (no workspace: the library's per-GPU scratch)
   index_scores_varlen(q_idx, k_idx, w, seq_lens)          -> scores (per-sequence cache lengths)
   topk_varlen(scores, K, seq_lens)                        -> idx
   forward_varlen(q_idx, k_idx, w, q, kv, K, scale, seq_lens, ...)
@@ -44,6 +45,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dsa.h")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
 DSA_BF16, DSA_F32 = 0, 1
+DSA_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/dsa.h: the scratch of dsa_forward_noalloc
 
 _lib = None
 
@@ -74,6 +76,8 @@ _SIGNATURES = {
     "dsa_forward_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),
     "dsa_forward": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
                                    _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "dsa_forward_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
+                                           _i32, _i32, _i32, _f32, _i32, _p]),
     "dsa_index_scores_varlen": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "dsa_topk_varlen": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]),
     "dsa_forward_varlen": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32,
@@ -233,9 +237,8 @@ def forward_workspace_size(B, Tq, N, H, DV, K, dtype) -> int:
     return int(library().dsa_forward_workspace_size(B, Tq, N, H, DV, K, dt))
 
 
-def forward(q_idx, k_idx, w, q, kv, K: int, scale: float, q_pos0: int = 0, DV: int = 512, out=None, lse=True,
-            idx_out=None, return_idx: bool = False, workspace=None, stream=None):
-    """Indexer -> top-K -> sparse MLA in one call.  Returns (out, lse, idx or None)."""
+def _forward_args(q_idx, k_idx, w, q, kv, K, q_pos0, DV, out, lse, idx_out, return_idx):
+    """Checks and marshals the arguments shared by the fused entry points."""
     B, Tq, H_I, D_I = q_idx.shape
     N = k_idx.shape[1]
     H, D = q.shape[2], q.shape[3]
@@ -256,11 +259,30 @@ def forward(q_idx, k_idx, w, q, kv, K: int, scale: float, q_pos0: int = 0, DV: i
     if return_idx and idx_out is None:
         idx_out = torch.empty((B, Tq, K), dtype=torch.int32, device=q.device)
     pi = _dev(idx_out, "idx_out", 3, torch.int32) if idx_out is not None else None
+    args = (pqi, pki, pw, pq, pkv, po, pl, pi, B, Tq, N, q_pos0, H_I, D_I, H, D, DV, K)
+    return args, (B, Tq, N, H), out, lse_t, idx_out
+
+
+def forward(q_idx, k_idx, w, q, kv, K: int, scale: float, q_pos0: int = 0, DV: int = 512, out=None, lse=True,
+            idx_out=None, return_idx: bool = False, workspace=None, stream=None):
+    """Indexer -> top-K -> sparse MLA in one call.  Returns (out, lse, idx or None)."""
+    args, (B, Tq, N, H), out, lse_t, idx_out = _forward_args(q_idx, k_idx, w, q, kv, K, q_pos0, DV, out, lse,
+                                                              idx_out, return_idx)
     lib = library()
     code = _dtype_code(q)
     ws, nbytes = _workspace(lib.dsa_forward_workspace_size(B, Tq, N, H, DV, K, code), q.device, workspace)
-    _check(lib.dsa_forward(pqi, pki, pw, pq, pkv, po, pl, pi, B, Tq, N, q_pos0, H_I, D_I, H, D, DV, K, scale,
-                           code, ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    _check(lib.dsa_forward(*args, scale, code, ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    return out, lse_t, idx_out
+
+
+def forward_noalloc(q_idx, k_idx, w, q, kv, K: int, scale: float, q_pos0: int = 0, DV: int = 512, out=None,
+                    lse=True, idx_out=None, return_idx: bool = False, stream=None):
+    """forward() through dsa_forward_noalloc: the library's static per-GPU scratch replaces the
+    workspace (at most DSA_NOALLOC_SCRATCH_BYTES).  Pass out / lse / idx_out to allocate nothing
+    on the Python side either."""
+    args, _, out, lse_t, idx_out = _forward_args(q_idx, k_idx, w, q, kv, K, q_pos0, DV, out, lse, idx_out,
+                                                 return_idx)
+    _check(library().dsa_forward_noalloc(*args, scale, _dtype_code(q), _stream(stream)))
     return out, lse_t, idx_out
 
 

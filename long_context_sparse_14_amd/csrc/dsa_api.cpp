@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -209,6 +210,90 @@ dsa_status check_proj_common(const void* a, const void* b, const void* c, int64_
   return DSA_OK;
 }
 
+// Validation shared by the fused entry points (everything but the workspace).
+dsa_status check_forward(const void* q_idx, const void* k_idx, const void* w, const void* q, const void* kv,
+                         const void* out, const float* lse, const int32_t* idx_out, int64_t B, int64_t Tq, int64_t N,
+                         int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t H, int32_t D, int32_t DV, int32_t K,
+                         float scale, int32_t dtype) {
+  dsa_status st = check_index_scores(q_idx, k_idx, w, nullptr, B, Tq, N, q_pos0, H_I, D_I, dtype, false);
+  if (st != DSA_OK) return st;
+  st = check_mla(q, kv, nullptr, out, lse, B, Tq, N, H, D, DV, K, scale, dtype, nullptr, 0, false);
+  if (st != DSA_OK) return st;
+  if (idx_out && !aligned16(idx_out)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 16-byte aligned");
+  return DSA_OK;
+}
+
+// Indexer -> top-k -> sparse MLA on one stream over a validated problem and a
+// workspace of forward_layout(...).total bytes.
+dsa_status run_forward(const void* q_idx, const void* k_idx, const void* w, const void* q, const void* kv, void* out,
+                       float* lse, int32_t* idx_out, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I,
+                       int32_t D_I, int32_t H, int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype,
+                       void* workspace, hipStream_t s) {
+  const ForwardLayout L = forward_layout(B, Tq, N, H, DV, K, dtype);
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  void* mla_ws = ws + L.mla;
+  void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
+
+  hipError_t e;
+  if (dtype == DSA_BF16)
+    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s);
+  else
+    e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
+                                     static_cast<const float*>(w), scores, B, Tq, N, q_pos0, H_I, D_I, s);
+  if (e != hipSuccess) return hip_status(e, "index scores launch");
+  e = dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
+  if (e != hipSuccess) return hip_status(e, "top-k launch");
+  if (dtype == DSA_BF16)
+    e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
+                                    static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, mla_ws, s);
+  else
+    e = dsa::launch_sparse_mla_f32(static_cast<const float*>(q), static_cast<const float*>(kv), idx,
+                                   static_cast<float*>(out), lse, B, Tq, N, H, D, DV, K, scale, s);
+  return hip_status(e, "sparse MLA launch");
+}
+
+}  // namespace
+
+// Scratch of dsa_forward_noalloc: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  In host code its name is
+// only a stand-in for the symbol; the device address of each GPU's copy comes
+// from hipGetSymbolAddress and is the only thing ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch copy of the device `stream` runs on, looked
+// up once per device with that device current.
+dsa_status scratch_of_stream_device(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "finding the stream's device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,40 +373,33 @@ dsa_status dsa_forward(const void* q_idx, const void* k_idx, const void* w, cons
                        float* lse, int32_t* idx_out, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I,
                        int32_t D_I, int32_t H, int32_t D, int32_t DV, int32_t K, float scale, int32_t dtype,
                        void* workspace, size_t ws_bytes, void* stream) {
-  dsa_status st = check_index_scores(q_idx, k_idx, w, nullptr, B, Tq, N, q_pos0, H_I, D_I, dtype, false);
+  dsa_status st = check_forward(q_idx, k_idx, w, q, kv, out, lse, idx_out, B, Tq, N, q_pos0, H_I, D_I, H, D, DV, K,
+                                scale, dtype);
   if (st != DSA_OK) return st;
-  st = check_mla(q, kv, nullptr, out, lse, B, Tq, N, H, D, DV, K, scale, dtype, nullptr, 0, false);
-  if (st != DSA_OK) return st;
-  if (idx_out && !aligned16(idx_out)) return fail(DSA_ERR_INVALID_ARG, "idx_out must be 16-byte aligned");
-  const ForwardLayout L = forward_layout(B, Tq, N, H, DV, K, dtype);
-  if (!workspace || ws_bytes < L.total)
-    return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+  const size_t need = forward_layout(B, Tq, N, H, DV, K, dtype).total;
+  if (!workspace || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes (got %zu)", need, ws_bytes);
   if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return run_forward(q_idx, k_idx, w, q, kv, out, lse, idx_out, B, Tq, N, q_pos0, H_I, D_I, H, D, DV, K, scale, dtype,
+                     workspace, static_cast<hipStream_t>(stream));
+}
 
-  char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws + L.scores);
-  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
-  void* mla_ws = ws + L.mla;
-  void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
+dsa_status dsa_forward_noalloc(const void* q_idx, const void* k_idx, const void* w, const void* q, const void* kv,
+                               void* out, float* lse, int32_t* idx_out, int64_t B, int64_t Tq, int64_t N,
+                               int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t H, int32_t D, int32_t DV, int32_t K,
+                               float scale, int32_t dtype, void* stream) {
+  dsa_status st = check_forward(q_idx, k_idx, w, q, kv, out, lse, idx_out, B, Tq, N, q_pos0, H_I, D_I, H, D, DV, K,
+                                scale, dtype);
+  if (st != DSA_OK) return st;
+  const size_t need = forward_layout(B, Tq, N, H, DV, K, dtype).total;
+  if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+    return fail(DSA_ERR_WORKSPACE, "this problem needs %zu bytes of scratch; dsa_forward_noalloc holds at most %zu "
+                "(use dsa_forward with a workspace)", need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
   hipStream_t s = static_cast<hipStream_t>(stream);
-
-  hipError_t e;
-  if (dtype == DSA_BF16)
-    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s);
-  else
-    e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
-                                     static_cast<const float*>(w), scores, B, Tq, N, q_pos0, H_I, D_I, s);
-  if (e != hipSuccess) return hip_status(e, "index scores launch");
-  e = dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
-  if (e != hipSuccess) return hip_status(e, "top-k launch");
-  if (dtype == DSA_BF16)
-    e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
-                                    static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, mla_ws, s);
-  else
-    e = dsa::launch_sparse_mla_f32(static_cast<const float*>(q), static_cast<const float*>(kv), idx,
-                                   static_cast<float*>(out), lse, B, Tq, N, H, D, DV, K, scale, s);
-  return hip_status(e, "sparse MLA launch");
+  void* ws = nullptr;
+  if ((st = scratch_of_stream_device(s, &ws)) != DSA_OK) return st;
+  return run_forward(q_idx, k_idx, w, q, kv, out, lse, idx_out, B, Tq, N, q_pos0, H_I, D_I, H, D, DV, K, scale, dtype,
+                     ws, s);
 }
 
 dsa_status dsa_index_scores_varlen(const void* q_idx, const void* k_idx, const void* w, float* scores,

@@ -1,6 +1,10 @@
 """The C-ABI library loads, exports every declared symbol, and rejects bad
 arguments on the host before anything reaches the device (no GPU needed: every
-call here fails validation, so no kernel is ever launched)."""
+call here fails validation, so no kernel is ever launched).
+
+The calls pass a fake device address, so the module runs only where no GPU is
+visible: should a validation check ever regress, the call would then launch a
+kernel on that address, which must not happen on a real device."""
 import ctypes
 import os
 
@@ -8,7 +12,13 @@ import pytest
 
 import long_context_sparse_14_amd as dsa
 
-pytestmark = pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH), reason="libdsa.so not built")
+def _gpu_visible() -> bool:
+    import torch
+    return torch.cuda.device_count() > 0   # counts devices without initialising one
+
+
+pytestmark = [pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH), reason="libdsa.so not built"),
+              pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: run only where no GPU is visible")]
 
 BF16, F32 = dsa.DSA_BF16, dsa.DSA_F32
 P = 4096  # a 16-byte aligned fake address; never dereferenced (validation fails first)
@@ -100,6 +110,37 @@ def test_forward_validation_and_workspace_size():
     bad = list(args)
     bad[0] = None
     assert L.dsa_forward(*bad, P, need, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_forward_noalloc_validation():
+    """The scratch-backed fused call validates like dsa_forward and refuses a
+    problem larger than its scratch before any HIP call is made."""
+    L = lib()
+    s = 0.07
+    args = [P, P, P, P, P, P, None, None, 32, 1, 131072, 131071, 64, 128, 128, 576, 512, 2048, s, BF16]
+    assert L.dsa_forward_workspace_size(32, 1, 131072, 128, 512, 2048, BF16) <= dsa.DSA_NOALLOC_SCRATCH_BYTES
+    big = list(args)
+    big[8], big[10], big[11] = 1, 16384, 0           # a 16384-token prefill: 1 GiB of scores
+    big[9] = 16384
+    assert L.dsa_forward_workspace_size(1, 16384, 16384, 128, 512, 2048, BF16) > dsa.DSA_NOALLOC_SCRATCH_BYTES
+    assert L.dsa_forward_noalloc(*big, None) == dsa.DSA_ERR_WORKSPACE
+    assert "scratch" in last()
+    bad = list(args)
+    bad[12] = 32  # H_I
+    assert L.dsa_forward_noalloc(*bad, None) == dsa.DSA_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[4] = None  # kv
+    assert L.dsa_forward_noalloc(*bad, None) == dsa.DSA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[7] = P + 4  # misaligned idx_out
+    assert L.dsa_forward_noalloc(*bad, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_scratch_size_constant_matches_the_header():
+    import re
+    with open(dsa.HEADER_PATH) as f:
+        m = re.search(r"#define DSA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == dsa.DSA_NOALLOC_SCRATCH_BYTES
 
 
 def test_python_binding_refuses_host_tensors():
