@@ -374,8 +374,11 @@ dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_
  * num_blocks * block_size are below 2^31.  seq_lens int64 [B] (device) gives
  * each sequence's length; its Tq queries are its last Tq tokens, exactly as
  * for the varlen entry points, and only table entries of blocks that hold
- * rows < seq_lens[b] are read.  An entry outside [0, num_blocks) is read as
- * block 0 (caller error: wrong results, never an access outside the pool).
+ * rows < seq_lens[b] are read.  A table entry outside [0, num_blocks) marks
+ * an unset block: the paged append writes nothing into it, the paged sparse
+ * MLA masks every index that falls into it (as an index of -1), and the paged
+ * indexer reads it as block 0 (a caller error there: wrong scores, never an
+ * access outside the pool).
  * Every paged call equals the matching static-cache call on the caches
  * gathered through the table (scores over the logical axis of length
  * max_blocks * block_size, indices logical).
@@ -391,7 +394,7 @@ dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_
  *   workspace dsa_paged_workspace_size(...) bytes; idx_out (optional)
  *   receives the logical indices.
  * dsa_cache_append_paged: as dsa_cache_append, pos[b] logical; entries of pos
- *   outside [0, max_blocks * block_size) write nothing.
+ *   outside [0, max_blocks * block_size), or in an unset block, write nothing.
  */
 size_t dsa_paged_workspace_size(int64_t B, int64_t Tq, int64_t max_blocks, int32_t block_size, int32_t H,
                                 int32_t DV, int32_t K, int32_t dtype);

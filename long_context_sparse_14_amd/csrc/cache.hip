@@ -13,17 +13,18 @@
 namespace dsa {
 namespace {
 
-// Pool row of logical row r of sequence b (entries outside the pool read as block 0).
+// Pool row of logical row r of sequence b, or -1 when the sequence's table
+// entry for that block lies outside [0, num_blocks) (an unset block).
 __device__ __forceinline__ int64_t paged_row(const Paged& pg, int64_t b, int64_t r) {
-  int32_t e = pg.table[b * pg.max_blocks + (r >> pg.shift)];
-  if ((uint32_t)e >= (uint32_t)pg.num_blocks) e = 0;
+  const int32_t e = pg.table[b * pg.max_blocks + (r >> pg.shift)];
+  if ((uint32_t)e >= (uint32_t)pg.num_blocks) return -1;
   return ((int64_t)e << pg.shift) | (r & ((1 << pg.shift) - 1));
 }
 
 // One workgroup per sequence: copies the new indexer key row and the new
 // latent row into place, in 2-byte units (every supported row is a whole
 // number of them).  With PAGED, N is the logical capacity max_blocks << shift
-// and the caches are pools.
+// and the caches are pools; a row whose block is unset is not written.
 template <bool PAGED>
 __global__ __launch_bounds__(256) void cache_append_kernel(uint16_t* __restrict__ k_idx, uint16_t* __restrict__ kv,
                                                            const uint16_t* __restrict__ new_k_idx,
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(uint16_t* __restrict_
   const int64_t p = pos[b];
   if (p < 0 || p >= N) return;
   const int64_t row = PAGED ? paged_row(pg, b, p) : b * N + p;
+  if (row < 0) return;
   if (k_idx != nullptr)
     for (int64_t i = threadIdx.x; i < wk; i += blockDim.x) k_idx[row * wk + i] = new_k_idx[b * wk + i];
   if (kv != nullptr)
@@ -41,7 +43,8 @@ __global__ __launch_bounds__(256) void cache_append_kernel(uint16_t* __restrict_
 }
 
 // Logical key indices [R, K] (rows of Tq per sequence) -> pool rows; entries
-// outside [0, max_blocks << shift) become -1 (masked, as before).
+// outside [0, max_blocks << shift), and those whose block is unset, become -1
+// (masked by the sparse MLA).
 __global__ __launch_bounds__(256) void page_translate_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ out,
                                                              int64_t total, int64_t Tq, int K, Paged pg) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;

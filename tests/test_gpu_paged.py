@@ -179,3 +179,40 @@ def test_cache_append_paged_then_attend():
     torch.cuda.synchronize()
     for a, b_ in zip(full, again):
         assert torch.equal(a, b_)
+
+
+def test_unset_blocks_are_never_written_and_are_masked():
+    """A table entry of -1 marks an unset block: an append that lands in it writes nothing (block 0 and
+    every other pool row keep their bytes), and the paged sparse MLA masks the indices that fall into it,
+    giving the attention of the same row with those indices set to -1."""
+    dsa = _dsa()
+    lens, bs, K = [700, 300], 64, 256
+    wl, x, table, num_blocks, pools = _case(lens, bs, K, seed=12)
+    tt = torch.from_numpy(table).cuda()
+    kp, vp = dev(pools["k_idx"]), dev(pools["kv"])
+    k0, v0 = kp.clone(), vp.clone()
+    # sequence 0 appends at logical row 800 (block 12, unset); sequence 1 at row 320 (block 5, unset)
+    pos = [800, 320]
+    assert all(table[b, p // bs] == -1 for b, p in enumerate(pos))
+    new_k = torch.stack([dev(x["k_idx"][b, 5]) for b in range(2)])
+    new_kv = torch.stack([dev(x["kv"][b, 5]) for b in range(2)])
+    dsa.cache_append_paged(kp, vp, new_k, new_kv, _lens(pos), tt, bs)
+    torch.cuda.synchronize()
+    assert torch.equal(kp, k0) and torch.equal(vp, v0), "an append into an unset block wrote into the pool"
+    # indices 640..699 of sequence 0 lie in block 10, which is set; unset its entry so they must be masked
+    table2 = table.copy()
+    table2[0, 10] = -1
+    rng = np.random.default_rng(13)
+    idx = np.full((2, 1, K), -1, dtype=np.int32)
+    for b, n in enumerate(lens):
+        idx[b, 0, :K - 9] = rng.choice(n, size=K - 9, replace=False)
+    assert ((idx[0, 0] >= 640) & (idx[0, 0] < 700)).any()
+    out, lse = dsa.sparse_mla_paged(dev(x["q"]), vp, torch.from_numpy(idx).cuda(), torch.from_numpy(table2).cuda(),
+                                    bs, wl.scale)
+    masked = idx.copy()
+    masked[0, 0][(masked[0, 0] >= 640) & (masked[0, 0] < 704)] = -1
+    out_s, lse_s = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), torch.from_numpy(masked).cuda(), wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_s) and torch.equal(lse, lse_s), "indices in an unset block must be masked"
+    o, l = oracle.sparse_mla_rows(x["q"][0, 0], x["kv"][0], masked[0, 0], wl.scale, wl.DV)
+    assert_close(host64(out[0, 0]), o, "bf16", "attention with the unset block masked")
