@@ -10,7 +10,7 @@ Prints one JSON line: throughput in queries/s over the timed steps (inputs
 resident in HBM), the roofline position of the dominant kernel measured with
 HIP events on the launch stream, and the CPU oracle timed on a bounded sample
 of the same workload.  Timed steps call the fused entry point where the
-workload has one; every tenth step runs the stages as separate calls with
+workload has one; every few steps (at least five per run) run the stages as separate calls with
 events between them, which gives each kernel's duration inside the timed
 region.
 
@@ -73,9 +73,9 @@ def _parse():
 # Source files each timed kernel is built from: stored counter readings stay
 # valid until one of them changes.
 KERNEL_SOURCES = {
-    "indexer_dma_bf16": ["indexer.hip", "device_common.h"],
-    "indexer_tiled_bf16": ["indexer.hip", "device_common.h"],
-    "indexer_dma_fp8": ["indexer.hip", "device_common.h"],
+    "indexer_dma_bf16": ["indexer.hip", "device_common.h", "select_common.h", "launch.h"],
+    "indexer_tiled_bf16": ["indexer.hip", "device_common.h", "select_common.h", "launch.h"],
+    "indexer_dma_fp8": ["indexer.hip", "device_common.h", "select_common.h", "launch.h"],
     "sparse_mla_bf16_kernel": ["sparse_mla.hip", "device_common.h"],
 }
 
@@ -471,10 +471,12 @@ def main():
     # Argument tuples built once: the timed loop only enqueues work through the C ABI.
     calls = {}
     if has_idx:
-        calls["index"] = (lib.dsa_index_scores, (ptr(d["q_idx"]), ptr(d["k_idx"]), ptr(d["w"]), ptr(scores), B, Tq,
-                                                 N, wl.q_pos0, wl.H_I, wl.D_I, code, sp))
-        calls["topk"] = (lib.dsa_topk, (ptr(scores), ptr(idx), B, Tq, N, wl.q_pos0, wl.K, ptr(topk_ws),
-                                        topk_ws.numel(), sp))
+        # the staged pair that the fused call runs (the decode indexer leaves a pre-selection for the top-k)
+        calls["index"] = (lib.dsa_index_scores_presel, (ptr(d["q_idx"]), ptr(d["k_idx"]), ptr(d["w"]), ptr(scores),
+                                                        B, Tq, N, wl.q_pos0, wl.H_I, wl.D_I, wl.K, code, ptr(topk_ws),
+                                                        topk_ws.numel(), sp))
+        calls["topk"] = (lib.dsa_topk_presel, (ptr(scores), ptr(idx), B, Tq, N, wl.q_pos0, wl.K, code, ptr(topk_ws),
+                                               topk_ws.numel(), sp))
     if has_mla:
         calls["mla"] = (lib.dsa_sparse_mla_fwd, (ptr(d["q"]), ptr(d["kv"]), ptr(idx), ptr(out), ptr(lse), B, Tq, N,
                                                  wl.H, wl.D, wl.DV, wl.K, wl.scale, code, ptr(mla_ws),
@@ -502,6 +504,8 @@ def main():
                                                            wl.D_I, code, sp))
         calls["index"] = (lib.dsa_index_scores_fp8, (ptr(q8), ptr(qs), ptr(k8), ptr(ks), ptr(d["w"]), ptr(scores),
                                                      B, Tq, N, wl.q_pos0, wl.H_I, wl.D_I, code, sp))
+        calls["topk"] = (lib.dsa_topk, (ptr(scores), ptr(idx), B, Tq, N, wl.q_pos0, wl.K, ptr(topk_ws),
+                                        topk_ws.numel(), sp))
         if has_mla:
             calls["fused"] = (lib.dsa_forward_fp8, (ptr(q8), ptr(qs), ptr(k8), ptr(ks), ptr(d["w"]), ptr(d["q"]),
                                                     ptr(d["kv"]), ptr(out), ptr(lse), None, B, Tq, N, wl.q_pos0,
@@ -539,11 +543,12 @@ def main():
         run("fused")
 
     # Steps run the fused entry point where the workload has one (one C-ABI
-    # call); every INSTR-th step of the timed region instead runs the stages as
-    # separate calls with HIP events between them, which measures each
-    # kernel's duration live on the launch stream (--staged: every step).
+    # call); every INSTR-th step of the timed region (at least five of them,
+    # at most every tenth) instead runs the stages as separate calls with HIP
+    # events between them, which measures each kernel's duration live on the
+    # launch stream (--staged: every step).
     has_fused = has_idx and has_mla
-    INSTR = 1 if (args.staged or not has_fused) else 10
+    INSTR = 1 if (args.staged or not has_fused) else max(2, min(10, args.steps // 5))
     for _ in range(args.warmup):
         fused_step() if has_fused else step()
     torch.cuda.synchronize()

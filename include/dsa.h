@@ -120,6 +120,37 @@ dsa_status dsa_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, in
                     int64_t q_pos0, int32_t K, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Steps 1 and 2 as the fused forward runs them at long-context decode shapes.
+ * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)":
+ *  the lightning indexer scores each query against every earlier key, and
+ *  fine-grained token selection keeps the index_topk best.)
+ *
+ * dsa_index_scores_presel: dsa_index_scores (same scores, same rules), and in
+ *   `workspace` (dsa_topk_workspace_size(B, Tq, N, K) bytes) a pre-selection
+ *   of each query's row: the bf16 decode indexer scores every row in segments
+ *   of keys, and each segment also lists, in index order, all of its keys at
+ *   or above a threshold it picks from its own scores (a few times the
+ *   segment's expected share of the row's K best).
+ * dsa_topk_presel: dsa_topk (same indices) for scores and a workspace that
+ *   dsa_index_scores_presel filled with the same B, Tq, N, q_pos0, K and
+ *   dtype.  It selects among the listed keys; where some list's threshold
+ *   lies above the row's K-th key (the listed keys cannot be shown to hold
+ *   the row's top K) that row is selected from its full scores instead, so
+ *   the result is exact in every case.
+ * Where no pre-selection applies (fp32, more than 4 queries per sequence,
+ * rows of at most 16384 keys, K > 4096, or too many segments per row for the
+ * lists) the pair is exactly dsa_index_scores then dsa_topk.  Arguments,
+ * layouts and errors are those of dsa_index_scores and dsa_topk.
+ */
+dsa_status dsa_index_scores_presel(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                                   int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I,
+                                   int32_t D_I, int32_t K, int32_t dtype, void* workspace, size_t ws_bytes,
+                                   void* stream);
+dsa_status dsa_topk_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N,
+                           int64_t q_pos0, int32_t K, int32_t dtype, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/*
  * Step 3 -- sparse MLA in absorbed latent form over the selected keys.
  * (DeepSeek-V3.2 documentation, section "DeepSeek Sparse Attention (DSA)",
  *  paragraph on fine-grained token selection: attention restricted to the
@@ -158,7 +189,8 @@ dsa_status dsa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* idx,
  *
  * Same arguments as the three steps above.  The intermediate scores (and the
  * indices, when idx_out is NULL) live in the workspace; pass idx_out
- * [B, Tq, K] int32 to also receive the selection.  The result equals
+ * [B, Tq, K] int32 to also receive the selection.  Steps 1 and 2 run as
+ * dsa_index_scores_presel and dsa_topk_presel.  The result equals
  * dsa_sparse_mla_fwd(dsa_topk(dsa_index_scores(...))) bit for bit.
  */
 size_t dsa_forward_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t DV,

@@ -10,6 +10,8 @@ works but the first call raises.
 Functions mirror the C entry points:
   index_scores(q_idx, k_idx, w, q_pos0=0)                 -> scores [B,Tq,N] float32
   topk(scores, K, q_pos0=0)                               -> idx [B,Tq,K] int32
+  index_scores_presel(q_idx, k_idx, w, K, q_pos0=0)       -> (scores, top-k workspace with the pre-selection)
+  topk_presel(scores, K, workspace, dtype, q_pos0=0)      -> idx (from the pre-selection)
   sparse_mla(q, kv, idx, scale, DV=512)                   -> (out [B,Tq,H,DV], lse [B,Tq,H])
   forward(q_idx, k_idx, w, q, kv, K, scale, q_pos0=0, DV=512, return_idx=False)
   forward_noalloc(q_idx, k_idx, w, q, kv, K, scale, ...) (no workspace: the library's per-GPU scratch)
@@ -70,6 +72,9 @@ _SIGNATURES = {
     "dsa_index_scores": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "dsa_topk_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "dsa_topk": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]),
+    "dsa_index_scores_presel": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p,
+                                               _sz, _p]),
+    "dsa_topk_presel": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _p, _sz, _p]),
     "dsa_sparse_mla_workspace_size": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32]),
     "dsa_sparse_mla_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _f32,
                                           _i32, _p, _sz, _p]),
@@ -284,6 +289,38 @@ def forward_noalloc(q_idx, k_idx, w, q, kv, K: int, scale: float, q_pos0: int = 
                                                  return_idx)
     _check(library().dsa_forward_noalloc(*args, scale, _dtype_code(q), _stream(stream)))
     return out, lse_t, idx_out
+
+
+def index_scores_presel(q_idx, k_idx, w, K: int, q_pos0: int = 0, scores=None, workspace=None, stream=None):
+    """index_scores plus the decode indexer's pre-selection lists, kept in a top-k workspace.
+    Returns (scores, workspace): pass both to topk_presel."""
+    B, Tq, H_I, D_I = q_idx.shape
+    N = k_idx.shape[1]
+    dt = q_idx.dtype
+    pq, pk, pw = _dev(q_idx, "q_idx", 4, dt), _dev(k_idx, "k_idx", 3, dt), _dev(w, "w", 3, dt)
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q_idx.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    lib = library()
+    ws, nbytes = _workspace(lib.dsa_topk_workspace_size(B, Tq, N, K), q_idx.device, workspace)
+    _check(lib.dsa_index_scores_presel(pq, pk, pw, ps, B, Tq, N, q_pos0, H_I, D_I, K, _dtype_code(q_idx),
+                                       ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    return scores, ws
+
+
+def topk_presel(scores, K: int, workspace, dtype, q_pos0: int = 0, idx=None, stream=None) -> torch.Tensor:
+    """topk for scores and the workspace index_scores_presel filled (dtype: that call's torch dtype)."""
+    B, Tq, N = scores.shape
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if idx is None:
+        idx = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+    pi = _dev(idx, "idx", 3, torch.int32)
+    code = DSA_BF16 if dtype == torch.bfloat16 else DSA_F32
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(library().dsa_topk_presel(ps, pi, B, Tq, N, q_pos0, K, code,
+                                     workspace.data_ptr() if workspace is not None else None, nbytes,
+                                     _stream(stream)))
+    return idx
 
 
 def _seq_lens(seq_lens, B: int) -> int:

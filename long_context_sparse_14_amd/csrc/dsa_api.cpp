@@ -210,6 +210,37 @@ dsa_status check_proj_common(const void* a, const void* b, const void* c, int64_
   return DSA_OK;
 }
 
+// Whether the bf16 decode indexer leaves a pre-selection of each row for the
+// top-k (see PreselWs): decode rows too long for the one-workgroup top-k.
+bool presel_applies(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int32_t K, int32_t dtype, dsa::PreselWs* ps) {
+  if (dtype != DSA_BF16 || dsa::presel_workspace_bytes(B, Tq, N, K) == 0) return false;
+  dsa::PreselWs g;
+  if (!dsa::presel_geometry(B, Tq, N, nmax, K, g)) return false;
+  if (ps) *ps = g;
+  return true;
+}
+
+// Steps 1 and 2 of a bf16 forward: the indexer with the pre-selection and its
+// top-k where it applies, else the plain indexer and top-k.
+hipError_t index_and_topk_bf16(const void* q_idx, const void* k_idx, const void* w, float* scores, int32_t* idx,
+                               int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t K, void* topk_ws,
+                               hipStream_t s, const int64_t* seq_lens = nullptr, const dsa::Paged* pg = nullptr) {
+  const int64_t nmax = seq_lens != nullptr ? N : std::min(N, q_pos0 + Tq);
+  const auto qi = static_cast<const uint16_t*>(q_idx);
+  const auto ki = static_cast<const uint16_t*>(k_idx);
+  const auto wi = static_cast<const uint16_t*>(w);
+  hipError_t e;
+  if (presel_applies(B, Tq, N, nmax, K, DSA_BF16, nullptr)) {
+    const dsa::PreselWs ps = dsa::presel_ws(topk_ws, B, Tq, N, nmax, K);
+    e = dsa::launch_index_scores_bf16(qi, ki, wi, scores, B, Tq, N, q_pos0, s, seq_lens, 1, pg, &ps);
+    if (e != hipSuccess) return e;
+    return dsa::launch_topk_presel(scores, idx, B, Tq, N, q_pos0, K, ps, s, seq_lens);
+  }
+  e = dsa::launch_index_scores_bf16(qi, ki, wi, scores, B, Tq, N, q_pos0, s, seq_lens, 1, pg);
+  if (e != hipSuccess) return e;
+  return dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s, seq_lens);
+}
+
 // Validation shared by the fused entry points (everything but the workspace).
 dsa_status check_forward(const void* q_idx, const void* k_idx, const void* w, const void* q, const void* kv,
                          const void* out, const float* lse, const int32_t* idx_out, int64_t B, int64_t Tq, int64_t N,
@@ -237,15 +268,16 @@ dsa_status run_forward(const void* q_idx, const void* k_idx, const void* w, cons
   void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
 
   hipError_t e;
-  if (dtype == DSA_BF16)
-    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s);
-  else
+  if (dtype == DSA_BF16) {
+    e = index_and_topk_bf16(q_idx, k_idx, w, scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
+    if (e != hipSuccess) return hip_status(e, "index scores / top-k launch");
+  } else {
     e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
                                      static_cast<const float*>(w), scores, B, Tq, N, q_pos0, H_I, D_I, s);
-  if (e != hipSuccess) return hip_status(e, "index scores launch");
-  e = dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
-  if (e != hipSuccess) return hip_status(e, "top-k launch");
+    if (e != hipSuccess) return hip_status(e, "index scores launch");
+    e = dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
+    if (e != hipSuccess) return hip_status(e, "top-k launch");
+  }
   if (dtype == DSA_BF16)
     e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
                                     static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, mla_ws, s);
@@ -340,6 +372,47 @@ dsa_status dsa_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, in
   if (st != DSA_OK) return st;
   return hip_status(dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, static_cast<hipStream_t>(stream)),
                     "top-k launch");
+}
+
+dsa_status dsa_index_scores_presel(const void* q_idx, const void* k_idx, const void* w, float* scores, int64_t B,
+                                   int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t K,
+                                   int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_index_scores(q_idx, k_idx, w, scores, B, Tq, N, q_pos0, H_I, D_I, dtype, true);
+  if (st != DSA_OK) return st;
+  if (K < 1 || K > kMaxK) return fail(DSA_ERR_INVALID_ARG, "K must be in [1, 65536] (got %d)", K);
+  const size_t need = dsa::topk_workspace_bytes(B, Tq, N, K);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "top-k workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nmax = std::min(N, q_pos0 + Tq);
+  hipError_t e;
+  if (presel_applies(B, Tq, N, nmax, K, dtype, nullptr)) {
+    const dsa::PreselWs ps = dsa::presel_ws(workspace, B, Tq, N, nmax, K);
+    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s, nullptr, 1,
+                                      nullptr, &ps);
+  } else if (dtype == DSA_BF16) {
+    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s);
+  } else {
+    e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
+                                     static_cast<const float*>(w), scores, B, Tq, N, q_pos0, H_I, D_I, s);
+  }
+  return hip_status(e, "index scores launch");
+}
+
+dsa_status dsa_topk_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                           int32_t K, int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nmax = std::min(N, q_pos0 + Tq);
+  if (presel_applies(B, Tq, N, nmax, K, dtype, nullptr))
+    return hip_status(dsa::launch_topk_presel(scores, idx, B, Tq, N, q_pos0, K,
+                                              dsa::presel_ws(workspace, B, Tq, N, nmax, K), s),
+                      "top-k launch");
+  return hip_status(dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, s), "top-k launch");
 }
 
 size_t dsa_sparse_mla_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t DV, int32_t K, int32_t dtype) {
@@ -457,15 +530,16 @@ dsa_status dsa_forward_varlen(const void* q_idx, const void* k_idx, const void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e;
-  if (dtype == DSA_BF16)
-    e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                      static_cast<const uint16_t*>(w), scores, B, Tq, N, 0, s, seq_lens);
-  else
+  if (dtype == DSA_BF16) {
+    e = index_and_topk_bf16(q_idx, k_idx, w, scores, idx, B, Tq, N, 0, K, topk_ws, s, seq_lens);
+    if (e != hipSuccess) return hip_status(e, "index scores / top-k launch");
+  } else {
     e = dsa::launch_index_scores_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
                                      static_cast<const float*>(w), scores, B, Tq, N, 0, H_I, D_I, s, seq_lens);
-  if (e != hipSuccess) return hip_status(e, "index scores launch");
-  e = dsa::launch_topk(scores, idx, B, Tq, N, 0, K, topk_ws, s, seq_lens);
-  if (e != hipSuccess) return hip_status(e, "top-k launch");
+    if (e != hipSuccess) return hip_status(e, "index scores launch");
+    e = dsa::launch_topk(scores, idx, B, Tq, N, 0, K, topk_ws, s, seq_lens);
+    if (e != hipSuccess) return hip_status(e, "top-k launch");
+  }
   if (dtype == DSA_BF16)
     e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
                                     static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, mla_ws, s);
@@ -719,12 +793,8 @@ dsa_status dsa_forward_paged(const void* q_idx, const void* k_pool, const void* 
   void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
   int32_t* phys = reinterpret_cast<int32_t*>(ws + L.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_pool),
-                                               static_cast<const uint16_t*>(w), scores, B, Tq, N, 0, s, seq_lens, 1,
-                                               &pg);
-  if (e != hipSuccess) return hip_status(e, "paged index scores launch");
-  e = dsa::launch_topk(scores, idx, B, Tq, N, 0, K, topk_ws, s, seq_lens);
-  if (e != hipSuccess) return hip_status(e, "top-k launch");
+  const hipError_t e = index_and_topk_bf16(q_idx, k_pool, w, scores, idx, B, Tq, N, 0, K, topk_ws, s, seq_lens, &pg);
+  if (e != hipSuccess) return hip_status(e, "paged index scores / top-k launch");
   return run_paged_mla(q, kv_pool, idx, phys, out, lse, B, Tq, K, scale, pg, ws + L.mla, s);
 }
 

@@ -23,8 +23,8 @@
 //    128-key tiles staged in LDS, double-buffered; within a tile each wave
 //    overlaps the MFMAs of one 32-key block with the epilogue of the previous
 //    one; the causal triangle is walked longest query block first.
-#include "device_common.h"
 #include "launch.h"
+#include "select_common.h"
 
 namespace dsa {
 namespace {
@@ -108,6 +108,155 @@ struct PageRows {
   }
 };
 
+// Order key -> the float it stands for (inverse of float_order_key; keys
+// between those of two finite floats stand for finite floats).
+__device__ __forceinline__ float order_key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Pre-selection epilogue of a decode workgroup (WAVES waves), run once its
+// n <= SCAP scores sit in LDS (sl) and before any of them is stored: its
+// barriers settle LDS only, so nothing waits for global stores, and its own
+// global stores come at its end.  It picks a threshold c such that at most
+// cap scores of the segment are >= c and about PRE_M * tgt are (tgt: a few
+// times the segment's expected share of the row's K best), then lists every
+// score >= c (order key and key index) in index order.  Thread t owns the
+// run of scores [PER*t, PER*t + PER); scores 0, 8, 16 and 24 of every run form
+// a systematic sample, and one histogram of the sample over its own key range
+// gives candidate thresholds: the lower edges of the bins holding the sample
+// ranks expected to leave PRE_M[j] * tgt scores at or above them.  The first
+// candidate whose exact count fits in cap is taken (each count is one pass
+// of compares into a per-thread bit mask); if none fits, nothing is listed
+// and thr is all ones, so the row falls back.  thr = c's order key, or 0 when
+// every score of the segment is listed.  The list is staged in LDS and leaves
+// in whole consecutive entries.  The epilogue is short because every pass
+// over a thread's PER scores is one compare per score.
+// lds: 2048 + 2 * kPreselMaxCap + 4 * WAVES + 8 words of free LDS.
+template <int WAVES, int SCAP>
+__device__ __forceinline__ void presel_segment(const float* sl, int n, int64_t k_begin, int64_t row, int g,
+                                               const PreselWs& ps, uint32_t* lds) {
+  constexpr int NTH = WAVES * 64, PER = SCAP / NTH;  // scores per thread, consecutive
+  constexpr int HBITS = 11, NBINS = 1 << HBITS, BPT = NBINS / NTH;
+  static_assert(PER == 32 && BPT * NTH == NBINS, "presel geometry: one 32-bit mask per thread");
+  constexpr int NC = 3;
+  constexpr float PRE_M[NC] = {1.5f, 1.0f, 0.6f};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i0 = PER * tid;
+  const int nv = max(0, min(PER, n - i0));  // scores of this thread's run
+  float v[PER];
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(&sl[i0 + 4 * q]);  // slots past n hold stale values
+    v[4 * q + 0] = x.x;
+    v[4 * q + 1] = x.y;
+    v[4 * q + 2] = x.z;
+    v[4 * q + 3] = x.w;
+  }
+  uint32_t* h = lds;                                      // NBINS words
+  uint2* s_list = reinterpret_cast<uint2*>(lds + NBINS);  // kPreselMaxCap entries
+  uint32_t* s_red = lds + NBINS + 2 * kPreselMaxCap;      // 4 * WAVES words
+  uint32_t* s_cand = s_red + 4 * WAVES;                   // NC words
+  const int cap = ps.cap;
+  const uint32_t valid_mask = nv == PER ? 0xffffffffu : ((1u << nv) - 1u);
+  uint32_t m = valid_mask;  // scores to list
+  uint32_t thr = 0u;
+  if (n > cap) {
+    // the sample: scores 0, 8, 16 and 24 of every run
+    constexpr int SPT = 4, SSTEP = PER / SPT;
+    uint32_t skey[SPT];
+    uint32_t smn = 0xffffffffu, smx = 0u;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+      skey[e] = float_order_key(v[SSTEP * e]);
+      if (SSTEP * e < nv) {
+        smn = min(smn, skey[e]);
+        smx = max(smx, skey[e]);
+      }
+    }
+    const uint32_t smin = wave_min(smn), smax = wave_max(smx);
+    if (lane == 0) {
+      s_red[wave] = smin;
+      s_red[WAVES + wave] = smax;
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) h[BPT * tid + u] = 0u;
+    lds_barrier();
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      lo = min(lo, s_red[w]);
+      hi = max(hi, s_red[WAVES + w]);
+    }
+    const int shift = max(0, bit_width(hi - lo) - HBITS);
+#pragma unroll
+    for (int e = 0; e < SPT; ++e)
+      if (SSTEP * e < nv) atomicAdd(&h[(skey[e] - lo) >> shift], 1u);
+    lds_barrier();
+    // thread t owns bins NBINS-1-BPT*t-u, descending
+    uint32_t cnt[BPT], tsum = 0u;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      cnt[u] = h[NBINS - 1 - BPT * tid - u];
+      tsum += cnt[u];
+    }
+    uint32_t ns;  // the sample's size
+    uint32_t run = block_excl_scan_w<WAVES, false, true>(tsum, ns, s_red + 2 * WAVES);
+    // candidate j: the bin holding sample rank R_j (1-based, from the top)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int R = max(1, min((int)ns, (int)(PRE_M[j] * (float)ps.tgt * (float)ns / (float)n + 0.5f)));
+      uint32_t r2 = run;
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) {
+        if (r2 < (uint32_t)R && (uint32_t)R <= r2 + cnt[u]) s_cand[j] = lo + ((uint32_t)(NBINS - 1 - BPT * tid - u) << shift);
+        r2 += cnt[u];
+      }
+    }
+    lds_barrier();
+    uint32_t ck[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) ck[j] = s_cand[j];
+    m = 0u;
+    thr = 0xffffffffu;  // no candidate fits: list nothing
+#pragma unroll 1
+    for (int j = 0; j < NC; ++j) {
+      const float c = order_key_float(ck[j]);
+      uint32_t mj = 0u;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) mj |= (v[u] >= c ? 1u : 0u) << u;
+      mj &= valid_mask;
+      const uint32_t t = wave_sum((uint32_t)__popc(mj));
+      if (lane == 0) s_red[NC * wave + j] = t;
+      lds_barrier();
+      uint32_t tot = 0u;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) tot += s_red[NC * w + j];
+      if (tot <= (uint32_t)cap) {
+        m = mj;
+        thr = ck[j];
+        break;
+      }
+    }
+    lds_barrier();  // s_red is reused by the scan below
+  }
+  // the listed scores, in index order: staged in LDS, then copied out whole
+  uint32_t listed;
+  uint32_t pos = block_excl_scan_w<WAVES, false, true>((uint32_t)__popc(m), listed, s_red);
+  while (m != 0u) {
+    const int u = __builtin_ctz(m);
+    m &= m - 1u;
+    s_list[pos++] = make_uint2(float_order_key(sl[i0 + u]), (uint32_t)(k_begin + i0 + u));
+  }
+  lds_barrier();
+  const size_t seg = (size_t)row * ps.G + g;
+  uint2* list = ps.list + seg * ps.cap;
+  for (int i = tid; i < (int)listed; i += NTH) list[i] = s_list[i];
+  if (tid == 0) {
+    ps.count[seg] = listed;
+    ps.thr[seg] = thr;
+  }
+}
+
 // Decode kernel with the key tiles staged through LDS.  A wave owns a ring
 // of NBUF tiles of 32 keys (8 KiB) in LDS and keeps NBUF-1 of them in flight
 // with direct-to-LDS loads.  Each load instruction fetches 1 KiB of
@@ -124,10 +273,11 @@ struct PageRows {
 // chunk c of tile key r sits at slot 16r + (c ^ (r & 15)).  The operand read
 // of k-step s (chunk 8*half + s of key col) then spreads every 16 lanes over
 // all 64 banks.
-template <int WAVES, int NBUF, int SCAP, bool PAGED = false>
+template <int WAVES, int NBUF, int SCAP, bool PAGED = false, bool PRESEL = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
-    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, Vis vis, int64_t keys_per_wg, Paged pg) {
+    float* __restrict__ scores, int64_t Tq, int64_t N, int64_t q_pos0, Vis vis, int64_t keys_per_wg, Paged pg,
+    PreselWs ps) {
   constexpr int TILE_BYTES = 32 * ID * 2;
   static_assert(NBUF >= 2 && NBUF <= 5, "the vmcnt waits below cover up to four tiles in flight");
   static_assert(WAVES * NBUF * TILE_BYTES + SCAP * 4 <= 160 * 1024, "LDS budget");
@@ -214,6 +364,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
   }
   __syncthreads();
   const int n = (int)(k_end - k_begin);
+  if constexpr (PRESEL) {
+    // the key rings are idle: every wave awaited its last tile before the barrier above
+    presel_segment<WAVES, SCAP>(sl, n, k_begin, row, (int)blockIdx.x, ps, reinterpret_cast<uint32_t*>(&kt[0][0][0]));
+  }
   float* dst = sr + k_begin;
   if (((row * N) & 3) == 0) {  // 16-byte aligned row segment (k_begin is a multiple of 32)
     for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * WAVES * 64) {
@@ -609,35 +763,100 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
 
 }  // namespace
 
+namespace {
+
+// Launch shape of the bf16 decode kernel.  One workgroup per compute unit at
+// a time (each holds all of LDS).  One round of 256 workgroups, split evenly
+// over the rows, when the rows fit in at most SCAP keys per workgroup, else
+// two rounds (at most 512), so that no partly filled round appears; whole
+// tiles for every wave.  A second round costs a second workgroup start: at
+// one or four queries of 128K keys one round was 27% and 11% faster.
+constexpr int DEC_WAVES = 4, DEC_NBUF = 4, DEC_SCAP = 8192;
+struct DecodeGeom {
+  int64_t kpw, G;  // keys per workgroup, workgroups per row
+};
+DecodeGeom decode_geometry(int64_t rows, int64_t nmax) {
+  int64_t per_row = 256 / rows > 1 ? 256 / rows : 1;
+  if ((nmax + per_row - 1) / per_row > DEC_SCAP) per_row = 512 / rows > 1 ? 512 / rows : 1;
+  int64_t kpw = (nmax + per_row - 1) / per_row;
+  kpw = (kpw + 32 * DEC_WAVES - 1) / (32 * DEC_WAVES) * (32 * DEC_WAVES);
+  if (kpw > DEC_SCAP) kpw = DEC_SCAP;
+  if (kpw < 32 * DEC_WAVES) kpw = 32 * DEC_WAVES;
+  return {kpw, (nmax + kpw - 1) / kpw};
+}
+
+}  // namespace
+
+// Pre-selection applies to decode rows too long for the one-workgroup top-k
+// (more than 16384 keys, K <= 4096) whose segments can each list several times
+// their expected share K * kpw / nmax of the row's K best keys within the
+// row's list budget.
+bool presel_geometry(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K, PreselWs& ps) {
+  if (Tq > 4 || nmax <= 16384 || N > 0x7fffffff || K > 4096 || nmax < K) return false;
+  const DecodeGeom g = decode_geometry(B * Tq, nmax);
+  if (g.G > 512) return false;
+  const int64_t cap = min((int64_t)kPreselMaxCap, (int64_t)kPreselRowCap / g.G);
+  const double share = (double)K * (double)g.kpw / (double)nmax;
+  if ((double)cap < 1.4 * (share + 6.0 * sqrt(share) + 8.0)) return false;
+  ps.kpw = g.kpw;
+  ps.G = (int32_t)g.G;
+  ps.cap = (int32_t)cap;
+  // list target: the expected share plus six standard deviations of it (keys i.i.d. over the row)
+  ps.tgt = (int32_t)min((double)cap, share + 6.0 * sqrt(share) + 8.0);
+  return true;
+}
+
+static size_t presel_align(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t presel_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K) {
+  PreselWs ps;
+  if (!presel_geometry(B, Tq, N, N, K, ps)) return 0;
+  // any longest row <= N: G <= 512 segments and G * cap <= kPreselRowCap entries per row
+  const size_t R = (size_t)(B * Tq);
+  return 2 * presel_align(R * 512 * sizeof(uint32_t)) + presel_align(R * kPreselRowCap * sizeof(uint2));
+}
+
+PreselWs presel_ws(void* workspace, int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K) {
+  PreselWs ps{};
+  presel_geometry(B, Tq, N, nmax, K, ps);
+  const size_t R = (size_t)(B * Tq);
+  char* p = static_cast<char*>(workspace);
+  ps.count = reinterpret_cast<uint32_t*>(p);
+  ps.thr = reinterpret_cast<uint32_t*>(p + presel_align(R * 512 * sizeof(uint32_t)));
+  ps.list = reinterpret_cast<uint2*>(p + 2 * presel_align(R * 512 * sizeof(uint32_t)));
+  return ps;
+}
+
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                                    hipStream_t stream, const int64_t* seq_lens, int m, const Paged* pg) {
+                                    hipStream_t stream, const int64_t* seq_lens, int m, const Paged* pg,
+                                    const PreselWs* ps) {
   const Vis vis{seq_lens, m};
   // longest visible row: with per-sequence lengths only N is known on the host
   const int64_t nmax = seq_lens != nullptr ? N : min(N, (q_pos0 + Tq) / m);
   if (nmax <= 0) return hipSuccess;  // no query sees a row
   if (Tq <= 4) {
-    // One workgroup per compute unit at a time (each holds all of LDS).  One
-    // round of 256 workgroups, split evenly over the rows, when the rows fit
-    // in at most SCAP keys per workgroup, else two rounds (at most 512), so
-    // that no partly filled round appears; whole tiles for every wave.  A
-    // second round costs a second workgroup start: at one or four queries of
-    // 128K keys one round was 27% and 11% faster.
-    constexpr int WAVES = 4, NBUF = 4, SCAP = 8192;
-    const int64_t rows = B * Tq;
-    int64_t per_row = 256 / rows > 1 ? 256 / rows : 1;
-    if ((nmax + per_row - 1) / per_row > SCAP) per_row = 512 / rows > 1 ? 512 / rows : 1;
-    int64_t kpw = (nmax + per_row - 1) / per_row;
-    kpw = (kpw + 32 * WAVES - 1) / (32 * WAVES) * (32 * WAVES);
-    if (kpw > SCAP) kpw = SCAP;
-    if (kpw < 32 * WAVES) kpw = 32 * WAVES;
-    dim3 grid((unsigned)((nmax + kpw - 1) / kpw), (unsigned)Tq, (unsigned)B);
-    if (pg != nullptr)
-      hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP, true>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx,
-                         w, scores, Tq, N, q_pos0, vis, kpw, *pg);
-    else
-      hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w,
-                         scores, Tq, N, q_pos0, vis, kpw, Paged{});
+    constexpr int WAVES = DEC_WAVES, NBUF = DEC_NBUF, SCAP = DEC_SCAP;
+    const DecodeGeom geo = decode_geometry(B * Tq, nmax);
+    const int64_t kpw = geo.kpw;
+    if (ps != nullptr && (m != 1 || ps->kpw != kpw || ps->G != geo.G)) return hipErrorInvalidValue;
+    dim3 grid((unsigned)geo.G, (unsigned)Tq, (unsigned)B);
+    const PreselWs none{};
+    if (pg != nullptr) {
+      if (ps != nullptr)
+        hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP, true, true>), grid, dim3(WAVES * 64), 0, stream,
+                           q_idx, k_idx, w, scores, Tq, N, q_pos0, vis, kpw, *pg, *ps);
+      else
+        hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP, true>), grid, dim3(WAVES * 64), 0, stream, q_idx,
+                           k_idx, w, scores, Tq, N, q_pos0, vis, kpw, *pg, none);
+    } else {
+      if (ps != nullptr)
+        hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP, false, true>), grid, dim3(WAVES * 64), 0, stream,
+                           q_idx, k_idx, w, scores, Tq, N, q_pos0, vis, kpw, Paged{}, *ps);
+      else
+        hipLaunchKernelGGL((indexer_dma_bf16<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q_idx, k_idx, w,
+                           scores, Tq, N, q_pos0, vis, kpw, Paged{}, none);
+    }
   } else {
     if (pg != nullptr) return hipErrorInvalidValue;  // paged caches: decode shapes only
     constexpr int WAVES = 8;

@@ -9,8 +9,10 @@ namespace dsa {
 
 // A paged cache: rows live in a pool of num_blocks blocks of 2^shift rows;
 // row r of sequence b is pool row table[b * max_blocks + (r >> shift)] *
-// 2^shift + (r & (2^shift - 1)).  Table entries outside [0, num_blocks) are
-// read as block 0 (a caller error that must not become a wild access).
+// 2^shift + (r & (2^shift - 1)).  A table entry outside [0, num_blocks) marks
+// an unset block: appends skip it, index translation masks it, and the
+// indexer reads it as block 0 (a caller error that must not become a wild
+// access).
 struct Paged {
   const int32_t* table;
   int64_t max_blocks;
@@ -18,16 +20,44 @@ struct Paged {
   int32_t num_blocks;
 };
 
+// Pre-selection lists of the decode indexer (workspace of the top-k): each
+// workgroup of the indexer scores one segment of kpw keys of one row, and
+// lists, in index order, every key of the segment whose order key is at least
+// thr (at most cap entries, about tgt); thr = 0 means the list holds the whole
+// segment.
+// The top-k then selects among the lists of a row and falls back to the full
+// row when some truncated list's thr lies above the row's K-th key.
+constexpr int kPreselRowCap = 8192;  // list entries the top-k can hold for one row
+constexpr int kPreselMaxCap = 512;   // entries of one segment's list
+struct PreselWs {
+  uint32_t* count;  // [R][G] entries in each list
+  uint32_t* thr;    // [R][G]
+  uint2* list;      // [R][G][cap] (order key, key index)
+  int64_t kpw;      // keys per segment
+  int32_t G;        // segments per row (the indexer's grid)
+  int32_t cap;      // entries per list
+  int32_t tgt;      // entries a list aims to hold (a few times the segment's expected share)
+};
+// The pre-selection geometry of a decode problem, or false when it does not
+// apply (then the indexer runs plain and the top-k takes its usual methods).
+bool presel_geometry(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K, PreselWs& ps);
+size_t presel_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
+// Places the lists in `workspace` (presel_workspace_bytes large).
+PreselWs presel_ws(void* workspace, int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K);
+
 // seq_lens (device, [B], may be null): per-sequence lengths in tokens; when
 // given, the queries of sequence b sit at positions seq_lens[b] - Tq + t and
 // q_pos0 is ignored.  m: compression rate of the key axis (row w becomes
 // visible to the query at position p when w < (p + 1) / m; m = 1: causal).
 // pg (may be null): the key cache is a paged pool (decode shapes, Tq <= 4;
 // seq_lens required); N is then the logical capacity max_blocks << shift.
+// ps (may be null): also write the pre-selection lists (decode shapes whose
+// geometry presel_geometry accepts; ps must come from presel_ws with the same
+// B, Tq, N and longest row).
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
                                     hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1,
-                                    const Paged* pg = nullptr);
+                                    const Paged* pg = nullptr, const PreselWs* ps = nullptr);
 hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const float* w, float* scores,
                                    int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int H_I, int D_I,
                                    hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1);
@@ -42,6 +72,10 @@ hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uin
                                    const Paged* pg = nullptr);
 
 size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
+// The top-k from the indexer's pre-selection lists (scores: the full rows,
+// read only by rows that fall back).
+hipError_t launch_topk_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                              int K, const PreselWs& ps, hipStream_t stream, const int64_t* seq_lens = nullptr);
 hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
                        int K, void* workspace, hipStream_t stream, const int64_t* seq_lens = nullptr,
                        int m = 1);

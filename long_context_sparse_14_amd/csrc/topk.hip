@@ -42,8 +42,8 @@
 // (a sample, a candidate list) each thread first counts its own repeated bins
 // in registers.  Each thread owns a run of consecutive keys, so one
 // block-wide prefix sum orders a whole chunk.
-#include "device_common.h"
 #include "launch.h"
+#include "select_common.h"
 
 namespace dsa {
 namespace {
@@ -71,64 +71,10 @@ __device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N,
 // another barrier before sbuf[0 .. TK_WAVES) is written again.
 template <bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, uint32_t* sbuf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t x = wave_incl_scan(v);
-  if (lane == 63) sbuf[wave] = x;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < TK_WAVES; ++w) {
-    const uint32_t s = sbuf[w];
-    tot += s;
-    before += (w < wave) ? s : 0u;
-  }
-  if (TRAIL) __syncthreads();
-  total = tot;
-  return before + x - v;
+  return block_excl_scan_w<TK_WAVES, TRAIL>(v, total, sbuf);
 }
 
 // ------------------------------------------------- range-adaptive select
-
-// Histogram insertion for crowded bins (a row's keys, a sample or a candidate
-// list often sit in a narrow range, so a whole wave's plain LDS atomics would
-// queue on one address): a thread counts its first two distinct bins in
-// registers and sends only other bins to LDS; each register count then goes
-// out with one atomic, or with one atomic per wave when every lane of the
-// wave holds the same bin.  flush() must be called by all 64 lanes of a wave.
-struct HotBins {
-  uint32_t b0 = 0u, c0 = 0u, b1 = 0u, c1 = 0u;
-  __device__ __forceinline__ void add(uint32_t bin, uint32_t* h) {
-    if (c0 != 0u && bin == b0) {
-      ++c0;
-    } else if (c1 != 0u && bin == b1) {
-      ++c1;
-    } else if (c0 == 0u) {
-      b0 = bin;
-      c0 = 1u;
-    } else if (c1 == 0u) {
-      b1 = bin;
-      c1 = 1u;
-    } else {
-      atomicAdd(&h[bin], 1u);
-    }
-  }
-  __device__ __forceinline__ static void flush_one(uint32_t b, uint32_t c, uint32_t* h) {
-    const uint32_t bl = __builtin_amdgcn_readfirstlane(b);
-    if (__ballot(c == 0u || b == bl) == ~0ull) {
-      const uint32_t t = wave_sum(c);
-      if ((threadIdx.x & 63) == 0 && t != 0u) atomicAdd(&h[bl], t);
-    } else if (c != 0u) {
-      atomicAdd(&h[b], c);
-    }
-  }
-  __device__ __forceinline__ void flush(uint32_t* h) const {
-    flush_one(b0, c0, h);
-    flush_one(b1, c1, h);
-  }
-};
-
-// Number of bits needed for x (0 for x == 0).
-__device__ __forceinline__ int bit_width(uint32_t x) { return x == 0u ? 0 : 32 - __clz(x); }
 
 // Given a histogram h of 2^FBITS bins, find for each of two descending ranks
 // ra, rb (1-based, at most the histogram total) the bin that holds it;
@@ -717,6 +663,131 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __rest
   seg_final_row(scores, ws, idx, blockIdx.x, Tq, N, q_pos0, vis, K, G, sm);
 }
 
+// ------------------------------------------- rows pre-selected by the indexer
+
+// Shared memory of the pre-selected final step.
+struct PreselSmem {
+  uint32_t h[FB];               // FB >= HB: also the fallback's histogram
+  uint32_t sbuf[3 * TK_WAVES];
+  uint32_t s_res[8];
+  uint32_t small[65];
+  uint32_t s_loff[513];         // list offsets of the row's segments (at most 512)
+  uint32_t s_thr[512];
+};
+constexpr int PLPT = kPreselRowCap / TK_THREADS;  // list entries per thread
+static_assert(PLPT * TK_THREADS == kPreselRowCap, "whole list entries per thread");
+
+// One workgroup per row.  The row's segment lists, concatenated, are one list
+// in index order holding, for every segment, all of its keys at or above its
+// threshold.  If they hold at least K keys, the K-th largest of them, T, is
+// found by an exact select; when every truncated segment's threshold is at
+// most T, every key >= T of the row is listed, so T is the row's K-th key and
+// the kept keys (> T, and the first keq equal to T) are exactly the row's
+// top K; one block prefix sum writes them in index order.  Otherwise the row
+// runs the one-workgroup method over its scores in global memory.
+__global__ __launch_bounds__(TK_THREADS) void topk_presel_final(const float* __restrict__ scores, PreselWs ps,
+                                                                int32_t* __restrict__ idx, int64_t Tq, int64_t N,
+                                                                int64_t q_pos0, Vis vis, int K) {
+  __shared__ PreselSmem sm;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t n = n_visible(row, Tq, N, q_pos0, vis);
+  int32_t* out = idx + row * K;
+  if (n <= K) {
+    for (int64_t i = tid; i < K; i += TK_THREADS) out[i] = i < n ? (int32_t)i : -1;
+    return;
+  }
+  const int nseg = (int)((n + ps.kpw - 1) / ps.kpw);  // segments the indexer ran for this row
+  const size_t s0 = (size_t)row * ps.G;
+  for (int b = tid; b < FB; b += TK_THREADS) sm.h[b] = 0u;
+  if (tid == 0) sm.small[64] = 0u;
+  uint32_t total;
+  {
+    const uint32_t c = tid < nseg ? ps.count[s0 + tid] : 0u;
+    if (tid < nseg) sm.s_thr[tid] = ps.thr[s0 + tid];
+    const uint32_t ex = block_excl_scan(c, total, sm.sbuf);  // its barriers publish the bins and s_thr
+    if (tid < nseg) sm.s_loff[tid] = ex;
+    if (tid == 0) sm.s_loff[nseg] = total;
+  }
+  bool ok = total >= (uint32_t)K && total <= (uint32_t)kPreselRowCap;
+  uint32_t ck[PLPT];
+  int32_t ci[PLPT];
+  uint32_t T = 0u, keq = 0u;
+  if (ok) {
+    __syncthreads();  // s_loff visible
+    const uint32_t j0 = (uint32_t)PLPT * (uint32_t)tid;
+    int g = 0;  // segment of entry j0: the largest g with s_loff[g] <= j0
+    if (j0 < total) {
+      int lo = 0, hi = nseg;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm.s_loff[mid] <= j0) lo = mid;
+        else hi = mid;
+      }
+      g = lo;
+    }
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int u = 0; u < PLPT; ++u) {
+      const uint32_t j = j0 + u;
+      ck[u] = 0u;
+      ci[u] = -1;
+      if (j < total) {
+        while (sm.s_loff[g + 1] <= j) ++g;
+        const uint2 v = ps.list[(s0 + g) * ps.cap + (j - sm.s_loff[g])];
+        ck[u] = v.x;
+        ci[u] = (int32_t)v.y;
+        mn = min(mn, v.x);
+        mx = max(mx, v.x);
+      }
+    }
+    uint32_t kmin, kmax;
+    block_min_max(mn, mx, kmin, kmax, sm.sbuf + TK_WAVES);
+    auto add_cand = [&](HotBins& hb, uint32_t lo, uint32_t hi, int shift) {
+#pragma unroll
+      for (int u = 0; u < PLPT; ++u)
+        if (ci[u] >= 0 && ck[u] >= lo && ck[u] <= hi) hb.add((ck[u] - lo) >> shift, sm.h);
+    };
+    auto each_cand = [&](uint32_t lo, uint32_t hi, auto fn) {
+#pragma unroll
+      for (int u = 0; u < PLPT; ++u)
+        if (ci[u] >= 0 && ck[u] >= lo && ck[u] <= hi) fn(ck[u]);
+    };
+    uint32_t above;
+    T = select_rank<FB_BITS>(add_cand, each_cand, kmin, kmax, (uint32_t)K, above, sm.h, sm.sbuf, sm.s_res,
+                             sm.small);
+    keq = (uint32_t)K - above;
+    // every truncated list must reach down to T
+    const bool bad = tid < nseg && sm.s_thr[tid] != 0u && sm.s_thr[tid] > T;
+    ok = __syncthreads_or(bad) == 0;
+  }
+  if (!ok) {
+    select_row(scores + row * N, n, K, out, nullptr, sm.h, sm.sbuf, sm.s_res, sm.small);
+    return;
+  }
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int u = 0; u < PLPT; ++u) {
+    gt += ci[u] >= 0 && ck[u] > T;
+    eq += ci[u] >= 0 && ck[u] == T;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sm.sbuf);
+  gt = ex & 0xffffu;
+  eq = ex >> 16;
+#pragma unroll
+  for (int u = 0; u < PLPT; ++u) {
+    if (ci[u] < 0) continue;
+    if (ck[u] > T) {
+      out[gt + min(eq, keq)] = ci[u];
+      ++gt;
+    } else if (ck[u] == T) {
+      if (eq < keq) out[gt + eq] = ci[u];
+      ++eq;
+    }
+  }
+}
+
 int long_segments(int64_t N) { return (int)((N + SEG - 1) / SEG); }
 
 bool use_long_path(int64_t B, int64_t Tq, int64_t N, int K) {
@@ -726,8 +797,18 @@ bool use_long_path(int64_t B, int64_t Tq, int64_t N, int K) {
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K) {
-  if (!use_long_path(B, Tq, N, K)) return 0;
-  return long_ws_bytes(B * Tq, long_segments(N), K);
+  const size_t pre = presel_workspace_bytes(B, Tq, N, K);
+  if (!use_long_path(B, Tq, N, K)) return pre;
+  const size_t lw = long_ws_bytes(B * Tq, long_segments(N), K);
+  return lw > pre ? lw : pre;
+}
+
+hipError_t launch_topk_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                              int K, const PreselWs& ps, hipStream_t stream, const int64_t* seq_lens) {
+  const Vis vis{seq_lens, 1};
+  hipLaunchKernelGGL(topk_presel_final, dim3((unsigned)(B * Tq)), dim3(TK_THREADS), 0, stream, scores, ps, idx, Tq, N,
+                     q_pos0, vis, K);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
