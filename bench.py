@@ -363,7 +363,7 @@ def bench_next(args):
             rows.append({"call": "dsa_linear (wq_b)", "M": M, "N": 8192, "K": 1536, "us": round(us, 2),
                          "GB_per_s": round(nb / us / 1e3, 1), "TFLOP_per_s": round(2.0 * M * 8192 * 1536 / us / 1e6, 1)})
     elif args.next == "paged":
-        B, N, K, bs = 28, 131072, 2048, 64
+        B, N, K, bs = 32, 131072, 2048, 64
         q_idx, k_idx = ints(-4, 4, B, 1, 64, 128), ints(-4, 4, B, N, 128)
         w = torch.pow(2.0, -torch.randint(0, 5, (B, 1, 64), device="cuda", generator=g).float()).to(bf)
         q, kv = rnd(B, 1, 128, 576), rnd(B, N, 576)

@@ -41,9 +41,7 @@
  *  - Compiled shapes.  DSA_BF16: indexer H_I = 64, D_I = 128; MLA H = 128,
  *    D = 576, DV = 512.  DSA_F32 (small reference-size problems): indexer
  *    H_I <= 64, D_I <= 256; MLA H <= 128, D <= 1024, DV <= min(D, 512).
- *    Other shapes return DSA_ERR_UNSUPPORTED.  The bf16 sparse MLA also needs
- *    one sequence's latent cache below 4 GiB (N * 1152 bytes < 2^32, i.e.
- *    N <= 3728270).
+ *    Other shapes return DSA_ERR_UNSUPPORTED.
  *  - Sizes: 1 <= B, Tq, N; N < 2^31; 1 <= K <= 65536; q_pos0 >= 0.
  *  - Calls are reentrant; concurrent calls on different streams may share
  *    inputs but not outputs or workspaces.
@@ -419,8 +417,8 @@ dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_
  *   max_blocks * block_size]; Tq <= 4 (DSA_ERR_UNSUPPORTED otherwise).
  *   Select with dsa_topk_varlen.
  * dsa_sparse_mla_fwd_paged: idx [B, Tq, K] logical; the pool is gathered as
- *   one array, so num_blocks * block_size * D * 2 bytes must stay below
- *   4 GiB (DSA_ERR_UNSUPPORTED otherwise).  Workspace:
+ *   one array of num_blocks * block_size rows (any size below 2^31 rows).
+ *   Workspace:
  *   dsa_paged_workspace_size(...) bytes (covers this call and the next).
  * dsa_forward_paged: indexer -> top-k -> sparse MLA over paged caches;
  *   workspace dsa_paged_workspace_size(...) bytes; idx_out (optional)

@@ -82,6 +82,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                : "memory", "m0");
 }
 
+// The same direct-to-LDS load from a full 64-bit per-lane address (no scalar
+// base), for sources whose per-lane offsets do not fit 32 bits.
+__device__ __forceinline__ void dma16_addr(const void* addr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   typedef const __attribute__((address_space(3))) char* lds_ptr;

@@ -137,7 +137,8 @@ __device__ __forceinline__ void presel_segment(const float* sl, int n, int64_t k
                                                const PreselWs& ps, uint32_t* lds) {
   constexpr int NTH = WAVES * 64, PER = SCAP / NTH;  // scores per thread, consecutive
   constexpr int HBITS = 11, NBINS = 1 << HBITS, BPT = NBINS / NTH;
-  static_assert(PER == 32 && BPT * NTH == NBINS, "presel geometry: one 32-bit mask per thread");
+  static_assert(PER >= 8 && PER <= 32 && PER % 4 == 0 && BPT * NTH == NBINS,
+                "presel geometry: one 32-bit mask per thread");
   constexpr int NC = 3;
   constexpr float PRE_M[NC] = {1.5f, 1.0f, 0.6f};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -157,7 +158,7 @@ __device__ __forceinline__ void presel_segment(const float* sl, int n, int64_t k
   uint32_t* s_red = lds + NBINS + 2 * kPreselMaxCap;      // 4 * WAVES words
   uint32_t* s_cand = s_red + 4 * WAVES;                   // NC words
   const int cap = ps.cap;
-  const uint32_t valid_mask = nv == PER ? 0xffffffffu : ((1u << nv) - 1u);
+  const uint32_t valid_mask = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
   uint32_t m = valid_mask;  // scores to list
   uint32_t thr = 0u;
   if (n > cap) {
@@ -772,12 +773,13 @@ namespace {
 // tiles for every wave.  A second round costs a second workgroup start: at
 // one or four queries of 128K keys one round was 27% and 11% faster.
 constexpr int DEC_WAVES = 4, DEC_NBUF = 4, DEC_SCAP = 8192;
+constexpr int DEC_ROUND = 256;  // workgroups resident at once (one per compute unit)
 struct DecodeGeom {
   int64_t kpw, G;  // keys per workgroup, workgroups per row
 };
 DecodeGeom decode_geometry(int64_t rows, int64_t nmax) {
-  int64_t per_row = 256 / rows > 1 ? 256 / rows : 1;
-  if ((nmax + per_row - 1) / per_row > DEC_SCAP) per_row = 512 / rows > 1 ? 512 / rows : 1;
+  int64_t per_row = DEC_ROUND / rows > 1 ? DEC_ROUND / rows : 1;
+  if ((nmax + per_row - 1) / per_row > DEC_SCAP) per_row = 2 * DEC_ROUND / rows > 1 ? 2 * DEC_ROUND / rows : 1;
   int64_t kpw = (nmax + per_row - 1) / per_row;
   kpw = (kpw + 32 * DEC_WAVES - 1) / (32 * DEC_WAVES) * (32 * DEC_WAVES);
   if (kpw > DEC_SCAP) kpw = DEC_SCAP;

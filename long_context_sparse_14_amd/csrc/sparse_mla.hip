@@ -41,6 +41,8 @@
 // With more than one split, each split writes its normalised partial output
 // (bf16) and its log2-sum-exp (fp32) to the workspace and a combine kernel
 // merges them in fp32.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -100,6 +102,10 @@ __device__ __forceinline__ void mfma_s_last(f32x16& c, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 
+// ADDR64: the gathered rows' byte offsets within the sequence need 64 bits
+// (a latent cache of 4 GiB or more, e.g. a large paged pool); the gathers then
+// take full per-lane addresses.
+template <bool ADDR64>
 __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
@@ -185,6 +191,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   const uint32_t gsw = (uint32_t)((lane & 7) ^ row_swizzle(grow));
   // gather_begin records the rows' validity and returns the per-lane source
   // offset; gather_line(u) then issues instruction u.
+  typedef typename std::conditional<ADDR64, uint64_t, uint32_t>::type GOff;
   auto gather_begin = [&](int it, uint32_t& lds0) {
     const int buf = it % NBUF;
     const int32_t v = sidx[it * NT + grow];
@@ -193,12 +200,15 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
     if ((lane & 7) == 0) vflag[buf][grow] = ok;
     const bool full = __ballot(ok) == ~0ull;
     if (lane == 0) tfull[buf][wave] = full;
-    return (uint32_t)(ok ? v : 0) * (uint32_t)(MD * 2) + 16u * gsw;
+    return (GOff)(ok ? v : 0) * (GOff)(MD * 2) + (GOff)(16u * gsw);
   };
-  auto gather_line = [&](uint32_t voff, uint32_t lds0, int u) { dma16(kvb8 + 128 * u, voff, lds0 + 1024 * u); };
+  auto gather_line = [&](GOff voff, uint32_t lds0, int u) {
+    if constexpr (ADDR64) dma16_addr(kvb8 + voff + 128 * u, lds0 + 1024 * u);
+    else dma16(kvb8 + 128 * u, voff, lds0 + 1024 * u);
+  };
   auto gather = [&](int it) {
     uint32_t lds0;
-    const uint32_t voff = gather_begin(it, lds0);
+    const GOff voff = gather_begin(it, lds0);
 #pragma unroll
     for (int u = 0; u < GU; ++u) gather_line(voff, lds0, u);
   };
@@ -354,7 +364,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
   // pout.
   auto tile_fused = [&](const uint16_t* tV, const uint16_t* pbuf, const uint16_t* tS, int ts, uint16_t* pout,
                         int gt) {
-    uint32_t g_lds0 = 0, g_voff = 0;
+    uint32_t g_lds0 = 0;
+    GOff g_voff = 0;
     if (gt >= 0) g_voff = gather_begin(gt, g_lds0);
     bf16x8 ring[SLOOK], pb[4], vring[PVLOOK];
 #pragma unroll
@@ -723,8 +734,12 @@ hipError_t launch_sparse_mla_bf16(const uint16_t* q, const uint16_t* kv, const i
     part_o = static_cast<uint16_t*>(workspace);
     part_lse = reinterpret_cast<float*>(part_o + (size_t)splits * R * MH * MDV);
   }
-  hipLaunchKernelGGL(sparse_mla_bf16_kernel, dim3((unsigned)(R * splits)), dim3(MLA_THREADS), 0, stream, q, kv,
-                     idx, out, lse, part_o, part_lse, R, Tq, N, K, splits, kps, scale * LOG2E);
+  if (N * (int64_t)MD * 2 > (int64_t)0xffffffffLL)
+    hipLaunchKernelGGL(sparse_mla_bf16_kernel<true>, dim3((unsigned)(R * splits)), dim3(MLA_THREADS), 0, stream, q,
+                       kv, idx, out, lse, part_o, part_lse, R, Tq, N, K, splits, kps, scale * LOG2E);
+  else
+    hipLaunchKernelGGL(sparse_mla_bf16_kernel<false>, dim3((unsigned)(R * splits)), dim3(MLA_THREADS), 0, stream, q,
+                       kv, idx, out, lse, part_o, part_lse, R, Tq, N, K, splits, kps, scale * LOG2E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if (splits > 64) return hipErrorInvalidValue;  // the combine holds one split per lane

@@ -260,11 +260,9 @@ def test_paged_validation():
         dsa.DSA_ERR_UNSUPPORTED                                             # decode shapes only
     assert L.dsa_index_scores_paged(P, P, P, P, P, P, 2, 1, 1 << 25, 64, 40, 64, 128, BF16, None) == \
         dsa.DSA_ERR_INVALID_ARG                                             # logical capacity >= 2^31
-    # the MLA gathers the pool with 32-bit offsets
     need = L.dsa_paged_workspace_size(2, 1, 10, 64, 128, 512, 64, BF16)
-    big = (1 << 22) // 64 * 2                                             # 8.4M pool rows: beyond 4 GiB
-    assert L.dsa_sparse_mla_fwd_paged(P, P, P, P, P, P, 2, 1, 10, 64, big, 128, 576, 512, 64, 0.07, BF16, P,
-                                      need, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_sparse_mla_fwd_paged(P, P, P, P, P, P, 2, 1, 10, 64, 1 << 25, 128, 576, 512, 64, 0.07, BF16, P,
+                                      need, None) == dsa.DSA_ERR_INVALID_ARG  # pool of 2^31 rows
     assert L.dsa_sparse_mla_fwd_paged(P, P, P, P, P, P, 2, 1, 10, 64, 40, 128, 576, 512, 64, 0.07, BF16, P,
                                       16, None) == dsa.DSA_ERR_WORKSPACE
     assert L.dsa_forward_paged(P, P, P, P, P, P, P, None, P, P, 2, 1, 10, 64, 40, 64, 128, 128, 576, 512, 64, 0.07,

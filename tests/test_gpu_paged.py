@@ -216,3 +216,38 @@ def test_unset_blocks_are_never_written_and_are_masked():
     assert torch.equal(out, out_s) and torch.equal(lse, lse_s), "indices in an unset block must be masked"
     o, l = oracle.sparse_mla_rows(x["q"][0, 0], x["kv"][0], masked[0, 0], wl.scale, wl.DV)
     assert_close(host64(out[0, 0]), o, "bf16", "attention with the unset block masked")
+
+
+def test_forward_paged_pool_beyond_4gib():
+    """32 sequences of 131072 tokens in one pool of 2^22 latent rows (4.8 GB, past the reach of 32-bit byte
+    offsets): the gather takes 64-bit addresses, and the paged forward still equals the static-cache forward
+    bit for bit (whose parity with the oracle the full-size decode test checks)."""
+    dsa = _dsa()
+    wl = WL["dsa_decode_b32_128k"]
+    B, N, bs = wl.B, wl.N, 64
+    print(f"paged pool beyond 4 GiB: B={B} N={N} block_size={bs}", flush=True)
+    x = synth.make_inputs(wl)
+    d = {k: dev(v) for k, v in x.items()}
+    del x
+    mb = N // bs
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    table = torch.randperm(B * mb, device="cuda", generator=g).to(torch.int32).view(B, mb).contiguous()
+    prow = (table.long()[:, :, None] * bs + torch.arange(bs, device="cuda")).reshape(-1)
+    k_pool = torch.empty(B * N, wl.D_I, dtype=torch.bfloat16, device="cuda")
+    k_pool[prow] = d["k_idx"].reshape(-1, wl.D_I)
+    kv_pool = torch.empty(B * N, wl.D, dtype=torch.bfloat16, device="cuda")
+    kv_pool[prow] = d["kv"].reshape(-1, wl.D)
+    del prow
+    assert kv_pool.numel() * 2 >= 1 << 32
+    lens = _lens([N] * B)
+    out_p, lse_p, idx_p = dsa.forward_paged(d["q_idx"], k_pool, d["w"], d["q"], kv_pool, wl.K, wl.scale, lens,
+                                            table, bs, return_idx=True)
+    out_s, lse_s, idx_s = dsa.forward_varlen(d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], wl.K, wl.scale, lens,
+                                             return_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx_s), "paged vs static indices"
+    # the selection reaches pool rows whose byte offset needs more than 32 bits
+    phys = table.long().gather(1, idx_p[:, 0].long() // bs) * bs + idx_p[:, 0].long() % bs
+    assert int((phys * wl.D * 2 >= 1 << 32).sum()) > 1000
+    assert torch.equal(out_p, out_s) and torch.equal(lse_p, lse_s), "paged vs static attention"
