@@ -21,6 +21,9 @@ region.
   python bench.py --record-traffic --workload NAME --pmc-fetch F.csv --pmc-write W.csv
                   --calib-fetch CF.csv --calib-write CW.csv --commands "..."
                                    (store the dominant kernel's HBM bytes per launch)
+  python bench.py --record-mfma --workload NAME --kernel K --pmc-mfma M.csv --pmc-util U.csv
+                  --ktrace T.csv --commands "..."
+                                   (store a matrix-core kernel's MFMA counters per launch)
 """
 from __future__ import annotations
 
@@ -67,6 +70,13 @@ def _parse():
     ap.add_argument("--calib-fetch")
     ap.add_argument("--calib-write")
     ap.add_argument("--commands", default="", help="the rocprofv3 command lines, recorded with the traffic")
+    ap.add_argument("--record-mfma", action="store_true",
+                    help="store one kernel's matrix-core counters (rocprofv3 -f csv counter and kernel-trace files)")
+    ap.add_argument("--kernel", help="--record-mfma: the kernel (name prefix)")
+    ap.add_argument("--pmc-mfma", help="--record-mfma: counter file with SQ_INSTS_VALU_MFMA_MOPS_BF16, "
+                    "SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, GRBM_GUI_ACTIVE")
+    ap.add_argument("--pmc-util", help="--record-mfma: counter file with the derived MfmaUtil and LdsBankConflict")
+    ap.add_argument("--ktrace", help="--record-mfma: kernel-trace file of the same run as --pmc-mfma")
     return ap.parse_args()
 
 
@@ -169,6 +179,96 @@ def record_traffic(args):
     with open(traffic_path(wl.name, kname), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def mfma_path(workload: str, kernel: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_mfma.json")
+
+
+def kernel_flops(wl, kernel: str) -> int:
+    """Algorithmic matrix flops of one launch of a matrix-core kernel on the whole workload."""
+    B, Tq, N, q0, K = wl.B, wl.Tq, wl.N, wl.q_pos0, wl.K
+    vis = [min(N, q0 + t + 1) for t in range(Tq)]
+    if kernel.startswith("indexer"):
+        return 2 * wl.H_I * wl.D_I * B * sum(vis)
+    if kernel.startswith("sparse_mla"):
+        return 2 * wl.H * (wl.D + wl.DV) * B * sum(min(v, K) for v in vis)
+    raise SystemExit(f"no flop count for {kernel}")
+
+
+def record_mfma(args):
+    """One kernel's matrix-core counters per launch, from a rocprofv3 --pmc run
+    (with its kernel trace) and a second run of the derived utilisation metrics:
+    bf16 MFMA flops counted by the hardware (MOPS x 512) against the algorithmic
+    count, the counted and algorithmic rates against the dense bf16 peak, and
+    the profiler's MfmaUtil (matrix-core busy cycles per SIMD and active cycle)."""
+    import csv
+
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    kname = args.kernel
+
+    import re
+    named = re.compile(r"(?<![A-Za-z0-9_])" + re.escape(kname) + r"(?![A-Za-z0-9_])")
+
+    def per_dispatch(path, counter):
+        vals = [v for k, v in _pmc_rows(path, counter) if named.search(k)]
+        if not vals:
+            raise SystemExit(f"{path}: no {counter} for a kernel named {kname!r}")
+        return _median(vals), len(vals)
+
+    raw = {}
+    for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT",
+              "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"):
+        raw[c], n = per_dispatch(args.pmc_mfma, c)
+    util = {c: per_dispatch(args.pmc_util, c)[0] for c in ("MfmaUtil", "LdsBankConflict")}
+    durs = []
+    with open(args.ktrace, newline="") as f:
+        for row in csv.DictReader(f):
+            if named.search(row.get("Kernel_Name", "")):
+                durs.append((float(row["End_Timestamp"]) - float(row["Start_Timestamp"])) * 1e-9)
+    if not durs:
+        raise SystemExit(f"{args.ktrace}: no dispatch of {kname}")
+    sec = _median(durs)
+    counted = raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+    algo = kernel_flops(wl, kname)
+    rec = {
+        "workload": wl.name,
+        "kernel": kname,
+        "kernel_sources_digest": kernel_sources_digest(kname),
+        "dispatches": n,
+        "kernel_us_median": round(sec * 1e6, 2),
+        "counters_per_launch": raw,
+        "derived_per_launch": util,
+        "mfma_flops_counted": counted,
+        "mfma_flops_algorithmic": algo,
+        "counted_over_algorithmic": round(counted / algo, 4),
+        "counted_tflops": round(counted / sec / 1e12, 1),
+        "algorithmic_tflops": round(algo / sec / 1e12, 1),
+        "peak_tflops": BF16_PEAK_TFLOPS,
+        "frac_counted": round(counted / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "frac_algorithmic": round(algo / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "mfma_util_pct": round(util["MfmaUtil"], 2),
+        "lds_bank_conflict_pct": round(util["LdsBankConflict"], 2),
+        "lds_conflicts_per_access": round(raw["SQ_LDS_BANK_CONFLICT"] /
+                                          max(1.0, raw["SQ_LDS_IDX_ACTIVE"] - raw["SQ_LDS_BANK_CONFLICT"]), 4),
+        "commands": args.commands,
+    }
+    with open(mfma_path(wl.name, kname), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def stored_mfma(workload: str, kernel: str):
+    """The stored matrix-core counter record of a kernel, if taken on its current sources."""
+    path = mfma_path(workload, kernel)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_digest") != kernel_sources_digest(kernel):
+        return None
+    return {k: rec[k] for k in ("frac_counted", "counted_over_algorithmic", "mfma_util_pct", "kernel_us_median")}
 
 
 def dominant_stage(wl, fp8=False):
@@ -420,6 +520,9 @@ def main():
     if args.record_traffic:
         record_traffic(args)
         return
+    if args.record_mfma:
+        record_mfma(args)
+        return
     import numpy as np
     import torch
 
@@ -619,6 +722,8 @@ def main():
             roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
         roof["traffic"] = stored_traffic(wl.name, kname)
+        if bound == "mfma":
+            roof["counters"] = stored_mfma(wl.name, kname)
         roof["kernel"] = kname
         roof["kernel_avg_us"] = round(stage_ms[stage] * 1e3, 2)
         roof["algorithmic_" + ("bytes" if wunit == "B" else "flops") + "_per_launch"] = int(work)
