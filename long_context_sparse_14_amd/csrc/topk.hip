@@ -40,7 +40,8 @@
 //    method reading the row from global memory.
 // Histograms use plain LDS atomics; where the keys crowd into a narrow range
 // (a sample, a candidate list) each thread first counts its own repeated bins
-// in registers.  Each thread owns a run of consecutive keys, so one
+// in registers.  The compactions give each wave (one-workgroup method) or
+// each thread (lists held in registers) a run of consecutive keys, so one
 // block-wide prefix sum orders a whole chunk.
 #include "launch.h"
 #include "select_common.h"
@@ -59,11 +60,18 @@ constexpr int ROW_CAND_CAP = 4096;    // candidates the final step can hold for 
 constexpr int LONG_MAX_K = 4096;      // largest K of the long-row method
 constexpr int64_t LONG_MAX_SEGS = 4096;  // bound on rows x segments (workspace size)
 constexpr int LONG_MAX_G = TK_THREADS;   // bound on segments per row (one thread per segment)
-constexpr int RUN = 16;                  // consecutive keys per thread in a chunk
+constexpr int RUN = 16;                  // keys per lane in a chunk of the compaction
 constexpr int CHUNK = RUN * TK_THREADS;  // keys ordered by one block prefix sum
+constexpr int WRUN = RUN * 64;           // consecutive keys of one wave in a chunk
+constexpr int PT = TK_CAP / TK_THREADS;  // keys per thread of a row staged in LDS
 
 __device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, const Vis& vis) {
   return visible_keys(vis, seq_q0(vis, row / Tq, Tq, q_pos0), row % Tq, N);
+}
+
+// Set bits of a wave-uniform lane mask below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Exclusive block-wide prefix sum of v; `total` receives the block sum.
@@ -71,7 +79,7 @@ __device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N,
 // another barrier before sbuf[0 .. TK_WAVES) is written again.
 template <bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, uint32_t* sbuf) {
-  return block_excl_scan_w<TK_WAVES, TRAIL>(v, total, sbuf);
+  return block_excl_scan_w<TK_WAVES, TRAIL, true>(v, total, sbuf);
 }
 
 // ------------------------------------------------- range-adaptive select
@@ -114,7 +122,7 @@ __device__ __forceinline__ void find_two_bins(uint32_t* h, uint32_t ra, uint32_t
     }
     run += c[u];
   }
-  __syncthreads();
+  lds_barrier();
   ba = s_res[0];
   above_a = s_res[1];
   bb = s_res[2];
@@ -133,7 +141,7 @@ __device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t
     sbuf2[2 * wave] = mn;
     sbuf2[2 * wave + 1] = mx;
   }
-  __syncthreads();
+  lds_barrier();
   mn = 0xffffffffu;
   mx = 0u;
 #pragma unroll
@@ -166,7 +174,7 @@ __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo,
     HotBins hb;
     add_keys(hb, lo, hi, shift);
     hb.flush(h);
-    __syncthreads();
+    lds_barrier();
     uint32_t b, ab, b2, ab2, cnt;
     find_two_bins<FBITS, true>(h, r, r, b, ab, b2, ab2, cnt, sbuf, s_res);
     above += ab;
@@ -181,7 +189,7 @@ __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo,
         const uint32_t s = atomicAdd(&small[64], 1u);
         if (s < 64u) small[s] = k;
       });
-      __syncthreads();
+      lds_barrier();
       if (threadIdx.x < 64) {  // lane i: how many of the bin's keys exceed / equal its own
         const uint32_t i = threadIdx.x;
         const uint32_t ki = i < cnt ? small[i] : 0u;
@@ -197,70 +205,27 @@ __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo,
         }
         if (i == 0) small[64] = 0u;  // every append is done: reset the counter
       }
-      __syncthreads();
+      lds_barrier();
       above += s_res[6];
       return s_res[5];
     }
   }
 }
 
-// Writes the kept keys of the run [i0, i0 + RUN) (clipped to n) of one chunk:
-// gt/eq are the per-thread counts before this thread within the whole row.
-template <typename KeyAt>
-__device__ __forceinline__ void emit_run(KeyAt key_at, int i0, int n, uint32_t T, uint32_t keq,
-                                         uint32_t gt, uint32_t eq, int32_t* __restrict__ out) {
-  for (int u = 0; u < RUN; ++u) {
-    const int i = i0 + u;
-    if (i >= n) break;
-    const uint32_t k = key_at(i);
-    if (k > T) {
-      out[gt + min(eq, keq)] = (int32_t)i;
-      ++gt;
-    } else if (k == T) {
-      if (eq < keq) out[gt + eq] = (int32_t)i;
-      ++eq;
-    }
-  }
+// Writes a row with n <= K: 0..n-1, then -1.
+__device__ __forceinline__ void write_whole_row(int64_t n, int K, int32_t* __restrict__ out) {
+  for (int64_t i = threadIdx.x; i < K; i += TK_THREADS) out[i] = i < n ? (int32_t)i : -1;
 }
 
-// The one-workgroup method for one row.  skey: LDS stage of TK_CAP keys, or
-// nullptr to read the row from global memory on every pass.  hist: 2048 bins;
-// sbuf: 3 * TK_WAVES words; s_res: 8 words; small: 65 words.
-__device__ __forceinline__ void select_row(const float* __restrict__ src, int64_t n, int K, int32_t* __restrict__ out,
-                           uint32_t* skey, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res, uint32_t* small) {
+// The K-th largest key T of a row of n32 > K keys whose range is [kmin,
+// kmax], by histogram rounds over the whole row; `above` receives how many
+// keys exceed T.  key_at(i) returns key i.  hist (all bins zero) and
+// small[64] (zero) must have been published by a barrier.
+template <typename KeyAt>
+__device__ __forceinline__ uint32_t select_full(KeyAt key_at, int n32, int K, uint32_t kmin, uint32_t kmax,
+                                                uint32_t& above, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res,
+                                                uint32_t* small) {
   const int tid = threadIdx.x;
-  if (n <= K) {
-    for (int64_t i = tid; i < K; i += TK_THREADS) out[i] = i < n ? (int32_t)i : -1;
-    return;
-  }
-  // keys (staged in LDS when skey is given) and their range; eight loads in
-  // flight per thread
-  // (row offsets fit 32 bits: N < 2^31)
-  const int n32 = (int)n;
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int base = tid; base < n32; base += 8 * TK_THREADS) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * TK_THREADS;
-      v[u] = i < n32 ? src[i] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * TK_THREADS;
-      if (i < n32) {
-        const uint32_t k = float_order_key(v[u]);
-        if (skey != nullptr) skey[i] = k;
-        mn = min(mn, k);
-        mx = max(mx, k);
-      }
-    }
-  }
-  for (int b = tid; b < HB; b += TK_THREADS) hist[b] = 0u;  // the select starts from empty bins
-  if (tid == 0) small[64] = 0u;
-  uint32_t kmin, kmax;
-  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);  // its barrier also publishes skey and the bins
-  auto key_at = [&](int i) -> uint32_t { return skey != nullptr ? skey[i] : float_order_key(src[i]); };
   // (the bins span the keys' own range, so plain atomics rarely collide)
   auto add_row = [&](HotBins&, uint32_t lo, uint32_t hi, int shift) {
     for (int base = tid; base < n32; base += 8 * TK_THREADS) {
@@ -292,31 +257,119 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_
       }
     }
   };
-  uint32_t above;
-  const uint32_t T = select_rank<11>(add_row, each_row, kmin, kmax, (uint32_t)K, above, hist, sbuf, s_res, small);
-  const uint32_t keq = (uint32_t)K - above;
+  return select_rank<11>(add_row, each_row, kmin, kmax, (uint32_t)K, above, hist, sbuf, s_res, small);
+}
 
-  // in-order compaction: thread t owns keys [base + RUN*t, base + RUN*t + RUN)
+// In-order compaction of a row of n32 keys with threshold T, keeping keq of
+// the keys equal to T.
+template <typename KeyAt>
+__device__ __forceinline__ void compact_row(KeyAt key_at, int n32, uint32_t T, uint32_t keq,
+                                            int32_t* __restrict__ out, uint32_t* sbuf) {
+  const int tid = threadIdx.x;
+  // In-order compaction, CHUNK keys at a time: wave w owns the run of WRUN
+  // consecutive keys starting at base + WRUN*w and reads it lane by lane (step
+  // u: key base + WRUN*w + 64u + lane), so every LDS read is conflict-free.
+  // Ballots give each step's keys above / equal to T; one block prefix sum
+  // over the per-wave totals orders the waves, and a kept key's slot is its
+  // wave's base plus the kept keys before it in the wave's run.
+  const int lane = tid & 63, wave = tid >> 6;
   uint32_t run_gt = 0, run_eq = 0;
   for (int base = 0; base < n32; base += CHUNK) {
-    const int i0 = base + RUN * tid;
-    uint32_t gt = 0, eq = 0;
+    const int w0 = base + WRUN * wave;
+    uint32_t bits = 0;  // bit u: this lane's key of step u is above T; bit RUN + u: equal to T
+    uint32_t cgt = 0, ceq = 0;
+#pragma unroll
     for (int u = 0; u < RUN; ++u) {
-      const int i = i0 + u;
-      if (i >= n32) break;
-      const uint32_t k = key_at(i);
-      gt += k > T;
-      eq += k == T;
+      const int i = w0 + 64 * u + lane;
+      const bool ok = i < n32;
+      const uint32_t k = ok ? key_at(i) : 0u;
+      bits |= (uint32_t)(ok && k > T) << u;
+      bits |= (uint32_t)(ok && k == T) << (RUN + u);
     }
+    cgt = wave_sum((uint32_t)__popc(bits & ((1u << RUN) - 1u)));
+    ceq = wave_sum((uint32_t)__popc(bits >> RUN));
     uint32_t tot;
-    const uint32_t ex = block_excl_scan((eq << 16) | gt, tot, sbuf);
-    emit_run(key_at, i0, n32, T, keq, run_gt + (ex & 0xffffu), run_eq + (ex >> 16), out);
+    const uint32_t ex = block_excl_scan(lane == 0 ? (ceq << 16) | cgt : 0u, tot, sbuf);
+    const uint32_t wex = __builtin_amdgcn_readfirstlane(ex);  // lane 0's prefix: the keys of earlier waves
+    uint32_t g = run_gt + (wex & 0xffffu), e = run_eq + (wex >> 16);
+#pragma unroll
+    for (int u = 0; u < RUN; ++u) {
+      const bool is_gt = (bits >> u) & 1u, is_eq = (bits >> (RUN + u)) & 1u;
+      const uint64_t mg = __ballot(is_gt), me = __ballot(is_eq);
+      const uint32_t bg = g + lanes_below(mg), be = e + lanes_below(me);
+      const int32_t i = w0 + 64 * u + lane;
+      if (is_gt) out[bg + min(be, keq)] = i;
+      else if (is_eq && be < keq) out[bg + be] = i;
+      g += (uint32_t)__popcll(mg);
+      e += (uint32_t)__popcll(me);
+    }
     run_gt += tot & 0xffffu;
     run_eq += tot >> 16;
   }
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(const float* __restrict__ scores,
+
+// The one-workgroup method for one row.  skey: LDS stage of TK_CAP keys, or
+// nullptr to read the row from global memory on every pass.  hist: 2048 bins;
+// sbuf: 3 * TK_WAVES words; s_res: 8 words; small: 65 words.
+__device__ __forceinline__ void select_row(const float* __restrict__ src, int64_t n, int K, int32_t* __restrict__ out,
+                           uint32_t* skey, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res, uint32_t* small) {
+  const int tid = threadIdx.x;
+  if (n <= K) {
+    write_whole_row(n, K, out);
+    return;
+  }
+  // keys (staged in LDS when skey is given: the whole row's loads in flight at
+  // once) and their range; a longer row, eight loads in flight per thread
+  // (row offsets fit 32 bits: N < 2^31)
+  const int n32 = (int)n;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  if (skey != nullptr) {
+    float v[PT];
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int i = tid + u * TK_THREADS;
+      v[u] = i < n32 ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int i = tid + u * TK_THREADS;
+      if (i < n32) {
+        const uint32_t k = float_order_key(v[u]);
+        skey[i] = k;
+        mn = min(mn, k);
+        mx = max(mx, k);
+      }
+    }
+  }
+  for (int base = tid; skey == nullptr && base < n32; base += 8 * TK_THREADS) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * TK_THREADS;
+      v[u] = i < n32 ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * TK_THREADS;
+      if (i < n32) {
+        const uint32_t k = float_order_key(v[u]);
+        mn = min(mn, k);
+        mx = max(mx, k);
+      }
+    }
+  }
+  for (int b = tid; b < HB; b += TK_THREADS) hist[b] = 0u;  // the select starts from empty bins
+  if (tid == 0) small[64] = 0u;
+  uint32_t kmin, kmax;
+  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);  // its barrier also publishes skey and the bins
+  auto key_at = [&](int i) -> uint32_t { return skey != nullptr ? skey[i] : float_order_key(src[i]); };
+  uint32_t above;
+  const uint32_t T = select_full(key_at, n32, K, kmin, kmax, above, hist, sbuf, s_res, small);
+  compact_row(key_at, n32, T, (uint32_t)K - above, out, sbuf);
+}
+
+__global__ __launch_bounds__(TK_THREADS, 8) void topk_rows_kernel(const float* __restrict__ scores,
                                                                int32_t* __restrict__ idx, int64_t Tq,
                                                                int64_t N, int64_t q_pos0, Vis vis, int K) {
   __shared__ uint32_t skey[TK_CAP];
