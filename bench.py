@@ -313,6 +313,54 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}), flush=True)
 
 
+def measured_ceilings(bound: str):
+    """What this GPU sustains, measured in the same process before the timed
+    steps (HIP events): a plain streaming read and a streaming copy of a
+    1 GiB device buffer with the library's calibration kernel (16-byte
+    accesses, the same kind as the HBM-bound kernels), and, for
+    matrix-core-bound workloads, the rate of the vendor library's bf16 GEMM
+    (torch.matmul on 8192^3, N(0,1) operands: dense bf16 matrix work is
+    power-limited on this part, so realistic data runs well below the
+    nominal peak)."""
+    import torch
+
+    import long_context_sparse_14_amd as dsa
+    out = {}
+
+    def rate(fn, reps):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    s = rate(lambda: dsa.calib_stream(a), 10)
+    out["read_GBps"] = round(n / s / 1e9, 1)
+    s = rate(lambda: dsa.calib_stream(a, b), 10)
+    out["copy_GBps"] = round(2 * n / s / 1e9, 1)
+    out["kernel"] = "dsa_calib_stream (16-byte streaming loads/stores, 1 GiB)"
+    del a, b
+    if bound == "mfma":
+        g = torch.Generator(device="cuda")
+        g.manual_seed(0)
+        m = 8192
+        x = torch.randn(m, m, device="cuda", generator=g).to(torch.bfloat16)
+        y = torch.randn(m, m, device="cuda", generator=g).to(torch.bfloat16)
+        z = torch.empty(m, m, device="cuda", dtype=torch.bfloat16)
+        s = rate(lambda: torch.matmul(x, y, out=z), 10)
+        out["library_gemm_bf16_TFLOPs"] = round(2 * m ** 3 / s / 1e12, 1)
+    torch.cuda.empty_cache()
+    return out
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -650,6 +698,7 @@ def main():
     # at most every tenth) instead runs the stages as separate calls with HIP
     # events between them, which measures each kernel's duration live on the
     # launch stream (--staged: every step).
+    ceilings = measured_ceilings(dominant_stage(wl, fp8)[2])
     has_fused = has_idx and has_mla
     INSTR = 1 if (args.staged or not has_fused) else max(2, min(10, args.steps // 5))
     for _ in range(args.warmup):
@@ -722,6 +771,11 @@ def main():
             roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
         roof["traffic"] = stored_traffic(wl.name, kname)
+        roof["measured_ceiling"] = ceilings
+        if bound == "hbm":
+            roof["frac_of_measured_read"] = round(ach / ceilings["read_GBps"], 4)
+        else:
+            roof["frac_of_library_gemm"] = round(ach / ceilings["library_gemm_bf16_TFLOPs"], 4)
         if bound == "mfma":
             roof["counters"] = stored_mfma(wl.name, kname)
         roof["kernel"] = kname

@@ -452,6 +452,16 @@ dsa_status dsa_cache_append_paged(void* k_pool, void* kv_pool, const void* new_k
                                   int32_t block_size, int64_t num_blocks, int32_t D_I, int32_t D, int32_t dtype,
                                   void* stream);
 
+/*
+ * Bandwidth calibration (not a step of the method): streams `bytes` of src
+ * through the device once, as a read only (dst NULL) or as a copy into dst,
+ * with 16-byte loads and stores, so that the HBM-bound kernels above can be
+ * set against what a plain stream reaches on the same device.  src and dst:
+ * device, 16-byte aligned, not overlapping; bytes a multiple of 16 (0 is a
+ * no-op).  DSA_ERR_INVALID_ARG otherwise.
+ */
+dsa_status dsa_calib_stream(const void* src, void* dst, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -94,6 +94,7 @@ _SIGNATURES = {
     "dsa_mla_absorb_q": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _p]),
     "dsa_mla_out_proj": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p]),
     "dsa_linear": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _p]),
+    "dsa_calib_stream": (ctypes.c_int, [_p, _p, _sz, _p]),
     "dsa_indexer_quantize_fp8": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _p]),
     "dsa_index_scores_fp8": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "dsa_forward_fp8": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32,
@@ -515,6 +516,20 @@ def linear(x, w, y=None, stream=None) -> torch.Tensor:
         raise ValueError("y must be [..., N]")
     _check(library().dsa_linear(px, pw, py, M, N, K, _dtype_code(x), _stream(stream)))
     return y
+
+
+def calib_stream(src, dst=None, stream=None):
+    """Stream src's bytes through the device once: a read (dst None) or a copy into dst (same size).
+    The bandwidth yardstick for the HBM-bound kernels."""
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    pd = None
+    if dst is not None:
+        if not (dst.is_cuda and dst.is_contiguous()) or dst.numel() * dst.element_size() != nbytes:
+            raise ValueError("dst must be a contiguous device tensor of src's size")
+        pd = dst.data_ptr()
+    _check(library().dsa_calib_stream(src.data_ptr(), pd, nbytes, _stream(stream)))
 
 
 def indexer_quantize_fp8(x, codes=None, scales=None, stream=None):

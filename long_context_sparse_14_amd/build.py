@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libdsa.so")
 OBJ_DIR = os.path.join(PKG, "_build")
-SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache.hip", "proj.hip", "dsa_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache.hip", "proj.hip", "calib.hip", "dsa_api.cpp"]
 ARCH = "gfx950"
 # Per-source flags.  The decode indexers keep their two MFMA accumulator
 # blocks in ordinary vector registers rather than accumulation registers, so

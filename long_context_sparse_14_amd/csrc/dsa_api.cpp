@@ -820,4 +820,17 @@ dsa_status dsa_cache_append_paged(void* k_pool, void* kv_pool, const void* new_k
                     "paged cache append launch");
 }
 
+dsa_status dsa_calib_stream(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return DSA_OK;
+  if (src == nullptr) return fail(DSA_ERR_INVALID_ARG, "src must not be NULL");
+  if (bytes % 16 != 0) return fail(DSA_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  if (dst != nullptr) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return fail(DSA_ERR_INVALID_ARG, "src and dst must not overlap");
+  }
+  return hip_status(dsa::launch_calib_stream(src, dst, bytes, static_cast<hipStream_t>(stream)), "calibration stream launch");
+}
+
 }  // extern "C"

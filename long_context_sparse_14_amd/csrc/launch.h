@@ -126,4 +126,8 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool b_nk, int64_t batch, hipStream_t stream);
 
+// Streaming read (dst null) or copy of `bytes` (a multiple of 16, 16-byte
+// aligned buffers): the bandwidth yardstick.
+hipError_t launch_calib_stream(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
 }  // namespace dsa

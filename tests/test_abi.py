@@ -271,3 +271,13 @@ def test_paged_validation():
         dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_cache_append_paged(P, P, P, P, P, P, 2, 10, 100, 40, 128, 576, BF16, None) == \
         dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_calib_stream_validation():
+    L = lib()
+    assert L.dsa_calib_stream(P, None, 0, None) == dsa.DSA_OK                      # nothing to stream
+    assert L.dsa_calib_stream(None, None, 64, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_calib_stream(P, None, 40, None) == dsa.DSA_ERR_INVALID_ARG        # not a multiple of 16
+    assert L.dsa_calib_stream(P + 4, None, 64, None) == dsa.DSA_ERR_INVALID_ARG    # misaligned source
+    assert L.dsa_calib_stream(P, P + 8, 64, None) == dsa.DSA_ERR_INVALID_ARG       # misaligned destination
+    assert L.dsa_calib_stream(P, P + 32, 64, None) == dsa.DSA_ERR_INVALID_ARG      # overlapping copy
