@@ -313,10 +313,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
     if (PAGED) {
       const int64_t r0 = pr.row(key0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) dma16(kb + (r0 + 4 * u) * (ID * 2), voff[u & 3], dst + 1024u * u);
+      for (int u = 0; u < 8; ++u) dma16_stream(kb + (r0 + 4 * u) * (ID * 2), voff[u & 3], dst + 1024u * u);
     } else if (key0 + 32 <= N) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) dma16(kb + (key0 + 4 * u) * (ID * 2), voff[u & 3], dst + 1024u * u);
+      for (int u = 0; u < 8; ++u) dma16_stream(kb + (key0 + 4 * u) * (ID * 2), voff[u & 3], dst + 1024u * u);
     } else {
       // last rows of the cache: clamp to a real row (those keys are never scored)
 #pragma unroll
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_bf16(
         const int64_t kbase = min(key0 + 4 * u, N - 1);
         const int64_t key = min(key0 + 4 * u + kk, N - 1);
         const uint32_t off = (uint32_t)(key - kbase) * 256u + (voff[u & 3] & 255u);
-        dma16(kb + kbase * (ID * 2), off, dst + 1024u * u);
+        dma16_stream(kb + kbase * (ID * 2), off, dst + 1024u * u);
       }
     }
   };
@@ -683,10 +683,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
     if (PAGED) {
       const int64_t r0 = pr.row(key0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dma16(kb + (r0 + 8 * u) * ID, voff, dst + 1024u * u);
+      for (int u = 0; u < 4; ++u) dma16_stream(kb + (r0 + 8 * u) * ID, voff, dst + 1024u * u);
     } else if (key0 + 32 <= N) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dma16(kb + (key0 + 8 * u) * ID, voff, dst + 1024u * u);
+      for (int u = 0; u < 4; ++u) dma16_stream(kb + (key0 + 8 * u) * ID, voff, dst + 1024u * u);
     } else {
       // last rows of the cache: clamp to a real row (those keys are never scored)
 #pragma unroll
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
         const int64_t kbase = min(key0 + 8 * u, N - 1);
         const int64_t key = min(key0 + 8 * u + (lane >> 3), N - 1);
         const uint32_t off = (uint32_t)(key - kbase) * 128u + (voff & 127u);
-        dma16(kb + kbase * ID, off, dst + 1024u * u);
+        dma16_stream(kb + kbase * ID, off, dst + 1024u * u);
       }
     }
   };
