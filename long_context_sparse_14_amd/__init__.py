@@ -42,7 +42,8 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdsa.so")
+# the in-tree library; DSA_LIB names another build of the same sources (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("DSA_LIB") or os.path.join(_HERE, "libdsa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dsa.h")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
