@@ -434,10 +434,20 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
   gload(0);
   lstore(0);
   __syncthreads();
+  // The query fragments' first use is inside the tile loop.  Consuming them
+  // here makes their loads complete before it, so the compiler puts no wait
+  // on them inside the loop; otherwise it waited, in every tile, for every
+  // load in flight, including the prefetch of the next tile.
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(f.a0[s]), "v"(f.a1[s]));
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const int64_t k0 = (int64_t)it * TK;
-    if (it + 1 < ntiles) gload(k0 + TK);
+    // Unconditional, like the LDS store below (past the last tile the keys are
+    // clamped to a real row and land in the idle buffer): with both under one
+    // condition the compiler assumed a path where the loads are never waited
+    // for, and waited for them at the top of every tile.
+    gload(k0 + TK);
     // Blocks of 32 keys, software-pipelined: the MFMAs of block nb are issued
     // before the ReLU / weighted-sum epilogue of block nb-1, so the vector
     // units work while the matrix cores run.  Blocks past this query's last
@@ -467,12 +477,13 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
       const float sc = weighted_relu_sum(f, cc[0], cc[1]);
       if (half == 0 && kk0 + col < n_valid) sr[kk0 + col] = sc;
     };
-    if (left >= TK) {
+    const bool full = left >= TK;
+    float scv[NBK];
+    if (full) {
       // Full tile (every key visible), branch-free: the scheduler is told to
       // put four vector instructions of block nb-1's epilogue after each of
       // block nb's MFMAs, so they issue while the matrix core runs instead of
-      // after it.  The scores leave after the last block.
-      float scv[NBK];
+      // after it.  The scores leave after the next tile's LDS store (below).
       mma_block(0, c[0]);
 #pragma unroll
       for (int nb = 1; nb < NBK; ++nb) {
@@ -498,9 +509,6 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
         __builtin_amdgcn_sched_barrier(0);
       }
       scv[NBK - 1] = weighted_relu_sum(f, c[(NBK - 1) & 1][0], c[(NBK - 1) & 1][1]);
-      if (half == 0)
-#pragma unroll
-        for (int nb = 0; nb < NBK; ++nb) sr[k0 + 32 * nb + col] = scv[nb];
     } else {
       if (nbv > 0) mma_block(0, c[0]);
 #pragma unroll
@@ -512,8 +520,14 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_tiled_bf16(
       }
       if (NBK - 1 < nbv) epi_block(NBK - 1, c[(NBK - 1) & 1]);
     }
-    if (it + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
+    lstore(buf ^ 1);
+    // The score stores come after the next tile's loads have been waited for,
+    // and the barrier settles LDS only: no wave waits for its score stores.
+    // (Buffer buf ^ 1 was last read before the previous barrier.)
+    if (full && half == 0)
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) sr[k0 + 32 * nb + col] = scv[nb];
+    lds_barrier();
   }
 }
 
