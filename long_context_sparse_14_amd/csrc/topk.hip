@@ -437,8 +437,13 @@ __device__ __forceinline__ void load_segment(const float* __restrict__ src, int6
       k[4 * u + 3] = float_order_key(v.w);
     }
   } else {
+    // every load issued (clamped to the row's last key), then the keys past
+    // the row dropped: loads under a condition each waited for the previous one
+    float v[SEG_PER_T];
 #pragma unroll
-    for (int u = 0; u < SEG_PER_T; ++u) k[u] = i0 + u < n ? float_order_key(src[i0 + u]) : 0u;
+    for (int u = 0; u < SEG_PER_T; ++u) v[u] = src[min(i0 + u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < SEG_PER_T; ++u) k[u] = i0 + u < n ? float_order_key(v[u]) : 0u;
   }
 }
 
@@ -459,11 +464,14 @@ __device__ __forceinline__ void sample_bounds(const float* __restrict__ src, int
   int S;
   if (n <= SAMPLES) {
     S = (int)n;
+    float v[SAMPLE_PER_T];
+#pragma unroll
+    for (int u = 0; u < SAMPLE_PER_T; ++u) v[u] = src[min((int)threadIdx.x + TK_THREADS * u, S - 1)];
 #pragma unroll
     for (int u = 0; u < SAMPLE_PER_T; ++u) {
       const int j = (int)threadIdx.x + TK_THREADS * u;
       valid[u] = j < S;
-      k[u] = valid[u] ? float_order_key(src[j]) : 0u;
+      k[u] = valid[u] ? float_order_key(v[u]) : 0u;
     }
   } else {
     S = SAMPLES;
@@ -638,12 +646,15 @@ __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, 
     select_row(scores + row * N, n, K, out, nullptr, sm.h, sm.sbuf, sm.s_res, sm.small);
     return;
   }
-  // this thread's entries of the row's list (every load independent)
+  // this thread's entries of the row's list: where each sits, then all of
+  // their loads at once (an entry past the list reads the row's first list
+  // slot, workspace memory, and is dropped)
   const uint32_t len = ndef + ncand;
   const uint32_t j0 = (uint32_t)LPT * (uint32_t)tid;
   uint32_t ck[LPT];
   int32_t ci[LPT];
   {
+    size_t off[LPT];
     int g = 0;  // segment of entry j0: the largest g with s_loff[g] <= j0
     if (j0 < len) {
       int lo = 0, hi = nseg;
@@ -657,14 +668,20 @@ __device__ __forceinline__ void seg_final_row(const float* __restrict__ scores, 
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const uint32_t j = j0 + u;
-      ck[u] = 0u;
-      ci[u] = -1;
+      off[u] = s0 * ws.cap;
       if (j < len) {
         while (sm.s_loff[g + 1] <= j) ++g;
-        const uint2 v = ws.list[(s0 + g) * ws.cap + (j - sm.s_loff[g])];
-        ck[u] = v.x;
-        ci[u] = (int32_t)v.y;
+        off[u] = (s0 + g) * ws.cap + (j - sm.s_loff[g]);
       }
+    }
+    uint2 lv[LPT];
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) lv[u] = ws.list[off[u]];
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const bool in = j0 + u < len;
+      ck[u] = in ? lv[u].x : 0u;
+      ci[u] = in ? (int32_t)lv[u].y : -1;
     }
   }
   const uint2 bnd = ws.bounds[row];
@@ -769,29 +786,44 @@ __global__ __launch_bounds__(TK_THREADS) void topk_presel_final(const float* __r
   if (ok) {
     __syncthreads();  // s_loff visible
     const uint32_t j0 = (uint32_t)PLPT * (uint32_t)tid;
-    int g = 0;  // segment of entry j0: the largest g with s_loff[g] <= j0
-    if (j0 < total) {
-      int lo = 0, hi = nseg;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (sm.s_loff[mid] <= j0) lo = mid;
-        else hi = mid;
+    // Where each of this thread's entries sits (segment g: the largest g with
+    // s_loff[g] <= j), then all of their loads at once: an entry past the list
+    // reads the row's first list slot (workspace memory) and is dropped.  With
+    // the search between the loads, each load waited for the previous one.
+    size_t off[PLPT];
+    {
+      int g = 0;
+      if (j0 < total) {
+        int lo = 0, hi = nseg;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (sm.s_loff[mid] <= j0) lo = mid;
+          else hi = mid;
+        }
+        g = lo;
       }
-      g = lo;
+#pragma unroll
+      for (int u = 0; u < PLPT; ++u) {
+        const uint32_t j = j0 + u;
+        off[u] = s0 * ps.cap;
+        if (j < total) {
+          while (sm.s_loff[g + 1] <= j) ++g;
+          off[u] = (s0 + g) * ps.cap + (j - sm.s_loff[g]);
+        }
+      }
     }
+    uint2 lv[PLPT];
+#pragma unroll
+    for (int u = 0; u < PLPT; ++u) lv[u] = ps.list[off[u]];
     uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
     for (int u = 0; u < PLPT; ++u) {
-      const uint32_t j = j0 + u;
-      ck[u] = 0u;
-      ci[u] = -1;
-      if (j < total) {
-        while (sm.s_loff[g + 1] <= j) ++g;
-        const uint2 v = ps.list[(s0 + g) * ps.cap + (j - sm.s_loff[g])];
-        ck[u] = v.x;
-        ci[u] = (int32_t)v.y;
-        mn = min(mn, v.x);
-        mx = max(mx, v.x);
+      const bool in = j0 + u < total;
+      ck[u] = in ? lv[u].x : 0u;
+      ci[u] = in ? (int32_t)lv[u].y : -1;
+      if (in) {
+        mn = min(mn, lv[u].x);
+        mx = max(mx, lv[u].x);
       }
     }
     uint32_t kmin, kmax;
