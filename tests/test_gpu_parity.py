@@ -200,6 +200,21 @@ def test_topk_long_rows_heavy_ties(kind):
         assert np.array_equal(idx[0, t], exp), f"{kind} row {t}"
 
 
+def test_topk_long_rows_unaligned():
+    """An odd row length: every row after the first starts off a 16-byte
+    boundary, so the segmented method loads all of its keys one by one (with
+    the ragged last segment besides), not in 16-byte vectors."""
+    dsa = _dsa()
+    rng = np.random.default_rng(17)
+    N, Tq, K = 40001, 3, 2048
+    vals = rng.integers(-50, 50, size=(1, Tq, N)).astype(np.float32)   # integer-valued: ties at the cut
+    print(f"unaligned long rows: N={N} Tq={Tq} K={K}", flush=True)
+    idx = dsa.topk(torch.from_numpy(vals).cuda(), K, N - Tq).cpu().numpy()
+    for t in range(Tq):
+        exp = oracle.topk_row(vals[0, t, :oracle.n_valid_keys(t, N - Tq, N)], K)
+        assert np.array_equal(idx[0, t], exp), f"row {t}"
+
+
 def test_topk_long_rows_sample_bounds_miss():
     """The segmented method bounds the threshold from 64 evenly spaced runs of
     64 keys.  Here every large score lies outside those runs, so the bounds
