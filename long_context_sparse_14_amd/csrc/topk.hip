@@ -153,6 +153,35 @@ __device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t
   kmax = mx;
 }
 
+// Block-wide smallest and largest of per-thread values (mn, mx) and the sum
+// of per-thread counts c.  sbuf3: 3 * TK_WAVES words, written once per
+// workgroup (no closing barrier).
+__device__ __forceinline__ void block_min_max_sum(uint32_t mn, uint32_t mx, uint32_t c, uint32_t& kmin,
+                                                  uint32_t& kmax, uint32_t& sum, uint32_t* sbuf3) {
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  c = wave_sum(c);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sbuf3[3 * wave] = mn;
+    sbuf3[3 * wave + 1] = mx;
+    sbuf3[3 * wave + 2] = c;
+  }
+  lds_barrier();
+  mn = 0xffffffffu;
+  mx = 0u;
+  c = 0u;
+#pragma unroll
+  for (int w = 0; w < TK_WAVES; ++w) {
+    mn = min(mn, sbuf3[3 * w]);
+    mx = max(mx, sbuf3[3 * w + 1]);
+    c += sbuf3[3 * w + 2];
+  }
+  kmin = mn;
+  kmax = mx;
+  sum = c;
+}
+
 // Exact select among the keys in [lo, hi] of a key set: the key value at
 // descending rank r (1 <= r <= their number), and in `above` how many of them
 // exceed it.  Each round splits the remaining key range into 2^FBITS bins of
@@ -741,8 +770,6 @@ struct PreselSmem {
   uint32_t sbuf[3 * TK_WAVES];
   uint32_t s_res[8];
   uint32_t small[65];
-  uint32_t s_loff[513];         // list offsets of the row's segments (at most 512)
-  uint32_t s_thr[512];
 };
 constexpr int PLPT = kPreselRowCap / TK_THREADS;  // list entries per thread
 static_assert(PLPT * TK_THREADS == kPreselRowCap, "whole list entries per thread");
@@ -769,65 +796,48 @@ __global__ __launch_bounds__(TK_THREADS) void topk_presel_final(const float* __r
   }
   const int nseg = (int)((n + ps.kpw - 1) / ps.kpw);  // segments the indexer ran for this row
   const size_t s0 = (size_t)row * ps.G;
+  const int cap = ps.cap;
   for (int b = tid; b < FB; b += TK_THREADS) sm.h[b] = 0u;
   if (tid == 0) sm.small[64] = 0u;
-  uint32_t total;
-  {
-    const uint32_t c = tid < nseg ? ps.count[s0 + tid] : 0u;
-    if (tid < nseg) sm.s_thr[tid] = ps.thr[s0 + tid];
-    const uint32_t ex = block_excl_scan(c, total, sm.sbuf);  // its barriers publish the bins and s_thr
-    if (tid < nseg) sm.s_loff[tid] = ex;
-    if (tid == 0) sm.s_loff[nseg] = total;
-  }
-  bool ok = total >= (uint32_t)K && total <= (uint32_t)kPreselRowCap;
+  // The row's lists as the workspace holds them, each at its full capacity:
+  // slot p is entry p % cap of segment p / cap, at list + s0 * cap + p (the
+  // G * cap <= kPreselRowCap slots of a row lie inside the workspace).
+  // Thread t takes slots PLPT*t .. PLPT*t + PLPT - 1, which span at most two
+  // segments (cap >= 16), and loads them together with those segments' counts
+  // and, for thread g < nseg, segment g's threshold: one round trip.  A slot is
+  // an entry iff its segment ran and its position is below that segment's
+  // count; thread order is then index order.
+  const int p0 = PLPT * tid;
+  const int ga = p0 / cap, gb = (p0 + PLPT - 1) / cap;
+  const uint32_t cnt_a = ps.count[s0 + min(ga, nseg - 1)], cnt_b = ps.count[s0 + min(gb, nseg - 1)];
+  const uint32_t thr_own = tid < nseg ? ps.thr[s0 + tid] : 0u;
+  uint2 lv[PLPT];
+#pragma unroll
+  for (int u = 0; u < PLPT; ++u) lv[u] = ps.list[s0 * cap + p0 + u];
   uint32_t ck[PLPT];
   int32_t ci[PLPT];
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int u = 0; u < PLPT; ++u) {
+    const int p = p0 + u;
+    const int g = p / cap;
+    const bool in = g < nseg && (uint32_t)(p - g * cap) < (g == ga ? cnt_a : cnt_b);
+    ck[u] = in ? lv[u].x : 0u;
+    ci[u] = in ? (int32_t)lv[u].y : -1;
+    if (in) {
+      mn = min(mn, lv[u].x);
+      mx = max(mx, lv[u].x);
+    }
+  }
+  // the row's entry count: each segment's count from the thread holding its first slot
+  uint32_t own = 0u;
+  if (p0 % cap == 0) own = ga < nseg ? cnt_a : 0u;   // segment ga starts at p0
+  else if (gb > ga) own = gb < nseg ? cnt_b : 0u;   // segment gb starts inside this thread's slots
+  uint32_t kmin, kmax, total;
+  block_min_max_sum(mn, mx, own, kmin, kmax, total, sm.sbuf);  // its barrier also publishes the cleared bins
+  bool ok = total >= (uint32_t)K;
   uint32_t T = 0u, keq = 0u;
   if (ok) {
-    __syncthreads();  // s_loff visible
-    const uint32_t j0 = (uint32_t)PLPT * (uint32_t)tid;
-    // Where each of this thread's entries sits (segment g: the largest g with
-    // s_loff[g] <= j), then all of their loads at once: an entry past the list
-    // reads the row's first list slot (workspace memory) and is dropped.  With
-    // the search between the loads, each load waited for the previous one.
-    size_t off[PLPT];
-    {
-      int g = 0;
-      if (j0 < total) {
-        int lo = 0, hi = nseg;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (sm.s_loff[mid] <= j0) lo = mid;
-          else hi = mid;
-        }
-        g = lo;
-      }
-#pragma unroll
-      for (int u = 0; u < PLPT; ++u) {
-        const uint32_t j = j0 + u;
-        off[u] = s0 * ps.cap;
-        if (j < total) {
-          while (sm.s_loff[g + 1] <= j) ++g;
-          off[u] = (s0 + g) * ps.cap + (j - sm.s_loff[g]);
-        }
-      }
-    }
-    uint2 lv[PLPT];
-#pragma unroll
-    for (int u = 0; u < PLPT; ++u) lv[u] = ps.list[off[u]];
-    uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-    for (int u = 0; u < PLPT; ++u) {
-      const bool in = j0 + u < total;
-      ck[u] = in ? lv[u].x : 0u;
-      ci[u] = in ? (int32_t)lv[u].y : -1;
-      if (in) {
-        mn = min(mn, lv[u].x);
-        mx = max(mx, lv[u].x);
-      }
-    }
-    uint32_t kmin, kmax;
-    block_min_max(mn, mx, kmin, kmax, sm.sbuf + TK_WAVES);
     auto add_cand = [&](HotBins& hb, uint32_t lo, uint32_t hi, int shift) {
 #pragma unroll
       for (int u = 0; u < PLPT; ++u)
@@ -843,10 +853,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_presel_final(const float* __r
                              sm.small);
     keq = (uint32_t)K - above;
     // every truncated list must reach down to T
-    const bool bad = tid < nseg && sm.s_thr[tid] != 0u && sm.s_thr[tid] > T;
+    const bool bad = tid < nseg && thr_own != 0u && thr_own > T;
     ok = __syncthreads_or(bad) == 0;
   }
   if (!ok) {
+    lds_barrier();  // every wave has read the reduction's words in sbuf before the fallback reuses them
     select_row(scores + row * N, n, K, out, nullptr, sm.h, sm.sbuf, sm.s_res, sm.small);
     return;
   }
