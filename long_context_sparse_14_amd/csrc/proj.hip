@@ -20,9 +20,10 @@
 // Tiling for many rows: a 256-thread workgroup (4 waves) owns a 128 x 128
 // tile of C; each wave a 64 x 64 block, four 32x32x16 MFMA chains fed by two A
 // and two B operand reads per k-step (few rows take the split-K kernel below).
-// K advances 32 at a time through double-buffered LDS tiles,
+// K advances 32 at a time (64 for a [N][K] B when K allows it) through
+// double-buffered LDS tiles,
 // and global loads run two tiles ahead through registers.  A and a [N][K] B
-// sit in LDS row-major with k contiguous (80-byte pitch), so an operand is
+// sit in LDS row-major with k contiguous (80- or 144-byte pitch), so an operand is
 // one 16-byte read.  A [K][N] B keeps its global layout in LDS (n contiguous,
 // 288-byte pitch) and reaches the MFMA through the gfx950 transposing read
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
@@ -36,8 +37,6 @@
 namespace dsa {
 namespace {
 
-constexpr int GK = 32;            // k per LDS tile
-constexpr int APITCH = GK + 8;    // bf16 per LDS row of A and of a [N][K] B
 constexpr int GN = 128;           // columns of C per workgroup
 constexpr int KNPITCH = GN + 16;  // bf16 per LDS k-row of a [K][N] B
 
@@ -49,15 +48,20 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
 }
 
-// WM x WN MFMA tiles per wave, WAVES_M x WAVES_N waves (4 in all).
-template <int WM, int WN, int WAVES_M, bool B_NK>
-__global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
+// WM x WN MFMA tiles per wave, WAVES_M x WAVES_N waves (4 in all); GK k per
+// LDS tile (32, or 64 when K allows it: each tile's loads are a round trip
+// that the two tiles of prefetch do not fully hide, so fewer, larger tiles
+// expose fewer of them).
+template <int WM, int WN, int WAVES_M, bool B_NK, int GK>
+__global__ __launch_bounds__(256, GK == 32 ? 3 : 2) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int APITCH = GK + 8;    // bf16 per LDS row of A and of a [N][K] B
+  constexpr int CPR = GK / 8;       // 16-byte chunks per row of an A tile
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int BM = 32 * WM * WAVES_M;
   static_assert(32 * WN * WAVES_N == GN, "a workgroup covers 128 columns");
   constexpr int A_CHUNKS = BM * GK / 8;                   // 16-byte chunks of an A tile
   constexpr int A_PER = (A_CHUNKS + 255) / 256;
-  constexpr int B_PER = GN * GK / 8 / 256;                // 2
+  constexpr int B_PER = GN * GK / 8 / 256;                // 2 or 4
   constexpr int B_LDS = B_NK ? GN * APITCH : GK * KNPITCH;
   constexpr int CPITCH = GN + 8;                          // bf16 per staged output row
   constexpr int LDS_ELEMS = 2 * BM * APITCH + 2 * B_LDS;
@@ -70,36 +74,45 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int half = lane >> 5, col = lane & 31;
   // Workgroups are dealt to the 8 XCDs round-robin by launch order; renumber
-  // them so that each XCD runs a contiguous range of tiles, and the column
-  // blocks that share rows of A run on one XCD and find them in its L2.
+  // them so that each XCD runs a contiguous range of tiles.  Within a batch
+  // entry the tiles go in groups of up to GROUP_M row blocks, the column
+  // index advancing once per group's sweep down its rows, so that the
+  // workgroups resident on one XCD at a time share both their rows of A and
+  // their columns of B in its L2 (row block after row block, every row block
+  // streamed all of B through it).
+  constexpr int64_t GROUP_M = 8;
   const int64_t gx = gridDim.x, gy = gridDim.y;
   const int64_t total = gx * gy * gridDim.z;
   int64_t P = blockIdx.x + gx * (blockIdx.y + gy * (int64_t)blockIdx.z);
   if ((total & 7) == 0) P = (P & 7) * (total >> 3) + (P >> 3);
   const int64_t z = P / (gx * gy);
-  const int64_t m0 = ((P / gx) % gy) * BM;
-  const int n0 = (int)(P % gx) * GN;
+  const int64_t local = P % (gx * gy);
+  const int64_t first_m = local / (GROUP_M * gx) * GROUP_M;
+  const int64_t gsz = min(gy - first_m, GROUP_M);
+  const int64_t in_group = local % (GROUP_M * gx);
+  const int64_t m0 = (first_m + in_group % gsz) * BM;
+  const int n0 = (int)(in_group / gsz) * GN;
   const uint16_t* A = g.A + z * g.sA;
   const uint16_t* B = g.B + z * g.sB;
   uint16_t* C = g.C + z * g.sC;
 
-  // Chunk c of an A tile: row c >> 2, k-chunk c & 3.  Of a [N][K] B tile: the
-  // same with n for the row.  Of a [K][N] B tile: k-row c >> 4, n-chunk c & 15.
+  // Chunk c of an A tile: row c / CPR, k-chunk c % CPR.  Of a [N][K] B tile:
+  // the same with n for the row.  Of a [K][N] B tile: k-row c >> 4, n-chunk c & 15.
   typedef u32x4 Stage[A_PER + B_PER];
   auto gload = [&](Stage& r, int k0) {
 #pragma unroll
     for (int u = 0; u < A_PER; ++u) {
       const int c = tid + 256 * u;
-      const int64_t m = m0 + (c >> 2);
-      r[u] = (c < A_CHUNKS && m < g.M) ? *reinterpret_cast<const u32x4*>(A + m * g.lda + k0 + 8 * (c & 3))
+      const int64_t m = m0 + c / CPR;
+      r[u] = (c < A_CHUNKS && m < g.M) ? *reinterpret_cast<const u32x4*>(A + m * g.lda + k0 + 8 * (c % CPR))
                                        : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < B_PER; ++u) {
       const int c = tid + 256 * u;
       if (B_NK) {
-        const int n = n0 + (c >> 2);
-        r[A_PER + u] = n < g.N ? *reinterpret_cast<const u32x4*>(B + (int64_t)n * g.ldb + k0 + 8 * (c & 3))
+        const int n = n0 + c / CPR;
+        r[A_PER + u] = n < g.N ? *reinterpret_cast<const u32x4*>(B + (int64_t)n * g.ldb + k0 + 8 * (c % CPR))
                                : u32x4{0, 0, 0, 0};
       } else {
         const int n = n0 + 8 * (c & 15);
@@ -112,13 +125,13 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int u = 0; u < A_PER; ++u) {
       const int c = tid + 256 * u;
-      if (c < A_CHUNKS) *reinterpret_cast<u32x4*>(&As[buf][(c >> 2) * APITCH + 8 * (c & 3)]) = r[u];
+      if (c < A_CHUNKS) *reinterpret_cast<u32x4*>(&As[buf][(c / CPR) * APITCH + 8 * (c % CPR)]) = r[u];
     }
 #pragma unroll
     for (int u = 0; u < B_PER; ++u) {
       const int c = tid + 256 * u;
       if (B_NK)
-        *reinterpret_cast<u32x4*>(&Bs[buf][(c >> 2) * APITCH + 8 * (c & 3)]) = r[A_PER + u];
+        *reinterpret_cast<u32x4*>(&Bs[buf][(c / CPR) * APITCH + 8 * (c % CPR)]) = r[A_PER + u];
       else
         *reinterpret_cast<u32x4*>(&Bs[buf][(c >> 4) * KNPITCH + 8 * (c & 15)]) = r[A_PER + u];
     }
@@ -337,10 +350,16 @@ template <int WM, int WN, int WAVES_M>
 hipError_t launch_tiles(const GemmArgs& g, bool b_nk, int64_t batch, hipStream_t stream) {
   constexpr int BM = 32 * WM * WAVES_M;
   const dim3 grid((unsigned)((g.N + GN - 1) / GN), (unsigned)((g.M + BM - 1) / BM), (unsigned)batch);
-  if (b_nk)
-    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, WAVES_M, true>), grid, dim3(256), 0, stream, g);
+  // 64-wide k tiles for [N][K] weights when K allows it (the output
+  // projection at M = 16384: 713 -> 649 us; the linear layer unchanged); the
+  // [K][N] absorption weight keeps 32 (with K = 128, the larger tiles' two
+  // workgroups per compute unit ran it 17% slower than three).
+  if (b_nk && g.K % 64 == 0)  // K is a multiple of 32 (checked on entry)
+    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, WAVES_M, true, 64>), grid, dim3(256), 0, stream, g);
+  else if (b_nk)
+    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, WAVES_M, true, 32>), grid, dim3(256), 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, WAVES_M, false>), grid, dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, WAVES_M, false, 32>), grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 

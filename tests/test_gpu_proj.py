@@ -48,6 +48,7 @@ def normal_bf16(shape, tensor_id, pow2=0, seed=0):
     (37, 4, 128, 64, 512),     # ragged rows, the V3.2 head shape
     (32, 128, 128, 64, 512),   # the 128K decode batch, all 128 heads
     (130, 3, 32, 0, 40),       # no rope part, a column block cut at 40
+    (200, 2, 128, 64, 512),    # 128-row tiles, four k tiles
 ])
 def test_absorb_q(M, H, d_nope, d_rope, d_c):
     dsa = _dsa()
@@ -64,6 +65,7 @@ def test_absorb_q(M, H, d_nope, d_rope, d_c):
     (37, 4, 512, 128),
     (32, 128, 512, 128),
     (70, 2, 64, 40),
+    (150, 2, 512, 128),        # eight 64-wide k steps, ragged rows
 ])
 def test_out_proj(M, H, d_c, d_v):
     dsa = _dsa()
@@ -79,6 +81,8 @@ def test_out_proj(M, H, d_c, d_v):
     (1, 200, 64),
     (300, 200, 96),     # 128-row tiles, ragged rows and columns, an odd number of k tiles
     (70, 64, 32),       # a single k tile
+    (260, 136, 1536),   # 24 k tiles of 64, ragged rows and columns
+    (140, 96, 320),     # an odd number (5) of 64-wide k tiles
 ])
 def test_linear(M, N, K):
     dsa = _dsa()
