@@ -61,9 +61,7 @@ constexpr int LONG_MAX_K = 4096;      // largest K of the long-row method
 constexpr int64_t LONG_MAX_SEGS = 4096;  // bound on rows x segments (workspace size)
 constexpr int LONG_MAX_G = TK_THREADS;   // bound on segments per row (one thread per segment)
 constexpr int RUN = 16;                  // keys per lane in a chunk of the compaction
-constexpr int CHUNK = RUN * TK_THREADS;  // keys ordered by one block prefix sum
 constexpr int WRUN = RUN * 64;           // consecutive keys of one wave in a chunk
-constexpr int PT = TK_CAP / TK_THREADS;  // keys per thread of a row staged in LDS
 
 __device__ __forceinline__ int64_t n_visible(int64_t row, int64_t Tq, int64_t N, int64_t q_pos0, const Vis& vis) {
   return visible_keys(vis, seq_q0(vis, row / Tq, Tq, q_pos0), row % Tq, N);
@@ -77,9 +75,9 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 // Exclusive block-wide prefix sum of v; `total` receives the block sum.
 // Without TRAIL the closing barrier is left out, and the caller must pass
 // another barrier before sbuf[0 .. TK_WAVES) is written again.
-template <bool TRAIL = true>
+template <bool TRAIL = true, int NTH = TK_THREADS>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, uint32_t* sbuf) {
-  return block_excl_scan_w<TK_WAVES, TRAIL, true>(v, total, sbuf);
+  return block_excl_scan_w<NTH / 64, TRAIL, true>(v, total, sbuf);
 }
 
 // ------------------------------------------------- range-adaptive select
@@ -90,12 +88,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total,
 // lie in bin ba.  s_res: 8 words; words 0..4 stay valid until the next call
 // (whose own barriers precede its writes).  With ZERO each thread clears the
 // bins it read, and the closing barrier publishes the cleared histogram.
-template <int FBITS, bool ZERO = false>
+template <int FBITS, bool ZERO = false, int NTH = TK_THREADS>
 __device__ __forceinline__ void find_two_bins(uint32_t* h, uint32_t ra, uint32_t rb, uint32_t& ba,
                                               uint32_t& above_a, uint32_t& bb, uint32_t& above_b,
                                               uint32_t& count_a, uint32_t* sbuf, uint32_t* s_res) {
-  constexpr int NB = 1 << FBITS, PER_T = NB / TK_THREADS;
-  static_assert(PER_T * TK_THREADS == NB, "whole bins per thread");
+  constexpr int NB = 1 << FBITS, PER_T = NB / NTH;
+  static_assert(PER_T * NTH == NB, "whole bins per thread");
   const int tid = threadIdx.x;
   uint32_t c[PER_T], t = 0;
 #pragma unroll
@@ -107,7 +105,7 @@ __device__ __forceinline__ void find_two_bins(uint32_t* h, uint32_t ra, uint32_t
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) h[NB - 1 - PER_T * tid - u] = 0u;
   uint32_t tot;
-  uint32_t run = block_excl_scan<false>(t, tot, sbuf);  // the s_res barrier below closes it
+  uint32_t run = block_excl_scan<false, NTH>(t, tot, sbuf);  // the s_res barrier below closes it
 #pragma unroll
   for (int u = 0; u < PER_T; ++u) {
     const uint32_t b = (uint32_t)(NB - 1 - PER_T * tid - u);
@@ -130,8 +128,10 @@ __device__ __forceinline__ void find_two_bins(uint32_t* h, uint32_t ra, uint32_t
   count_a = s_res[4];
 }
 
-// Block-wide smallest and largest of per-thread values (mn, mx).
-// sbuf2: 2 * TK_WAVES words, written once per workgroup (no closing barrier).
+// Block-wide smallest and largest of per-thread values (mn, mx) over NTH
+// threads.  sbuf2: 2 * NTH / 64 words, written once per workgroup (no closing
+// barrier).
+template <int NTH = TK_THREADS>
 __device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t& kmin, uint32_t& kmax,
                                               uint32_t* sbuf2) {
   mn = wave_min(mn);
@@ -145,7 +145,7 @@ __device__ __forceinline__ void block_min_max(uint32_t mn, uint32_t mx, uint32_t
   mn = 0xffffffffu;
   mx = 0u;
 #pragma unroll
-  for (int w = 0; w < TK_WAVES; ++w) {
+  for (int w = 0; w < NTH / 64; ++w) {
     mn = min(mn, sbuf2[2 * w]);
     mx = max(mx, sbuf2[2 * w + 1]);
   }
@@ -193,7 +193,7 @@ __device__ __forceinline__ void block_min_max_sum(uint32_t mn, uint32_t mx, uint
 // ranks them directly, in place of further histogram rounds.  On entry all
 // 2^FBITS bins of h and the counter small[64] must be zero, made visible by a
 // barrier; each round's bin search clears the histogram for the next one.
-template <int FBITS, typename AddKeys, typename EachKey>
+template <int FBITS, int NTH = TK_THREADS, typename AddKeys, typename EachKey>
 __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo, uint32_t hi, uint32_t r,
                                 uint32_t& above, uint32_t* h, uint32_t* sbuf, uint32_t* s_res, uint32_t* small) {
   above = 0;
@@ -205,7 +205,7 @@ __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo,
     hb.flush(h);
     lds_barrier();
     uint32_t b, ab, b2, ab2, cnt;
-    find_two_bins<FBITS, true>(h, r, r, b, ab, b2, ab2, cnt, sbuf, s_res);
+    find_two_bins<FBITS, true, NTH>(h, r, r, b, ab, b2, ab2, cnt, sbuf, s_res);
     above += ab;
     r -= ab;
     const uint32_t nlo = lo + (b << shift);
@@ -242,58 +242,61 @@ __device__ uint32_t select_rank(AddKeys add_keys, EachKey each_key, uint32_t lo,
 }
 
 // Writes a row with n <= K: 0..n-1, then -1.
+template <int NTH = TK_THREADS>
 __device__ __forceinline__ void write_whole_row(int64_t n, int K, int32_t* __restrict__ out) {
-  for (int64_t i = threadIdx.x; i < K; i += TK_THREADS) out[i] = i < n ? (int32_t)i : -1;
+  for (int64_t i = threadIdx.x; i < K; i += NTH) out[i] = i < n ? (int32_t)i : -1;
 }
 
 // The K-th largest key T of a row of n32 > K keys whose range is [kmin,
-// kmax], by histogram rounds over the whole row; `above` receives how many
-// keys exceed T.  key_at(i) returns key i.  hist (all bins zero) and
-// small[64] (zero) must have been published by a barrier.
-template <typename KeyAt>
+// kmax], by histogram rounds of 2^HBITS bins over the whole row (NTH
+// threads); `above` receives how many keys exceed T.  key_at(i) returns key
+// i.  hist (all bins zero) and small[64] (zero) must have been published by a
+// barrier.
+template <int NTH = TK_THREADS, int HBITS = 11, typename KeyAt>
 __device__ __forceinline__ uint32_t select_full(KeyAt key_at, int n32, int K, uint32_t kmin, uint32_t kmax,
                                                 uint32_t& above, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res,
                                                 uint32_t* small) {
   const int tid = threadIdx.x;
   // (the bins span the keys' own range, so plain atomics rarely collide)
   auto add_row = [&](HotBins&, uint32_t lo, uint32_t hi, int shift) {
-    for (int base = tid; base < n32; base += 8 * TK_THREADS) {
+    for (int base = tid; base < n32; base += 8 * NTH) {
       uint32_t k[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = base + u * TK_THREADS;
+        const int i = base + u * NTH;
         k[u] = i < n32 ? key_at(i) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = base + u * TK_THREADS;
+        const int i = base + u * NTH;
         if (i < n32 && k[u] >= lo && k[u] <= hi) atomicAdd(&hist[(k[u] - lo) >> shift], 1u);
       }
     }
   };
   auto each_row = [&](uint32_t lo, uint32_t hi, auto fn) {
-    for (int base = tid; base < n32; base += 8 * TK_THREADS) {
+    for (int base = tid; base < n32; base += 8 * NTH) {
       uint32_t k[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = base + u * TK_THREADS;
+        const int i = base + u * NTH;
         k[u] = i < n32 ? key_at(i) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = base + u * TK_THREADS;
+        const int i = base + u * NTH;
         if (i < n32 && k[u] >= lo && k[u] <= hi) fn(k[u]);
       }
     }
   };
-  return select_rank<11>(add_row, each_row, kmin, kmax, (uint32_t)K, above, hist, sbuf, s_res, small);
+  return select_rank<HBITS, NTH>(add_row, each_row, kmin, kmax, (uint32_t)K, above, hist, sbuf, s_res, small);
 }
 
 // In-order compaction of a row of n32 keys with threshold T, keeping keq of
-// the keys equal to T.
-template <typename KeyAt>
+// the keys equal to T (NTH threads).
+template <int NTH = TK_THREADS, typename KeyAt>
 __device__ __forceinline__ void compact_row(KeyAt key_at, int n32, uint32_t T, uint32_t keq,
                                             int32_t* __restrict__ out, uint32_t* sbuf) {
+  constexpr int CHUNK = RUN * NTH;  // keys ordered by one block prefix sum
   const int tid = threadIdx.x;
   // In-order compaction, CHUNK keys at a time: wave w owns the run of WRUN
   // consecutive keys starting at base + WRUN*w and reads it lane by lane (step
@@ -318,7 +321,7 @@ __device__ __forceinline__ void compact_row(KeyAt key_at, int n32, uint32_t T, u
     cgt = wave_sum((uint32_t)__popc(bits & ((1u << RUN) - 1u)));
     ceq = wave_sum((uint32_t)__popc(bits >> RUN));
     uint32_t tot;
-    const uint32_t ex = block_excl_scan(lane == 0 ? (ceq << 16) | cgt : 0u, tot, sbuf);
+    const uint32_t ex = block_excl_scan<true, NTH>(lane == 0 ? (ceq << 16) | cgt : 0u, tot, sbuf);
     const uint32_t wex = __builtin_amdgcn_readfirstlane(ex);  // lane 0's prefix: the keys of earlier waves
     uint32_t g = run_gt + (wex & 0xffffu), e = run_eq + (wex >> 16);
 #pragma unroll
@@ -338,14 +341,17 @@ __device__ __forceinline__ void compact_row(KeyAt key_at, int n32, uint32_t T, u
 }
 
 
-// The one-workgroup method for one row.  skey: LDS stage of TK_CAP keys, or
-// nullptr to read the row from global memory on every pass.  hist: 2048 bins;
-// sbuf: 3 * TK_WAVES words; s_res: 8 words; small: 65 words.
+// The one-workgroup method for one row, NTH threads.  skey: LDS stage of CAP
+// keys, or nullptr to read the row from global memory on every pass.  hist:
+// 2^HBITS bins; sbuf: 3 * NTH / 64 words; s_res: 8 words; small: 65 words.
+template <int NTH = TK_THREADS, int CAP = TK_CAP, int HBITS = 11>
 __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_t n, int K, int32_t* __restrict__ out,
                            uint32_t* skey, uint32_t* hist, uint32_t* sbuf, uint32_t* s_res, uint32_t* small) {
+  constexpr int PTN = CAP / NTH;  // keys per thread of a row staged in LDS
+  static_assert(PTN * NTH == CAP, "whole keys per thread");
   const int tid = threadIdx.x;
   if (n <= K) {
-    write_whole_row(n, K, out);
+    write_whole_row<NTH>(n, K, out);
     return;
   }
   // keys (staged in LDS when skey is given: the whole row's loads in flight at
@@ -354,15 +360,15 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_
   const int n32 = (int)n;
   uint32_t mn = 0xffffffffu, mx = 0u;
   if (skey != nullptr) {
-    float v[PT];
+    float v[PTN];
 #pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int i = tid + u * TK_THREADS;
+    for (int u = 0; u < PTN; ++u) {
+      const int i = tid + u * NTH;
       v[u] = i < n32 ? src[i] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int i = tid + u * TK_THREADS;
+    for (int u = 0; u < PTN; ++u) {
+      const int i = tid + u * NTH;
       if (i < n32) {
         const uint32_t k = float_order_key(v[u]);
         skey[i] = k;
@@ -371,16 +377,16 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_
       }
     }
   }
-  for (int base = tid; skey == nullptr && base < n32; base += 8 * TK_THREADS) {
+  for (int base = tid; skey == nullptr && base < n32; base += 8 * NTH) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int i = base + u * TK_THREADS;
+      const int i = base + u * NTH;
       v[u] = i < n32 ? src[i] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int i = base + u * TK_THREADS;
+      const int i = base + u * NTH;
       if (i < n32) {
         const uint32_t k = float_order_key(v[u]);
         mn = min(mn, k);
@@ -388,27 +394,42 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_
       }
     }
   }
-  for (int b = tid; b < HB; b += TK_THREADS) hist[b] = 0u;  // the select starts from empty bins
+  for (int b = tid; b < (1 << HBITS); b += NTH) hist[b] = 0u;  // the select starts from empty bins
   if (tid == 0) small[64] = 0u;
   uint32_t kmin, kmax;
-  block_min_max(mn, mx, kmin, kmax, sbuf + TK_WAVES);  // its barrier also publishes skey and the bins
+  block_min_max<NTH>(mn, mx, kmin, kmax, sbuf + NTH / 64);  // its barrier also publishes skey and the bins
   auto key_at = [&](int i) -> uint32_t { return skey != nullptr ? skey[i] : float_order_key(src[i]); };
   uint32_t above;
-  const uint32_t T = select_full(key_at, n32, K, kmin, kmax, above, hist, sbuf, s_res, small);
-  compact_row(key_at, n32, T, (uint32_t)K - above, out, sbuf);
+  const uint32_t T = select_full<NTH, HBITS>(key_at, n32, K, kmin, kmax, above, hist, sbuf, s_res, small);
+  compact_row<NTH>(key_at, n32, T, (uint32_t)K - above, out, sbuf);
 }
 
-__global__ __launch_bounds__(TK_THREADS, 8) void topk_rows_kernel(const float* __restrict__ scores,
-                                                               int32_t* __restrict__ idx, int64_t Tq,
-                                                               int64_t N, int64_t q_pos0, Vis vis, int K) {
-  __shared__ uint32_t skey[TK_CAP];
-  __shared__ uint32_t hist[HB];
-  __shared__ uint32_t sbuf[3 * TK_WAVES];
+// Rows of at most SHORT_KEYS keys run on 512-thread workgroups with a 32 KiB
+// stage and 10-bit histogram rounds (36 KiB of LDS, four workgroups per
+// compute unit); longer rows on 1024-thread workgroups with a 64 KiB stage
+// and 11-bit rounds (two per compute unit).  A row's time is mostly fixed
+// latency (its load, the select's barriers, the compaction's stores), so
+// twice the rows in flight serve short rows faster.
+constexpr int SHORT_KEYS = 8192;
+
+// Grid: (row index within the sequence from t_begin, sequence).  Each
+// instance takes only its own rows (SHORT: at most SHORT_KEYS keys).
+template <int NTH, int CAP, int HBITS, bool SHORT>
+__global__ __launch_bounds__(NTH, 8) void topk_rows_kernel(const float* __restrict__ scores,
+                                                           int32_t* __restrict__ idx, int64_t Tq, int64_t N,
+                                                           int64_t q_pos0, Vis vis, int K, int64_t t_begin) {
+  __shared__ uint32_t skey[CAP];
+  __shared__ uint32_t hist[1 << HBITS];
+  __shared__ uint32_t sbuf[3 * NTH / 64];
   __shared__ uint32_t s_res[8];
   __shared__ uint32_t small[65];
-  const int64_t row = blockIdx.x;
+  const int64_t t = t_begin + blockIdx.x;
+  if (t >= Tq) return;
+  const int64_t row = (int64_t)blockIdx.y * Tq + t;
   const int64_t n = n_visible(row, Tq, N, q_pos0, vis);
-  select_row(scores + row * N, n, K, idx + row * K, n <= TK_CAP ? skey : nullptr, hist, sbuf, s_res, small);
+  if (SHORT != (n <= SHORT_KEYS)) return;  // the other instance's row (whole workgroup)
+  select_row<NTH, CAP, HBITS>(scores + row * N, n, K, idx + row * K, n <= CAP ? skey : nullptr, hist, sbuf, s_res,
+                              small);
 }
 
 // ---------------------------------------------------------------- long rows
@@ -914,8 +935,31 @@ hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq,
   // longest visible row: with per-sequence lengths only N is known on the host
   const int64_t nmax = seq_lens != nullptr ? N : min(N, (q_pos0 + Tq) / m);
   if (nmax <= TK_CAP || !use_long_path(B, Tq, N, K)) {
-    hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)R), dim3(TK_THREADS), 0, stream, scores, idx, Tq, N, q_pos0,
-                       vis, K);
+    // Without per-sequence lengths a row's key count grows with t, the same
+    // in every sequence: rows t < t_split have at most SHORT_KEYS keys.  With
+    // them, both instances run over every row and each keeps its own.
+    int64_t t_split = Tq;
+    if (seq_lens == nullptr) {
+      auto n_at = [&](int64_t t) {
+        const int64_t p1 = q_pos0 + t + 1;
+        return p1 <= 0 ? (int64_t)0 : min(N, p1 / m);
+      };
+      int64_t lo = 0, hi = Tq;  // first t in [0, Tq) with more than SHORT_KEYS keys, or Tq
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (n_at(mid) > SHORT_KEYS) hi = mid;
+        else lo = mid + 1;
+      }
+      t_split = lo;
+    }
+    const int64_t short_rows = t_split, long_begin = seq_lens == nullptr ? t_split : 0;
+    if (short_rows > 0)
+      hipLaunchKernelGGL((topk_rows_kernel<512, SHORT_KEYS, 10, true>), dim3((unsigned)short_rows, (unsigned)B),
+                         dim3(512), 0, stream, scores, idx, Tq, N, q_pos0, vis, K, (int64_t)0);
+    if (Tq - long_begin > 0)
+      hipLaunchKernelGGL((topk_rows_kernel<TK_THREADS, TK_CAP, 11, false>),
+                         dim3((unsigned)(Tq - long_begin), (unsigned)B), dim3(TK_THREADS), 0, stream, scores, idx, Tq,
+                         N, q_pos0, vis, K, long_begin);
     return hipGetLastError();
   }
   const int G = long_segments(N);
