@@ -406,18 +406,125 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int64_
 
 // Rows of at most SHORT_KEYS keys run on 512-thread workgroups with a 32 KiB
 // stage and 10-bit histogram rounds (36 KiB of LDS, four workgroups per
-// compute unit); longer rows on 1024-thread workgroups with a 64 KiB stage
-// and 11-bit rounds (two per compute unit).  A row's time is mostly fixed
-// latency (its load, the select's barriers, the compaction's stores), so
-// twice the rows in flight serve short rows faster.
+// compute unit); rows of up to 2 * SHORT_KEYS keys on the same workgroups
+// with their second half in registers (select_row_split); longer rows on
+// 1024-thread workgroups that read the row from global memory on every pass.
+// A row's time is mostly fixed latency (its load, the select's barriers, the
+// compaction's stores), so four rows in flight per compute unit, where a
+// 64 KiB stage allowed two, serve rows faster.
 constexpr int SHORT_KEYS = 8192;
+constexpr int SPLIT_NTH = 512;
 
-// Grid: (row index within the sequence from t_begin, sequence).  Each
-// instance takes only its own rows (SHORT: at most SHORT_KEYS keys).
-template <int NTH, int CAP, int HBITS, bool SHORT>
-__global__ __launch_bounds__(NTH, 8) void topk_rows_kernel(const float* __restrict__ scores,
-                                                           int32_t* __restrict__ idx, int64_t Tq, int64_t N,
-                                                           int64_t q_pos0, Vis vis, int K, int64_t t_begin) {
+// One row of SHORT_KEYS < n <= 2 * SHORT_KEYS keys (n > K) on SPLIT_NTH
+// threads: keys [0, SHORT_KEYS) staged in LDS (thread t: keys t + 512u), the
+// rest in registers in the order the compaction reads them (thread of wave w,
+// lane l: key SHORT_KEYS + WRUN*w + 64u + l, u < RUN), so that the second
+// compaction chunk is each thread's own registers.
+__device__ __forceinline__ void select_row_split(const float* __restrict__ src, int64_t n, int K,
+                                                 int32_t* __restrict__ out, uint32_t* skey, uint32_t* hist,
+                                                 uint32_t* sbuf, uint32_t* s_res, uint32_t* small) {
+  constexpr int NTH = SPLIT_NTH, HBITS = 10, PTN = SHORT_KEYS / NTH;
+  static_assert(PTN == RUN && WRUN * (NTH / 64) == SHORT_KEYS, "the register half is one compaction chunk");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = (int)n;
+  // every load issued at once (the register half clamped to the row's last key)
+  float v[PTN], w[PTN];
+#pragma unroll
+  for (int u = 0; u < PTN; ++u) v[u] = src[tid + u * NTH];
+#pragma unroll
+  for (int u = 0; u < PTN; ++u) w[u] = src[min(SHORT_KEYS + WRUN * wave + 64 * u + lane, n32 - 1)];
+  uint32_t mn = 0xffffffffu, mx = 0u, rk[PTN], rvm = 0u;  // rvm bit u: register key u lies in the row
+#pragma unroll
+  for (int u = 0; u < PTN; ++u) {
+    const uint32_t k = float_order_key(v[u]);
+    skey[tid + u * NTH] = k;
+    mn = min(mn, k);
+    mx = max(mx, k);
+  }
+#pragma unroll
+  for (int u = 0; u < PTN; ++u) {
+    const bool in = SHORT_KEYS + WRUN * wave + 64 * u + lane < n32;
+    rk[u] = in ? float_order_key(w[u]) : 0u;
+    rvm |= (uint32_t)in << u;
+    if (in) {
+      mn = min(mn, rk[u]);
+      mx = max(mx, rk[u]);
+    }
+  }
+  for (int b = tid; b < (1 << HBITS); b += NTH) hist[b] = 0u;  // the select starts from empty bins
+  if (tid == 0) small[64] = 0u;
+  uint32_t kmin, kmax;
+  block_min_max<NTH>(mn, mx, kmin, kmax, sbuf + NTH / 64);  // its barrier also publishes skey and the bins
+  auto add_row = [&](HotBins&, uint32_t lo, uint32_t hi, int shift) {
+#pragma unroll
+    for (int u = 0; u < PTN; ++u) {
+      const uint32_t k = skey[tid + u * NTH];
+      if (k >= lo && k <= hi) atomicAdd(&hist[(k - lo) >> shift], 1u);
+    }
+#pragma unroll
+    for (int u = 0; u < PTN; ++u)
+      if (((rvm >> u) & 1u) && rk[u] >= lo && rk[u] <= hi) atomicAdd(&hist[(rk[u] - lo) >> shift], 1u);
+  };
+  auto each_row = [&](uint32_t lo, uint32_t hi, auto fn) {
+#pragma unroll
+    for (int u = 0; u < PTN; ++u) {
+      const uint32_t k = skey[tid + u * NTH];
+      if (k >= lo && k <= hi) fn(k);
+    }
+#pragma unroll
+    for (int u = 0; u < PTN; ++u)
+      if (((rvm >> u) & 1u) && rk[u] >= lo && rk[u] <= hi) fn(rk[u]);
+  };
+  uint32_t above;
+  const uint32_t T = select_rank<HBITS, NTH>(add_row, each_row, kmin, kmax, (uint32_t)K, above, hist, sbuf, s_res,
+                                             small);
+  const uint32_t keq = (uint32_t)K - above;
+  // In-order compaction in two chunks of SHORT_KEYS keys, as in compact_row:
+  // wave w owns keys c0 + WRUN*w + 64u + lane (u < RUN) of chunk c0.
+  uint32_t run_gt = 0, run_eq = 0;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int w0 = SHORT_KEYS * c + WRUN * wave;
+    uint32_t bits = 0;  // bit u: key u above T; bit RUN + u: equal to T
+#pragma unroll
+    for (int u = 0; u < RUN; ++u) {
+      const bool ok = c == 0 || ((rvm >> u) & 1u);
+      const uint32_t k = c == 0 ? skey[w0 + 64 * u + lane] : rk[u];
+      bits |= (uint32_t)(ok && k > T) << u;
+      bits |= (uint32_t)(ok && k == T) << (RUN + u);
+    }
+    const uint32_t cgt = wave_sum((uint32_t)__popc(bits & ((1u << RUN) - 1u)));
+    const uint32_t ceq = wave_sum((uint32_t)__popc(bits >> RUN));
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<true, NTH>(lane == 0 ? (ceq << 16) | cgt : 0u, tot, sbuf);
+    const uint32_t wex = __builtin_amdgcn_readfirstlane(ex);  // lane 0's prefix: the keys of earlier waves
+    uint32_t g = run_gt + (wex & 0xffffu), e = run_eq + (wex >> 16);
+#pragma unroll
+    for (int u = 0; u < RUN; ++u) {
+      const bool is_gt = (bits >> u) & 1u, is_eq = (bits >> (RUN + u)) & 1u;
+      const uint64_t mg = __ballot(is_gt), me = __ballot(is_eq);
+      const uint32_t bg = g + lanes_below(mg), be = e + lanes_below(me);
+      const int32_t i = w0 + 64 * u + lane;
+      if (is_gt) out[bg + min(be, keq)] = i;
+      else if (is_eq && be < keq) out[bg + be] = i;
+      g += (uint32_t)__popcll(mg);
+      e += (uint32_t)__popcll(me);
+    }
+    run_gt += tot & 0xffffu;
+    run_eq += tot >> 16;
+  }
+}
+
+// Grid: (row index within the sequence from t_begin, sequence).  MODE 0:
+// rows of at most SHORT_KEYS keys; 1: rows of up to 2 * SHORT_KEYS; 2: longer
+// rows (read from global memory on every pass).  Each instance takes only its
+// own rows.
+template <int MODE>
+__global__ __launch_bounds__(MODE == 2 ? TK_THREADS : SPLIT_NTH, 8) void topk_rows_kernel(
+    const float* __restrict__ scores, int32_t* __restrict__ idx, int64_t Tq, int64_t N, int64_t q_pos0, Vis vis, int K,
+    int64_t t_begin) {
+  constexpr int NTH = MODE == 2 ? TK_THREADS : SPLIT_NTH, HBITS = MODE == 2 ? 11 : 10;
+  constexpr int CAP = MODE == 2 ? TK_THREADS : SHORT_KEYS;  // MODE 2 stages nothing (a one-key-per-thread stub)
   __shared__ uint32_t skey[CAP];
   __shared__ uint32_t hist[1 << HBITS];
   __shared__ uint32_t sbuf[3 * NTH / 64];
@@ -427,9 +534,15 @@ __global__ __launch_bounds__(NTH, 8) void topk_rows_kernel(const float* __restri
   if (t >= Tq) return;
   const int64_t row = (int64_t)blockIdx.y * Tq + t;
   const int64_t n = n_visible(row, Tq, N, q_pos0, vis);
-  if (SHORT != (n <= SHORT_KEYS)) return;  // the other instance's row (whole workgroup)
-  select_row<NTH, CAP, HBITS>(scores + row * N, n, K, idx + row * K, n <= CAP ? skey : nullptr, hist, sbuf, s_res,
-                              small);
+  const int mode = n <= SHORT_KEYS ? 0 : (n <= 2 * SHORT_KEYS ? 1 : 2);
+  if (mode != MODE) return;  // another instance's row (whole workgroup)
+  if constexpr (MODE == 1) {
+    if (n <= K) write_whole_row<NTH>(n, K, idx + row * K);
+    else select_row_split(scores + row * N, n, K, idx + row * K, skey, hist, sbuf, s_res, small);
+  } else {
+    select_row<NTH, CAP, HBITS>(scores + row * N, n, K, idx + row * K, MODE == 0 ? skey : nullptr, hist, sbuf, s_res,
+                                small);
+  }
 }
 
 // ---------------------------------------------------------------- long rows
@@ -936,30 +1049,37 @@ hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq,
   const int64_t nmax = seq_lens != nullptr ? N : min(N, (q_pos0 + Tq) / m);
   if (nmax <= TK_CAP || !use_long_path(B, Tq, N, K)) {
     // Without per-sequence lengths a row's key count grows with t, the same
-    // in every sequence: rows t < t_split have at most SHORT_KEYS keys.  With
-    // them, both instances run over every row and each keeps its own.
-    int64_t t_split = Tq;
+    // in every sequence: rows [0, t1) have at most SHORT_KEYS keys, rows
+    // [t1, t2) at most 2 * SHORT_KEYS.  With them, every instance runs over
+    // every row and each keeps its own.
+    int64_t t1 = 0, t2 = 0;
     if (seq_lens == nullptr) {
       auto n_at = [&](int64_t t) {
         const int64_t p1 = q_pos0 + t + 1;
         return p1 <= 0 ? (int64_t)0 : min(N, p1 / m);
       };
-      int64_t lo = 0, hi = Tq;  // first t in [0, Tq) with more than SHORT_KEYS keys, or Tq
-      while (lo < hi) {
-        const int64_t mid = (lo + hi) / 2;
-        if (n_at(mid) > SHORT_KEYS) hi = mid;
-        else lo = mid + 1;
-      }
-      t_split = lo;
+      auto first_above = [&](int64_t keys) {  // first t in [0, Tq) with more than `keys` keys, or Tq
+        int64_t lo = 0, hi = Tq;
+        while (lo < hi) {
+          const int64_t mid = (lo + hi) / 2;
+          if (n_at(mid) > keys) hi = mid;
+          else lo = mid + 1;
+        }
+        return lo;
+      };
+      t1 = first_above(SHORT_KEYS);
+      t2 = first_above(2 * SHORT_KEYS);
     }
-    const int64_t short_rows = t_split, long_begin = seq_lens == nullptr ? t_split : 0;
-    if (short_rows > 0)
-      hipLaunchKernelGGL((topk_rows_kernel<512, SHORT_KEYS, 10, true>), dim3((unsigned)short_rows, (unsigned)B),
-                         dim3(512), 0, stream, scores, idx, Tq, N, q_pos0, vis, K, (int64_t)0);
-    if (Tq - long_begin > 0)
-      hipLaunchKernelGGL((topk_rows_kernel<TK_THREADS, TK_CAP, 11, false>),
-                         dim3((unsigned)(Tq - long_begin), (unsigned)B), dim3(TK_THREADS), 0, stream, scores, idx, Tq,
-                         N, q_pos0, vis, K, long_begin);
+    const int64_t b0[3] = {0, t1, t2}, b1[3] = {seq_lens == nullptr ? t1 : Tq, seq_lens == nullptr ? t2 : Tq, Tq};
+    if (b1[0] > b0[0])
+      hipLaunchKernelGGL(topk_rows_kernel<0>, dim3((unsigned)(b1[0] - b0[0]), (unsigned)B), dim3(SPLIT_NTH), 0,
+                         stream, scores, idx, Tq, N, q_pos0, vis, K, b0[0]);
+    if (b1[1] > b0[1])
+      hipLaunchKernelGGL(topk_rows_kernel<1>, dim3((unsigned)(b1[1] - b0[1]), (unsigned)B), dim3(SPLIT_NTH), 0,
+                         stream, scores, idx, Tq, N, q_pos0, vis, K, b0[1]);
+    if (b1[2] > b0[2])
+      hipLaunchKernelGGL(topk_rows_kernel<2>, dim3((unsigned)(b1[2] - b0[2]), (unsigned)B), dim3(TK_THREADS), 0,
+                         stream, scores, idx, Tq, N, q_pos0, vis, K, b0[2]);
     return hipGetLastError();
   }
   const int G = long_segments(N);

@@ -163,6 +163,11 @@ def test_indexer_bf16_negative_weights_exact():
     (70000, 2048, 69990, 3), # segmented long-row method, 5 segments, last one ragged
     (131072, 4096, 131071, 1),  # the largest K of the segmented method
     (40000, 4097, 39999, 1), # K above the segmented method's limit: one workgroup per row
+    (16400, 2048, 8188, 8),  # 8189..8196 keys: rows staged whole / half staged, half in registers
+    (16400, 4097, 16380, 8), # 16381..16388 keys: half in registers / read from global memory
+    (12345, 3000, 12000, 3), # the register half ends inside a wave's run
+    (9000, 8999, 8997, 3),   # n <= K and n == K + 1 among rows of the register-half instance
+    (16384, 1, 16381, 3),    # K = 1 up to the longest register-half row
 ])
 def test_topk_exact_with_ties(N, K, q_pos0, Tq):
     dsa = _dsa()

@@ -57,6 +57,7 @@ def test_indexer_varlen_exact(Tq, N, lens):
 @pytest.mark.parametrize("Tq,N,K,lens", [
     (1, 20000, 2048, [20000, 17000, 5000, 2]),  # segmented long-row method
     (3, 3000, 64, [3000, 1000, 2]),             # one-workgroup method, negative positions in the last
+    (3, 20000, 5000, [20000, 12000, 8194, 300]),  # every row instance of the one-workgroup method in one call
 ])
 def test_topk_varlen_exact(Tq, N, K, lens):
     dsa = _dsa()
