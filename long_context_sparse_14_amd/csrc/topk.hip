@@ -555,6 +555,7 @@ static_assert(SAMPLE_PER_T * TK_THREADS == SAMPLES && SAMPLE_RUN % SAMPLE_PER_T 
 
 constexpr int FB_BITS = 12;               // bins of the long-row histograms: 4096
 constexpr int FB = 1 << FB_BITS;
+static_assert(FB >= HB, "a long-row histogram also serves the one-workgroup fallback's 11-bit rounds");
 
 // A segment's list holds its keys at or above t_lo in index order, definite
 // and candidate keys together: at most K + CAND_CAP entries whenever the
@@ -734,7 +735,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_classify(const float* __r
 
 // Shared memory of the final step.
 struct FinalSmem {
-  uint32_t h[FB];               // FB >= HB: also the fallback's histogram
+  uint32_t h[FB];               // also the fallback's histogram
   uint32_t sbuf[3 * TK_WAVES];
   uint32_t s_res[8];
   uint32_t small[65];
@@ -900,7 +901,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_seg_final(const float* __rest
 
 // Shared memory of the pre-selected final step.
 struct PreselSmem {
-  uint32_t h[FB];               // FB >= HB: also the fallback's histogram
+  uint32_t h[FB];               // also the fallback's histogram
   uint32_t sbuf[3 * TK_WAVES];
   uint32_t s_res[8];
   uint32_t small[65];

@@ -163,6 +163,8 @@ def test_indexer_bf16_negative_weights_exact():
     (70000, 2048, 69990, 3), # segmented long-row method, 5 segments, last one ragged
     (131072, 4096, 131071, 1),  # the largest K of the segmented method
     (40000, 4097, 39999, 1), # K above the segmented method's limit: one workgroup per row
+    (16400, 2048, 4092, 8),  # 4093..4100 keys, staged whole
+    (5000, 4095, 4093, 4),   # n <= K, n == K + 1 and K + 2 among staged rows
     (16400, 2048, 8188, 8),  # 8189..8196 keys: rows staged whole / half staged, half in registers
     (16400, 4097, 16380, 8), # 16381..16388 keys: half in registers / read from global memory
     (12345, 3000, 12000, 3), # the register half ends inside a wave's run

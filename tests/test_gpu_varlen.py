@@ -58,6 +58,7 @@ def test_indexer_varlen_exact(Tq, N, lens):
     (1, 20000, 2048, [20000, 17000, 5000, 2]),  # segmented long-row method
     (3, 3000, 64, [3000, 1000, 2]),             # one-workgroup method, negative positions in the last
     (3, 20000, 5000, [20000, 12000, 8194, 300]),  # every row instance of the one-workgroup method in one call
+    (3, 16384, 1000, [16384, 9000, 4097, 2500, 300]),  # staged and register-half rows longer than K, and n <= K
 ])
 def test_topk_varlen_exact(Tq, N, K, lens):
     dsa = _dsa()
