@@ -165,4 +165,31 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
 }
 
+// Largest value and sum of a float over the 64 lanes of a wave (wave-uniform
+// results), with the same lane moves.  The sum adds in the scan's order, so
+// it rounds as that order does.
+__device__ __forceinline__ float wave_fmax(float x) {
+  const int id = __float_as_int(-INFINITY);
+#define DSA_FMAX_STEP(ctrl, rows) x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(x), ctrl, rows, 0xf, false)))
+  DSA_FMAX_STEP(0x111, 0xf);
+  DSA_FMAX_STEP(0x112, 0xf);
+  DSA_FMAX_STEP(0x114, 0xf);
+  DSA_FMAX_STEP(0x118, 0xf);
+  DSA_FMAX_STEP(0x142, 0xa);
+  DSA_FMAX_STEP(0x143, 0xc);
+#undef DSA_FMAX_STEP
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ float wave_fsum(float x) {
+#define DSA_FSUM_STEP(ctrl, rows) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rows, 0xf, false))
+  DSA_FSUM_STEP(0x111, 0xf);
+  DSA_FSUM_STEP(0x112, 0xf);
+  DSA_FSUM_STEP(0x114, 0xf);
+  DSA_FSUM_STEP(0x118, 0xf);
+  DSA_FSUM_STEP(0x142, 0xa);
+  DSA_FSUM_STEP(0x143, 0xc);
+#undef DSA_FSUM_STEP
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 }  // namespace dsa

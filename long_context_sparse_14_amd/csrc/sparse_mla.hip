@@ -588,7 +588,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 // partial row is one 1 KiB load, and the splits' loads are independent.
 constexpr int COMBINE_WAVES = 4;
 constexpr int COMBINE_CHUNK = 8;  // partial rows in flight per lane
-__global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
+__global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const uint16_t* part_o,  // not restrict: see below
                                                                         const float* __restrict__ part_lse,
                                                                         uint16_t* __restrict__ out,
                                                                         float* __restrict__ lse, int64_t R,
@@ -597,28 +597,32 @@ __global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const u
   const int64_t rh = (int64_t)blockIdx.x * COMBINE_WAVES + (threadIdx.x >> 6);
   const int64_t stride = R * MH;
   if (rh >= stride) return;  // whole waves only
-  // lane s < splits holds split s's log2-sum-exp (splits <= 64, checked at launch)
-  const float ls = lane < splits ? part_lse[lane * stride + rh] : -INFINITY;
-  float M = ls;
+  // Lane s < splits holds split s's log2-sum-exp (2 <= splits <= 64, checked at
+  // launch).  Its load goes out first and the first chunk's partial rows right
+  // behind it, so the weights' reductions wait for the log-sums alone and run
+  // while the rows arrive: one memory round trip rather than two in a row.
+  const float ls_raw = part_lse[min(lane, splits - 1) * stride + rh];
+  const uint16_t* base = part_o + rh * MDV + 8 * lane;
+  uint4 v[COMBINE_CHUNK];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  for (int c = 0; c < COMBINE_CHUNK; ++c)  // past the last split: reread it with weight 0
+    v[c] = *reinterpret_cast<const uint4*>(base + min(c, splits - 1) * stride * MDV);
+  asm volatile("" ::: "memory");  // keeps the loads here, ahead of the reductions (part_o may alias it)
+  const float ls = lane < splits ? ls_raw : -INFINITY;
+  const float M = wave_fmax(ls);
   const float e = M == -INFINITY ? 0.f : exp2f(ls - M);  // exp2(-inf) = 0 for empty splits
-  float den = e;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+  const float den = wave_fsum(e);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const uint16_t* base = part_o + rh * MDV + 8 * lane;
   for (int s0 = 0; s0 < splits; s0 += COMBINE_CHUNK) {
-    uint4 v[COMBINE_CHUNK];
+    if (s0 > 0)
 #pragma unroll
-    for (int c = 0; c < COMBINE_CHUNK; ++c) {  // past the last split: reread it with weight 0
-      const int s = min(s0 + c, splits - 1);
-      v[c] = *reinterpret_cast<const uint4*>(base + s * stride * MDV);
-    }
+      for (int c = 0; c < COMBINE_CHUNK; ++c)
+        v[c] = *reinterpret_cast<const uint4*>(base + min(s0 + c, splits - 1) * stride * MDV);
 #pragma unroll
     for (int c = 0; c < COMBINE_CHUNK; ++c) {
-      const float w = s0 + c < splits ? __shfl(e, s0 + c) * inv : 0.f;
+      // lane s0 + c <= 63 (splits <= 64, chunks of 8); lanes at or past splits hold e = 0
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), s0 + c)) * inv;
       const uint32_t wd[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
