@@ -653,10 +653,12 @@ def main():
         del d["k_idx"]
         calls["quant_q"] = (lib.dsa_indexer_quantize_fp8, (ptr(d["q_idx"]), ptr(q8), ptr(qs), B * Tq * wl.H_I,
                                                            wl.D_I, code, sp))
-        calls["index"] = (lib.dsa_index_scores_fp8, (ptr(q8), ptr(qs), ptr(k8), ptr(ks), ptr(d["w"]), ptr(scores),
-                                                     B, Tq, N, wl.q_pos0, wl.H_I, wl.D_I, code, sp))
-        calls["topk"] = (lib.dsa_topk, (ptr(scores), ptr(idx), B, Tq, N, wl.q_pos0, wl.K, ptr(topk_ws),
-                                        topk_ws.numel(), sp))
+        # the staged pair that the fused FP8 call runs (its indexer also pre-selects at decode shapes)
+        calls["index"] = (lib.dsa_index_scores_fp8_presel, (ptr(q8), ptr(qs), ptr(k8), ptr(ks), ptr(d["w"]),
+                                                            ptr(scores), B, Tq, N, wl.q_pos0, wl.H_I, wl.D_I, wl.K,
+                                                            code, ptr(topk_ws), topk_ws.numel(), sp))
+        calls["topk"] = (lib.dsa_topk_presel_fp8, (ptr(scores), ptr(idx), B, Tq, N, wl.q_pos0, wl.K, ptr(topk_ws),
+                                                   topk_ws.numel(), sp))
         if has_mla:
             calls["fused"] = (lib.dsa_forward_fp8, (ptr(q8), ptr(qs), ptr(k8), ptr(ks), ptr(d["w"]), ptr(d["q"]),
                                                     ptr(d["kv"]), ptr(out), ptr(lse), None, B, Tq, N, wl.q_pos0,

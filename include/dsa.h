@@ -369,8 +369,21 @@ dsa_status dsa_linear(const void* x, const void* w, void* y, int64_t M, int32_t 
  *   compiled for H_I = 64, D_I = 128.  The key cache is streamed once per
  *   query (the decode shape); prefill works but re-reads the cache per query.
  *
+ * dsa_index_scores_fp8_presel / dsa_topk_presel_fp8: steps 1 and 2 as
+ *   dsa_forward_fp8 runs them.  The first is dsa_index_scores_fp8 (same
+ *   scores) and, at the decode shapes where dsa_index_scores_presel lists
+ *   (more than 16384 keys per row, at most 4 queries per sequence, K <= 4096)
+ *   and the FP8 kernel's segments leave room for the lists, the same
+ *   pre-selection over those segments, kept in `workspace`
+ *   (dsa_topk_workspace_size(B, Tq, N, K) bytes).  The second returns
+ *   dsa_topk's indices for those scores, from the lists where they apply
+ *   (with the same exact fallback as dsa_topk_presel), else by dsa_topk
+ *   itself.  Pass both calls the same B, Tq, N, q_pos0, K and workspace.
+ *   Arguments, layouts and errors as for dsa_index_scores_fp8 and dsa_topk.
+ *
  * dsa_forward_fp8: dsa_forward with the FP8 indexer in place of the bf16 one
- *   (same outputs, workspace size from dsa_forward_workspace_size).
+ *   (same outputs, workspace size from dsa_forward_workspace_size); steps 1
+ *   and 2 run as dsa_index_scores_fp8_presel and dsa_topk_presel_fp8.
  *
  * All pointers: device memory, 16-byte aligned, owned by the caller.  Errors
  * as for dsa_index_scores / dsa_forward; fp32 head weights or other shapes
@@ -381,6 +394,12 @@ dsa_status dsa_indexer_quantize_fp8(const void* x, uint8_t* codes, float* scales
 dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
                                 const void* w, float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
                                 int32_t H_I, int32_t D_I, int32_t dtype, void* stream);
+dsa_status dsa_index_scores_fp8_presel(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                                       const float* k_scale, const void* w, float* scores, int64_t B, int64_t Tq,
+                                       int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t K,
+                                       int32_t dtype, void* workspace, size_t ws_bytes, void* stream);
+dsa_status dsa_topk_presel_fp8(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N,
+                               int64_t q_pos0, int32_t K, void* workspace, size_t ws_bytes, void* stream);
 dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
                            const void* w, const void* q, const void* kv, void* out, float* lse, int32_t* idx_out,
                            int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t H,

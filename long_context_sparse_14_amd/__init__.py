@@ -98,6 +98,9 @@ _SIGNATURES = {
     "dsa_calib_stream": (ctypes.c_int, [_p, _p, _sz, _p]),
     "dsa_indexer_quantize_fp8": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _p]),
     "dsa_index_scores_fp8": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
+    "dsa_index_scores_fp8_presel": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
+                                                   _i32, _p, _sz, _p]),
+    "dsa_topk_presel_fp8": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]),
     "dsa_forward_fp8": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "dsa_paged_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32]),
@@ -571,6 +574,37 @@ def index_scores_fp8(q8, q_scale, k8, k_scale, w, q_pos0: int = 0, scores=None, 
         raise ValueError("scores must be [B,Tq,N]")
     _check(library().dsa_index_scores_fp8(*ptrs, ps, B, Tq, N, q_pos0, H_I, D_I, DSA_BF16, _stream(stream)))
     return scores
+
+
+def index_scores_fp8_presel(q8, q_scale, k8, k_scale, w, K: int, q_pos0: int = 0, scores=None, workspace=None,
+                            stream=None):
+    """index_scores_fp8 plus the pre-selection lists over the FP8 kernel's segments, kept in a top-k
+    workspace.  Returns (scores, workspace): pass both to topk_presel_fp8."""
+    ptrs, (B, Tq, N, H_I, D_I) = _fp8_indexer_args(q8, q_scale, k8, k_scale, w)
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q8.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if tuple(scores.shape) != (B, Tq, N):
+        raise ValueError("scores must be [B,Tq,N]")
+    lib = library()
+    ws, nbytes = _workspace(lib.dsa_topk_workspace_size(B, Tq, N, K), q8.device, workspace)
+    _check(lib.dsa_index_scores_fp8_presel(*ptrs, ps, B, Tq, N, q_pos0, H_I, D_I, K, DSA_BF16,
+                                           ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    return scores, ws
+
+
+def topk_presel_fp8(scores, K: int, workspace, q_pos0: int = 0, idx=None, stream=None) -> torch.Tensor:
+    """topk for scores and the workspace index_scores_fp8_presel filled."""
+    B, Tq, N = scores.shape
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if idx is None:
+        idx = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+    pi = _dev(idx, "idx", 3, torch.int32)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(library().dsa_topk_presel_fp8(ps, pi, B, Tq, N, q_pos0, K,
+                                         workspace.data_ptr() if workspace is not None else None, nbytes,
+                                         _stream(stream)))
+    return idx
 
 
 def forward_fp8(q8, q_scale, k8, k_scale, w, q, kv, K: int, scale: float, q_pos0: int = 0, DV: int = 512,

@@ -207,12 +207,14 @@ dsa_status check_proj_common(const void* a, const void* b, const void* c, int64_
   return DSA_OK;
 }
 
-// Whether the bf16 decode indexer leaves a pre-selection of each row for the
-// top-k (see PreselWs): decode rows too long for the one-workgroup top-k.
-bool presel_applies(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int32_t K, int32_t dtype, dsa::PreselWs* ps) {
+// Whether the bf16 decode indexer (or with fp8 the FP8 one) leaves a
+// pre-selection of each row for the top-k (see PreselWs): decode rows too long
+// for the one-workgroup top-k.
+bool presel_applies(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int32_t K, int32_t dtype, dsa::PreselWs* ps,
+                    bool fp8 = false) {
   if (dtype != DSA_BF16 || dsa::presel_workspace_bytes(B, Tq, N, K) == 0) return false;
   dsa::PreselWs g;
-  if (!dsa::presel_geometry(B, Tq, N, nmax, K, g)) return false;
+  if (!dsa::presel_geometry(B, Tq, N, nmax, K, g, fp8)) return false;
   if (ps) *ps = g;
   return true;
 }
@@ -660,6 +662,57 @@ dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const u
                     "FP8 index scores launch");
 }
 
+namespace {
+
+// Steps 1 and 2 with the FP8 indexer, as the fused FP8 forward runs them: the
+// indexer also lists each segment's best keys where the FP8 geometry admits a
+// pre-selection, and the top-k then selects among the lists; else the plain
+// indexer and top-k.  topk_ws: dsa::topk_workspace_bytes(B, Tq, N, K) bytes.
+hipError_t index_fp8_presel(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks, const void* w,
+                            float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t K,
+                            void* topk_ws, hipStream_t s) {
+  const auto wi = static_cast<const uint16_t*>(w);
+  const int64_t nmax = std::min(N, q_pos0 + Tq);
+  if (presel_applies(B, Tq, N, nmax, K, DSA_BF16, nullptr, true)) {
+    const dsa::PreselWs ps = dsa::presel_ws(topk_ws, B, Tq, N, nmax, K, true);
+    return dsa::launch_index_scores_fp8(q8, qs, k8, ks, wi, scores, B, Tq, N, q_pos0, s, nullptr, nullptr, &ps);
+  }
+  return dsa::launch_index_scores_fp8(q8, qs, k8, ks, wi, scores, B, Tq, N, q_pos0, s);
+}
+hipError_t topk_fp8_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                           int32_t K, void* topk_ws, hipStream_t s) {
+  const int64_t nmax = std::min(N, q_pos0 + Tq);
+  if (presel_applies(B, Tq, N, nmax, K, DSA_BF16, nullptr, true))
+    return dsa::launch_topk_presel(scores, idx, B, Tq, N, q_pos0, K, dsa::presel_ws(topk_ws, B, Tq, N, nmax, K, true),
+                                   s);
+  return dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
+}
+
+}  // namespace
+
+dsa_status dsa_index_scores_fp8_presel(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                                       const float* k_scale, const void* w, float* scores, int64_t B, int64_t Tq,
+                                       int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t K, int32_t dtype,
+                                       void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_index_scores_fp8(q8, q_scale, k8, k_scale, w, scores, B, Tq, N, q_pos0, H_I, D_I, dtype, true);
+  if (st != DSA_OK) return st;
+  if (K < 1 || K > kMaxK) return fail(DSA_ERR_INVALID_ARG, "K must be in [1, 65536] (got %d)", K);
+  const size_t need = dsa::topk_workspace_bytes(B, Tq, N, K);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "top-k workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  return hip_status(index_fp8_presel(q8, q_scale, k8, k_scale, w, scores, B, Tq, N, q_pos0, K, workspace,
+                                     static_cast<hipStream_t>(stream)),
+                    "FP8 index scores launch");
+}
+
+dsa_status dsa_topk_presel_fp8(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
+                               int32_t K, void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  return hip_status(topk_fp8_presel(scores, idx, B, Tq, N, q_pos0, K, workspace, static_cast<hipStream_t>(stream)),
+                    "top-k launch");
+}
+
 dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
                            const void* w, const void* q, const void* kv, void* out, float* lse, int32_t* idx_out,
                            int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t H_I, int32_t D_I, int32_t H,
@@ -680,10 +733,9 @@ dsa_status dsa_forward_fp8(const uint8_t* q8, const float* q_scale, const uint8_
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
   void* topk_ws = ws + L.total - align256(dsa::topk_workspace_bytes(B, Tq, N, K));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dsa::launch_index_scores_fp8(q8, q_scale, k8, k_scale, static_cast<const uint16_t*>(w), scores, B,
-                                              Tq, N, q_pos0, s);
+  hipError_t e = index_fp8_presel(q8, q_scale, k8, k_scale, w, scores, B, Tq, N, q_pos0, K, topk_ws, s);
   if (e != hipSuccess) return hip_status(e, "FP8 index scores launch");
-  e = dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
+  e = topk_fp8_presel(scores, idx, B, Tq, N, q_pos0, K, topk_ws, s);
   if (e != hipSuccess) return hip_status(e, "top-k launch");
   e = dsa::launch_sparse_mla_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
                                   static_cast<uint16_t*>(out), lse, B, Tq, N, K, scale, ws + L.mla, s);

@@ -663,11 +663,12 @@ __device__ __forceinline__ void load_query_fp8(QFrags& f, const uint8_t* __restr
 // (L & 7) ^ (L >> 3) of key L >> 3 and lands at slot L, so chunk c of tile key
 // r sits at slot 8r + (c ^ (r & 7)).  The key scales are applied when the
 // workgroup's scores leave LDS.
-template <int WAVES, int NBUF, int SCAP, bool PAGED = false>
+template <int WAVES, int NBUF, int SCAP, bool PAGED = false, bool PRESEL = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const uint16_t* __restrict__ w, float* __restrict__ scores, int64_t Tq, int64_t N,
-    int64_t q_pos0, Vis vis, int64_t keys_per_wg, Paged pg) {
+    int64_t q_pos0, Vis vis, int64_t keys_per_wg, Paged pg, PreselWs ps) {
+  static_assert(!(PAGED && PRESEL), "the pre-selecting FP8 kernel reads a contiguous cache");
   constexpr int TILE_BYTES = 32 * ID;
   static_assert(NBUF >= 2 && NBUF <= 8, "the vmcnt waits below cover up to seven tiles in flight");
   static_assert(WAVES * NBUF * TILE_BYTES + SCAP * 4 <= 160 * 1024, "LDS budget");
@@ -714,6 +715,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
   };
   QFrags f;
   load_query_fp8(f, q8, qs, w, row, half, col);
+  // With the pre-selection the key scales are applied to the scores in LDS
+  // before the lists are drawn: each thread's scales (keys k_begin + t +
+  // 64*WAVES*j) are loaded here, with the queries, so that the epilogue does
+  // not wait for them.
+  constexpr int KSPT = PRESEL ? SCAP / (WAVES * 64) : 1;
+  float ksv[KSPT];
+  if constexpr (PRESEL) {
+    const int nk = (int)(k_end - k_begin);
+    const float* ksr = ks + b * N + k_begin;
+#pragma unroll
+    for (int j = 0; j < KSPT; ++j) ksv[j] = ksr[min((int)threadIdx.x + WAVES * 64 * j, nk - 1)];
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
@@ -762,6 +775,28 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
     return;
   }
   const float* ksr = ks + b * N + k_begin;
+  if constexpr (PRESEL) {
+    // the key scales applied in LDS, so that the lists hold the final scores
+    // (the same products the store pass below would form)
+#pragma unroll
+    for (int j = 0; j < KSPT; ++j) {
+      const int i = (int)threadIdx.x + WAVES * 64 * j;
+      if (i < n) sl[i] *= ksv[j];
+    }
+    lds_barrier();
+    // the key rings are idle: every wave awaited its last tile before the first barrier
+    presel_segment<WAVES, SCAP>(sl, n, k_begin, row, (int)blockIdx.x, ps, reinterpret_cast<uint32_t*>(&kt[0][0][0]));
+    if (((row * N) & 3) == 0) {
+      for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * WAVES * 64) {
+        if (i + 4 <= n) __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sl[i]), reinterpret_cast<f32x4*>(dst + i));
+        else
+          for (int e = i; e < n; ++e) dst[e] = sl[e];
+      }
+    } else {
+      for (int i = (int)threadIdx.x; i < n; i += WAVES * 64) dst[i] = sl[i];
+    }
+    return;
+  }
   if (((row * N) & 3) == 0 && ((b * N) & 3) == 0) {
     for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * WAVES * 64) {
       if (i + 4 <= n) {
@@ -801,15 +836,43 @@ DecodeGeom decode_geometry(int64_t rows, int64_t nmax) {
   return {kpw, (nmax + kpw - 1) / kpw};
 }
 
+// Launch shape of the FP8 decode kernel.  Two workgroups resident per compute
+// unit (72 KiB of LDS each), three 4 KiB tiles in flight per wave.  One round
+// of 512 workgroups when the rows fit in at most FP8_SCAP keys per workgroup
+// (at one and four queries of 128K keys, 31% and 32% faster than four
+// rounds), else about eight workgroups per compute unit over the launch, in
+// whole rounds: the best of a sweep over waves (2, 4, 8), ring depth (2..8)
+// and keys per workgroup (1024..8192) at the 128K decode batch.
+//
+// The pre-selecting instance runs one list epilogue per workgroup, so it takes
+// fewer, longer segments: up to FP8P_SCAP = 8192 keys with a ring of three
+// tiles (two tiles in flight per wave; 80 KiB of LDS, two per compute unit),
+// 512 workgroups at the 128K decode batch.  There, against 2048-key segments
+// and four rounds, the fused FP8 forward took 146 rather than 155 us (4096-key
+// segments: 150 us; 8192 keys with a four-tile ring, one workgroup per unit:
+// 160 us).
+constexpr int FP8_WAVES = 4, FP8_NBUF = 4, FP8_SCAP = 2048;
+constexpr int FP8P_NBUF = 3, FP8P_SCAP = 8192;
+DecodeGeom fp8_decode_geometry(int64_t rows, int64_t nmax, bool presel = false) {
+  const int64_t scap = presel ? FP8P_SCAP : FP8_SCAP;
+  int64_t per_row = 512 / rows > 1 ? 512 / rows : 1;
+  if (!presel && (nmax + per_row - 1) / per_row > scap) per_row = 2048 / rows > 1 ? 2048 / rows : 1;
+  int64_t kpw = (nmax + per_row - 1) / per_row;
+  kpw = (kpw + 32 * FP8_WAVES - 1) / (32 * FP8_WAVES) * (32 * FP8_WAVES);
+  if (kpw > scap) kpw = scap;
+  if (kpw < 32 * FP8_WAVES) kpw = 32 * FP8_WAVES;
+  return {kpw, (nmax + kpw - 1) / kpw};
+}
+
 }  // namespace
 
 // Pre-selection applies to decode rows too long for the one-workgroup top-k
 // (more than 16384 keys, K <= 4096) whose segments can each list several times
 // their expected share K * kpw / nmax of the row's K best keys within the
 // row's list budget.
-bool presel_geometry(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K, PreselWs& ps) {
+bool presel_geometry(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K, PreselWs& ps, bool fp8) {
   if (Tq > 4 || nmax <= 16384 || N > 0x7fffffff || K > 4096 || nmax < K) return false;
-  const DecodeGeom g = decode_geometry(B * Tq, nmax);
+  const DecodeGeom g = fp8 ? fp8_decode_geometry(B * Tq, nmax, true) : decode_geometry(B * Tq, nmax);
   if (g.G > 512) return false;
   const int64_t cap = min((int64_t)kPreselMaxCap, (int64_t)kPreselRowCap / g.G);
   const double share = (double)K * (double)g.kpw / (double)nmax;
@@ -826,15 +889,15 @@ static size_t presel_align(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t presel_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K) {
   PreselWs ps;
-  if (!presel_geometry(B, Tq, N, N, K, ps)) return 0;
+  if (!presel_geometry(B, Tq, N, N, K, ps) && !presel_geometry(B, Tq, N, N, K, ps, true)) return 0;
   // any longest row <= N: G <= 512 segments and G * cap <= kPreselRowCap entries per row
   const size_t R = (size_t)(B * Tq);
   return 2 * presel_align(R * 512 * sizeof(uint32_t)) + presel_align(R * kPreselRowCap * sizeof(uint2));
 }
 
-PreselWs presel_ws(void* workspace, int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K) {
+PreselWs presel_ws(void* workspace, int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K, bool fp8) {
   PreselWs ps{};
-  presel_geometry(B, Tq, N, nmax, K, ps);
+  presel_geometry(B, Tq, N, nmax, K, ps, fp8);
   const size_t R = (size_t)(B * Tq);
   char* p = static_cast<char*>(workspace);
   ps.count = reinterpret_cast<uint32_t*>(p);
@@ -905,32 +968,26 @@ hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* codes, float* scales,
 
 hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
                                    const uint16_t* w, float* scores, int64_t B, int64_t Tq, int64_t N,
-                                   int64_t q_pos0, hipStream_t stream, const int64_t* seq_lens, const Paged* pg) {
+                                   int64_t q_pos0, hipStream_t stream, const int64_t* seq_lens, const Paged* pg,
+                                   const PreselWs* ps) {
   const Vis vis{seq_lens, 1};
   const int64_t nmax = seq_lens != nullptr ? N : min(N, q_pos0 + Tq);
   if (nmax <= 0) return hipSuccess;  // no query sees a key
-  // Two workgroups resident per compute unit (72 KiB of LDS each), three
-  // 4 KiB tiles in flight per wave.  One round of 512 workgroups when the rows
-  // fit in at most SCAP keys per workgroup (at one and four queries of 128K
-  // keys, 31% and 32% faster than four rounds), else about eight workgroups
-  // per compute unit over the launch, in whole rounds: the best of a sweep
-  // over waves (2, 4, 8), ring depth (2..8) and keys per workgroup
-  // (1024..8192) at the 128K decode batch.
-  constexpr int WAVES = 4, NBUF = 4, SCAP = 2048;
-  const int64_t rows = B * Tq;
-  int64_t per_row = 512 / rows > 1 ? 512 / rows : 1;
-  if ((nmax + per_row - 1) / per_row > SCAP) per_row = 2048 / rows > 1 ? 2048 / rows : 1;
-  int64_t kpw = (nmax + per_row - 1) / per_row;
-  kpw = (kpw + 32 * WAVES - 1) / (32 * WAVES) * (32 * WAVES);
-  if (kpw > SCAP) kpw = SCAP;
-  if (kpw < 32 * WAVES) kpw = 32 * WAVES;
-  dim3 grid((unsigned)((nmax + kpw - 1) / kpw), (unsigned)Tq, (unsigned)B);
+  constexpr int WAVES = FP8_WAVES, NBUF = FP8_NBUF, SCAP = FP8_SCAP;
+  const DecodeGeom geo = fp8_decode_geometry(B * Tq, nmax, ps != nullptr);
+  const int64_t kpw = geo.kpw;
+  if (ps != nullptr && (pg != nullptr || ps->kpw != kpw || ps->G != geo.G)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)geo.G, (unsigned)Tq, (unsigned)B);
+  const PreselWs none{};
   if (pg != nullptr)
     hipLaunchKernelGGL((indexer_dma_fp8<WAVES, NBUF, SCAP, true>), grid, dim3(WAVES * 64), 0, stream, q8, qs, k8, ks, w,
-                       scores, Tq, N, q_pos0, vis, kpw, *pg);
+                       scores, Tq, N, q_pos0, vis, kpw, *pg, none);
+  else if (ps != nullptr)
+    hipLaunchKernelGGL((indexer_dma_fp8<WAVES, FP8P_NBUF, FP8P_SCAP, false, true>), grid, dim3(WAVES * 64), 0, stream,
+                       q8, qs, k8, ks, w, scores, Tq, N, q_pos0, vis, kpw, Paged{}, *ps);
   else
     hipLaunchKernelGGL((indexer_dma_fp8<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q8, qs, k8, ks, w,
-                       scores, Tq, N, q_pos0, vis, kpw, Paged{});
+                       scores, Tq, N, q_pos0, vis, kpw, Paged{}, none);
   return hipGetLastError();
 }
 

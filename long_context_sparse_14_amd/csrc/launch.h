@@ -38,12 +38,15 @@ struct PreselWs {
   int32_t cap;      // entries per list
   int32_t tgt;      // entries a list aims to hold (a few times the segment's expected share)
 };
-// The pre-selection geometry of a decode problem, or false when it does not
-// apply (then the indexer runs plain and the top-k takes its usual methods).
-bool presel_geometry(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K, PreselWs& ps);
+// The pre-selection geometry of a decode problem for the bf16 indexer, or
+// with fp8 for the FP8 indexer (whose segments are the FP8 kernel's
+// workgroups), or false when it does not apply (then the indexer runs plain
+// and the top-k takes its usual methods).
+bool presel_geometry(int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K, PreselWs& ps, bool fp8 = false);
+// Workspace of the lists: nonzero when either indexer's geometry applies.
 size_t presel_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
 // Places the lists in `workspace` (presel_workspace_bytes large).
-PreselWs presel_ws(void* workspace, int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K);
+PreselWs presel_ws(void* workspace, int64_t B, int64_t Tq, int64_t N, int64_t nmax, int K, bool fp8 = false);
 
 // seq_lens (device, [B], may be null): per-sequence lengths in tokens; when
 // given, the queries of sequence b sit at positions seq_lens[b] - Tq + t and
@@ -64,12 +67,13 @@ hipError_t launch_index_scores_f32(const float* q_idx, const float* k_idx, const
 
 // FP8 indexer: rows of 128 bf16 -> Hadamard-rotated OCP E4M3 codes and one
 // power-of-two scale per row; scores from codes and scales (decode kernel,
-// any Tq, causal with q_pos0).
+// any Tq, causal with q_pos0).  ps (may be null, non-paged only): also write the
+// pre-selection lists, as for the bf16 indexer (presel_ws with fp8).
 hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* codes, float* scales, int64_t R, hipStream_t stream);
 hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
                                    const uint16_t* w, float* scores, int64_t B, int64_t Tq, int64_t N,
                                    int64_t q_pos0, hipStream_t stream, const int64_t* seq_lens = nullptr,
-                                   const Paged* pg = nullptr);
+                                   const Paged* pg = nullptr, const PreselWs* ps = nullptr);
 
 size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
 // The top-k from the indexer's pre-selection lists (scores: the full rows,

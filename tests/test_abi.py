@@ -243,6 +243,20 @@ def test_fp8_validation():
     bad = list(args)
     bad[5] = None  # q
     assert L.dsa_forward_fp8(*bad, P, need, None) == dsa.DSA_ERR_INVALID_ARG
+    # the staged pre-selection pair: the top-k workspace, K in range, the scores of dsa_index_scores_fp8
+    tw = L.dsa_topk_workspace_size(B, Tq, N, K)
+    assert tw > 0
+    pargs = [P, P, P, P, P, P, B, Tq, N, N - 1, 64, 128]
+    assert L.dsa_index_scores_fp8_presel(*pargs, K, BF16, P, tw - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_index_scores_fp8_presel(*pargs, K, BF16, None, tw, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_index_scores_fp8_presel(*pargs, 0, BF16, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_scores_fp8_presel(*pargs, K, F32, P, tw, None) == dsa.DSA_ERR_UNSUPPORTED
+    nos = list(pargs)
+    nos[5] = None  # scores
+    assert L.dsa_index_scores_fp8_presel(*nos, K, BF16, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_presel_fp8(P, P, B, Tq, N, N - 1, K, P, tw - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_topk_presel_fp8(P, None, B, Tq, N, N - 1, K, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_presel_fp8(P, P, B, Tq, N, N - 1, 70000, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
 
 
 def test_paged_validation():

@@ -165,3 +165,51 @@ def test_index_scores_fp8_full_decode_sampled():
         tol = _score_bound(q8b, qsb, k8b, ksb, w[b], 0, N)
         err = np.abs(got[b, 0].cpu().numpy().astype(np.float64) - ref)
         assert np.all(err <= tol), f"b={b}: worst excess {np.max(err - tol):.3e}"
+
+
+@pytest.mark.parametrize("B,Tq,N,plant", [
+    (8, 4, 40000, None),      # 32 rows of ~40000 keys: 16 segments of 2560 keys (the last one ragged), lists of 512
+    (8, 4, 40000, "ties"),    # 3000 tied top keys: their segments cannot list them, the rows fall back
+    (32, 1, 131072, None),    # the 128K decode batch: 16 segments of 8192 keys, lists of 512
+])
+def test_forward_fp8_presel(B, Tq, N, plant):
+    """At these decode shapes the FP8 indexer also lists each segment's best keys and the top-k selects
+    among the lists.  The fused forward must equal the staged plain FP8 indexer + top-k + sparse MLA on
+    the GPU bit for bit, and sampled rows must select what the oracle's scores fix."""
+    dsa = _dsa()
+    K, q_pos0 = 2048, N - Tq
+    print(f"fp8 presel case: B={B} Tq={Tq} N={N} plant={plant}", flush=True)
+    q = gen((B, Tq, 64, 128), 12, synth.INT4, seed=2)
+    w = gen((B, Tq, 64), 13, synth.POW2_M4_0, seed=2)
+    k = gen((B, N, 128), 14, synth.INT4, seed=2)
+    if plant == "ties":
+        w[:, :, 0] = 0x3F80                                   # bf16 1.0 on head 0
+        k[:, 1000:4000] = q[:, 0, 0][:, None, :]              # keys equal to query 0's head 0: a tied top block
+    q8, qs = dsa.indexer_quantize_fp8(dev(q))
+    k8, ks = dsa.indexer_quantize_fp8(torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda())
+    wd = dev(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(B * N + Tq)
+    qm = (torch.randn((B, Tq, 128, 576), device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    kv = (torch.randn((B, N, 576), device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    scale = 192 ** -0.5
+    out, lse, idx = dsa.forward_fp8(q8, qs, k8, ks, wd, qm, kv, K, scale, q_pos0, return_idx=True)
+    # entries past a row's visible keys are never written: start both score buffers equal
+    fill = lambda: torch.full((B, Tq, N), -3.5, dtype=torch.float32, device="cuda")
+    scores = dsa.index_scores_fp8(q8, qs, k8, ks, wd, q_pos0, scores=fill())
+    plain_idx = dsa.topk(scores, K, q_pos0)
+    plain_out, plain_lse = dsa.sparse_mla(qm, kv, plain_idx, scale)
+    pre_scores, ws = dsa.index_scores_fp8_presel(q8, qs, k8, ks, wd, K, q_pos0, scores=fill())
+    pre_idx = dsa.topk_presel_fp8(pre_scores, K, ws, q_pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(pre_scores, scores), "the pre-selecting FP8 indexer must write the same scores"
+    assert torch.equal(pre_idx, plain_idx), "the staged pre-selection pair differs from the plain top-k"
+    assert torch.equal(idx, plain_idx), "pre-selected FP8 top-k differs from the plain top-k"
+    assert torch.equal(out, plain_out) and torch.equal(lse, plain_lse), "attention differs from the staged path"
+    for b in sorted({0, B - 1}):
+        k8b, ksb, q8b, qsb = u8(k8[b]), ks[b].cpu().numpy(), u8(q8[b]), qs[b].cpu().numpy()
+        ts = list(range(Tq))
+        ref = oracle.index_scores_fp8_rows(q8b, qsb, k8b, ksb, w[b], ts, q_pos0)
+        for t in ts:
+            tol = _score_bound(q8b, qsb, k8b, ksb, w[b], t, len(ref[t]))
+            _check_selection(idx[b, t].cpu().numpy(), ref[t], tol, K)
