@@ -170,7 +170,8 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 // it rounds as that order does.
 __device__ __forceinline__ float wave_fmax(float x) {
   const int id = __float_as_int(-INFINITY);
-#define DSA_FMAX_STEP(ctrl, rows) x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(x), ctrl, rows, 0xf, false)))
+#define DSA_FMAX_STEP(ctrl, rows) \
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(x), ctrl, rows, 0xf, false)))
   DSA_FMAX_STEP(0x111, 0xf);
   DSA_FMAX_STEP(0x112, 0xf);
   DSA_FMAX_STEP(0x114, 0xf);
@@ -181,7 +182,8 @@ __device__ __forceinline__ float wave_fmax(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 __device__ __forceinline__ float wave_fsum(float x) {
-#define DSA_FSUM_STEP(ctrl, rows) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rows, 0xf, false))
+#define DSA_FSUM_STEP(ctrl, rows) \
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rows, 0xf, false))
   DSA_FSUM_STEP(0x111, 0xf);
   DSA_FSUM_STEP(0x112, 0xf);
   DSA_FSUM_STEP(0x114, 0xf);

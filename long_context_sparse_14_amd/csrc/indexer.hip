@@ -788,7 +788,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
     presel_segment<WAVES, SCAP>(sl, n, k_begin, row, (int)blockIdx.x, ps, reinterpret_cast<uint32_t*>(&kt[0][0][0]));
     if (((row * N) & 3) == 0) {
       for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * WAVES * 64) {
-        if (i + 4 <= n) __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sl[i]), reinterpret_cast<f32x4*>(dst + i));
+        if (i + 4 <= n)
+          __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sl[i]), reinterpret_cast<f32x4*>(dst + i));
         else
           for (int e = i; e < n; ++e) dst[e] = sl[e];
       }
@@ -849,18 +850,18 @@ DecodeGeom decode_geometry(int64_t rows, int64_t nmax) {
 // tiles (two tiles in flight per wave; 80 KiB of LDS, two per compute unit),
 // 512 workgroups at the 128K decode batch.  There, against 2048-key segments
 // and four rounds, the fused FP8 forward took 146 rather than 155 us (4096-key
-// segments: 150 us; 8192 keys with a four-tile ring, one workgroup per unit:
-// 160 us).
+// segments: 150 us; one workgroup per unit with a ring of 4, 6 or 8 tiles, or
+// of 8 waves with 4 tiles each: 152-167 us).
 constexpr int FP8_WAVES = 4, FP8_NBUF = 4, FP8_SCAP = 2048;
-constexpr int FP8P_NBUF = 3, FP8P_SCAP = 8192;
+constexpr int FP8P_WAVES = 4, FP8P_NBUF = 3, FP8P_SCAP = 8192;
 DecodeGeom fp8_decode_geometry(int64_t rows, int64_t nmax, bool presel = false) {
-  const int64_t scap = presel ? FP8P_SCAP : FP8_SCAP;
+  const int64_t scap = presel ? FP8P_SCAP : FP8_SCAP, tile_keys = 32 * (presel ? FP8P_WAVES : FP8_WAVES);
   int64_t per_row = 512 / rows > 1 ? 512 / rows : 1;
   if (!presel && (nmax + per_row - 1) / per_row > scap) per_row = 2048 / rows > 1 ? 2048 / rows : 1;
   int64_t kpw = (nmax + per_row - 1) / per_row;
-  kpw = (kpw + 32 * FP8_WAVES - 1) / (32 * FP8_WAVES) * (32 * FP8_WAVES);
+  kpw = (kpw + tile_keys - 1) / tile_keys * tile_keys;  // whole tiles for every wave
   if (kpw > scap) kpw = scap;
-  if (kpw < 32 * FP8_WAVES) kpw = 32 * FP8_WAVES;
+  if (kpw < tile_keys) kpw = tile_keys;
   return {kpw, (nmax + kpw - 1) / kpw};
 }
 
@@ -983,8 +984,8 @@ hipError_t launch_index_scores_fp8(const uint8_t* q8, const float* qs, const uin
     hipLaunchKernelGGL((indexer_dma_fp8<WAVES, NBUF, SCAP, true>), grid, dim3(WAVES * 64), 0, stream, q8, qs, k8, ks, w,
                        scores, Tq, N, q_pos0, vis, kpw, *pg, none);
   else if (ps != nullptr)
-    hipLaunchKernelGGL((indexer_dma_fp8<WAVES, FP8P_NBUF, FP8P_SCAP, false, true>), grid, dim3(WAVES * 64), 0, stream,
-                       q8, qs, k8, ks, w, scores, Tq, N, q_pos0, vis, kpw, Paged{}, *ps);
+    hipLaunchKernelGGL((indexer_dma_fp8<FP8P_WAVES, FP8P_NBUF, FP8P_SCAP, false, true>), grid, dim3(FP8P_WAVES * 64),
+                       0, stream, q8, qs, k8, ks, w, scores, Tq, N, q_pos0, vis, kpw, Paged{}, *ps);
   else
     hipLaunchKernelGGL((indexer_dma_fp8<WAVES, NBUF, SCAP>), grid, dim3(WAVES * 64), 0, stream, q8, qs, k8, ks, w,
                        scores, Tq, N, q_pos0, vis, kpw, Paged{}, none);

@@ -588,7 +588,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
 // partial row is one 1 KiB load, and the splits' loads are independent.
 constexpr int COMBINE_WAVES = 4;
 constexpr int COMBINE_CHUNK = 8;  // partial rows in flight per lane
-__global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const uint16_t* part_o,  // not restrict: see below
+// part_o is not declared restrict, so that the compiler barrier below keeps
+// its loads ahead of the reductions.
+__global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const uint16_t* part_o,
                                                                         const float* __restrict__ part_lse,
                                                                         uint16_t* __restrict__ out,
                                                                         float* __restrict__ lse, int64_t R,
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const u
 #pragma unroll
   for (int c = 0; c < COMBINE_CHUNK; ++c)  // past the last split: reread it with weight 0
     v[c] = *reinterpret_cast<const uint4*>(base + min(c, splits - 1) * stride * MDV);
-  asm volatile("" ::: "memory");  // keeps the loads here, ahead of the reductions (part_o may alias it)
+  asm volatile("" ::: "memory");  // keeps the loads here, ahead of the reductions
   const float ls = lane < splits ? ls_raw : -INFINITY;
   const float M = wave_fmax(ls);
   const float e = M == -INFINITY ? 0.f : exp2f(ls - M);  // exp2(-inf) = 0 for empty splits
