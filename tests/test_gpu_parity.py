@@ -157,7 +157,7 @@ def test_indexer_bf16_negative_weights_exact():
 @pytest.mark.parametrize("N,K,q_pos0,Tq", [
     (3000, 5, 2900, 37),     # rows staged in LDS, all longer than K
     (3000, 2048, 0, 40),     # short rows: closed form 0..t, -1
-    (20000, 2048, 19900, 6), # rows longer than the LDS stage: streamed passes
+    (20000, 2048, 19900, 6), # rows of more than 16384 keys, few rows: the segmented method
     (20000, 1, 19990, 4),    # K = 1
     (17, 16, 0, 17),         # n == K and n == K + 1 boundary
     (70000, 2048, 69990, 3), # segmented long-row method, 5 segments, last one ragged
