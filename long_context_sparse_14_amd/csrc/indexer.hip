@@ -662,7 +662,9 @@ __device__ __forceinline__ void load_query_fp8(QFrags& f, const uint8_t* __restr
 // direct-to-LDS loads of eight keys each; lane L of a load fetches chunk
 // (L & 7) ^ (L >> 3) of key L >> 3 and lands at slot L, so chunk c of tile key
 // r sits at slot 8r + (c ^ (r & 7)).  The key scales are applied when the
-// workgroup's scores leave LDS.
+// workgroup's scores leave LDS; with PRESEL they are applied in LDS first, and
+// the segment's pre-selection list (presel_segment) is drawn from the scaled
+// scores before they leave.
 template <int WAVES, int NBUF, int SCAP, bool PAGED = false, bool PRESEL = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void indexer_dma_fp8(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
