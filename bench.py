@@ -81,7 +81,7 @@ def _parse():
 
 
 # Source files each timed kernel is built from: stored counter readings stay
-# valid until one of them changes.
+# valid until the code of one of them changes (comments and layout aside).
 KERNEL_SOURCES = {
     "indexer_dma_bf16": ["indexer.hip", "device_common.h", "select_common.h", "launch.h"],
     "indexer_tiled_bf16": ["indexer.hip", "device_common.h", "select_common.h", "launch.h"],
@@ -90,14 +90,40 @@ KERNEL_SOURCES = {
 }
 
 
+def code_only(text: str) -> str:
+    """A C++ source without its comments, whitespace runs collapsed to one
+    space: what the compiler sees of it (string and character literals kept
+    whole)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif text[i] in "\"'":
+            q, j = text[i], i + 1
+            while j < n and text[j] != q:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_sources_digest(kernel: str) -> str:
-    """Digest of the HIP sources of one kernel and their per-file compile flags."""
+    """Digest of the code of one kernel's HIP sources (comments and layout
+    aside) and of their per-file compile flags."""
     from long_context_sparse_14_amd import build as _build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_sparse_14_amd", "csrc")
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update((name + "\n" + code_only(f.read())).encode())
         h.update(" ".join(_build.EXTRA_FLAGS.get(name, [])).encode())
     return h.hexdigest()[:16]
 

@@ -40,6 +40,15 @@ def test_traffic_digest_follows_sources_and_flags(monkeypatch):
     assert bench.kernel_sources_digest("indexer_dma_bf16") != base, "a compile flag changes the kernel"
 
 
+def test_traffic_digest_ignores_comments_not_code():
+    src = 'int f(int x) {  // doubles x\n  return 2 * x; /* no overflow check */\n}\nconst char* s = "a // b";\n'
+    same = 'int f(int x) {\n  return 2 * x;\n}\n// a note\nconst char* s = "a // b";\n'
+    assert bench.code_only(src) == bench.code_only(same)
+    assert bench.code_only(src) != bench.code_only(src.replace("2 * x", "3 * x")), "a code change is seen"
+    assert bench.code_only(src) != bench.code_only(src.replace('"a // b"', '"a b"')), "string literals are code"
+    assert '"a // b"' in bench.code_only(src)
+
+
 def _write_csv(path, header, rows):
     import csv
     with open(path, "w", newline="") as f:
