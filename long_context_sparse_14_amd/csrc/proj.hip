@@ -33,6 +33,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "select_common.h"
 
 namespace dsa {
 namespace {
@@ -230,6 +231,178 @@ __global__ __launch_bounds__(256, GK == 32 ? 3 : 2) void gemm_bf16_kernel(GemmAr
   }
 }
 
+// The [K][N] weight with short K (K <= KMAX, the absorption's d_nope) and many
+// rows.  With K = 128 a 128 x 128 tile is only eight k-steps of work, so the
+// tiled kernel above spends most of each workgroup on its own start and
+// epilogue, and fetches each block of A once per column block.  Here a
+// 256-thread workgroup owns 128 rows of one batch entry and walks all of N,
+// 128 columns at a time:
+//   * A [128 x K] is staged once through LDS into registers (the MFMA A
+//     operands of the wave's 64 rows for every k-step: 64 registers at
+//     K = 128);
+//   * B column blocks [K x 128] alternate between two LDS buffers, the next
+//     one's global loads in flight while the current one is multiplied, and
+//     reach the MFMA through the transposing read as above;
+//   * each 128 x 128 output block is staged as bf16 in the buffer just
+//     consumed and leaves in 16-byte row chunks;
+//   * the row copy (the absorbed query's rope part) rides along at the end.
+// The barriers inside the walk settle LDS only.  Workgroups are renumbered so
+// that each XCD runs a contiguous range, in groups of WALK_HG batch entries
+// with the entry advancing fastest: the workgroups resident together write
+// neighbouring pieces of the same output rows and share those entries' B in
+// L2.  Requires 16-byte aligned A, B, C and row pitches that are multiples of
+// 8 elements.
+constexpr int64_t WALK_HG = 16;
+template <int KMAX>
+__global__ __launch_bounds__(256, 2) void gemm_kn_walk_kernel(GemmArgs g) {
+  constexpr int WM = 2, WN = 2, WAVES_M = 2, BM = 128, KS = KMAX / 16;
+  constexpr int APITCH = KMAX + 8;        // bf16 per staged A row
+  constexpr int B_LDS = KMAX * KNPITCH;   // one [KMAX][128] column block of B
+  constexpr int CPITCH = GN + 8;          // bf16 per staged output row
+  constexpr int CHUNKS = BM * KMAX / 8;   // 16-byte chunks of A, and of a B block (KMAX x 16)
+  constexpr int PER = CHUNKS / 256;
+  static_assert(BM * APITCH <= B_LDS && BM * CPITCH <= B_LDS, "A and the output block stage in a B buffer");
+  static_assert(KMAX % 32 == 0 && PER * 256 == CHUNKS && GN == 128, "walk geometry");
+  __shared__ __align__(16) uint16_t lds[2 * B_LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int half = lane >> 5, col = lane & 31;
+  const int64_t gy = (g.M + BM - 1) / BM;
+  const int64_t total = gridDim.x, nz = total / gy;
+  int64_t P = blockIdx.x;
+  if ((total & 7) == 0) P = (P & 7) * (total >> 3) + (P >> 3);
+  const int64_t first_z = P / (WALK_HG * gy) * WALK_HG;
+  const int64_t zsz = min(nz - first_z, WALK_HG);
+  const int64_t in_group = P - first_z * gy;
+  const int64_t z = first_z + in_group % zsz;
+  const int64_t m0 = in_group / zsz * BM;
+  const uint16_t* A = g.A + z * g.sA;
+  const uint16_t* B = g.B + z * g.sB;
+  uint16_t* C = g.C + z * g.sC;
+  const int K = g.K, N = g.N, kc = K / 8;  // K: a multiple of 32, at most KMAX; N: a multiple of 8
+  const int nblk = (N + GN - 1) / GN;
+
+  // chunk c of A: row c / kc, k-chunk c % kc; of B block n0: k-row c >> 4, columns n0 + 8 * (c & 15)
+  auto gload_b = [&](u32x4 (&r)[PER], int n0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u;
+      const int n = n0 + 8 * (c & 15);
+      r[u] = (c < K * 16 && n < N) ? *reinterpret_cast<const u32x4*>(B + (int64_t)(c >> 4) * g.ldb + n)
+                                   : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto lstore_b = [&](const u32x4 (&r)[PER], int buf) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u;
+      if (c < K * 16) *reinterpret_cast<u32x4*>(&lds[buf * B_LDS + (c >> 4) * KNPITCH + 8 * (c & 15)]) = r[u];
+    }
+  };
+
+  // A into buffer 1 (through registers), B block 0 into buffer 0
+  u32x4 ra[PER], rb[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = tid + 256 * u;
+    const int64_t m = m0 + c / kc;
+    ra[u] = (c < BM * kc && m < g.M) ? *reinterpret_cast<const u32x4*>(A + m * g.lda + 8 * (c % kc))
+                                     : u32x4{0, 0, 0, 0};
+  }
+  gload_b(rb, 0);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = tid + 256 * u;
+    if (c < BM * kc) *reinterpret_cast<u32x4*>(&lds[B_LDS + (c / kc) * APITCH + 8 * (c % kc)]) = ra[u];
+  }
+  lstore_b(rb, 0);
+  __syncthreads();
+  bf16x8 a[WM][KS];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      if (16 * ks < K)
+        a[i][ks] = *reinterpret_cast<const bf16x8*>(&lds[B_LDS + (32 * (WM * wm + i) + col) * APITCH + 16 * ks +
+                                                        8 * half]);
+  __syncthreads();  // buffer 1 is free for B block 1
+
+  const int g16 = lane >> 4, i16 = lane & 15;
+  for (int nb = 0; nb < nblk; ++nb) {
+    const int buf = nb & 1, n0 = nb * GN;
+    if (nb + 1 < nblk) gload_b(rb, n0 + GN);
+    f32x16 acc[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[i][j] = f32x16{};
+    const uint16_t* Bs = &lds[buf * B_LDS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (16 * ks >= K) break;
+      bf16x8 b[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int nc = 32 * (WN * wn + j);
+        const uint16_t* p = Bs + (16 * ks + 8 * (g16 >> 1) + (i16 >> 2)) * KNPITCH + nc + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const s16x4 lo = lds_read_tr16(p);
+        const s16x4 hi = lds_read_tr16(p + 4 * KNPITCH);
+        b[j] = __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32x32x16(a[i][ks], b[j], acc[i][j]);
+    }
+    lds_barrier();  // every wave has read this B block and copied the previous output block out of LDS
+    uint16_t* Cs = &lds[buf * B_LDS];
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          Cs[(32 * (WM * wm + i) + mfma_row(e, half)) * CPITCH + 32 * (WN * wn + j) + col] =
+              (uint16_t)float_to_bf16_bits(acc[i][j][e]);
+    if (nb + 1 < nblk) lstore_b(rb, buf ^ 1);
+    lds_barrier();
+    for (int c = tid; c < BM * (GN / 8); c += 256) {
+      const int r = c / (GN / 8), ch = c % (GN / 8);
+      const int64_t m = m0 + r;
+      const int n = n0 + 8 * ch;
+      if (m < g.M && n < N)
+        *reinterpret_cast<u32x4*>(C + m * g.ldc + n) = *reinterpret_cast<const u32x4*>(&Cs[r * CPITCH + 8 * ch]);
+    }
+  }
+
+  // Optional row copy (the rope part of an absorbed query): cp_w bf16 per row,
+  // in 16-byte chunks, four per thread at a time with every load issued before
+  // the stores (source and destination may alias, so the compiler otherwise
+  // keeps each load behind the previous store: four round trips in a row).
+  if (g.cp_dst != nullptr) {
+    const int chunks = g.cp_w / 8, tot = BM * chunks;
+    for (int c0 = 0; c0 < tot; c0 += 4 * 256) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + tid + 256 * u;
+        const int64_t m = m0 + c / chunks;
+        v[u] = (c < tot && m < g.M)
+                   ? *reinterpret_cast<const u32x4*>(g.cp_src + z * g.cp_ss + m * g.cp_lds + 8 * (c % chunks))
+                   : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + tid + 256 * u;
+        const int64_t m = m0 + c / chunks;
+        if (c < tot && m < g.M)
+          *reinterpret_cast<u32x4*>(g.cp_dst + z * g.cp_sd + m * g.cp_ldd + 8 * (c % chunks)) = v[u];
+      }
+    }
+  }
+}
+
 // Few rows (M <= 64), where the weights' bytes bound the time.  A workgroup
 // of WK x WN waves owns a 32 x 32*WN tile of C over the whole of K: wave
 // (wk, wn) computes columns 32*wn .. +32 from every WK-th k-step of 16
@@ -377,6 +550,17 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool b_nk, int64_t batch, hipStre
     if (b_nk && few) return launch_skinny<true, 16, 1, 4>(g, batch, stream);
     if (b_nk) return launch_skinny<true, 8, 1, 4>(g, batch, stream);
     return launch_skinny<false, 2, 4, 4>(g, batch, stream);
+  }
+  const bool aligned = ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
+                         reinterpret_cast<uintptr_t>(g.C)) & 15) == 0 &&
+                       (g.lda | g.ldb | g.ldc | g.sA | g.sB | g.sC) % 8 == 0 && g.N % 8 == 0 &&
+                       (g.cp_dst == nullptr || ((reinterpret_cast<uintptr_t>(g.cp_src) |
+                                                 reinterpret_cast<uintptr_t>(g.cp_dst)) & 15) == 0);
+  if (!b_nk && g.K <= 128 && aligned) {
+    // the absorption's short K: one workgroup per 128 rows of a batch entry, walking all of N
+    const int64_t wgs = (g.M + 127) / 128 * batch;
+    hipLaunchKernelGGL((gemm_kn_walk_kernel<128>), dim3((unsigned)wgs), dim3(256), 0, stream, g);
+    return hipGetLastError();
   }
   return launch_tiles<2, 2, 2>(g, b_nk, batch, stream);                  // 128 x 128 tiles
 }

@@ -48,7 +48,10 @@ def normal_bf16(shape, tensor_id, pow2=0, seed=0):
     (37, 4, 128, 64, 512),     # ragged rows, the V3.2 head shape
     (32, 128, 128, 64, 512),   # the 128K decode batch, all 128 heads
     (130, 3, 32, 0, 40),       # no rope part, a column block cut at 40
-    (200, 2, 128, 64, 512),    # 128-row tiles, four k tiles
+    (200, 2, 128, 64, 512),    # 128-row blocks walking four column blocks, eight k-steps
+    (300, 3, 64, 64, 264),     # short K, a last column block of 8
+    (129, 2, 96, 32, 136),     # K = 96 (six k-steps), one row in the last row block
+    (100, 2, 160, 0, 128),     # K above the column walk's 128: the tiled kernel
 ])
 def test_absorb_q(M, H, d_nope, d_rope, d_c):
     dsa = _dsa()
