@@ -236,33 +236,41 @@ __global__ __launch_bounds__(256, GK == 32 ? 3 : 2) void gemm_bf16_kernel(GemmAr
 // tiled kernel above spends most of each workgroup on its own start and
 // epilogue, and fetches each block of A once per column block.  Here a
 // 256-thread workgroup owns 128 rows of one batch entry and walks all of N,
-// 128 columns at a time:
+// BN columns at a time:
 //   * A [128 x K] is staged once through LDS into registers (the MFMA A
-//     operands of the wave's 64 rows for every k-step: 64 registers at
-//     K = 128);
-//   * B column blocks [K x 128] alternate between two LDS buffers, the next
+//     operands of the wave's rows for every k-step);
+//   * B column blocks [K x BN] alternate between two LDS buffers, the next
 //     one's global loads in flight while the current one is multiplied, and
 //     reach the MFMA through the transposing read as above;
-//   * each 128 x 128 output block is staged as bf16 in the buffer just
+//   * each 128 x BN output block is staged as bf16 in the buffer just
 //     consumed and leaves in 16-byte row chunks;
 //   * the row copy (the absorbed query's rope part) rides along at the end.
-// The barriers inside the walk settle LDS only.  Workgroups are renumbered so
-// that each XCD runs a contiguous range, in groups of WALK_HG batch entries
-// with the entry advancing fastest: the workgroups resident together write
-// neighbouring pieces of the same output rows and share those entries' B in
-// L2.  Requires 16-byte aligned A, B, C and row pitches that are multiples of
-// 8 elements.
+// BN = 64 with each wave on 32 rows (120 registers, 40 KiB of LDS: four
+// workgroups per compute unit) ran the absorption at M = 16384 in 0.69-0.70
+// ms against 0.75-0.76 with BN = 128 and 64-row waves (242 registers, 72 KiB,
+// two per unit): each block's wait for the next B block also waits for the
+// previous block's output stores (loads and stores share one counter), and
+// more resident workgroups cover it.  The barriers inside the walk settle LDS
+// only.  Workgroups are renumbered so that each XCD runs a contiguous range,
+// in groups of WALK_HG batch entries with the entry advancing fastest: the
+// workgroups resident together write neighbouring pieces of the same output
+// rows and share those entries' B in L2.  Requires 16-byte aligned A, B, C
+// and row pitches that are multiples of 8 elements.
 constexpr int64_t WALK_HG = 16;
-template <int KMAX>
-__global__ __launch_bounds__(256, 2) void gemm_kn_walk_kernel(GemmArgs g) {
-  constexpr int WM = 2, WN = 2, WAVES_M = 2, BM = 128, KS = KMAX / 16;
-  constexpr int APITCH = KMAX + 8;        // bf16 per staged A row
-  constexpr int B_LDS = KMAX * KNPITCH;   // one [KMAX][128] column block of B
-  constexpr int CPITCH = GN + 8;          // bf16 per staged output row
-  constexpr int CHUNKS = BM * KMAX / 8;   // 16-byte chunks of A, and of a B block (KMAX x 16)
-  constexpr int PER = CHUNKS / 256;
-  static_assert(BM * APITCH <= B_LDS && BM * CPITCH <= B_LDS, "A and the output block stage in a B buffer");
-  static_assert(KMAX % 32 == 0 && PER * 256 == CHUNKS && GN == 128, "walk geometry");
+template <int KMAX, int BN>
+__global__ __launch_bounds__(256, BN == 128 ? 2 : 4) void gemm_kn_walk_kernel(GemmArgs g) {
+  constexpr int BM = 128, KS = KMAX / 16;
+  constexpr int WAVES_M = BN == 128 ? 2 : 4, WAVES_N = 4 / WAVES_M;
+  constexpr int WM = BM / 32 / WAVES_M, WN = BN / 32 / WAVES_N;
+  constexpr int BPITCH = BN + 16;          // bf16 per LDS k-row of a B block
+  constexpr int APITCH = KMAX + 8;         // bf16 per staged A row
+  constexpr int B_LDS = KMAX * BPITCH;     // one [KMAX][BN] column block of B
+  constexpr int CPITCH = BN + 8;           // bf16 per staged output row
+  constexpr int BCH = BN / 8;              // 16-byte chunks per k-row of a B block
+  constexpr int PER_A = BM * KMAX / 8 / 256, PER_B = KMAX * BCH / 256;
+  static_assert(BM * APITCH <= 2 * B_LDS && BM * CPITCH <= B_LDS, "A and the output block stage in the B buffers");
+  static_assert(KMAX % 32 == 0 && PER_A * 256 * 8 == BM * KMAX && PER_B * 256 == KMAX * BCH, "walk geometry");
+  static_assert(WM * 32 * WAVES_M == BM && WN * 32 * WAVES_N == BN, "waves cover the block");
   __shared__ __align__(16) uint16_t lds[2 * B_LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -281,30 +289,30 @@ __global__ __launch_bounds__(256, 2) void gemm_kn_walk_kernel(GemmArgs g) {
   const uint16_t* B = g.B + z * g.sB;
   uint16_t* C = g.C + z * g.sC;
   const int K = g.K, N = g.N, kc = K / 8;  // K: a multiple of 32, at most KMAX; N: a multiple of 8
-  const int nblk = (N + GN - 1) / GN;
+  const int nblk = (N + BN - 1) / BN;
 
-  // chunk c of A: row c / kc, k-chunk c % kc; of B block n0: k-row c >> 4, columns n0 + 8 * (c & 15)
-  auto gload_b = [&](u32x4 (&r)[PER], int n0) {
+  // chunk c of A: row c / kc, k-chunk c % kc; of B block n0: k-row c / BCH, columns n0 + 8 * (c % BCH)
+  auto gload_b = [&](u32x4 (&r)[PER_B], int n0) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
+    for (int u = 0; u < PER_B; ++u) {
       const int c = tid + 256 * u;
-      const int n = n0 + 8 * (c & 15);
-      r[u] = (c < K * 16 && n < N) ? *reinterpret_cast<const u32x4*>(B + (int64_t)(c >> 4) * g.ldb + n)
-                                   : u32x4{0, 0, 0, 0};
+      const int n = n0 + 8 * (c % BCH);
+      r[u] = (c < K * BCH && n < N) ? *reinterpret_cast<const u32x4*>(B + (int64_t)(c / BCH) * g.ldb + n)
+                                    : u32x4{0, 0, 0, 0};
     }
   };
-  auto lstore_b = [&](const u32x4 (&r)[PER], int buf) {
+  auto lstore_b = [&](const u32x4 (&r)[PER_B], int buf) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
+    for (int u = 0; u < PER_B; ++u) {
       const int c = tid + 256 * u;
-      if (c < K * 16) *reinterpret_cast<u32x4*>(&lds[buf * B_LDS + (c >> 4) * KNPITCH + 8 * (c & 15)]) = r[u];
+      if (c < K * BCH) *reinterpret_cast<u32x4*>(&lds[buf * B_LDS + (c / BCH) * BPITCH + 8 * (c % BCH)]) = r[u];
     }
   };
 
-  // A into buffer 1 (through registers), B block 0 into buffer 0
-  u32x4 ra[PER], rb[PER];
+  // A staged at the start of LDS (through registers) while B block 0 is fetched
+  u32x4 ra[PER_A], rb[PER_B];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
+  for (int u = 0; u < PER_A; ++u) {
     const int c = tid + 256 * u;
     const int64_t m = m0 + c / kc;
     ra[u] = (c < BM * kc && m < g.M) ? *reinterpret_cast<const u32x4*>(A + m * g.lda + 8 * (c % kc))
@@ -312,11 +320,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kn_walk_kernel(GemmArgs g) {
   }
   gload_b(rb, 0);
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
+  for (int u = 0; u < PER_A; ++u) {
     const int c = tid + 256 * u;
-    if (c < BM * kc) *reinterpret_cast<u32x4*>(&lds[B_LDS + (c / kc) * APITCH + 8 * (c % kc)]) = ra[u];
+    if (c < BM * kc) *reinterpret_cast<u32x4*>(&lds[(c / kc) * APITCH + 8 * (c % kc)]) = ra[u];
   }
-  lstore_b(rb, 0);
   __syncthreads();
   bf16x8 a[WM][KS];
 #pragma unroll
@@ -324,14 +331,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kn_walk_kernel(GemmArgs g) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       if (16 * ks < K)
-        a[i][ks] = *reinterpret_cast<const bf16x8*>(&lds[B_LDS + (32 * (WM * wm + i) + col) * APITCH + 16 * ks +
-                                                        8 * half]);
-  __syncthreads();  // buffer 1 is free for B block 1
+        a[i][ks] = *reinterpret_cast<const bf16x8*>(&lds[(32 * (WM * wm + i) + col) * APITCH + 16 * ks + 8 * half]);
+  lds_barrier();  // A is in registers: the buffers are free
+  lstore_b(rb, 0);
+  lds_barrier();
 
   const int g16 = lane >> 4, i16 = lane & 15;
   for (int nb = 0; nb < nblk; ++nb) {
-    const int buf = nb & 1, n0 = nb * GN;
-    if (nb + 1 < nblk) gload_b(rb, n0 + GN);
+    const int buf = nb & 1, n0 = nb * BN;
+    if (nb + 1 < nblk) gload_b(rb, n0 + BN);
     f32x16 acc[WM][WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i)
@@ -345,9 +353,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kn_walk_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const int nc = 32 * (WN * wn + j);
-        const uint16_t* p = Bs + (16 * ks + 8 * (g16 >> 1) + (i16 >> 2)) * KNPITCH + nc + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const uint16_t* p = Bs + (16 * ks + 8 * (g16 >> 1) + (i16 >> 2)) * BPITCH + nc + 16 * (g16 & 1) + 4 * (i16 & 3);
         const s16x4 lo = lds_read_tr16(p);
-        const s16x4 hi = lds_read_tr16(p + 4 * KNPITCH);
+        const s16x4 hi = lds_read_tr16(p + 4 * BPITCH);
         b[j] = __builtin_bit_cast(bf16x8, s16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
       }
 #pragma unroll
@@ -367,8 +375,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kn_walk_kernel(GemmArgs g) {
               (uint16_t)float_to_bf16_bits(acc[i][j][e]);
     if (nb + 1 < nblk) lstore_b(rb, buf ^ 1);
     lds_barrier();
-    for (int c = tid; c < BM * (GN / 8); c += 256) {
-      const int r = c / (GN / 8), ch = c % (GN / 8);
+    for (int c = tid; c < BM * BCH; c += 256) {
+      const int r = c / BCH, ch = c % BCH;
       const int64_t m = m0 + r;
       const int n = n0 + 8 * ch;
       if (m < g.M && n < N)
@@ -402,6 +410,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kn_walk_kernel(GemmArgs g) {
     }
   }
 }
+
+constexpr int WALK_BN = 64;
 
 // Few rows (M <= 64), where the weights' bytes bound the time.  A workgroup
 // of WK x WN waves owns a 32 x 32*WN tile of C over the whole of K: wave
@@ -559,7 +569,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool b_nk, int64_t batch, hipStre
   if (!b_nk && g.K <= 128 && aligned) {
     // the absorption's short K: one workgroup per 128 rows of a batch entry, walking all of N
     const int64_t wgs = (g.M + 127) / 128 * batch;
-    hipLaunchKernelGGL((gemm_kn_walk_kernel<128>), dim3((unsigned)wgs), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((gemm_kn_walk_kernel<128, WALK_BN>), dim3((unsigned)wgs), dim3(256), 0, stream, g);
     return hipGetLastError();
   }
   return launch_tiles<2, 2, 2>(g, b_nk, batch, stream);                  // 128 x 128 tiles
