@@ -15,12 +15,19 @@
 // fewer than k_eq equal keys precede it; its output slot is
 //   #{j < i : key_j > T} + min(#{j < i : key_j == T}, k_eq).
 //
-// Two schedules:
-//  * rows of up to 16384 keys (prefill): one 1024-thread workgroup per row,
-//    the row staged once in LDS with its key range, then exact select rounds
-//    that each split the remaining range into 2048 bins (ceil(bits / 11)
-//    rounds for a range of that many bits), then an in-order compaction with
-//    one block prefix sum per 16384 keys;
+// Three schedules:
+//  * rows of up to 16384 keys (prefill): one workgroup per row, the row held
+//    on chip with its key range, then exact select rounds that each split the
+//    remaining range into 2^HBITS bins, then an in-order compaction with one
+//    block prefix sum per chunk.  Rows of at most 8192 keys are staged in LDS
+//    by 512 threads; rows of up to 16384 keep their first 8192 keys in LDS and
+//    the rest in registers on 512 threads (four workgroups per compute unit
+//    either way); longer rows that the long-row method below does not take
+//    run on 1024 threads from global memory;
+//  * decode rows that the indexer pre-selected (topk_presel_final): one
+//    workgroup per row selects among the indexer's per-segment lists and
+//    falls back to the row's full scores when a list cannot be shown to hold
+//    the row's top K;
 //  * long rows (decode at long context): each row is cut into 16384-key
 //    segments, and two kernels replace the serial passes:
 //      1. one workgroup per segment holds its keys in registers, finds bounds
@@ -51,7 +58,7 @@ namespace {
 
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_CAP = 16384;         // longest row staged in LDS by the one-workgroup method
+constexpr int TK_CAP = 16384;         // longest row the one-workgroup method holds on chip
 constexpr int SEG = 16384;            // segment length of the long-row method
 constexpr int SEG_PER_T = SEG / TK_THREADS;
 constexpr int HB = 2048;              // bins of an 11-bit digit
