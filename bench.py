@@ -578,10 +578,18 @@ def bench_next(args):
         us_i = timed(lib.dsa_index_scores_compressed, (P(q_idx), P(k_idx), P(w), P(scores), B, 1, N, T - 1, m, 64, 128,
                                                        dsa.DSA_BF16, sp))
         us_t = timed(lib.dsa_topk_compressed, (P(scores), P(idx), B, 1, N, T - 1, m, K, P(tws), tws.numel(), sp))
+        # the pair with the decode pre-selection (the lists share the top-k workspace, so the indexer runs first)
+        us_ip = timed(lib.dsa_index_scores_compressed_presel, (P(q_idx), P(k_idx), P(w), P(scores), B, 1, N, T - 1, m,
+                                                               64, 128, K, dsa.DSA_BF16, P(tws), tws.numel(), sp))
+        us_tp = timed(lib.dsa_topk_compressed_presel, (P(scores), P(idx), B, 1, N, T - 1, m, K, dsa.DSA_BF16, P(tws),
+                                                       tws.numel(), sp))
         nb = B * N * 128 * 2 + B * N * 4
         rows.append({"call": "dsa_index_scores_compressed", "batch": B, "tokens": T, "rate_m": m, "entries": N,
                      "us": round(us_i, 2), "GB_per_s": round(nb / us_i / 1e3, 1)})
         rows.append({"call": "dsa_topk_compressed", "batch": B, "entries": N, "K": K, "us": round(us_t, 2)})
+        rows.append({"call": "dsa_index_scores_compressed_presel", "batch": B, "tokens": T, "rate_m": m,
+                     "entries": N, "us": round(us_ip, 2), "GB_per_s": round(nb / us_ip / 1e3, 1)})
+        rows.append({"call": "dsa_topk_compressed_presel", "batch": B, "entries": N, "K": K, "us": round(us_tp, 2)})
     print(json.dumps({"next": args.next, "launches_per_call": reps, "calls": rows}), flush=True)
 
 

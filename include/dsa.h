@@ -272,6 +272,17 @@ dsa_status dsa_forward_varlen(const void* q_idx, const void* k_idx, const void* 
  * launches nothing.  Arguments, layouts, workspace and the other errors are
  * those of dsa_index_scores / dsa_topk.  When no query sees an entry the
  * indexer launches nothing and leaves scores untouched.
+ *
+ * dsa_index_scores_compressed_presel / dsa_topk_compressed_presel: the same
+ * two steps with the decode pre-selection of dsa_index_scores_presel and
+ * dsa_topk_presel over the visible entries (rows of more than 16384 visible
+ * entries, at most 4 queries per sequence, K <= 4096): the indexer also lists
+ * each segment's best entries in `workspace` (dsa_topk_workspace_size(B, Tq,
+ * N, K) bytes), and the top-k selects among the lists, with the same exact
+ * fallback to a row's full scores.  The indices equal dsa_topk_compressed's.
+ * Pass both calls the same B, Tq, N, q_pos0, m, K, dtype and workspace; where
+ * no pre-selection applies the pair is dsa_index_scores_compressed then
+ * dsa_topk_compressed.
  */
 dsa_status dsa_index_scores_compressed(const void* q_idx, const void* k_idx, const void* w, float* scores,
                                        int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t m, int32_t H_I,
@@ -279,6 +290,13 @@ dsa_status dsa_index_scores_compressed(const void* q_idx, const void* k_idx, con
 dsa_status dsa_topk_compressed(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N,
                                int64_t q_pos0, int32_t m, int32_t K, void* workspace, size_t ws_bytes,
                                void* stream);
+dsa_status dsa_index_scores_compressed_presel(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                                              int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t m,
+                                              int32_t H_I, int32_t D_I, int32_t K, int32_t dtype, void* workspace,
+                                              size_t ws_bytes, void* stream);
+dsa_status dsa_topk_compressed_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N,
+                                      int64_t q_pos0, int32_t m, int32_t K, int32_t dtype, void* workspace,
+                                      size_t ws_bytes, void* stream);
 
 /*
  * Cache append: one new token per sequence.

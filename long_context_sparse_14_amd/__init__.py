@@ -92,6 +92,9 @@ _SIGNATURES = {
     "dsa_index_scores_compressed": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
                                                    _p]),
     "dsa_topk_compressed": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _p, _sz, _p]),
+    "dsa_index_scores_compressed_presel": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
+                                                          _i32, _i32, _p, _sz, _p]),
+    "dsa_topk_compressed_presel": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p, _sz, _p]),
     "dsa_mla_absorb_q": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _p]),
     "dsa_mla_out_proj": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p]),
     "dsa_linear": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _p]),
@@ -467,6 +470,45 @@ def topk_compressed(scores, K: int, m: int, q_pos0: int = 0, idx=None, workspace
     ws, nbytes = _workspace(lib.dsa_topk_workspace_size(B, Tq, N, K), scores.device, workspace)
     _check(lib.dsa_topk_compressed(ps, pi, B, Tq, N, q_pos0, m, K, ws.data_ptr() if ws is not None else None, nbytes,
                                    _stream(stream)))
+    return idx
+
+
+def index_scores_compressed_presel(q_idx, k_idx, w, m: int, K: int, q_pos0: int = 0, scores=None, workspace=None,
+                                   stream=None):
+    """index_scores_compressed plus the decode pre-selection lists, kept in a top-k workspace.
+    Returns (scores, workspace): pass both to topk_compressed_presel."""
+    B, Tq, H_I, D_I = q_idx.shape
+    N = k_idx.shape[1]
+    dt = q_idx.dtype
+    pq, pk, pw = _dev(q_idx, "q_idx", 4), _dev(k_idx, "k_idx", 3, dt), _dev(w, "w", 3, dt)
+    if tuple(k_idx.shape) != (B, N, D_I) or tuple(w.shape) != (B, Tq, H_I):
+        raise ValueError("k_idx must be [B,N,D_I] and w [B,Tq,H_I]")
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q_idx.device)
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if tuple(scores.shape) != (B, Tq, N):
+        raise ValueError("scores must be [B,Tq,N]")
+    lib = library()
+    ws, nbytes = _workspace(lib.dsa_topk_workspace_size(B, Tq, N, K), q_idx.device, workspace)
+    _check(lib.dsa_index_scores_compressed_presel(pq, pk, pw, ps, B, Tq, N, q_pos0, m, H_I, D_I, K, _dtype_code(q_idx),
+                                                  ws.data_ptr() if ws is not None else None, nbytes, _stream(stream)))
+    return scores, ws
+
+
+def topk_compressed_presel(scores, K: int, m: int, workspace, dtype, q_pos0: int = 0, idx=None,
+                           stream=None) -> torch.Tensor:
+    """topk_compressed for scores and the workspace index_scores_compressed_presel filled (dtype: that
+    call's torch dtype)."""
+    B, Tq, N = scores.shape
+    ps = _dev(scores, "scores", 3, torch.float32)
+    if idx is None:
+        idx = torch.empty((B, Tq, K), dtype=torch.int32, device=scores.device)
+    pi = _dev(idx, "idx", 3, torch.int32)
+    code = DSA_BF16 if dtype == torch.bfloat16 else DSA_F32
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(library().dsa_topk_compressed_presel(ps, pi, B, Tq, N, q_pos0, m, K, code,
+                                                workspace.data_ptr() if workspace is not None else None, nbytes,
+                                                _stream(stream)))
     return idx
 
 

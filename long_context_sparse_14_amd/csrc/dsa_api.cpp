@@ -577,6 +577,46 @@ dsa_status dsa_topk_compressed(const float* scores, int32_t* idx, int64_t B, int
                     "top-k launch");
 }
 
+dsa_status dsa_index_scores_compressed_presel(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                                              int64_t B, int64_t Tq, int64_t N, int64_t q_pos0, int32_t m,
+                                              int32_t H_I, int32_t D_I, int32_t K, int32_t dtype, void* workspace,
+                                              size_t ws_bytes, void* stream) {
+  dsa_status st = check_index_scores(q_idx, k_idx, w, scores, B, Tq, N, q_pos0, H_I, D_I, dtype, true);
+  if (st != DSA_OK) return st;
+  if (m < 1) return fail(DSA_ERR_INVALID_ARG, "the compression rate m must be >= 1 (got %d)", m);
+  if (K < 1 || K > kMaxK) return fail(DSA_ERR_INVALID_ARG, "K must be in [1, 65536] (got %d)", K);
+  const size_t need = dsa::topk_workspace_bytes(B, Tq, N, K);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "top-k workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nmax = std::min(N, (q_pos0 + Tq) / m);
+  if (presel_applies(B, Tq, N, nmax, K, dtype, nullptr)) {
+    const dsa::PreselWs ps = dsa::presel_ws(workspace, B, Tq, N, nmax, K);
+    return hip_status(dsa::launch_index_scores_bf16(static_cast<const uint16_t*>(q_idx),
+                                                    static_cast<const uint16_t*>(k_idx),
+                                                    static_cast<const uint16_t*>(w), scores, B, Tq, N, q_pos0, s,
+                                                    nullptr, m, nullptr, &ps),
+                      "index scores launch");
+  }
+  return dsa_index_scores_compressed(q_idx, k_idx, w, scores, B, Tq, N, q_pos0, m, H_I, D_I, dtype, stream);
+}
+
+dsa_status dsa_topk_compressed_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N,
+                                      int64_t q_pos0, int32_t m, int32_t K, int32_t dtype, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  dsa_status st = check_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  if (m < 1) return fail(DSA_ERR_INVALID_ARG, "the compression rate m must be >= 1 (got %d)", m);
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nmax = std::min(N, (q_pos0 + Tq) / m);
+  if (presel_applies(B, Tq, N, nmax, K, dtype, nullptr))
+    return hip_status(dsa::launch_topk_presel(scores, idx, B, Tq, N, q_pos0, K,
+                                              dsa::presel_ws(workspace, B, Tq, N, nmax, K), s, nullptr, m),
+                      "top-k launch");
+  return hip_status(dsa::launch_topk(scores, idx, B, Tq, N, q_pos0, K, workspace, s, nullptr, m), "top-k launch");
+}
+
 dsa_status dsa_cache_append(void* k_idx, void* kv, const void* new_k_idx, const void* new_kv, const int64_t* pos,
                             int64_t B, int64_t N, int32_t D_I, int32_t D, int32_t dtype, void* stream) {
   if (B < 1 || N < 1) return fail(DSA_ERR_INVALID_ARG, "B and N must be >= 1 (got %lld, %lld)", (long long)B,

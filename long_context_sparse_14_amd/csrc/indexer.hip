@@ -921,7 +921,7 @@ hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx
     constexpr int WAVES = DEC_WAVES, NBUF = DEC_NBUF, SCAP = DEC_SCAP;
     const DecodeGeom geo = decode_geometry(B * Tq, nmax);
     const int64_t kpw = geo.kpw;
-    if (ps != nullptr && (m != 1 || ps->kpw != kpw || ps->G != geo.G)) return hipErrorInvalidValue;
+    if (ps != nullptr && (ps->kpw != kpw || ps->G != geo.G)) return hipErrorInvalidValue;
     dim3 grid((unsigned)geo.G, (unsigned)Tq, (unsigned)B);
     const PreselWs none{};
     if (pg != nullptr) {

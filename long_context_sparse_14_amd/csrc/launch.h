@@ -56,7 +56,7 @@ PreselWs presel_ws(void* workspace, int64_t B, int64_t Tq, int64_t N, int64_t nm
 // seq_lens required); N is then the logical capacity max_blocks << shift.
 // ps (may be null): also write the pre-selection lists (decode shapes whose
 // geometry presel_geometry accepts; ps must come from presel_ws with the same
-// B, Tq, N and longest row).
+// B, Tq, N and longest visible row, n entries at rate m).
 hipError_t launch_index_scores_bf16(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w,
                                     float* scores, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
                                     hipStream_t stream, const int64_t* seq_lens = nullptr, int m = 1,
@@ -79,7 +79,8 @@ size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K);
 // The top-k from the indexer's pre-selection lists (scores: the full rows,
 // read only by rows that fall back).
 hipError_t launch_topk_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                              int K, const PreselWs& ps, hipStream_t stream, const int64_t* seq_lens = nullptr);
+                              int K, const PreselWs& ps, hipStream_t stream, const int64_t* seq_lens = nullptr,
+                              int m = 1);
 hipError_t launch_topk(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
                        int K, void* workspace, hipStream_t stream, const int64_t* seq_lens = nullptr,
                        int m = 1);

@@ -1042,8 +1042,8 @@ size_t topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N, int K) {
 }
 
 hipError_t launch_topk_presel(const float* scores, int32_t* idx, int64_t B, int64_t Tq, int64_t N, int64_t q_pos0,
-                              int K, const PreselWs& ps, hipStream_t stream, const int64_t* seq_lens) {
-  const Vis vis{seq_lens, 1};
+                              int K, const PreselWs& ps, hipStream_t stream, const int64_t* seq_lens, int m) {
+  const Vis vis{seq_lens, m};
   hipLaunchKernelGGL(topk_presel_final, dim3((unsigned)(B * Tq)), dim3(TK_THREADS), 0, stream, scores, ps, idx, Tq, N,
                      q_pos0, vis, K);
   return hipGetLastError();

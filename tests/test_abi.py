@@ -259,6 +259,23 @@ def test_fp8_validation():
     assert L.dsa_topk_presel_fp8(P, P, B, Tq, N, N - 1, 70000, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
 
 
+def test_compressed_presel_validation():
+    L = lib()
+    B, Tq, N, K, m = 32, 1, 32768, 512, 4
+    tw = L.dsa_topk_workspace_size(B, Tq, N, K)
+    assert tw > 0
+    args = [P, P, P, P, B, Tq, N, 4 * N - 1]
+    assert L.dsa_index_scores_compressed_presel(*args, m, 64, 128, K, BF16, P, tw - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_index_scores_compressed_presel(*args, 0, 64, 128, K, BF16, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_scores_compressed_presel(*args, m, 64, 128, 0, BF16, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[3] = None  # scores
+    assert L.dsa_index_scores_compressed_presel(*bad, m, 64, 128, K, BF16, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_compressed_presel(P, P, B, Tq, N, 4 * N - 1, m, K, BF16, P, tw - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_topk_compressed_presel(P, P, B, Tq, N, 4 * N - 1, 0, K, BF16, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_compressed_presel(P, P, B, Tq, N, 4 * N - 1, m, K, 7, P, tw, None) == dsa.DSA_ERR_INVALID_ARG
+
+
 def test_paged_validation():
     L = lib()
     # block size: a power of two of at least 64; the table must be given and aligned

@@ -90,3 +90,38 @@ def test_compressed_index_then_topk_example():
     assert np.all(idx[:3] == -1)
     assert np.all(idx[3:7, 0] == 0) and np.all(idx[3:7, 1] == -1)
     assert np.all(idx[7:] >= 0)
+
+
+@pytest.mark.parametrize("B,Tq,N,m,q_pos0,K,plant", [
+    (8, 1, 32768, 4, 131071, 512, None),     # the V4 decode shape: 32 segments of 1024 entries, lists of 256
+    (4, 3, 40000, 4, 150000, 2048, None),    # 37500 visible entries: 21 segments, the last one ragged
+    (2, 1, 40000, 2, 79999, 2048, "ties"),   # 3000 tied top entries: their segments cannot list them
+])
+def test_compressed_presel_equals_plain(B, Tq, N, m, q_pos0, K, plant):
+    """At decode shapes the compressed indexer also lists each segment's best entries and the top-k
+    selects among the lists.  Scores and indices must equal the plain compressed pair bit for bit,
+    and sampled rows the oracle's."""
+    dsa = _dsa()
+    wl = WL["indexer_topk_prefill_8k"].replace(B=B, Tq=Tq, N=N, q_pos0=q_pos0, K=K)
+    x = synth.make_inputs(wl)
+    if plant == "ties":
+        for b in range(B):
+            x["w"][b, 0, 0] = 0x3F80                            # bf16 1.0 on head 0
+            x["k_idx"][b, 1000:4000] = x["q_idx"][b, 0, 0]      # entries equal to query 0's head 0
+    print(f"compressed presel case: B={B} Tq={Tq} N={N} m={m} q_pos0={q_pos0} K={K} plant={plant}", flush=True)
+    d = {k: dev(x[k]) for k in ("q_idx", "k_idx", "w")}
+    fill = lambda: torch.full((B, Tq, N), -3.5, dtype=torch.float32, device="cuda")
+    scores, ws = dsa.index_scores_compressed_presel(d["q_idx"], d["k_idx"], d["w"], m, K, q_pos0, scores=fill())
+    idx = dsa.topk_compressed_presel(scores, K, m, ws, torch.bfloat16, q_pos0)
+    plain_scores = dsa.index_scores_compressed(d["q_idx"], d["k_idx"], d["w"], m, q_pos0=q_pos0, scores=fill())
+    plain_idx = dsa.topk_compressed(plain_scores, K, m, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(scores, plain_scores), "the pre-selecting indexer must write the same scores"
+    assert torch.equal(idx, plain_idx), "pre-selected top-k differs from the plain compressed top-k"
+    ix = idx.cpu().numpy()
+    for b in sorted({0, B - 1}):
+        t = Tq - 1
+        n = oracle.n_valid_keys(t, q_pos0, N, m)
+        ref = oracle.index_scores_rows(x["q_idx"][b], x["k_idx"][b], x["w"][b], [t], q_pos0, m)[0]
+        exp = oracle.topk_row(np.asarray(ref[:n], dtype=np.float32), K)
+        assert np.array_equal(ix[b, t], exp), f"row {b},{t} (n={n}) differs from the oracle"
