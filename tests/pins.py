@@ -453,8 +453,19 @@ def pin_fwht(fwht_f32, hadamard) -> bool:
     if y is None:
         return False
     H = hadamard(128)
-    return np.array_equal(y.astype(np.float64), x.astype(np.float64) @ H.T) and \
-        np.array_equal(fwht_f32(y).astype(np.float64), 128.0 * x)
+    if not (np.array_equal(y.astype(np.float64), x.astype(np.float64) @ H.T) and
+            np.array_equal(fwht_f32(y).astype(np.float64), 128.0 * x)):
+        return False
+    # Real-valued rows: whatever order the float32 butterflies add in, each of
+    # the log2(128) = 7 levels rounds a partial sum of at most sum|x| once, so
+    # the result lies within 7 * 2^-24 * sum|x| of the exact product.
+    g = r.standard_normal((16, 128)).astype(np.float32)
+    yg = _safe(fwht_f32, g)
+    if yg is None:
+        return False
+    exact = g.astype(np.float64) @ H.T
+    bound = 7.0 * 2.0 ** -24 * np.abs(g.astype(np.float64)).sum(axis=1, keepdims=True)
+    return bool(np.all(np.abs(yg.astype(np.float64) - exact) <= bound))
 
 
 def pin_pow2_scale(pow2_scale_exp) -> bool:
