@@ -918,12 +918,12 @@ static_assert(PLPT * TK_THREADS == kPreselRowCap, "whole list entries per thread
 
 // One workgroup per row.  The row's segment lists, concatenated, are one list
 // in index order holding, for every segment, all of its keys at or above its
-// threshold.  If they hold at least K keys, the K-th largest of them, T, is
-// found by an exact select; when every truncated segment's threshold is at
-// most T, every key >= T of the row is listed, so T is the row's K-th key and
-// the kept keys (> T, and the first keq equal to T) are exactly the row's
-// top K; one block prefix sum writes them in index order.  Otherwise the row
-// runs the one-workgroup method over its scores in global memory.
+// threshold.  With L the largest threshold of a truncated list, every key >= L
+// of the row is listed; if at least K listed keys are >= L, the K-th largest
+// of them, T, found by an exact select among those alone, is the row's K-th
+// key, and the kept keys (> T, and the first keq equal to T) are exactly the
+// row's top K; one block prefix sum writes them in index order.  Otherwise
+// the row runs the one-workgroup method over its scores in global memory.
 __global__ __launch_bounds__(TK_THREADS) void topk_presel_final(const float* __restrict__ scores, PreselWs ps,
                                                                 int32_t* __restrict__ idx, int64_t Tq, int64_t N,
                                                                 int64_t q_pos0, Vis vis, int K) {
@@ -946,38 +946,44 @@ __global__ __launch_bounds__(TK_THREADS) void topk_presel_final(const float* __r
   // G * cap <= kPreselRowCap slots of a row lie inside the workspace).
   // Thread t takes slots PLPT*t .. PLPT*t + PLPT - 1, which span at most two
   // segments (cap >= 16), and loads them together with those segments' counts
-  // and, for thread g < nseg, segment g's threshold: one round trip.  A slot is
+  // and, in every wave, the segments' thresholds: one round trip.  A slot is
   // an entry iff its segment ran and its position is below that segment's
   // count; thread order is then index order.
   const int p0 = PLPT * tid;
   const int ga = p0 / cap, gb = (p0 + PLPT - 1) / cap;
   const uint32_t cnt_a = ps.count[s0 + min(ga, nseg - 1)], cnt_b = ps.count[s0 + min(gb, nseg - 1)];
-  const uint32_t thr_own = tid < nseg ? ps.thr[s0 + tid] : 0u;
+  uint32_t tl = 0u;
+  for (int g = tid & 63; g < nseg; g += 64) tl = max(tl, ps.thr[s0 + g]);
   uint2 lv[PLPT];
 #pragma unroll
   for (int u = 0; u < PLPT; ++u) lv[u] = ps.list[s0 * cap + p0 + u];
+  // L: the largest threshold of a truncated list (0 when every list holds its
+  // whole segment).  Every key of the row at or above L is listed, so when at
+  // least K listed keys are >= L, the row's K-th key T is the K-th of those,
+  // T >= L, and the keys of the row equal to T are all listed: only entries
+  // >= L take part.  With fewer, T < L, and a truncated list may hide keys of
+  // the row's top K: the row falls back.  (A list with no room for any of its
+  // candidate thresholds has thr all ones, so its row always falls back.)
+  const uint32_t L = wave_max(tl);
   uint32_t ck[PLPT];
   int32_t ci[PLPT];
-  uint32_t mn = 0xffffffffu, mx = 0u;
+  uint32_t mn = 0xffffffffu, mx = 0u, own = 0u;
 #pragma unroll
   for (int u = 0; u < PLPT; ++u) {
     const int p = p0 + u;
     const int g = p / cap;
-    const bool in = g < nseg && (uint32_t)(p - g * cap) < (g == ga ? cnt_a : cnt_b);
+    const bool in = g < nseg && (uint32_t)(p - g * cap) < (g == ga ? cnt_a : cnt_b) && lv[u].x >= L;
     ck[u] = in ? lv[u].x : 0u;
     ci[u] = in ? (int32_t)lv[u].y : -1;
     if (in) {
       mn = min(mn, lv[u].x);
       mx = max(mx, lv[u].x);
+      ++own;
     }
   }
-  // the row's entry count: each segment's count from the thread holding its first slot
-  uint32_t own = 0u;
-  if (p0 % cap == 0) own = ga < nseg ? cnt_a : 0u;   // segment ga starts at p0
-  else if (gb > ga) own = gb < nseg ? cnt_b : 0u;   // segment gb starts inside this thread's slots
   uint32_t kmin, kmax, total;
   block_min_max_sum(mn, mx, own, kmin, kmax, total, sm.sbuf);  // its barrier also publishes the cleared bins
-  bool ok = total >= (uint32_t)K;
+  const bool ok = total >= (uint32_t)K;
   uint32_t T = 0u, keq = 0u;
   if (ok) {
     auto add_cand = [&](HotBins& hb, uint32_t lo, uint32_t hi, int shift) {
@@ -994,9 +1000,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_presel_final(const float* __r
     T = select_rank<FB_BITS>(add_cand, each_cand, kmin, kmax, (uint32_t)K, above, sm.h, sm.sbuf, sm.s_res,
                              sm.small);
     keq = (uint32_t)K - above;
-    // every truncated list must reach down to T
-    const bool bad = tid < nseg && thr_own != 0u && thr_own > T;
-    ok = __syncthreads_or(bad) == 0;
   }
   if (!ok) {
     lds_barrier();  // every wave has read the reduction's words in sbuf before the fallback reuses them
