@@ -575,10 +575,17 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_bf16_kernel(
       const u32x4 v3 = *reinterpret_cast<const u32x4*>(sp4 + 3 * EPITCH);
       __builtin_amdgcn_sched_barrier(0);
       uint16_t* dp4 = dst + (64 * q + 16 * wave + 4 * g) * MDV + 8 * elane;
-      __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(dp4));
-      __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(dp4 + MDV));
-      __builtin_nontemporal_store(v2, reinterpret_cast<u32x4*>(dp4 + 2 * MDV));
-      __builtin_nontemporal_store(v3, reinterpret_cast<u32x4*>(dp4 + 3 * MDV));
+      if (splits == 1) {  // the output: streaming stores
+        __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(dp4));
+        __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(dp4 + MDV));
+        __builtin_nontemporal_store(v2, reinterpret_cast<u32x4*>(dp4 + 2 * MDV));
+        __builtin_nontemporal_store(v3, reinterpret_cast<u32x4*>(dp4 + 3 * MDV));
+      } else {  // a split partial: kept in this XCD's cache for the combine, which runs on the same XCD
+        *reinterpret_cast<u32x4*>(dp4) = v0;
+        *reinterpret_cast<u32x4*>(dp4 + MDV) = v1;
+        *reinterpret_cast<u32x4*>(dp4 + 2 * MDV) = v2;
+        *reinterpret_cast<u32x4*>(dp4 + 3 * MDV) = v3;
+      }
     }
   }
 }
@@ -596,7 +603,17 @@ __global__ __launch_bounds__(64 * COMBINE_WAVES) void mla_combine_kernel(const u
                                                                         float* __restrict__ lse, int64_t R,
                                                                         int splits) {
   const int lane = threadIdx.x & 63;
-  const int64_t rh = (int64_t)blockIdx.x * COMBINE_WAVES + (threadIdx.x >> 6);
+  // (query, head) of this wave.  When the rows split evenly over the 8 XCDs,
+  // the MLA kernel ran every split of query r on XCD r & 7 (workgroups are
+  // dealt round-robin to the XCDs), and its partials are read on that XCD too.
+  int64_t rh;
+  if ((R & 7) == 0) {
+    constexpr int PER = MH / COMBINE_WAVES;  // workgroups per query
+    const int64_t c = blockIdx.x, x = c & 7, j = c >> 3;
+    rh = (x + 8 * (j / PER)) * MH + (j % PER) * COMBINE_WAVES + (threadIdx.x >> 6);
+  } else {
+    rh = (int64_t)blockIdx.x * COMBINE_WAVES + (threadIdx.x >> 6);
+  }
   const int64_t stride = R * MH;
   if (rh >= stride) return;  // whole waves only
   // Lane s < splits holds split s's log2-sum-exp (2 <= splits <= 64, checked at
