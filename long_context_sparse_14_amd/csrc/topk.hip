@@ -952,11 +952,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_presel_final(const float* __r
   const int p0 = PLPT * tid;
   const int ga = p0 / cap, gb = (p0 + PLPT - 1) / cap;
   const uint32_t cnt_a = ps.count[s0 + min(ga, nseg - 1)], cnt_b = ps.count[s0 + min(gb, nseg - 1)];
-  uint32_t tl = 0u;
-  for (int g = tid & 63; g < nseg; g += 64) tl = max(tl, ps.thr[s0 + g]);
+  // (the first threshold load's address is clamped rather than the load
+  // skipped, so that it goes out with the list loads)
+  const uint32_t thr0 = ps.thr[s0 + min(tid & 63, nseg - 1)];
   uint2 lv[PLPT];
 #pragma unroll
   for (int u = 0; u < PLPT; ++u) lv[u] = ps.list[s0 * cap + p0 + u];
+  uint32_t tl = (tid & 63) < nseg ? thr0 : 0u;
+  for (int g = (tid & 63) + 64; g < nseg; g += 64) tl = max(tl, ps.thr[s0 + g]);  // rows of more than 64 segments
   // L: the largest threshold of a truncated list (0 when every list holds its
   // whole segment).  Every key of the row at or above L is listed, so when at
   // least K listed keys are >= L, the row's K-th key T is the K-th of those,
