@@ -579,6 +579,26 @@ def test_sparse_mla_split_shapes(B, K):
         assert_lse_close(lse[b, 0], l, f"lse b={b}")
 
 
+@pytest.mark.parametrize("B,K", [
+    (8, 2048),    # 32 splits of 2 tiles
+    (16, 2048),   # 16 splits of 4 tiles
+    (24, 1000),   # 8 splits of 4 tiles (the last one ragged)
+])
+def test_sparse_mla_split_shapes_rows_in_eights(B, K):
+    """Row counts that divide over the 8 XCDs: the MLA runs every split of row r on XCD r & 7 and the
+    combine reads them there, with its own workgroup order; every row is checked, so a row merged from
+    another row's partials cannot pass."""
+    dsa = _dsa()
+    wl, x = _mla_case(B, 1, 3000, K, seed=3 * B + K, n_masked=5, empty_row=False)
+    out, lse = dsa.sparse_mla(dev(x["q"]), dev(x["kv"]), dev(x["idx"]), wl.scale, wl.DV)
+    torch.cuda.synchronize()
+    out, lse = host64(out), host64(lse)
+    for b in range(B):
+        o, l = oracle.sparse_mla_rows(x["q"][b, 0], oracle.as_f64(x["kv"][b]), x["idx"][b, 0], wl.scale, wl.DV)
+        assert_close(out[b, 0], o, "bf16", f"out b={b}")
+        assert_lse_close(lse[b, 0], l, f"lse b={b}")
+
+
 def test_indexer_decode_batch_of_28_exact():
     """28 rows: the launch divides two rounds of workgroups evenly over the rows."""
     dsa = _dsa()
